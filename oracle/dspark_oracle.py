@@ -1,0 +1,400 @@
+"""Plain, slow fp64 CPU oracle of one DSpark draft-and-verify sampling step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything under
+``oracle/``.  The GPU library never calls it and shares no code with it.
+
+Sources (three web pages on DSpark; cited by site and section):
+
+* [weigao]   weigao.cc, "DSpark 与 MTP：DeepSeek 投机解码调研",
+             section "DSpark 的核心设计" (parts 2 Markov head, 3 confidence
+             head, 4 hardware-aware prefix scheduler).
+* [billytse] billytse.dev, "DSpark：DeepSeek 點樣「一次估多個、驗證前綴、
+             錯咗即修正」", sections 1 (Guess -> Verify -> Fix), 3.2/3.3
+             (sequential head, Markov head and its sampling loop), 5
+             (confidence head), 6 (hardware-aware prefix scheduler), 7
+             (lossless scheduling).
+* [xhh]      xhh.club, "DeepSeek-V4.1 模型结构（6）：解码，DSpark", the
+             Q&A on the acceptance rule and on the scheduler, and the
+             note on non-anticipating truncation.
+
+Everything is computed in float64 from the exact values of the stored
+inputs (bf16 bit patterns are decoded exactly).  Positions are 0-based in
+storage: draft position k (0..gamma-1) draws token x_{k+1} of the pages.
+
+Uniform layout (the pages fix none; this is the reading used throughout):
+``uniforms[b, k, 0]`` draws draft token k, ``uniforms[b, k, 1]`` is the
+accept test of draft token k, ``uniforms[b, gamma, 0]`` draws the single
+final token (residual or bonus); ``uniforms[b, gamma, 1]`` is unused.
+
+Every function below is pinned by tests under ``tests/test_oracle_*.py``
+against values the pages print, closed forms, textbook special cases and
+exhaustive enumeration; no function here is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "f64",
+    "markov_bias",
+    "inverse_cdf",
+    "draft_row",
+    "draft_block",
+    "draft_forced",
+    "confidence",
+    "survival",
+    "schedule",
+    "target_probs",
+    "verify",
+]
+
+
+# ----------------------------------------------------------------------------
+# input decoding
+# ----------------------------------------------------------------------------
+
+def f64(a) -> np.ndarray:
+    """Exact float64 value of an input array.
+
+    ``uint16`` arrays are bf16 bit patterns: the bf16 value is the float32
+    whose upper 16 bits are the pattern and whose lower 16 bits are zero.
+    """
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# (1) semi-autoregressive block drafting with the vanilla Markov head
+# ----------------------------------------------------------------------------
+
+def markov_bias(W1, W2t, prev: int) -> np.ndarray:
+    """Transition bias B(prev, .) = W1[prev] @ W2 over the whole vocabulary.
+
+    [weigao] part 2 and [billytse] 3.3: the V x V first-order transition
+    matrix is replaced by a rank-r product; the row for the previous token is
+    the previous token's r-vector times the r x V projection.  ``W2t`` holds
+    that projection stored as [V, r] (the weight layout of a linear map from
+    r to V), so bias[v] = sum_i W1[prev, i] * W2t[v, i].
+    """
+    W1 = f64(W1) if not (isinstance(W1, np.ndarray) and W1.dtype == np.float64) else W1
+    W2t = f64(W2t) if not (isinstance(W2t, np.ndarray) and W2t.dtype == np.float64) else W2t
+    return W2t @ W1[int(prev)]
+
+
+def inverse_cdf(weights: np.ndarray, u: float):
+    """Inverse-CDF draw from non-negative ``weights`` with one uniform ``u``.
+
+    Returns ``(x, lo, hi, total)``: x is the lowest index whose cumulative
+    weight exceeds u * total; [lo, hi) is the interval of u (in probability
+    units) that selects x.  Index order is ascending, so a zero-weight entry
+    can never be drawn.
+    """
+    C = np.cumsum(weights)
+    total = C[-1]
+    target = u * total
+    x = int(np.searchsorted(C, target, side="right"))
+    if x >= len(C):  # only reachable through rounding when u is 1 - ulp
+        x = int(np.nonzero(weights > 0)[0][-1])
+    lo = (C[x - 1] if x > 0 else 0.0) / total
+    hi = C[x] / total
+    return x, lo, hi, total
+
+
+def draft_row(z: np.ndarray, temperature: float, u: float):
+    """Sample one draft position from full logits z = U_k + bias.
+
+    [billytse] 3.2: p_k = softmax(U_k + B_k).  Temperature T divides the
+    logits; T == 0 is greedy (lowest-index argmax, q one-hot).
+    Returns dict with x, q (probability of x), m (max of z/T), logZ
+    (log of sum exp(z/T - m)), and the selecting interval [lo, hi) of u.
+    """
+    if temperature > 0.0:
+        y = z / temperature
+        m = float(np.max(y))
+        w = np.exp(y - m)
+        x, lo, hi, Z = inverse_cdf(w, u)
+        return dict(x=x, q=float(w[x] / Z), m=m, logZ=float(np.log(Z)), lo=lo, hi=hi)
+    m = float(np.max(z))
+    x = int(np.argmax(z))  # first maximum
+    return dict(x=x, q=1.0, m=m, logZ=0.0, lo=0.0, hi=1.0)
+
+
+def draft_block(U, W1, W2t, anchor, temperature, uniforms):
+    """Sequential Markov sampling over a block, per request.
+
+    [billytse] 3.3 sampling loop: start from the anchor token; at each block
+    position add the bias of the previous sampled token to the position's
+    base logits, take the softmax, sample, and make the sample the next
+    previous token.
+
+    U: [B, gamma, V]; W1: [V, r]; W2t: [V, r]; anchor: [B]; temperature: [B];
+    uniforms: [B, gamma+1, 2].  Returns arrays tokens [B,gamma] int64,
+    q_tok, row_max, row_logZ, lo, hi, margin [B,gamma] float64.  ``margin``
+    is the distance of u from the nearest edge of x's interval.
+    """
+    U = f64(U)
+    W1 = f64(W1)
+    W2t = f64(W2t)
+    uni = np.asarray(uniforms, dtype=np.float64)
+    B, gamma, V = U.shape
+    out = {k: np.zeros((B, gamma)) for k in ("q_tok", "row_max", "row_logZ", "lo", "hi", "margin")}
+    tokens = np.zeros((B, gamma), dtype=np.int64)
+    for b in range(B):
+        prev = int(anchor[b])
+        T = float(temperature[b])
+        for k in range(gamma):
+            z = U[b, k] + markov_bias(W1, W2t, prev)
+            u = float(uni[b, k, 0])
+            r = draft_row(z, T, u)
+            tokens[b, k] = r["x"]
+            out["q_tok"][b, k] = r["q"]
+            out["row_max"][b, k] = r["m"]
+            out["row_logZ"][b, k] = r["logZ"]
+            out["lo"][b, k] = r["lo"]
+            out["hi"][b, k] = r["hi"]
+            whole = r["lo"] <= 0.0 and r["hi"] >= 1.0
+            out["margin"][b, k] = np.inf if whole else min(u - r["lo"], r["hi"] - u)
+            prev = r["x"]
+    out["tokens"] = tokens
+    return out
+
+
+def draft_forced(U, W1, W2t, anchor, temperature, tokens, uniforms=None, rows=None):
+    """Draft statistics with the sampled tokens given (teacher forcing).
+
+    Computes, for the listed (b, k) rows (all rows if ``rows`` is None), the
+    draft distribution of position k with prev = tokens[b, k-1] (anchor for
+    k == 0), and reports q at tokens[b, k], the row stats, the interval of u
+    that selects tokens[b, k] and, when uniforms are given, the token the
+    oracle itself would draw with uniforms[b, k, 0] and its margin.
+    """
+    U_is64 = isinstance(U, np.ndarray) and U.dtype == np.float64
+    W1 = W1 if (isinstance(W1, np.ndarray) and W1.dtype == np.float64) else f64(W1)
+    W2t = W2t if (isinstance(W2t, np.ndarray) and W2t.dtype == np.float64) else f64(W2t)
+    B, gamma = np.asarray(tokens).shape
+    if rows is None:
+        rows = [(b, k) for b in range(B) for k in range(gamma)]
+    res = []
+    for b, k in rows:
+        prev = int(anchor[b]) if k == 0 else int(tokens[b, k - 1])
+        Urow = U[b, k] if U_is64 else f64(U[b, k])
+        z = Urow + markov_bias(W1, W2t, prev)
+        T = float(temperature[b])
+        x = int(tokens[b, k])
+        if T > 0:
+            y = z / T
+            m = float(np.max(y))
+            w = np.exp(y - m)
+            C = np.cumsum(w)
+            Z = C[-1]
+            lo = (C[x - 1] if x > 0 else 0.0) / Z
+            hi = C[x] / Z
+            d = dict(b=b, k=k, q=float(w[x] / Z), m=m, logZ=float(np.log(Z)), lo=lo, hi=hi)
+            if uniforms is not None:
+                u = float(uniforms[b, k, 0])
+                xo, lo2, hi2, _ = inverse_cdf(w, u)
+                whole = lo2 <= 0.0 and hi2 >= 1.0
+                d.update(x_oracle=xo, margin=np.inf if whole else min(u - lo2, hi2 - u))
+        else:
+            m = float(np.max(z))
+            am = int(np.argmax(z))
+            d = dict(b=b, k=k, q=1.0 if x == am else 0.0, m=m, logZ=0.0, lo=0.0, hi=1.0)
+            if uniforms is not None:
+                d.update(x_oracle=am, margin=np.inf)
+        res.append(d)
+    return res
+
+
+# ----------------------------------------------------------------------------
+# (2) confidence head
+# ----------------------------------------------------------------------------
+
+def confidence(hidden, W1, anchor, tokens, w, b0: float = 0.0) -> np.ndarray:
+    """c[b,k] = sigmoid(w . [h_k ; W1[prev_k]] + b0).
+
+    [weigao] part 3 and [billytse] 5: a linear layer on the concatenation of
+    the position's hidden state and the Markov embedding of the previous
+    token, squashed to a probability.  [xhh] (non-anticipating truncation):
+    the previous token is x_{k-1}, never x_k; the anchor for the first
+    position.  The Markov embedding is the W1 row of the previous token.
+    """
+    h = f64(hidden)
+    W1 = f64(W1)
+    w = f64(w)
+    B, gamma, H = h.shape
+    tokens = np.asarray(tokens)
+    c = np.zeros((B, gamma))
+    for b in range(B):
+        for k in range(gamma):
+            prev = int(anchor[b]) if k == 0 else int(tokens[b, k - 1])
+            feat = np.concatenate([h[b, k], W1[prev]])
+            logit = float(np.dot(w, feat)) + b0
+            c[b, k] = 1.0 / (1.0 + np.exp(-logit))
+    return c
+
+
+# ----------------------------------------------------------------------------
+# (3) hardware-aware prefix scheduler
+# ----------------------------------------------------------------------------
+
+def survival(c) -> np.ndarray:
+    """a[r, j] = prod_{i <= j} c[r, i], accumulated left to right in fp64.
+
+    [weigao] part 4 / [billytse] 5: only a contiguous prefix can be accepted,
+    so a draft position survives only if it and every earlier one pass.
+    """
+    c = np.asarray(c, dtype=np.float64)
+    R, gamma = c.shape
+    a = np.zeros((R, gamma))
+    for r in range(R):
+        acc = 1.0
+        for j in range(gamma):
+            acc = acc * c[r, j]
+            a[r, j] = acc
+    return a
+
+
+def schedule(c, sps):
+    """Greedy verify-length choice maximising Theta = tau * SPS(Bt).
+
+    [billytse] 6: Bt = sum_r (1 + l_r) target tokens, tau = sum_r (1 + sum_{j
+    <= l_r} a_{r,j}) expected committed tokens; rank every extendable
+    position by survival, add them one at a time, and stop as soon as adding
+    the next one would not raise Theta ([xhh] scheduler Q&A: stop when Theta
+    no longer rises, so admission needs a strict rise; [billytse] 7: stop
+    early, never revise an earlier decision).
+
+    Ties in survival are broken by flat index r*gamma + j ascending.  SPS
+    entries that are absent (Bt beyond the table) or not positive are
+    inadmissible: the scan stops there.
+
+    c: [R, gamma] (any float), sps: 1-D table indexed by Bt.
+    Returns dict(ell [R] int64, order [R*gamma] int64, n_admitted, tau,
+    theta, a [R, gamma]).
+    """
+    a = survival(c)
+    R, gamma = a.shape
+    sps = np.asarray(sps, dtype=np.float64)
+    flat = a.reshape(-1)
+    order = sorted(range(R * gamma), key=lambda i: (-flat[i], i))
+    Bt = R
+    tau = float(R)
+    theta = tau * sps[Bt] if Bt < len(sps) else 0.0
+    ell = np.zeros(R, dtype=np.int64)
+    n = 0
+    for i in order:
+        nb = Bt + 1
+        if nb >= len(sps) or not (sps[nb] > 0.0):
+            break
+        tau_new = tau + flat[i]
+        theta_new = tau_new * sps[nb]
+        if theta_new > theta:
+            ell[i // gamma] += 1
+            Bt, tau, theta = nb, tau_new, theta_new
+            n += 1
+        else:
+            break
+    return dict(ell=ell, order=np.asarray(order, dtype=np.int64), n_admitted=n,
+                tau=tau, theta=theta, a=a)
+
+
+# ----------------------------------------------------------------------------
+# (4) lossless verification
+# ----------------------------------------------------------------------------
+
+def target_probs(trow: np.ndarray, temperature: float) -> np.ndarray:
+    """Target distribution of one slot: softmax(t / T), or one-hot at the
+    lowest-index argmax when T == 0 (greedy)."""
+    if temperature > 0.0:
+        y = trow / temperature
+        w = np.exp(y - np.max(y))
+        return w / np.sum(w)
+    p = np.zeros_like(trow)
+    p[int(np.argmax(trow))] = 1.0
+    return p
+
+
+def _draft_probs(z: np.ndarray, temperature: float) -> np.ndarray:
+    if temperature > 0.0:
+        y = z / temperature
+        w = np.exp(y - np.max(y))
+        return w / np.sum(w)
+    q = np.zeros_like(z)
+    q[int(np.argmax(z))] = 1.0
+    return q
+
+
+def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell):
+    """Speculative rejection sampling over each request's verified prefix.
+
+    [billytse] 1 and [xhh] acceptance-rule Q&A: draft token x_k (drawn from
+    q) is accepted with probability min(1, p(x)/q(x)); the scan stops at the
+    first rejection, where one token is drawn from the normalised residual
+    max(0, p - q); if every verified token passes, one bonus token is drawn
+    from the target slot after the last verified one.  The emitted tokens
+    are the accepted prefix plus that one token.
+
+    ``q_tok[b, k]`` is the draft probability of tokens[b, k].  At a reject
+    the full draft row q is recomputed from U, W1, W2t and the previous
+    token.  Accept iff u < p/q (written u*q < p; a ratio >= 1 always passes
+    since u < 1).  A residual with no mass (reachable only by rounding) falls
+    back to p and is flagged in ``degenerate``.
+
+    target: [B, gamma+1, V] slot logits (slot k verifies tokens[:, k]; slot
+    ell_b is the bonus slot).  Returns dict(out_tokens [B, gamma+1] (-1
+    padded), n_accepted [B], ratio [B, gamma] (NaN where untested),
+    final_lo, final_hi, final_margin [B], degenerate [B] bool).
+    """
+    W1 = W1 if (isinstance(W1, np.ndarray) and W1.dtype == np.float64) else f64(W1)
+    W2t = W2t if (isinstance(W2t, np.ndarray) and W2t.dtype == np.float64) else f64(W2t)
+    tokens = np.asarray(tokens)
+    B, gamma = tokens.shape
+    q_tok = np.asarray(q_tok, dtype=np.float64)
+    uni = np.asarray(uniforms, dtype=np.float64)
+    out = np.full((B, gamma + 1), -1, dtype=np.int64)
+    n_acc = np.zeros(B, dtype=np.int64)
+    ratio = np.full((B, gamma), np.nan)
+    f_lo = np.zeros(B)
+    f_hi = np.zeros(B)
+    f_margin = np.zeros(B)
+    degenerate = np.zeros(B, dtype=bool)
+    for b in range(B):
+        T = float(temperature[b])
+        L = int(ell[b])
+        uf = float(uni[b, gamma, 0])
+        rejected_at = -1
+        for k in range(L):
+            p = target_probs(f64(target[b, k]), T)
+            x = int(tokens[b, k])
+            ratio[b, k] = p[x] / q_tok[b, k]
+            if uni[b, k, 1] * q_tok[b, k] < p[x]:
+                continue
+            rejected_at = k
+            break
+        if rejected_at >= 0:
+            j = rejected_at
+            prev = int(anchor[b]) if j == 0 else int(tokens[b, j - 1])
+            z = f64(U[b, j]) + markov_bias(W1, W2t, prev)
+            q = _draft_probs(z, T)
+            res = np.maximum(0.0, p - q)
+            if not (np.sum(res) > 0.0):
+                res = p
+                degenerate[b] = True
+            y, lo, hi, _ = inverse_cdf(res, uf)
+            out[b, :j] = tokens[b, :j]
+            out[b, j] = y
+            n_acc[b] = j
+        else:
+            p = target_probs(f64(target[b, L]), T)
+            y, lo, hi, _ = inverse_cdf(p, uf)
+            out[b, :L] = tokens[b, :L]
+            out[b, L] = y
+            n_acc[b] = L
+        f_lo[b], f_hi[b] = lo, hi
+        f_margin[b] = np.inf if (lo <= 0.0 and hi >= 1.0) else min(uf - lo, hi - uf)
+    return dict(out_tokens=out, n_accepted=n_acc, ratio=ratio, final_lo=f_lo,
+                final_hi=f_hi, final_margin=f_margin, degenerate=degenerate)
