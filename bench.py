@@ -1,0 +1,187 @@
+"""Benchmark one decode step of the DSpark sampling path on one MI355X.
+
+A step = dspark_draft_block -> dspark_confidence -> dspark_schedule (or the
+fixed verify length) -> dspark_verify over one batch, inputs resident in
+HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+                    [--no-cpu-baseline] [--cpu-requests N]
+
+value      = B * gamma / (time per step), drafted-and-verified positions/s
+roofline   = the dominant kernel (draft_stats_kernel): algorithmic bytes per
+             launch / its mean duration, timed with per-launch HIP events in a
+             second pass over the same K steps (events are kept out of the
+             pass that gives `value`)
+cpu_baseline = the fp64 oracle on a bounded sample of the same workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "draft+verify positions/sec (B×γ per step) at V=151936; % of HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=0,
+                    help="requests in the oracle sample (0 = sized for ~15 s)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl, ell, n_acc):
+    """Bytes the step must move, each input read once."""
+    e = 2 if wl.dtype == "bf16" else 4
+    B, g, V, r, H = wl.B, wl.gamma, wl.V, wl.rank, wl.H
+    rejected = (n_acc < ell)
+    j_rows = (n_acc + 1).sum()                      # target slots 0..j_b read
+    u_rows = B * g + int(rejected.sum())            # every U row + re-read at rejects
+    return (e * V * (u_rows + int(j_rows)) + e * r * V + e * B * g * (H + r)
+            + 4 * B * (g + 1) * 2 + 4 * B * g * 4 + 4 * B * (g + 1))
+
+
+def draft_stats_bytes(wl):
+    """Algorithmic bytes of one draft_stats_kernel launch (one draft position)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    nT = (wl.V + 255) // 256
+    return (e * wl.B * wl.V              # the position's U rows
+            + e * wl.B * wl.rank         # gathered W1 rows
+            + e * wl.rank * wl.V / wl.gamma  # W2 read once per step, shared by gamma launches
+            + 4 * wl.B * nT * 6)         # tile max/argmax + 4 chunk sums per tile written
+
+
+def cpu_baseline(cfg, n_req):
+    import numpy as np
+
+    import oracle as O
+    from gen import make_config
+
+    wl = make_config(cfg, requests=range(n_req))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    W1, W2t = O.f64(wl.W1), O.f64(wl.W2t)
+    d = O.draft_block(wl.U, W1, W2t, wl.anchor, wl.temperature, wl.uniforms)
+    c = O.confidence(wl.hidden, W1, wl.anchor, d["tokens"], wl.w, wl.b0)
+    if wl.spec.scheduler and wl.sps is not None:
+        ell = O.schedule(c, wl.sps)["ell"]
+    else:
+        ell = np.full(wl.B, wl.gamma)
+    O.verify(wl.target, wl.U, W1, W2t, wl.anchor, d["tokens"], d["q_tok"], wl.temperature,
+             wl.uniforms, ell)
+    dt = time.perf_counter() - t0
+    return {"value": n_req * wl.gamma / dt, "unit": "positions/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"first {n_req} of {wl.spec.B} requests of config {cfg} "
+                      f"({n_req * wl.gamma} positions; scheduler over the sample), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sampling path "
+              "has no multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import draft_verify_sampling_block_amd as dv
+    from draft_verify_sampling_block_amd.step import Step, upload
+    from gen import SPECS, make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dv.load()
+    cfg = args.config
+    spec = SPECS[cfg]
+    t0 = time.perf_counter()
+    wl = make_config(cfg)
+    print(f"[bench] generated config {cfg} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    st = Step(upload(wl, "cuda"))
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        st.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} steps, {ms:.4f} ms/step", file=sys.stderr, flush=True)
+    status = int(st.status.item())
+    ell = st.ell_used().cpu().numpy()
+    n_acc = st.n_accepted.cpu().numpy()
+
+    # per-kernel durations (second pass, events between launches)
+    dv.dspark_trace_enable(True)
+    for _ in range(args.steps):
+        st.run()
+    torch.cuda.synchronize()
+    tr = dv.dspark_trace_summary()
+    dv.dspark_trace_enable(False)
+    dom = max(tr, key=lambda k: tr[k][1])
+    kern_ms = {k: v[1] / v[0] for k, v in tr.items()}
+    per_step_ms = {k: v[1] / args.steps for k, v in tr.items()}
+    stats_bytes = draft_stats_bytes(wl)
+    avg_s = kern_ms["draft_stats_kernel"] / 1e3
+    achieved = stats_bytes / avg_s / 1e9
+    bytes_step = algorithmic_bytes(wl, ell, n_acc)
+
+    out = {
+        "metric": METRIC,
+        "value": wl.B * wl.gamma / (ms / 1e3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; shapes and logit mixtures of the pages' workloads)",
+        "config": {"workload": f"config {cfg} {spec.name}: B={wl.B} gamma={wl.gamma} V={wl.V} "
+                               f"rank={wl.rank} H={wl.H} {wl.dtype}",
+                   "B": wl.B, "gamma": wl.gamma, "V": wl.V, "rank": wl.rank, "H": wl.H,
+                   "scheduler": bool(spec.scheduler), "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "draft_stats_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": stats_bytes,
+                     "mean_launch_us": avg_s * 1e6},
+        "step": {"bytes_alg": bytes_step, "hbm_gbs": bytes_step / (ms / 1e3) / 1e9,
+                 "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                 "mean_ell": float(ell.mean()), "mean_accepted": float(n_acc.mean()),
+                 "dominant_kernel": dom,
+                 "kernel_ms_per_step": {k: round(v, 5) for k, v in per_step_ms.items()},
+                 "device_status": status},
+    }
+    if not args.no_cpu_baseline:
+        n_req = args.cpu_requests or {0: 4, 1: 12, 2: 24, 3: 10, 4: 16}[cfg]
+        out["cpu_baseline"] = cpu_baseline(cfg, n_req)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,256 @@
+"""Python binding of libdspark (gfx950 HIP kernels behind a C ABI).
+
+Argument marshalling only: every step of the sampling path runs in the
+library's kernels.  torch supplies device memory and the current stream.
+The functions carry the C entry points' names:
+
+    dspark_draft_block, dspark_confidence, dspark_schedule, dspark_verify
+
+If ``libdspark.so`` is missing the import still succeeds (so the CPU test
+suite can run), but every entry point raises ``DsparkError``; nothing falls
+back to another implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = [
+    "DsparkError", "lib_path", "load", "dspark_draft_block", "dspark_confidence",
+    "dspark_schedule", "dspark_verify", "dspark_draft_block_workspace",
+    "dspark_verify_workspace", "dspark_schedule_workspace", "exported_names", "header_names",
+    "dspark_trace_enable", "dspark_trace_summary",
+    "DSPARK_F32", "DSPARK_BF16", "DEV_FLAGS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "dspark.h")
+DSPARK_F32, DSPARK_BF16 = 0, 1
+DEV_FLAGS = {1: "BAD_TOKEN", 2: "NONFINITE", 4: "DEGENERATE", 8: "BAD_ELL", 16: "BAD_CONF"}
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, "libdspark.so")
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "dspark_status_str": (ctypes.c_char_p, [_I]),
+    "dspark_last_error": (ctypes.c_char_p, []),
+    "dspark_version": (ctypes.c_char_p, []),
+    "dspark_draft_block_workspace": (_SZ, [_I, _I, _I, _I, _I]),
+    "dspark_draft_block": (_I, [_I, _I, _I, _I, _I] + [_P] * 11 + [_P, _SZ, _P]),
+    "dspark_confidence": (_I, [_I] * 6 + [_P] * 5 + [ctypes.c_float, _P, _P, _P]),
+    "dspark_schedule_workspace": (_SZ, [_I, _I]),
+    "dspark_schedule": (_I, [_I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dspark_verify_workspace": (_SZ, [_I, _I, _I, _I, _I]),
+    "dspark_verify": (_I, [_I] * 5 + [_P] * 15 + [_P, _P, _SZ, _P]),
+    "dspark_trace_enable": (_I, [_I]),
+    "dspark_trace_summary": (_I, [ctypes.c_char_p, _SZ]),
+}
+
+
+def load():
+    """Load libdspark.so (once).  Raises DsparkError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise DsparkError(-100, f"{path} is not built; run __graft_entry__.build() or "
+                                "python -m draft_verify_sampling_block_amd.build")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_names() -> list[str]:
+    """Function names declared in include/dspark.h."""
+    text = open(_HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(dspark_[a-z_]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def exported_names() -> list[str]:
+    lib = load()
+    return [n for n in header_names() if hasattr(lib, n)]
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load()
+        raise DsparkError(rc, f"{lib.dspark_status_str(rc).decode()}: {lib.dspark_last_error().decode()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSPARK_BF16
+    if t.dtype == torch.float32:
+        return DSPARK_F32
+    raise DsparkError(-2, f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise DsparkError(-1, f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise DsparkError(-1, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise DsparkError(-1, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise DsparkError(-2, f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise DsparkError(-1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def dspark_trace_enable(on: bool) -> None:
+    _check(load().dspark_trace_enable(1 if on else 0))
+
+
+def dspark_trace_summary() -> dict:
+    """{kernel: (launches, total_ms)} of the launches recorded since enabling."""
+    lib = load()
+    n = lib.dspark_trace_summary(None, 0)
+    if n < 0:
+        _check(n)
+    buf = ctypes.create_string_buffer(n + 1)
+    lib.dspark_trace_summary(buf, n + 1)
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out
+
+
+def dspark_draft_block_workspace(B, gamma, V, rank, dtype) -> int:
+    return int(load().dspark_draft_block_workspace(B, gamma, V, rank, dtype))
+
+
+def dspark_verify_workspace(B, gamma, V, rank, dtype) -> int:
+    return int(load().dspark_verify_workspace(B, gamma, V, rank, dtype))
+
+
+def dspark_schedule_workspace(R, gamma) -> int:
+    return int(load().dspark_schedule_workspace(R, gamma))
+
+
+def _workspace(nbytes: int, device, given=None):
+    if given is not None:
+        return given
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def dspark_draft_block(U, W1, W2t, anchor, temperature, uniforms, *, tokens=None, q_tok=None,
+                       row_max=None, row_logZ=None, status=None, workspace=None):
+    """Markov-head block drafting.  U [B,gamma,V]; W1, W2t [V,rank]; returns
+    dict(tokens, q_tok, row_max, row_logZ)."""
+    lib = load()
+    B, gamma, V = U.shape
+    rank = W1.shape[1]
+    dt = _dtype_code(U)
+    dev = U.device
+    _need(U, "U"); _need(W1, "W1", U.dtype, (V, rank)); _need(W2t, "W2t", U.dtype, (V, rank))
+    _need(anchor, "anchor", torch.int32, (B,)); _need(temperature, "temperature", torch.float32, (B,))
+    _need(uniforms, "uniforms", torch.float32, (B, gamma + 1, 2))
+    tokens = tokens if tokens is not None else torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    q_tok = q_tok if q_tok is not None else torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    row_max = row_max if row_max is not None else torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    row_logZ = row_logZ if row_logZ is not None else torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    need = dspark_draft_block_workspace(B, gamma, V, rank, dt)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.dspark_draft_block(B, gamma, V, rank, dt, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(anchor),
+                                  _ptr(temperature), _ptr(uniforms), _ptr(tokens), _ptr(q_tok),
+                                  _ptr(row_max), _ptr(row_logZ), _ptr(status), _ptr(ws),
+                                  ws.numel(), _stream()))
+    return dict(tokens=tokens, q_tok=q_tok, row_max=row_max, row_logZ=row_logZ)
+
+
+def dspark_confidence(hidden, W1, anchor, tokens, w, bias=0.0, *, conf=None, status=None):
+    """Confidence head; hidden [B,gamma,H]; w [H+rank] fp32; returns conf [B,gamma]."""
+    lib = load()
+    B, gamma, H = hidden.shape
+    V, rank = W1.shape
+    dt = _dtype_code(hidden)
+    _need(hidden, "hidden"); _need(W1, "W1", hidden.dtype)
+    _need(anchor, "anchor", torch.int32, (B,)); _need(tokens, "tokens", torch.int32, (B, gamma))
+    _need(w, "w", torch.float32, (H + rank,))
+    conf = conf if conf is not None else torch.empty((B, gamma), dtype=torch.float32, device=hidden.device)
+    _check(lib.dspark_confidence(B, gamma, H, V, rank, dt, _ptr(hidden), _ptr(W1), _ptr(anchor),
+                                 _ptr(tokens), _ptr(w), ctypes.c_float(bias), _ptr(conf),
+                                 _ptr(status), _stream()))
+    return conf
+
+
+def dspark_schedule(conf, sps, *, ell=None, order=None, stats=None, status=None, want_order=True):
+    """Prefix scheduler; conf [R,gamma] fp32, sps fp64 table; returns (ell, order, stats)."""
+    lib = load()
+    R, gamma = conf.shape
+    dev = conf.device
+    _need(conf, "conf", torch.float32); _need(sps, "sps", torch.float64)
+    ell = ell if ell is not None else torch.empty((R,), dtype=torch.int32, device=dev)
+    if order is None and want_order:
+        order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
+    stats = stats if stats is not None else torch.empty((3,), dtype=torch.float64, device=dev)
+    need = dspark_schedule_workspace(R, gamma)
+    ws = _workspace(need, dev) if need else None
+    _check(lib.dspark_schedule(R, gamma, _ptr(conf), _ptr(sps), int(sps.numel()), _ptr(ell),
+                               _ptr(order), _ptr(stats), _ptr(status), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream()))
+    return ell, order, stats
+
+
+def dspark_verify(target, U, W1, W2t, anchor, tokens, q_tok, row_max, row_logZ, temperature,
+                  uniforms, ell, *, out_tokens=None, n_accepted=None, ratio=None, status=None,
+                  workspace=None, want_ratio=True):
+    """Lossless verification; returns (out_tokens [B,gamma+1], n_accepted [B], ratio [B,gamma])."""
+    lib = load()
+    B, gamma, V = U.shape
+    rank = W1.shape[1]
+    dt = _dtype_code(U)
+    dev = U.device
+    _need(target, "target", U.dtype, (B, gamma + 1, V)); _need(U, "U")
+    _need(W1, "W1", U.dtype, (V, rank)); _need(W2t, "W2t", U.dtype, (V, rank))
+    for name, t, dtp in (("anchor", anchor, torch.int32), ("tokens", tokens, torch.int32),
+                         ("q_tok", q_tok, torch.float32), ("row_max", row_max, torch.float32),
+                         ("row_logZ", row_logZ, torch.float32), ("temperature", temperature, torch.float32),
+                         ("uniforms", uniforms, torch.float32), ("ell", ell, torch.int32)):
+        _need(t, name, dtp)
+    out_tokens = out_tokens if out_tokens is not None else torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    n_accepted = n_accepted if n_accepted is not None else torch.empty((B,), dtype=torch.int32, device=dev)
+    if ratio is None and want_ratio:
+        ratio = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    need = dspark_verify_workspace(B, gamma, V, rank, dt)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.dspark_verify(B, gamma, V, rank, dt, _ptr(target), _ptr(U), _ptr(W1), _ptr(W2t),
+                             _ptr(anchor), _ptr(tokens), _ptr(q_tok), _ptr(row_max), _ptr(row_logZ),
+                             _ptr(temperature), _ptr(uniforms), _ptr(ell), _ptr(out_tokens),
+                             _ptr(n_accepted), _ptr(ratio), _ptr(status), _ptr(ws), ws.numel(),
+                             _stream()))
+    return out_tokens, n_accepted, ratio

@@ -1,0 +1,169 @@
+// C ABI of libdspark: host-side validation, then the kernel launchers.
+// Every check runs before anything is enqueued; a failed check returns a
+// negative status, enqueues nothing and records a message for
+// dspark_last_error().
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/dspark.h"
+#include "dspark_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                      \
+  do {                                                                      \
+    if (!(p)) return fail(DSPARK_EINVAL, "%s: '%s' is NULL", fn, #p);       \
+    if (!aligned16(p)) return fail(DSPARK_EALIGN, "%s: '%s' is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+#define OPT_PTR(p)                                                          \
+  do {                                                                      \
+    if ((p) && !aligned16(p))                                               \
+      return fail(DSPARK_EALIGN, "%s: '%s' is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+int check_dims(const char* fn, int B, int gamma, int V, int rank, int dtype) {
+  if (dtype != DSPARK_F32 && dtype != DSPARK_BF16)
+    return fail(DSPARK_EDTYPE, "%s: dtype %d is neither DSPARK_F32 nor DSPARK_BF16", fn, dtype);
+  if (B < 1) return fail(DSPARK_EINVAL, "%s: B=%d must be >= 1", fn, B);
+  if (gamma < 1 || gamma > 64) return fail(DSPARK_EINVAL, "%s: gamma=%d outside [1,64]", fn, gamma);
+  if (V < 8 || V % 8) return fail(DSPARK_EINVAL, "%s: V=%d must be a positive multiple of 8", fn, V);
+  if (rank < 32 || rank > 512 || rank % 32)
+    return fail(DSPARK_EINVAL, "%s: rank=%d must be a multiple of 32 in [32,512]", fn, rank);
+  if ((long long)B * (gamma + 1) > (1LL << 31) / 2)
+    return fail(DSPARK_EUNSUPPORTED, "%s: B*(gamma+1) too large", fn);
+  return DSPARK_OK;
+}
+
+int hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(DSPARK_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dspark_status_str(int status) {
+  switch (status) {
+    case DSPARK_OK: return "DSPARK_OK";
+    case DSPARK_EINVAL: return "DSPARK_EINVAL: invalid argument";
+    case DSPARK_EDTYPE: return "DSPARK_EDTYPE: unknown dtype";
+    case DSPARK_EALIGN: return "DSPARK_EALIGN: pointer not 16-byte aligned";
+    case DSPARK_EWORKSPACE: return "DSPARK_EWORKSPACE: workspace missing or too small";
+    case DSPARK_EUNSUPPORTED: return "DSPARK_EUNSUPPORTED: outside supported sizes";
+    case DSPARK_EHIP: return "DSPARK_EHIP: HIP runtime error";
+    default: return "unknown dspark status";
+  }
+}
+
+const char* dspark_last_error(void) { return g_err; }
+
+const char* dspark_version(void) { return "libdspark 0.1 gfx950"; }
+
+size_t dspark_draft_block_workspace(int B, int gamma, int V, int rank, int dtype) {
+  if (check_dims("dspark_draft_block_workspace", B, gamma, V, rank, dtype) != DSPARK_OK) return 0;
+  return dspark::draft_workspace_bytes(B, gamma, V, rank, dtype);
+}
+
+int dspark_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U, const void* W1,
+                       const void* W2t, const int32_t* anchor, const float* temperature,
+                       const float* uniforms, int32_t* tokens, float* q_tok, float* row_max,
+                       float* row_logZ, int32_t* status, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  const char* fn = "dspark_draft_block";
+  int rc = check_dims(fn, B, gamma, V, rank, dtype);
+  if (rc) return rc;
+  REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2t); REQUIRE_PTR(anchor);
+  REQUIRE_PTR(temperature); REQUIRE_PTR(uniforms); REQUIRE_PTR(tokens); REQUIRE_PTR(q_tok);
+  REQUIRE_PTR(row_max); REQUIRE_PTR(row_logZ); OPT_PTR(status);
+  const size_t need = dspark::draft_workspace_bytes(B, gamma, V, rank, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
+  return hip_status(fn, dspark::launch_draft_block(B, gamma, V, rank, dtype, U, W1, W2t, anchor,
+                                                   temperature, uniforms, tokens, q_tok, row_max,
+                                                   row_logZ, status, workspace, stream));
+}
+
+int dspark_confidence(int B, int gamma, int H, int V, int rank, int dtype, const void* hidden,
+                      const void* W1, const int32_t* anchor, const int32_t* tokens,
+                      const float* w, float bias, float* conf, int32_t* status,
+                      hipStream_t stream) {
+  const char* fn = "dspark_confidence";
+  int rc = check_dims(fn, B, gamma, V, rank, dtype);
+  if (rc) return rc;
+  if (H < 8 || H % 8) return fail(DSPARK_EINVAL, "%s: H=%d must be a positive multiple of 8", fn, H);
+  REQUIRE_PTR(hidden); REQUIRE_PTR(W1); REQUIRE_PTR(anchor); REQUIRE_PTR(tokens);
+  REQUIRE_PTR(w); REQUIRE_PTR(conf); OPT_PTR(status);
+  return hip_status(fn, dspark::launch_confidence(B, gamma, H, V, rank, dtype, hidden, W1, anchor,
+                                                  tokens, w, bias, conf, status, stream));
+}
+
+size_t dspark_schedule_workspace(int R, int gamma) {
+  if (R < 1 || gamma < 1 || gamma > 64) return 0;
+  return dspark::schedule_workspace_bytes(R, gamma);
+}
+
+int dspark_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
+                    int32_t* ell, int32_t* order, double* stats, int32_t* status,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dspark_schedule";
+  if (R < 1) return fail(DSPARK_EINVAL, "%s: R=%d must be >= 1", fn, R);
+  if (gamma < 1 || gamma > 64) return fail(DSPARK_EINVAL, "%s: gamma=%d outside [1,64]", fn, gamma);
+  if ((long long)R * gamma > dspark::kScheduleMaxKeys)
+    return fail(DSPARK_EUNSUPPORTED, "%s: R*gamma=%lld exceeds %d candidates", fn,
+                (long long)R * gamma, dspark::kScheduleMaxKeys);
+  if (sps_len < 1) return fail(DSPARK_EINVAL, "%s: sps_len=%d must be >= 1", fn, sps_len);
+  REQUIRE_PTR(conf); REQUIRE_PTR(sps); REQUIRE_PTR(ell); OPT_PTR(order); OPT_PTR(stats);
+  OPT_PTR(status);
+  const size_t need = dspark::schedule_workspace_bytes(R, gamma);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+  return hip_status(fn, dspark::launch_schedule(R, gamma, conf, sps, sps_len, ell, order, stats,
+                                                status, workspace, stream));
+}
+
+size_t dspark_verify_workspace(int B, int gamma, int V, int rank, int dtype) {
+  if (check_dims("dspark_verify_workspace", B, gamma, V, rank, dtype) != DSPARK_OK) return 0;
+  return dspark::verify_workspace_bytes(B, gamma, V, rank, dtype);
+}
+
+int dspark_verify(int B, int gamma, int V, int rank, int dtype, const void* target, const void* U,
+                  const void* W1, const void* W2t, const int32_t* anchor, const int32_t* tokens,
+                  const float* q_tok, const float* row_max, const float* row_logZ,
+                  const float* temperature, const float* uniforms, const int32_t* ell,
+                  int32_t* out_tokens, int32_t* n_accepted, float* ratio, int32_t* status,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dspark_verify";
+  int rc = check_dims(fn, B, gamma, V, rank, dtype);
+  if (rc) return rc;
+  REQUIRE_PTR(target); REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2t); REQUIRE_PTR(anchor);
+  REQUIRE_PTR(tokens); REQUIRE_PTR(q_tok); REQUIRE_PTR(row_max); REQUIRE_PTR(row_logZ);
+  REQUIRE_PTR(temperature); REQUIRE_PTR(uniforms); REQUIRE_PTR(ell); REQUIRE_PTR(out_tokens);
+  REQUIRE_PTR(n_accepted); OPT_PTR(ratio); OPT_PTR(status);
+  const size_t need = dspark::verify_workspace_bytes(B, gamma, V, rank, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
+  return hip_status(fn, dspark::launch_verify(B, gamma, V, rank, dtype, target, U, W1, W2t, anchor,
+                                              tokens, q_tok, row_max, row_logZ, temperature,
+                                              uniforms, ell, out_tokens, n_accepted, ratio, status,
+                                              workspace, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Internal host-side launchers behind the C ABI (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+size_t draft_workspace_bytes(int B, int gamma, int V, int rank, int dtype);
+hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U,
+                              const void* W1, const void* W2t, const int32_t* anchor,
+                              const float* temperature, const float* uniforms, int32_t* tokens,
+                              float* q_tok, float* row_max, float* row_logZ, int32_t* status,
+                              void* ws, hipStream_t stream);
+
+hipError_t launch_confidence(int B, int gamma, int H, int V, int rank, int dtype,
+                             const void* hidden, const void* W1, const int32_t* anchor,
+                             const int32_t* tokens, const float* w, float bias, float* conf,
+                             int32_t* status, hipStream_t stream);
+
+constexpr int kScheduleMaxKeys = 8192;
+size_t schedule_workspace_bytes(int R, int gamma);
+hipError_t launch_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
+                           int32_t* ell, int32_t* order, double* stats, int32_t* status,
+                           void* ws, hipStream_t stream);
+
+size_t verify_workspace_bytes(int B, int gamma, int V, int rank, int dtype);
+hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const void* target,
+                         const void* U, const void* W1, const void* W2t, const int32_t* anchor,
+                         const int32_t* tokens, const float* q_tok, const float* row_max,
+                         const float* row_logZ, const float* temperature, const float* uniforms,
+                         const int32_t* ell, int32_t* out_tokens, int32_t* n_accepted,
+                         float* ratio, int32_t* status, void* ws, hipStream_t stream);
+
+}  // namespace dspark

@@ -1,0 +1,191 @@
+// dspark_schedule: hardware-aware prefix scheduler in one work-group.
+//
+// [weigao] part 4 / [billytse] 6: survival a[r,j] = prod_{i<=j} c[r,i];
+// rank every extendable position by survival and add them one at a time
+// while Theta = tau * SPS(Bt) rises, Bt = sum_r (1 + l_r) and tau = sum_r
+// (1 + sum_{j<=l_r} a[r,j]).  [xhh] scheduler Q&A: stop once Theta no longer
+// rises (strict rise to admit).  [billytse] 7: stopping early keeps the
+// admission of position j independent of later positions' confidences.
+//
+// Layout: 1024 threads, keys (fp64 survival) and flat ids in LDS (<= 8192
+// keys = 96 KB).  Steps:
+//   1. per-request cumulative product, left to right in fp64 (one thread per
+//      request; bit-identical to a sequential product);
+//   2. bitonic sort by (a desc, flat id asc) -- a total order, so the order
+//      is exact;
+//   3. tau_n = R + sum of the first n ranked survivals, computed as a
+//      double-double prefix scan and rounded once (the exact sum up to
+//      ~1e-30 relative; independent of association);
+//   4. candidate n is admitted iff Bt+1 is inside the table, SPS > 0 there,
+//      and tau_{n+1} * SPS[R+n+1] > tau_n * SPS[R+n]; the number admitted is
+//      the first n that fails (block min-reduction) -- no sequential loop.
+#include "dspark_common.hpp"
+#include "dspark_launch.hpp"
+#include "trace.hpp"
+
+namespace dspark {
+
+namespace {
+
+struct dd {
+  double hi, lo;
+};
+// sum of two double-doubles (inputs are non-negative: no cancellation)
+__device__ inline dd dd_add(dd a, dd b) {
+  double s = a.hi + b.hi;
+  double bb = s - a.hi;
+  double e = (a.hi - (s - bb)) + (b.hi - bb);
+  e += a.lo + b.lo;
+  double hi = s + e;
+  double lo = e - (hi - s);
+  return dd{hi, lo};
+}
+__device__ inline dd shfl_up_dd(dd v, int o) {
+  return dd{__shfl_up(v.hi, o, kWave), __shfl_up(v.lo, o, kWave)};
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
+                                                        const float* __restrict__ conf,
+                                                        const double* __restrict__ sps,
+                                                        int sps_len, int32_t* __restrict__ ell,
+                                                        int32_t* __restrict__ order,
+                                                        double* __restrict__ stats,
+                                                        int32_t* status) {
+  __shared__ double key[kScheduleMaxKeys];
+  __shared__ int idx[kScheduleMaxKeys];
+  __shared__ double wsum_hi[16], wsum_lo[16];
+  __shared__ int s_first_fail;
+  __shared__ double s_tau, s_theta;
+
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int N = R * gamma;
+  int P = 1;
+  while (P < N) P <<= 1;
+
+  // 1. survival products
+  for (int r = tid; r < R; r += nthr) {
+    double acc = 1.0;
+    for (int j = 0; j < gamma; ++j) {
+      float c = conf[(size_t)r * gamma + j];
+      if (!(c >= 0.f)) {  // negative or NaN
+        flag(status, DSPARK_DEV_BAD_CONF);
+        c = 0.f;
+      } else if (c > 1.f) {
+        flag(status, DSPARK_DEV_BAD_CONF);
+        c = 1.f;
+      }
+      acc = acc * (double)c;
+      key[r * gamma + j] = acc;
+      idx[r * gamma + j] = r * gamma + j;
+    }
+    ell[r] = 0;
+  }
+  for (int i = N + tid; i < P; i += nthr) {
+    key[i] = -1.0;
+    idx[i] = 0x7fffffff;
+  }
+  if (tid == 0) s_first_fail = N;
+  __syncthreads();
+
+  // 2. bitonic sort: position p precedes q iff (key desc, idx asc)
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < (P >> 1); t += nthr) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;  // this sub-sequence sorts in rank order
+        const double kl = key[lo], kh = key[hi];
+        const int il = idx[lo], ih = idx[hi];
+        const bool hi_first = (kh > kl) || (kh == kl && ih < il);
+        if (hi_first == up) {
+          key[lo] = kh; key[hi] = kl;
+          idx[lo] = ih; idx[hi] = il;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // 3. double-double prefix sums over ranked survivals, in thread-contiguous
+  //    blocks of `per` candidates
+  const int per = (N + nthr - 1) / nthr;
+  const int c0 = min(N, tid * per), c1 = min(N, c0 + per);
+  dd local{0.0, 0.0};
+  for (int i = c0; i < c1; ++i) local = dd_add(local, dd{key[i], 0.0});
+  const int lane = tid & 63, wave = tid >> 6;
+  dd incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    dd n = shfl_up_dd(incl, o);
+    if (lane >= o) incl = dd_add(n, incl);
+  }
+  dd excl = shfl_up_dd(incl, 1);
+  if (lane == 0) excl = dd{0.0, 0.0};
+  if (lane == 63) { wsum_hi[wave] = incl.hi; wsum_lo[wave] = incl.lo; }
+  __syncthreads();
+  dd base{(double)R, 0.0};
+  for (int w = 0; w < wave; ++w) base = dd_add(base, dd{wsum_hi[w], wsum_lo[w]});
+  dd run = dd_add(base, excl);
+
+  // 4. admission test of each candidate n in this thread's block
+  int fail = N;
+  for (int n = c0; n < c1; ++n) {
+    const double tau_n = run.hi + run.lo;
+    run = dd_add(run, dd{key[n], 0.0});
+    const double tau_n1 = run.hi + run.lo;
+    const int nb = R + n + 1;
+    bool ok = nb < sps_len && sps[nb] > 0.0;
+    if (ok) {
+      const double theta_n = tau_n * sps[nb - 1];
+      ok = tau_n1 * sps[nb] > theta_n;
+    }
+    if (!ok) { fail = n; break; }
+  }
+  // first failing candidate overall
+  fail = block_min_int(fail, reinterpret_cast<double*>(wsum_hi));
+  const int nadm = fail;
+  // tau and Theta after the last admitted candidate (thread holding n = nadm-1,
+  // or the start value when nothing is admitted)
+  if (tid == 0 && nadm == 0) {
+    s_tau = (double)R;
+    s_theta = R < sps_len ? (double)R * sps[R] : 0.0;
+  }
+  if (nadm > 0 && nadm - 1 >= c0 && nadm - 1 < c1) {
+    dd r2 = dd_add(base, excl);
+    for (int n = c0; n < nadm; ++n) r2 = dd_add(r2, dd{key[n], 0.0});
+    const double tau = r2.hi + r2.lo;
+    s_tau = tau;
+    s_theta = tau * sps[R + nadm];
+  }
+  __syncthreads();
+
+  // 5. outputs
+  for (int i = tid; i < N; i += nthr) {
+    if (order) order[i] = idx[i];
+    if (i < nadm) atomicAdd(&ell[idx[i] / gamma], 1);
+  }
+  if (tid == 0 && stats) {
+    stats[0] = (double)nadm;
+    stats[1] = s_tau;
+    stats[2] = s_theta;
+  }
+}
+
+size_t schedule_workspace_bytes(int R, int gamma) {
+  (void)R; (void)gamma;
+  return 0;
+}
+
+hipError_t launch_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
+                           int32_t* ell, int32_t* order, double* stats, int32_t* status,
+                           void* ws, hipStream_t stream) {
+  (void)ws;
+  TraceScope ts("schedule_kernel", stream);
+  schedule_kernel<<<dim3(1), dim3(1024), 0, stream>>>(R, gamma, conf, sps, sps_len, ell, order,
+                                                      stats, status);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

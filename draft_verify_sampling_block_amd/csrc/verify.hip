@@ -1,0 +1,490 @@
+// dspark_verify: lossless speculative rejection sampling.
+//
+// [billytse] 1 and [xhh] acceptance-rule Q&A: draft token x_k ~ q is
+// accepted with probability min(1, p(x_k)/q(x_k)); the first rejection ends
+// the scan and one token is drawn there from norm(max(0, p - q)); if all
+// verified tokens pass, one bonus token is drawn from the next target slot.
+//
+// Launches:
+//   verify_init_kernel    first_reject[b] = +inf
+//   verify_rows_kernel    one work-group per (slot k, request b), k-major, for
+//                         k <= ell[b]: target-row max / argmax / log-sum-exp,
+//                         p(x_k), ratio and accept test.  A row is skipped
+//                         once an earlier slot of the same request has
+//                         rejected (rows are claimed in slot order, so late
+//                         slots are mostly skipped: "row-lazy" without a
+//                         sequential dependency).
+//   verify_final_stats    vocabulary-parallel wave tiles (as in drafting):
+//                         per-chunk sums of the residual max(0, p_j - q_j)
+//                         (q_j recomputed bit-identically on the matrix
+//                         cores) or of the bonus slot's p.
+//   verify_finish_kernel  per request: fp64 scan of the chunk sums, exact
+//                         recompute of the crossing chunk, the drawn token,
+//                         and the outputs.
+#include "dspark_common.hpp"
+#include "dspark_launch.hpp"
+#include "trace.hpp"
+
+namespace dspark {
+
+namespace {
+
+struct VerifyWs {
+  int32_t* first_rej;  // [B]
+  float* rM;           // [B][gamma+1] target row max of y = t/T (max t when greedy)
+  float* rLZ;          // [B][gamma+1] log sum exp(y - max)
+  int32_t* rArg;       // [B][gamma+1] lowest argmax
+  float* wratio;       // [B][gamma]
+  int32_t* wacc;       // [B][gamma]
+  float* fchunk;       // [B][nC] residual (or bonus p) chunk sums
+  float* pchunk;       // [B][nC] p chunk sums of the residual slot (fallback)
+};
+
+VerifyWs carve(void* ws, int B, int gamma, int V) {
+  char* p = static_cast<char*>(ws);
+  const size_t nC = n_chunks(V);
+  VerifyWs w;
+  w.first_rej = reinterpret_cast<int32_t*>(p); p += align256((size_t)B * 4);
+  w.rM = reinterpret_cast<float*>(p); p += align256((size_t)B * (gamma + 1) * 4);
+  w.rLZ = reinterpret_cast<float*>(p); p += align256((size_t)B * (gamma + 1) * 4);
+  w.rArg = reinterpret_cast<int32_t*>(p); p += align256((size_t)B * (gamma + 1) * 4);
+  w.wratio = reinterpret_cast<float*>(p); p += align256((size_t)B * gamma * 4);
+  w.wacc = reinterpret_cast<int32_t*>(p); p += align256((size_t)B * gamma * 4);
+  w.fchunk = reinterpret_cast<float*>(p); p += align256((size_t)B * nC * 4);
+  w.pchunk = reinterpret_cast<float*>(p); p += align256((size_t)B * nC * 4);
+  return w;
+}
+
+__device__ inline int clamp_ell(const int32_t* ell, int b, int gamma, int32_t* status) {
+  int L = ell[b];
+  if (L < 0 || L > gamma) {
+    flag(status, DSPARK_DEV_BAD_ELL);
+    L = L < 0 ? 0 : gamma;
+  }
+  return L;
+}
+
+__device__ inline float inv_temp(float T) { return (T > 0.f) ? 1.f / T : 0.f; }
+
+}  // namespace
+
+__global__ void verify_init_kernel(int B, int32_t* first_rej) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) first_rej[b] = 0x7fffffff;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void verify_rows_kernel(
+    int B, int gamma, int V, const T* __restrict__ target, const int32_t* __restrict__ tokens,
+    const float* __restrict__ q_tok, const float* __restrict__ temperature,
+    const float* __restrict__ uniforms, const int32_t* __restrict__ ell, VerifyWs ws,
+    int32_t* status) {
+  __shared__ double red[8];
+  __shared__ int s_skip;
+  const int k = blockIdx.x / B, b = blockIdx.x % B;
+  const int tid = threadIdx.x;
+  const int L = clamp_ell(ell, b, gamma, tid == 0 ? status : nullptr);
+  if (k > L) return;  // uniform: every thread reads the same ell[b]
+  // skip the row if an earlier slot of this request already rejected; one
+  // thread reads the flag so the whole work-group takes the same branch
+  if (tid == 0)
+    s_skip = __hip_atomic_load(&ws.first_rej[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < k;
+  __syncthreads();
+  if (s_skip) return;
+
+  const float it = inv_temp(temperature[b]);
+  const bool greedy = !(it > 0.f);
+  const float scale = greedy ? 1.f : it;
+  const T* row = target + ((size_t)b * (gamma + 1) + k) * V;
+
+  float m = -INFINITY;
+  double s = 0.0;
+  int arg = 0x7fffffff;
+  for (int i = 8 * tid; i < V; i += 8 * 256) {
+    float y[8];
+    load8_f32_stream(row + i, y);
+    float gm = y[0] * scale;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      y[t] *= scale;
+      gm = fmaxf(gm, y[t]);
+    }
+    if (gm > m) {
+      if (greedy) {
+#pragma unroll
+        for (int t = 7; t >= 0; --t)
+          if (y[t] == gm) arg = i + t;
+      } else if (s > 0.0) {
+        s *= exp((double)m - (double)gm);
+      }
+      m = gm;
+    }
+    if (!greedy) {
+      float g = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) g += __expf(y[t] - m);
+      s += (double)g;
+    }
+  }
+  const float M = block_max(m, red);
+  int a = 0x7fffffff;
+  if (greedy) a = (m == M) ? arg : 0x7fffffff;
+  a = block_min_int(a, red);
+  double mine = (!greedy && m > -INFINITY) ? s * exp((double)m - (double)M) : 0.0;
+  const double Zt = block_sum(mine, red);
+
+  if (tid == 0) {
+    const size_t sk = (size_t)b * (gamma + 1) + k;
+    const bool fin = (M == M) && M > -INFINITY && M < INFINITY && (greedy || (Zt > 0.0 && Zt < INFINITY));
+    if (!fin) flag(status, DSPARK_DEV_NONFINITE);
+    ws.rM[sk] = M;
+    ws.rLZ[sk] = greedy ? 0.f : (float)log(Zt);
+    ws.rArg[sk] = (a >= 0 && a < V) ? a : 0;
+    if (k < L) {
+      const size_t bk = (size_t)b * gamma + k;
+      const int x = clamp_token(tokens[bk], V, status);
+      float p;
+      if (greedy) {
+        p = (x == a) ? 1.f : 0.f;
+      } else {
+        float tx;
+        if constexpr (sizeof(T) == 2) tx = bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[x]);
+        else tx = reinterpret_cast<const float*>(row)[x];
+        p = (float)((double)__expf(tx * scale - M) / Zt);
+      }
+      const float q = q_tok[bk];
+      const float u = uniforms[((size_t)b * (gamma + 1) + k) * 2 + 1];
+      const bool accept = u * q < p;
+      ws.wratio[bk] = p / q;
+      ws.wacc[bk] = accept ? 1 : 0;
+      if (!accept) atomicMin(&ws.first_rej[b], k);
+    }
+  }
+}
+
+// per-element residual / bonus weight; identical expression in both kernels
+__device__ inline void final_weights(const float yt[8], const float yq[8], float M, float LZ,
+                                     float mq, float lzq, bool residual, float r[8],
+                                     float p[8]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    p[t] = __expf(yt[t] - M - LZ);
+    if (residual) {
+      const float q = __expf(yq[t] - mq - lzq);
+      r[t] = fmaxf(0.f, p[t] - q);
+    } else {
+      r[t] = p[t];
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void verify_final_stats_kernel(
+    int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
+    const T* __restrict__ W1, const T* __restrict__ W2t, const int32_t* __restrict__ anchor,
+    const int32_t* __restrict__ tokens, const float* __restrict__ row_max,
+    const float* __restrict__ row_logZ, const float* __restrict__ temperature,
+    const int32_t* __restrict__ ell, VerifyWs ws, int32_t* status) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5;
+  const int nRB = (B + kTileM - 1) / kTileM;
+  const int nT = n_tiles(V), nC = n_chunks(V);
+  const int task = blockIdx.x * 4 + wave;
+  const bool active = task < nT * nRB;
+  const int vt = active ? task / nRB : 0, rb = active ? task % nRB : 0;
+  const int v0 = vt * kTileV;
+
+  // per row of the block: mode (0 none/greedy, 1 residual at slot j, 2 bonus at slot L)
+  __shared__ int sprev[4][kTileM];
+  __shared__ int sslot[4][kTileM];
+  __shared__ int smode[4][kTileM];
+  if (h == 0) {
+    const int b = rb * kTileM + c;
+    int prev = -1, slot = 0, mode = 0;
+    if (active && b < B) {
+      const int L = clamp_ell(ell, b, gamma, nullptr);
+      const int j = ws.first_rej[b];
+      const bool greedy = !(temperature[b] > 0.f);
+      if (!greedy) {
+        if (j < L) {
+          mode = 1;
+          slot = j;
+          prev = clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1], V, nullptr);
+        } else {
+          mode = 2;
+          slot = L;
+        }
+      }
+    }
+    sprev[wave][c] = prev;
+    sslot[wave][c] = slot;
+    smode[wave][c] = mode;
+  }
+  __syncthreads();
+  if (!active) return;
+
+  bool any_res = false;
+  for (int m = 0; m < kTileM; ++m) any_res |= smode[wave][m] == 1;
+  f32x16_t acc[8];
+  if (any_res) {
+    bias_tile<T>(W1, sprev[wave], W2t, v0, V, rank, 0, 32, acc);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = f32x16_t{};
+  }
+
+  const int vb = v0 + 8 * c;
+  const bool vok = vb < V;
+  for (int j = 0; j < 16; ++j) {
+    const int m = acc_row(j, h);
+    const int b = rb * kTileM + m;
+    const int mode = smode[wave][m];
+    if (b >= B || mode == 0) continue;  // uniform across the half-wave
+    const int slot = sslot[wave][m];
+    const float it = 1.f / temperature[b];
+    const size_t sk = (size_t)b * (gamma + 1) + slot;
+    const float M = ws.rM[sk], LZ = ws.rLZ[sk];
+    float yt[8], yq[8], r[8], p[8];
+    float mq = 0.f, lzq = 0.f;
+    if (vok) {
+      load8_f32_stream(target + sk * V + vb, yt);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) yt[t] *= it;
+      if (mode == 1) {
+        load8_f32_stream(U + ((size_t)b * gamma + slot) * V + vb, yq);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) yq[t] = (yq[t] + acc[t][j]) * it;
+        mq = row_max[(size_t)b * gamma + slot];
+        lzq = row_logZ[(size_t)b * gamma + slot];
+      }
+      final_weights(yt, yq, M, LZ, mq, lzq, mode == 1, r, p);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) { r[t] = 0.f; p[t] = 0.f; }
+    }
+    float sr = 0.f, sp = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) { sr += r[t]; sp += p[t]; }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      sr += __shfl_xor(sr, o, kWave);
+      sp += __shfl_xor(sp, o, kWave);
+    }
+    if ((c & 7) == 0) {
+      const size_t ci = (size_t)b * nC + vt * kChunksPerTile + (c >> 3);
+      ws.fchunk[ci] = sr;
+      ws.pchunk[ci] = sp;
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void verify_finish_kernel(
+    int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
+    const T* __restrict__ W1, const T* __restrict__ W2t, const int32_t* __restrict__ anchor,
+    const int32_t* __restrict__ tokens, const float* __restrict__ row_max,
+    const float* __restrict__ row_logZ, const float* __restrict__ temperature,
+    const float* __restrict__ uniforms, const int32_t* __restrict__ ell, VerifyWs ws,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ n_accepted,
+    float* __restrict__ ratio, int32_t* status) {
+  __shared__ double red[8];
+  __shared__ int s_chunk, s_pick;
+  __shared__ double s_before;
+  __shared__ int sprev[kTileM];
+  __shared__ float se[kChunk];
+
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int nC = n_chunks(V);
+  const int L = clamp_ell(ell, b, gamma, nullptr);
+  const int j = ws.first_rej[b];
+  const bool residual = j < L;
+  const int slot = residual ? j : L;
+  const int n = residual ? j : L;
+  const float Tb = temperature[b];
+  const bool greedy = !(Tb > 0.f);
+  const size_t sk = (size_t)b * (gamma + 1) + slot;
+
+  int y = 0;
+  if (greedy) {
+    y = ws.rArg[sk];
+  } else {
+    // residual chunk sums; fall back to p when the residual has no mass
+    const float* fc = ws.fchunk + (size_t)b * nC;
+    const float* pc = ws.pchunk + (size_t)b * nC;
+    const int per = (nC + blockDim.x - 1) / blockDim.x;
+    const int c0 = min(nC, tid * per), c1 = min(nC, c0 + per);
+    double local = 0.0;
+    for (int cc = c0; cc < c1; ++cc) local += (double)fc[cc];
+    double start, end;
+    double S = block_scan_interval(local, red, &start, &end);
+    bool use_p = false;
+    if (!(S > 0.0) && residual) {
+      use_p = true;
+      if (tid == 0) flag(status, DSPARK_DEV_DEGENERATE);
+      local = 0.0;
+      for (int cc = c0; cc < c1; ++cc) local += (double)pc[cc];
+      S = block_scan_interval(local, red, &start, &end);
+    }
+    const float* cs = use_p ? pc : fc;
+    const double u = (double)uniforms[((size_t)b * (gamma + 1) + gamma) * 2 + 0];
+    const double tgt = u * S;
+    const bool finite = S > 0.0 && isfinite(S);
+    const int last_pos = block_max_int(local > 0.0 ? tid : -1, red);
+    if (tid == 0) s_chunk = -1;
+    if (tid < kTileM) sprev[tid] = -1;
+    __syncthreads();
+    if (finite && local > 0.0 &&
+        ((start <= tgt && tgt < end) || (tid == last_pos && tgt >= end))) {
+      double run = start, before = start, lastb = start;
+      int found = -1, lastc = -1;
+      for (int cc = c0; cc < c1; ++cc) {
+        const double sc = (double)cs[cc];
+        if (sc > 0.0) { lastc = cc; lastb = run; }
+        if (sc > 0.0 && tgt < run + sc) { found = cc; before = run; break; }
+        run += sc;
+      }
+      if (found < 0) { found = lastc; before = lastb; }
+      s_chunk = found;
+      s_before = before;
+    }
+    const int mrow = b % kTileM;
+    if (tid == 0 && residual)
+      sprev[mrow] = clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1], V, nullptr);
+    __syncthreads();
+    const int cstar = s_chunk;
+    if (cstar < 0) {
+      if (tid == 0) flag(status, DSPARK_DEV_NONFINITE);
+      y = 0;
+    } else {
+      const int vt = cstar >> 2, q = cstar & 3;
+      if (tid < kWave) {
+        const int lane = tid, c = lane & 31, h = lane >> 5;
+        const int v0 = vt * kTileV;
+        f32x16_t acc[8];
+        if (residual) {
+          bias_tile<T>(W1, sprev, W2t, v0, V, rank, 8 * q, 8 * q + 8, acc);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[t] = f32x16_t{};
+        }
+        const int hm = (mrow >> 2) & 1;
+        const int jm = 4 * (mrow >> 3) + (mrow & 3);
+        if (h == hm && c >= 8 * q && c < 8 * q + 8) {
+          const int vb = v0 + 8 * c;
+          const float it = 1.f / Tb;
+          const float M = ws.rM[sk], LZ = ws.rLZ[sk];
+          float yt[8], yq[8], r[8], p[8];
+          float mq = 0.f, lzq = 0.f;
+          if (vb < V) {
+            load8_f32(target + sk * V + vb, yt);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) yt[t] *= it;
+            if (residual) {
+              load8_f32(U + ((size_t)b * gamma + slot) * V + vb, yq);
+#pragma unroll
+              for (int t = 0; t < 8; ++t) yq[t] = (yq[t] + acc[t][jm]) * it;
+              mq = row_max[(size_t)b * gamma + slot];
+              lzq = row_logZ[(size_t)b * gamma + slot];
+            }
+            final_weights(yt, yq, M, LZ, mq, lzq, residual, r, p);
+          } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) { r[t] = 0.f; p[t] = 0.f; }
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) se[(c - 8 * q) * 8 + t] = use_p ? p[t] : r[t];
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        const double rr = tgt - s_before;
+        double run = 0.0;
+        int pick = -1, lastp = -1;
+        for (int i = 0; i < kChunk; ++i) {
+          const double e = (double)se[i];
+          if (e > 0.0) lastp = i;
+          run += e;
+          if (e > 0.0 && rr < run) { pick = i; break; }
+        }
+        if (pick < 0) pick = lastp < 0 ? 0 : lastp;
+        s_pick = vt * kTileV + q * kChunk + pick;
+      }
+      __syncthreads();
+      y = s_pick;
+    }
+  }
+
+  // outputs: accepted prefix, the drawn token, -1 padding; ratios of tested slots
+  for (int i = tid; i <= gamma; i += blockDim.x) {
+    int v = -1;
+    if (i < n) v = tokens[(size_t)b * gamma + i];
+    else if (i == n) v = y;
+    out_tokens[(size_t)b * (gamma + 1) + i] = v;
+  }
+  if (ratio) {
+    for (int i = tid; i < gamma; i += blockDim.x)
+      ratio[(size_t)b * gamma + i] = (i < L && i <= j) ? ws.wratio[(size_t)b * gamma + i] : NAN;
+  }
+  if (tid == 0) n_accepted[b] = n;
+}
+
+size_t verify_workspace_bytes(int B, int gamma, int V, int rank, int dtype) {
+  (void)rank; (void)dtype;
+  const size_t nC = n_chunks(V);
+  return align256((size_t)B * 4) + 3 * align256((size_t)B * (gamma + 1) * 4) +
+         2 * align256((size_t)B * gamma * 4) + 2 * align256((size_t)B * nC * 4);
+}
+
+template <typename T>
+static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target, const T* U,
+                              const T* W1, const T* W2t, const int32_t* anchor,
+                              const int32_t* tokens, const float* q_tok, const float* row_max,
+                              const float* row_logZ, const float* temperature,
+                              const float* uniforms, const int32_t* ell, int32_t* out_tokens,
+                              int32_t* n_accepted, float* ratio, int32_t* status, void* wsp,
+                              hipStream_t stream) {
+  VerifyWs ws = carve(wsp, B, gamma, V);
+  {
+  TraceScope t0("verify_init_kernel", stream);
+  verify_init_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(B, ws.first_rej);
+  }
+  {
+  TraceScope t1("verify_rows_kernel", stream);
+  verify_rows_kernel<T><<<dim3(B * (gamma + 1)), dim3(256), 0, stream>>>(
+      B, gamma, V, target, tokens, q_tok, temperature, uniforms, ell, ws, status);
+  }
+  const int nRB = (B + kTileM - 1) / kTileM;
+  const int tasks = n_tiles(V) * nRB;
+  {
+  TraceScope t2("verify_final_stats_kernel", stream);
+  verify_final_stats_kernel<T><<<dim3((tasks + 3) / 4), dim3(256), 0, stream>>>(
+      B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature, ell,
+      ws, status);
+  }
+  TraceScope t3("verify_finish_kernel", stream);
+  verify_finish_kernel<T><<<dim3(B), dim3(256), 0, stream>>>(
+      B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
+      uniforms, ell, ws, out_tokens, n_accepted, ratio, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const void* target,
+                         const void* U, const void* W1, const void* W2t, const int32_t* anchor,
+                         const int32_t* tokens, const float* q_tok, const float* row_max,
+                         const float* row_logZ, const float* temperature, const float* uniforms,
+                         const int32_t* ell, int32_t* out_tokens, int32_t* n_accepted,
+                         float* ratio, int32_t* status, void* ws, hipStream_t stream) {
+  if (dtype == DSPARK_BF16)
+    return verify_impl<uint16_t>(
+        B, gamma, V, rank, static_cast<const uint16_t*>(target), static_cast<const uint16_t*>(U),
+        static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), anchor, tokens, q_tok,
+        row_max, row_logZ, temperature, uniforms, ell, out_tokens, n_accepted, ratio, status, ws,
+        stream);
+  return verify_impl<float>(B, gamma, V, rank, static_cast<const float*>(target),
+                            static_cast<const float*>(U), static_cast<const float*>(W1),
+                            static_cast<const float*>(W2t), anchor, tokens, q_tok, row_max,
+                            row_logZ, temperature, uniforms, ell, out_tokens, n_accepted, ratio,
+                            status, ws, stream);
+}
+
+}  // namespace dspark

@@ -259,3 +259,46 @@ def make_config(index: int, seed: int | None = None, requests=None, threads: int
         anchor=anchor[req].copy(), temperature=temperature[req].copy(),
         uniforms=uniforms[req].copy(), sps=sps_table(spec.sps_kind), requests=req,
     )
+
+
+def make_custom(B: int, gamma: int, V: int, rank: int, H: int, dtype: str = "bf16",
+                family: str = "mixture", seed: int = 0, temperature: float = 1.0,
+                greedy_frac: float = 0.0, sps_kind: str = "none", w_std: float = 0.02,
+                calibrated: bool = False, threads: int | None = None) -> Workload:
+    """A workload of arbitrary (small) shape drawn with the same recipes.
+
+    Used for parity tests that must span several tiles, a ragged vocabulary
+    tail and ragged request blocks while staying cheap for the oracle.
+    ``sps_kind`` may also be "linear:<Btmax>" for 2400*(1-0.55*Bt/Btmax).
+    """
+    spec = Spec(100, "custom", B, gamma, V, rank, H, dtype, family, w_std,
+                sps_kind != "none", temperature, greedy_frac=greedy_frac, sps_kind=sps_kind)
+    anchor, uniforms, low_class, temp = _global_draws(spec, seed)
+    W1 = _rng(seed, _C_W1).standard_normal((V, rank), dtype=np.float32) * np.float32(w_std)
+    W2t = _rng(seed, _C_W2).standard_normal((V, rank), dtype=np.float32) * np.float32(w_std)
+    w = (_rng(seed, _C_W).standard_normal(H + rank) * 0.1).astype(np.float32)
+    w_h = w[:H].astype(np.float64)
+    bf = dtype == "bf16"
+    sdt = np.uint16 if bf else np.float32
+    U = np.empty((B, gamma, V), dtype=sdt)
+    target = np.empty((B, gamma + 1, V), dtype=sdt)
+    hidden = np.empty((B, gamma, H), dtype=sdt)
+    for b in range(B):
+        base, tgt = _request_logits(spec, seed, b, bool(low_class[b]))
+        U[b] = to_bf16_bits(base[:gamma]) if bf else base[:gamma]
+        target[b] = to_bf16_bits(tgt) if bf else tgt
+        alpha = np.full(gamma, 0.8) if calibrated else None
+        h = _request_hidden(spec, seed, b, w_h, alpha)
+        hidden[b] = to_bf16_bits(h) if bf else h
+    if sps_kind.startswith("linear:"):
+        bmax = int(sps_kind.split(":")[1])
+        bt = np.arange(bmax + 1, dtype=np.float64)
+        sps = 2400.0 * (1.0 - 0.55 * bt / bmax)
+        sps[0] = 0.0
+    else:
+        sps = sps_table(sps_kind)
+    return Workload(spec=spec, B=B, gamma=gamma, V=V, rank=rank, H=H, dtype=dtype,
+                    U=U, target=target, W1=to_bf16_bits(W1) if bf else W1,
+                    W2t=to_bf16_bits(W2t) if bf else W2t, w=w, b0=0.0, hidden=hidden,
+                    anchor=anchor, temperature=temp, uniforms=uniforms, sps=sps,
+                    requests=np.arange(B))

@@ -1,0 +1,193 @@
+/*
+ * libdspark: the per-step sampling hot path of DSpark confidence-scheduled
+ * speculative decoding, as hand-written HIP kernels for CDNA4 (gfx950).
+ *
+ * Sources (web pages on DSpark, cited by site and section):
+ *   [weigao]   weigao.cc "DSpark 与 MTP：DeepSeek 投机解码调研", section
+ *              "DSpark 的核心设计" parts 2-4.
+ *   [billytse] billytse.dev "DSpark：DeepSeek 點樣「一次估多個、驗證前綴、
+ *              錯咗即修正」", sections 1, 3.2, 3.3, 5, 6, 7.
+ *   [xhh]      xhh.club "DeepSeek-V4.1 模型结构（6）：解码，DSpark", Q&A on
+ *              the acceptance rule and the scheduler; note on
+ *              non-anticipating truncation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every array pointer is a DEVICE pointer owned by the caller; the
+ *    library never frees or retains it.  Arrays are dense, row-major, and
+ *    16-byte aligned.  Nothing is allocated by the library.
+ *  - Calls are asynchronous on `stream` (NULL = the default stream), keep no
+ *    state between calls, and may be issued from several host threads.
+ *  - Arguments are validated on the host BEFORE anything is enqueued; on a
+ *    validation error the call returns a negative status, enqueues nothing,
+ *    and dspark_last_error() (thread-local) describes the problem.
+ *  - Data errors found on the device never abort: they OR bit flags
+ *    (DSPARK_DEV_*) into the optional int32 word `*status` (may be NULL),
+ *    which the caller clears before the step, and the affected outputs stay
+ *    in range (token ids within [0, V)).
+ *  - dtype selects the element type of the large tensors (U, target, W1,
+ *    W2t, hidden): DSPARK_BF16 (bit patterns, round-to-nearest-even) or
+ *    DSPARK_F32.  Accumulation is fp32 (bf16 inputs use MFMA), cross-tile
+ *    sums and cumulative sums are fp64.
+ *  - Shapes: V % 8 == 0, rank % 32 == 0 with 32 <= rank <= 512,
+ *    H % 8 == 0, 1 <= gamma <= 64, B >= 1.
+ *  - Positions are 0-based: draft position k (0..gamma-1) is the pages'
+ *    x_{k+1}.
+ *  - uniforms [B, gamma+1, 2] fp32 in [0,1): uniforms[b,k,0] draws draft
+ *    token k; uniforms[b,k,1] is the accept test of draft token k;
+ *    uniforms[b,gamma,0] draws the one final token (residual or bonus);
+ *    uniforms[b,gamma,1] is unused.
+ *  - temperature [B] fp32: logits are divided by T; T <= 0 (or NaN) means
+ *    greedy: lowest-index argmax, and q and p become one-hot.
+ *  - Inverse-CDF convention: the drawn token is the lowest index whose
+ *    cumulative probability exceeds u.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = -1,       /* bad size, count or NULL pointer            */
+  DSPARK_EDTYPE = -2,       /* unknown dtype                              */
+  DSPARK_EALIGN = -3,       /* pointer not 16-byte aligned                */
+  DSPARK_EWORKSPACE = -4,   /* workspace missing or too small             */
+  DSPARK_EUNSUPPORTED = -5, /* valid but outside what the kernels support */
+  DSPARK_EHIP = -6          /* a HIP runtime call failed                  */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* device-side data-error flags ORed into *status */
+#define DSPARK_DEV_BAD_TOKEN   1  /* anchor/token id outside [0,V); clamped     */
+#define DSPARK_DEV_NONFINITE   2  /* NaN/Inf logits or stats; token 0 emitted   */
+#define DSPARK_DEV_DEGENERATE  4  /* residual had no mass; drew from p instead  */
+#define DSPARK_DEV_BAD_ELL     8  /* ell outside [0,gamma]; clamped             */
+#define DSPARK_DEV_BAD_CONF   16  /* confidence NaN or outside [0,1]; clamped   */
+
+const char* dspark_status_str(int status);
+const char* dspark_last_error(void);
+/* library version, e.g. "libdspark 0.1 gfx950" */
+const char* dspark_version(void);
+
+/* ------------------------------------------------------------------------
+ * dspark_draft_block: semi-autoregressive block drafting with the vanilla
+ * Markov head ([billytse] 3.2-3.3; [weigao] part 2).
+ *
+ * For each request b, starting from prev = anchor[b], for k = 0..gamma-1:
+ *     z      = U[b,k,:] + W1[prev,:] @ W2          (rank-r transition bias)
+ *     x      = inverse-CDF draw from softmax(z / T_b) with uniforms[b,k,0]
+ *     prev   = x
+ * W2 (the rank -> V projection) is stored as W2t [V, rank], i.e. the weight
+ * layout of a linear map from rank to V: bias[v] = sum_i W1[prev,i]*W2t[v,i].
+ *
+ * in : U [B,gamma,V], W1 [V,rank], W2t [V,rank] (dtype); anchor [B] int32;
+ *      temperature [B], uniforms [B,gamma+1,2] fp32
+ * out: tokens [B,gamma] int32; q_tok [B,gamma] fp32 = q_k(x_k);
+ *      row_max [B,gamma] = max_v z/T (max z when greedy);
+ *      row_logZ [B,gamma] = log sum_v exp(z/T - row_max) (0 when greedy).
+ * workspace: dspark_draft_block_workspace(...) bytes of device memory.
+ * No full probability row is ever written.
+ * ---------------------------------------------------------------------- */
+size_t dspark_draft_block_workspace(int B, int gamma, int V, int rank, int dtype);
+int dspark_draft_block(int B, int gamma, int V, int rank, int dtype,
+                       const void* U, const void* W1, const void* W2t,
+                       const int32_t* anchor, const float* temperature,
+                       const float* uniforms,
+                       int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
+                       int32_t* status, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dspark_confidence: the confidence head ([weigao] part 3; [billytse] 5):
+ *     conf[b,k] = sigmoid( w[0:H] . hidden[b,k,:] + w[H:H+rank] . W1[prev_k,:]
+ *                          + bias )
+ * with prev_0 = anchor[b] and prev_k = tokens[b,k-1] -- the token BEFORE
+ * position k, never position k's own token ([xhh], non-anticipation).
+ * The Markov embedding of a token is its W1 row.
+ * in : hidden [B,gamma,H], W1 [V,rank] (dtype); anchor [B], tokens [B,gamma]
+ *      int32; w [H+rank] fp32; bias scalar
+ * out: conf [B,gamma] fp32
+ * ---------------------------------------------------------------------- */
+int dspark_confidence(int B, int gamma, int H, int V, int rank, int dtype,
+                      const void* hidden, const void* W1,
+                      const int32_t* anchor, const int32_t* tokens,
+                      const float* w, float bias, float* conf,
+                      int32_t* status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dspark_schedule: hardware-aware prefix scheduler ([weigao] part 4;
+ * [billytse] 6-7; [xhh] scheduler Q&A).
+ *     a[r,j]  = prod_{i<=j} conf[r,i]        (fp64, left to right)
+ *     rank all (r,j) by a descending, ties by flat index r*gamma+j ascending
+ *     Bt = R, tau = R, Theta = tau*sps[Bt]
+ *     for each candidate in rank order: stop if Bt+1 >= sps_len or
+ *       sps[Bt+1] <= 0; tau' = tau + a; Theta' = tau'*sps[Bt+1];
+ *       admit iff Theta' > Theta (strict rise), else stop.
+ *     ell[r] = number of admitted positions of request r (always a prefix)
+ * in : conf [R,gamma] fp32 (NaN / out of [0,1] clamped and flagged);
+ *      sps [sps_len] fp64, steps per second at target batch Bt (entry Bt)
+ * out: ell [R] int32; order [R*gamma] int32 flat ids in rank order (or
+ *      NULL); stats [3] fp64 {n_admitted, tau, Theta} (or NULL)
+ * Supports R*gamma <= 8192 (one work-group; the keys live in LDS).
+ * ---------------------------------------------------------------------- */
+size_t dspark_schedule_workspace(int R, int gamma);
+int dspark_schedule(int R, int gamma, const float* conf,
+                    const double* sps, int sps_len,
+                    int32_t* ell, int32_t* order, double* stats,
+                    int32_t* status, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dspark_verify: lossless speculative rejection sampling ([billytse] 1;
+ * [xhh] acceptance-rule Q&A).
+ * For request b with verify length L = ell[b] (0..gamma):
+ *   for k = 0..L-1: p = softmax(target[b,k,:]/T); accept draft token x_k iff
+ *     uniforms[b,k,1] < p(x_k)/q_tok[b,k]; stop at the first reject j.
+ *   reject at j: q_j is recomputed from U[b,j], W1, W2t and prev_j (bit-
+ *     identical to the draft's logits; row_max/row_logZ normalise it), and
+ *     one token is drawn from norm(max(0, p_j - q_j)) with uniforms[b,gamma,0].
+ *   no reject : one bonus token is drawn from softmax(target[b,L,:]/T) with
+ *     uniforms[b,gamma,0].
+ * in : target [B,gamma+1,V] (slot gamma is the bonus slot when ell = gamma),
+ *      U, W1, W2t (dtype); anchor, tokens int32; q_tok, row_max, row_logZ
+ *      (outputs of dspark_draft_block); temperature, uniforms; ell [B]
+ * out: out_tokens [B,gamma+1] int32: accepted prefix then the one drawn
+ *      token, -1 padded; n_accepted [B] int32 (emitted = n_accepted + 1;
+ *      the last emitted token is the next anchor); ratio [B,gamma] fp32 =
+ *      p(x_k)/q(x_k) at tested positions, NaN elsewhere (or NULL).
+ * workspace: dspark_verify_workspace(...) bytes.
+ * ---------------------------------------------------------------------- */
+size_t dspark_verify_workspace(int B, int gamma, int V, int rank, int dtype);
+int dspark_verify(int B, int gamma, int V, int rank, int dtype,
+                  const void* target, const void* U, const void* W1, const void* W2t,
+                  const int32_t* anchor, const int32_t* tokens, const float* q_tok,
+                  const float* row_max, const float* row_logZ,
+                  const float* temperature, const float* uniforms, const int32_t* ell,
+                  int32_t* out_tokens, int32_t* n_accepted, float* ratio,
+                  int32_t* status, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Optional per-kernel timing (not on the sampling path).
+ * dspark_trace_enable(1) clears earlier records and brackets every later
+ * kernel launch by a pair of hipEvents on its stream; (0) stops recording.
+ * dspark_trace_summary() waits for the recorded events and writes one line
+ * "<kernel> <launches> <total_ms>" per kernel into buf (NUL-terminated,
+ * truncated to len); returns the full text length or a negative status.
+ * Tracing adds event records between launches: time the step without it.
+ * ---------------------------------------------------------------------- */
+int dspark_trace_enable(int on);
+int dspark_trace_summary(char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSPARK_H */

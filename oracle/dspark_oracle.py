@@ -34,6 +34,8 @@ exhaustive enumeration; no function here is "parity unpinned".
 
 from __future__ import annotations
 
+from fractions import Fraction
+
 import numpy as np
 
 __all__ = [
@@ -270,7 +272,9 @@ def schedule(c, sps):
 
     Ties in survival are broken by flat index r*gamma + j ascending.  SPS
     entries that are absent (Bt beyond the table) or not positive are
-    inadmissible: the scan stops there.
+    inadmissible: the scan stops there.  tau is the exact (rational) sum of
+    R and the admitted survivals, rounded once to fp64, so it does not depend
+    on any summation order; Theta = tau * SPS[Bt] is one fp64 product.
 
     c: [R, gamma] (any float), sps: 1-D table indexed by Bt.
     Returns dict(ell [R] int64, order [R*gamma] int64, n_admitted, tau,
@@ -282,6 +286,7 @@ def schedule(c, sps):
     flat = a.reshape(-1)
     order = sorted(range(R * gamma), key=lambda i: (-flat[i], i))
     Bt = R
+    exact = Fraction(R)
     tau = float(R)
     theta = tau * sps[Bt] if Bt < len(sps) else 0.0
     ell = np.zeros(R, dtype=np.int64)
@@ -290,11 +295,12 @@ def schedule(c, sps):
         nb = Bt + 1
         if nb >= len(sps) or not (sps[nb] > 0.0):
             break
-        tau_new = tau + flat[i]
+        exact_new = exact + Fraction(float(flat[i]))
+        tau_new = float(exact_new)
         theta_new = tau_new * sps[nb]
         if theta_new > theta:
             ell[i // gamma] += 1
-            Bt, tau, theta = nb, tau_new, theta_new
+            Bt, tau, theta, exact = nb, tau_new, theta_new, exact_new
             n += 1
         else:
             break
@@ -328,7 +334,8 @@ def _draft_probs(z: np.ndarray, temperature: float) -> np.ndarray:
     return q
 
 
-def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell):
+def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell,
+           requests=None, keep_final=False):
     """Speculative rejection sampling over each request's verified prefix.
 
     [billytse] 1 and [xhh] acceptance-rule Q&A: draft token x_k (drawn from
@@ -348,6 +355,9 @@ def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell
     ell_b is the bonus slot).  Returns dict(out_tokens [B, gamma+1] (-1
     padded), n_accepted [B], ratio [B, gamma] (NaN where untested),
     final_lo, final_hi, final_margin [B], degenerate [B] bool).
+    ``requests`` restricts the work to those request indices (others stay at
+    their fill values); ``keep_final`` also returns, per processed request,
+    the normalised cumulative distribution of the final draw (``final_cdf``).
     """
     W1 = W1 if (isinstance(W1, np.ndarray) and W1.dtype == np.float64) else f64(W1)
     W2t = W2t if (isinstance(W2t, np.ndarray) and W2t.dtype == np.float64) else f64(W2t)
@@ -362,7 +372,8 @@ def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell
     f_hi = np.zeros(B)
     f_margin = np.zeros(B)
     degenerate = np.zeros(B, dtype=bool)
-    for b in range(B):
+    final_cdf = {}
+    for b in (range(B) if requests is None else requests):
         T = float(temperature[b])
         L = int(ell[b])
         uf = float(uni[b, gamma, 0])
@@ -385,16 +396,21 @@ def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell
                 res = p
                 degenerate[b] = True
             y, lo, hi, _ = inverse_cdf(res, uf)
+            if keep_final:
+                final_cdf[b] = np.cumsum(res) / np.sum(res)
             out[b, :j] = tokens[b, :j]
             out[b, j] = y
             n_acc[b] = j
         else:
             p = target_probs(f64(target[b, L]), T)
             y, lo, hi, _ = inverse_cdf(p, uf)
+            if keep_final:
+                final_cdf[b] = np.cumsum(p) / np.sum(p)
             out[b, :L] = tokens[b, :L]
             out[b, L] = y
             n_acc[b] = L
         f_lo[b], f_hi[b] = lo, hi
         f_margin[b] = np.inf if (lo <= 0.0 and hi >= 1.0) else min(uf - lo, hi - uf)
     return dict(out_tokens=out, n_accepted=n_acc, ratio=ratio, final_lo=f_lo,
-                final_hi=f_hi, final_margin=f_margin, degenerate=degenerate)
+                final_hi=f_hi, final_margin=f_margin, degenerate=degenerate,
+                final_cdf=final_cdf)

@@ -1,0 +1,125 @@
+"""Stage-wise comparison of device outputs with the fp64 oracle.
+
+TEST INFRASTRUCTURE ONLY (imported by tests/, __graft_entry__.smoke()).
+
+Each oracle stage is fed the device's upstream discrete outputs (tokens,
+verify lengths), so one near-tie cannot cascade.  Matching rules:
+
+* tokens: identical wherever the oracle's uniform lies more than BAND = 1e-5
+  (probability units) from a boundary of the drawn token's interval;
+  otherwise the device token's own oracle interval must lie within BAND of u;
+* accept decisions / accepted lengths: identical wherever |u - p/q| > BAND;
+* verify lengths, scheduler order and admitted count: bit-exact;
+* probabilities, ratios, confidences, row statistics: within 1e-4 absolute
+  or 1e-3 relative.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import dspark_oracle as O
+
+BAND = 1e-5
+TOL_ABS = 1e-4
+TOL_REL = 1e-3
+
+
+def close(a, b) -> bool:
+    a, b = float(a), float(b)
+    if np.isnan(a) and np.isnan(b):
+        return True
+    d = abs(a - b)
+    return d <= TOL_ABS or d <= TOL_REL * abs(b)
+
+
+class Mismatch(AssertionError):
+    pass
+
+
+def _req(cond, msg):
+    if not cond:
+        raise Mismatch(msg)
+
+
+def check_draft(wl, W1_64, W2t_64, tokens, q_tok, row_max, row_logZ, rows=None):
+    """tokens etc. are host numpy arrays of the device outputs."""
+    forced = O.draft_forced(wl.U, W1_64, W2t_64, wl.anchor, wl.temperature, tokens,
+                            uniforms=wl.uniforms, rows=rows)
+    rep = dict(rows=len(forced), identical=0, band=0)
+    for d in forced:
+        b, k = d["b"], d["k"]
+        x = int(tokens[b, k])
+        u = float(wl.uniforms[b, k, 0])
+        if x == d["x_oracle"]:
+            rep["identical"] += 1
+        else:
+            _req(d["margin"] <= BAND,
+                 f"draft token ({b},{k}): device {x} vs oracle {d['x_oracle']} (margin {d['margin']:.3g})")
+            _req(d["lo"] - BAND <= u <= d["hi"] + BAND,
+                 f"draft token ({b},{k}): device {x} interval [{d['lo']},{d['hi']}) far from u={u}")
+            rep["band"] += 1
+        _req(close(q_tok[b, k], d["q"]), f"q_tok ({b},{k}): {q_tok[b, k]} vs {d['q']}")
+        _req(close(row_max[b, k], d["m"]), f"row_max ({b},{k}): {row_max[b, k]} vs {d['m']}")
+        _req(close(row_logZ[b, k], d["logZ"]), f"row_logZ ({b},{k}): {row_logZ[b, k]} vs {d['logZ']}")
+    return rep
+
+
+def check_confidence(wl, tokens, conf):
+    c = O.confidence(wl.hidden, wl.W1, wl.anchor, tokens, wl.w, wl.b0)
+    bad = [(b, k) for b in range(c.shape[0]) for k in range(c.shape[1]) if not close(conf[b, k], c[b, k])]
+    _req(not bad, f"confidence mismatch at {bad[:5]} (device {[conf[i] for i in bad[:3]]}, "
+                  f"oracle {[c[i] for i in bad[:3]]})")
+    return dict(rows=c.size, max_abs=float(np.max(np.abs(conf - c))))
+
+
+def check_schedule(conf, sps, ell, order, stats):
+    s = O.schedule(conf.astype(np.float64), sps)
+    _req(np.array_equal(np.asarray(order, dtype=np.int64), s["order"]), "scheduler order differs")
+    _req(np.array_equal(np.asarray(ell, dtype=np.int64), s["ell"]),
+         f"ell differs at {np.nonzero(np.asarray(ell) != s['ell'])[0][:8]}")
+    _req(int(round(stats[0])) == s["n_admitted"], f"n_admitted {stats[0]} vs {s['n_admitted']}")
+    _req(abs(stats[1] - s["tau"]) <= 1e-12 * abs(s["tau"]), f"tau {stats[1]} vs {s['tau']}")
+    _req(abs(stats[2] - s["theta"]) <= 1e-12 * abs(s["theta"]), f"theta {stats[2]} vs {s['theta']}")
+    return dict(n_admitted=s["n_admitted"], mean_ell=float(np.mean(s["ell"])))
+
+
+def check_verify(wl, W1_64, W2t_64, tokens, ell, out_tokens, n_accepted, ratio, requests=None):
+    B, gamma = tokens.shape
+    reqs = list(range(B)) if requests is None else list(requests)
+    rows = [(b, k) for b in reqs for k in range(int(ell[b]))]
+    q = np.full((B, gamma), np.nan)
+    for d in O.draft_forced(wl.U, W1_64, W2t_64, wl.anchor, wl.temperature, tokens, rows=rows):
+        q[d["b"], d["k"]] = d["q"]
+    v = O.verify(wl.target, wl.U, W1_64, W2t_64, wl.anchor, tokens, q, wl.temperature,
+                 wl.uniforms, ell, requests=reqs, keep_final=True)
+    rep = dict(requests=len(reqs), accept_flips=0, final_identical=0, final_band=0)
+    for b in reqs:
+        L = int(ell[b])
+        n_o, n_g = int(v["n_accepted"][b]), int(n_accepted[b])
+        _req(0 <= n_g <= L, f"n_accepted[{b}]={n_g} outside [0,{L}]")
+        for k in range(min(n_o, n_g, L - 1) + 1 if L > 0 else 0):
+            _req(close(ratio[b, k], v["ratio"][b, k]), f"ratio ({b},{k}): {ratio[b, k]} vs {v['ratio'][b, k]}")
+        for k in range(gamma):
+            if not (k < L and k <= n_g):
+                _req(np.isnan(ratio[b, k]), f"ratio ({b},{k}) should be NaN (untested)")
+        _req(np.array_equal(out_tokens[b, :n_g], tokens[b, :n_g]), f"accepted prefix of {b} differs")
+        _req(np.all(out_tokens[b, n_g + 1:] == -1), f"padding of {b}")
+        if n_g != n_o:
+            k = min(n_g, n_o)
+            gap = abs(float(wl.uniforms[b, k, 1]) - v["ratio"][b, k])
+            _req(gap <= BAND, f"accept length of {b}: device {n_g} vs oracle {n_o} (|u-ratio|={gap:.3g})")
+            rep["accept_flips"] += 1
+            continue
+        y_g, y_o = int(out_tokens[b, n_g]), int(v["out_tokens"][b, n_o])
+        if y_g == y_o:
+            rep["final_identical"] += 1
+            continue
+        _req(v["final_margin"][b] <= BAND,
+             f"final token of {b}: device {y_g} vs oracle {y_o} (margin {v['final_margin'][b]:.3g})")
+        cdf = v["final_cdf"][b]
+        uf = float(wl.uniforms[b, gamma, 0])
+        lo = cdf[y_g - 1] if y_g > 0 else 0.0
+        _req(lo - BAND <= uf <= cdf[y_g] + BAND, f"final token of {b}: interval far from u")
+        rep["final_band"] += 1
+    return rep

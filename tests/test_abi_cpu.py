@@ -1,0 +1,65 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol
+the header declares, and validates arguments on the host (no compute)."""
+
+import ctypes
+import os
+
+import pytest
+
+import draft_verify_sampling_block_amd as dv
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dv.lib_path()):
+        from draft_verify_sampling_block_amd.build import build_library
+        build_library()
+    return dv.load()
+
+
+def test_header_symbols_are_exported(lib):
+    names = dv.header_names()
+    for n in ("dspark_draft_block", "dspark_confidence", "dspark_schedule", "dspark_verify",
+              "dspark_draft_block_workspace", "dspark_verify_workspace",
+              "dspark_schedule_workspace", "dspark_status_str", "dspark_last_error",
+              "dspark_version"):
+        assert n in names
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version(lib):
+    assert lib.dspark_status_str(0) == b"DSPARK_OK"
+    for code in (-1, -2, -3, -4, -5, -6):
+        assert lib.dspark_status_str(code).startswith(b"DSPARK_E")
+    assert b"gfx950" in lib.dspark_version()
+
+
+def test_workspace_queries(lib):
+    # per-tile max + argmax and per-64-entry chunk sums, 256-byte aligned
+    nT = (151936 + 255) // 256
+    expect = 2 * ((128 * nT * 4 + 255) // 256 * 256) + (128 * nT * 4 * 4 + 255) // 256 * 256
+    assert dv.dspark_draft_block_workspace(128, 15, 151936, 256, 1) == expect
+    assert dv.dspark_draft_block_workspace(128, 15, 151937, 256, 1) == 0  # invalid V
+    assert dv.dspark_verify_workspace(4, 5, 1024, 32, 0) > 0
+    assert dv.dspark_schedule_workspace(512, 7) == 0
+
+
+def test_host_validation_rejects_before_launch(lib):
+    P = [None] * 11
+    rc = lib.dspark_draft_block(4, 5, 1024, 32, 0, *P, None, 0, None)
+    assert rc == -1 and b"'U' is NULL" in lib.dspark_last_error()
+    assert lib.dspark_draft_block(0, 5, 1024, 32, 0, *P, None, 0, None) == -1
+    assert lib.dspark_draft_block(4, 65, 1024, 32, 0, *P, None, 0, None) == -1
+    assert lib.dspark_draft_block(4, 5, 1024, 32, 9, *P, None, 0, None) == -2
+    assert lib.dspark_draft_block(4, 5, 1020, 32, 0, *P, None, 0, None) == -1
+    assert lib.dspark_draft_block(4, 5, 1024, 48, 0, *P, None, 0, None) == -1
+    fake = 4096  # aligned, never dereferenced: validation fails first
+    assert lib.dspark_draft_block(4, 5, 1024, 32, 0, *([fake] * 11), fake, 16, None) == -4
+    assert lib.dspark_draft_block(4, 5, 1024, 32, 0, *([fake + 8] + [fake] * 10), fake, 1 << 30,
+                                  None) == -3
+    assert lib.dspark_schedule(9000, 1, fake, fake, 10, fake, None, None, None, None, 0, None) == -5
+    assert lib.dspark_schedule(4, 2, fake, fake, 0, fake, None, None, None, None, 0, None) == -1
+    assert lib.dspark_confidence(4, 5, 60, 1024, 32, 1, *([fake] * 5), ctypes.c_float(0.0), fake,
+                                 None, None) == -1  # H % 8
+    assert lib.dspark_verify(4, 5, 1024, 32, 1, *([fake] * 15), None, fake, 8, None) == -4

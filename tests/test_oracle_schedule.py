@@ -143,5 +143,17 @@ def test_exact_tie_is_not_admitted():
     s = O.schedule(np.array([[0.5, 0.5]]), np.array([0.0, 150.0, 100.0, 90.0]))
     assert s["ell"][0] == 0 and s["n_admitted"] == 0
     # a hair more survival and it is admitted
-    s = O.schedule(np.array([[0.5 + 2 ** -40, 0.5]]), np.array([0.0, 150.0, 100.0, 90.0]))
+    s = O.schedule(np.array([[0.5 + 2 ** -40, 0.5]]), np.array([0.0, 150.0, 100.0, 10.0]))
     assert s["ell"][0] == 1
+
+
+def test_tau_is_exact_sum_rounded_once():
+    # Ten survivals of 0.1 (not exact in binary) starting from R = 1: the
+    # sequential fp64 sum drifts, the exact sum rounded once does not.
+    s = O.schedule(np.ones((1, 10)), np.full(30, 5.0))
+    assert s["tau"] == 11.0
+    from fractions import Fraction
+    a = O.survival(np.full((2, 3), 0.1))
+    s = O.schedule(np.full((2, 3), 0.1), np.full(30, 5.0))
+    exact = Fraction(2) + sum(Fraction(float(x)) for x in a.reshape(-1))
+    assert s["tau"] == float(exact)
