@@ -178,7 +178,7 @@ def main():
                  "device_status": status},
     }
     if not args.no_cpu_baseline:
-        n_req = args.cpu_requests or {0: 4, 1: 12, 2: 24, 3: 10, 4: 16}[cfg]
+        n_req = args.cpu_requests or {0: 4, 1: 32, 2: 128, 3: 128, 4: 256}[cfg]
         out["cpu_baseline"] = cpu_baseline(cfg, n_req)
     print(json.dumps(out), flush=True)
 
