@@ -57,11 +57,11 @@ def algorithmic_bytes(wl, ell, n_acc):
 def draft_stats_bytes(wl):
     """Algorithmic bytes of one draft_stats_kernel launch (one draft position)."""
     e = 2 if wl.dtype == "bf16" else 4
-    nT = (wl.V + 255) // 256
+    nT = (wl.V + 127) // 128
     return (e * wl.B * wl.V              # the position's U rows
             + e * wl.B * wl.rank         # gathered W1 rows
             + e * wl.rank * wl.V / wl.gamma  # W2 read once per step, shared by gamma launches
-            + 4 * wl.B * nT * 6)         # tile max/argmax + 4 chunk sums per tile written
+            + 4 * wl.B * nT * 4)         # tile max/argmax + 2 chunk sums per tile written
 
 
 def cpu_baseline(cfg, n_req):

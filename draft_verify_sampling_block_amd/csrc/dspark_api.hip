@@ -40,6 +40,8 @@ int check_dims(const char* fn, int B, int gamma, int V, int rank, int dtype) {
   if (B < 1) return fail(DSPARK_EINVAL, "%s: B=%d must be >= 1", fn, B);
   if (gamma < 1 || gamma > 64) return fail(DSPARK_EINVAL, "%s: gamma=%d outside [1,64]", fn, gamma);
   if (V < 8 || V % 8) return fail(DSPARK_EINVAL, "%s: V=%d must be a positive multiple of 8", fn, V);
+  if (dtype == DSPARK_BF16 && rank != 32 && rank != 64 && rank != 128 && rank != 256)
+    return fail(DSPARK_EINVAL, "%s: bf16 rank=%d must be 32, 64, 128 or 256", fn, rank);
   if (rank < 32 || rank > 512 || rank % 32)
     return fail(DSPARK_EINVAL, "%s: rank=%d must be a multiple of 32 in [32,512]", fn, rank);
   if ((long long)B * (gamma + 1) > (1LL << 31) / 2)

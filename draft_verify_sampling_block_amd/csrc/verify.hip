@@ -163,11 +163,11 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
 }
 
 // per-element residual / bonus weight; identical expression in both kernels
-__device__ inline void final_weights(const float yt[8], const float yq[8], float M, float LZ,
-                                     float mq, float lzq, bool residual, float r[8],
-                                     float p[8]) {
+__device__ inline void final_weights(const float yt[4], const float yq[4], float M, float LZ,
+                                     float mq, float lzq, bool residual, float r[4],
+                                     float p[4]) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
+  for (int t = 0; t < 4; ++t) {
     p[t] = __expf(yt[t] - M - LZ);
     if (residual) {
       const float q = __expf(yq[t] - mq - lzq);
@@ -178,107 +178,140 @@ __device__ inline void final_weights(const float yt[8], const float yq[8], float
   }
 }
 
-template <typename T>
+// Final-draw row of request b: mode 0 = nothing to stream (greedy), 1 =
+// residual at the first rejected slot j, 2 = bonus at slot L.
+struct FinalRow {
+  int mode, slot, prev;
+};
+__device__ inline FinalRow final_row(int b, int B, int gamma, int V, const int32_t* ell,
+                                     const float* temperature, const int32_t* anchor,
+                                     const int32_t* tokens, const VerifyWs& ws) {
+  FinalRow f{0, 0, -1};
+  if (b >= B) return f;
+  const int L = clamp_ell(ell, b, gamma, nullptr);
+  const int j = ws.first_rej[b];
+  if (!(temperature[b] > 0.f)) return f;
+  if (j < L) {
+    f.mode = 1;
+    f.slot = j;
+    f.prev = clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1], V, nullptr);
+  } else {
+    f.mode = 2;
+    f.slot = L;
+  }
+  return f;
+}
+
+template <typename T, int KS>
 __global__ __launch_bounds__(256) void verify_final_stats_kernel(
     int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
     const T* __restrict__ W1, const T* __restrict__ W2t, const int32_t* __restrict__ anchor,
     const int32_t* __restrict__ tokens, const float* __restrict__ row_max,
     const float* __restrict__ row_logZ, const float* __restrict__ temperature,
     const int32_t* __restrict__ ell, VerifyWs ws, int32_t* status) {
+  constexpr bool bf = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) char w2s[bf ? kLdsTileBytes : 16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int nRB = (B + kTileM - 1) / kTileM;
-  const int nT = n_tiles(V), nC = n_chunks(V);
-  const int task = blockIdx.x * 4 + wave;
-  const bool active = task < nT * nRB;
-  const int vt = active ? task / nRB : 0, rb = active ? task % nRB : 0;
-  const int v0 = vt * kTileV;
-
-  // per row of the block: mode (0 none/greedy, 1 residual at slot j, 2 bonus at slot L)
-  __shared__ int sprev[4][kTileM];
-  __shared__ int sslot[4][kTileM];
-  __shared__ int smode[4][kTileM];
-  if (h == 0) {
-    const int b = rb * kTileM + c;
-    int prev = -1, slot = 0, mode = 0;
-    if (active && b < B) {
-      const int L = clamp_ell(ell, b, gamma, nullptr);
-      const int j = ws.first_rej[b];
-      const bool greedy = !(temperature[b] > 0.f);
-      if (!greedy) {
-        if (j < L) {
-          mode = 1;
-          slot = j;
-          prev = clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1], V, nullptr);
-        } else {
-          mode = 2;
-          slot = L;
-        }
-      }
-    }
-    sprev[wave][c] = prev;
-    sslot[wave][c] = slot;
-    smode[wave][c] = mode;
-  }
-  __syncthreads();
-  if (!active) return;
-
-  bool any_res = false;
-  for (int m = 0; m < kTileM; ++m) any_res |= smode[wave][m] == 1;
-  f32x16_t acc[8];
-  if (any_res) {
-    bias_tile<T>(W1, sprev[wave], W2t, v0, V, rank, 0, 32, acc);
-  } else {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = f32x16_t{};
-  }
-
-  const int vb = v0 + 8 * c;
+  const int nC = n_chunks(V);
+  const int vt = blockIdx.x, v0 = vt * kTileV;
+  const int vb = v0 + 4 * c;
   const bool vok = vb < V;
-  for (int j = 0; j < 16; ++j) {
-    const int m = acc_row(j, h);
-    const int b = rb * kTileM + m;
-    const int mode = smode[wave][m];
-    if (b >= B || mode == 0) continue;  // uniform across the half-wave
-    const int slot = sslot[wave][m];
-    const float it = 1.f / temperature[b];
-    const size_t sk = (size_t)b * (gamma + 1) + slot;
-    const float M = ws.rM[sk], LZ = ws.rLZ[sk];
-    float yt[8], yq[8], r[8], p[8];
-    float mq = 0.f, lzq = 0.f;
-    if (vok) {
-      load8_f32_stream(target + sk * V + vb, yt);
+
+  // does any request of the batch need the q recompute (a residual draw)?
+  int any = 0;
+  for (int b = threadIdx.x; b < B; b += blockDim.x)
+    any |= final_row(b, B, gamma, V, ell, temperature, anchor, tokens, ws).mode == 1;
+  const bool any_res = __syncthreads_or(any) != 0;
+  if (bf && any_res) stage_w2_rows(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s, 0,
+                                   kTileV);
+
+  for (int rb = wave; rb < nRB || (rb == wave); rb += 4) {
+    // one pass per 32-request block; the first pass of every wave also
+    // joins the barrier that publishes the LDS tile
+    const bool live = rb < nRB;
+    const FinalRow mine = final_row(live ? rb * kTileM + c : B, B, gamma, V, ell, temperature,
+                                    anchor, tokens, ws);
+    bf16x8_t afrag[KS];
+    if constexpr (bf) load_afrag<KS>(reinterpret_cast<const uint16_t*>(W1),
+                                     mine.mode == 1 ? mine.prev : -1, afrag);
+    raw4_t<T> tp[16], up[16];
+    int mode_j[16], slot_j[16];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) yt[t] *= it;
-      if (mode == 1) {
-        load8_f32_stream(U + ((size_t)b * gamma + slot) * V + vb, yq);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) yq[t] = (yq[t] + acc[t][j]) * it;
-        mq = row_max[(size_t)b * gamma + slot];
-        lzq = row_logZ[(size_t)b * gamma + slot];
-      }
-      final_weights(yt, yq, M, LZ, mq, lzq, mode == 1, r, p);
+    for (int j = 0; j < 16; ++j) {
+      const int m = acc_row(j, h);
+      mode_j[j] = __shfl(mine.mode, m, kWave);
+      slot_j[j] = __shfl(mine.slot, m, kWave);
+      const int b = rb * kTileM + m;
+      tp[j] = raw4_t<T>{};
+      up[j] = raw4_t<T>{};
+      if (live && vok && mode_j[j] != 0)
+        tp[j] = load4_raw(target + ((size_t)b * (gamma + 1) + slot_j[j]) * V + vb);
+      if (live && vok && mode_j[j] == 1)
+        up[j] = load4_raw(U + ((size_t)b * gamma + slot_j[j]) * V + vb);
+    }
+    if (rb == wave) {
+      if (bf && any_res) __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (!live) break;
+    const bool blk_res = __ballot(mine.mode == 1) != 0;
+    f32x16_t acc[kSub];
+    if (blk_res) {
+      if constexpr (bf)
+        bias_tile_lds<KS>(afrag, w2s, 0, 32, acc);
+      else
+        bias_tile_f32(reinterpret_cast<const float*>(W1), mine.mode == 1 ? mine.prev : -1,
+                      reinterpret_cast<const float*>(W2t), v0, V, rank, 0, 32, acc);
     } else {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) { r[t] = 0.f; p[t] = 0.f; }
+      for (int t = 0; t < kSub; ++t) acc[t] = f32x16_t{};
     }
-    float sr = 0.f, sp = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) { sr += r[t]; sp += p[t]; }
+    for (int j = 0; j < 16; ++j) {
+      const int m = acc_row(j, h);
+      const int b = rb * kTileM + m;
+      const int mode = mode_j[j];
+      if (b >= B || mode == 0) continue;  // uniform across the half-wave
+      const int slot = slot_j[j];
+      const float it = 1.f / temperature[b];
+      const size_t sk = (size_t)b * (gamma + 1) + slot;
+      const float M = ws.rM[sk], LZ = ws.rLZ[sk];
+      float yt[4], yq[4] = {0.f, 0.f, 0.f, 0.f}, r[4], p[4];
+      float mq = 0.f, lzq = 0.f;
+      if (vok) {
+        unpack4(tp[j], yt);
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      sr += __shfl_xor(sr, o, kWave);
-      sp += __shfl_xor(sp, o, kWave);
-    }
-    if ((c & 7) == 0) {
-      const size_t ci = (size_t)b * nC + vt * kChunksPerTile + (c >> 3);
-      ws.fchunk[ci] = sr;
-      ws.pchunk[ci] = sp;
+        for (int t = 0; t < 4; ++t) yt[t] *= it;
+        if (mode == 1) {
+          unpack4(up[j], yq);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) yq[t] = (yq[t] + acc[t][j]) * it;
+          mq = row_max[(size_t)b * gamma + slot];
+          lzq = row_logZ[(size_t)b * gamma + slot];
+        }
+        final_weights(yt, yq, M, LZ, mq, lzq, mode == 1, r, p);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) { r[t] = 0.f; p[t] = 0.f; }
+      }
+      float sr = r[0] + r[1] + r[2] + r[3], sp = p[0] + p[1] + p[2] + p[3];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        sr += __shfl_xor(sr, o, kWave);
+        sp += __shfl_xor(sp, o, kWave);
+      }
+      if ((c & 15) == 0) {
+        const size_t ci = (size_t)b * nC + vt * kChunksPerTile + (c >> 4);
+        ws.fchunk[ci] = sr;
+        ws.pchunk[ci] = sp;
+      }
     }
   }
 }
 
-template <typename T>
+template <typename T, int KS>
 __global__ __launch_bounds__(256) void verify_finish_kernel(
     int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
     const T* __restrict__ W1, const T* __restrict__ W2t, const int32_t* __restrict__ anchor,
@@ -287,10 +320,11 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
     const float* __restrict__ uniforms, const int32_t* __restrict__ ell, VerifyWs ws,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ n_accepted,
     float* __restrict__ ratio, int32_t* status) {
+  constexpr bool bf = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) char w2s[bf ? kLdsTileBytes : 16];
   __shared__ double red[8];
   __shared__ int s_chunk, s_pick;
   __shared__ double s_before;
-  __shared__ int sprev[kTileM];
   __shared__ float se[kChunk];
 
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -331,7 +365,6 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
     const bool finite = S > 0.0 && isfinite(S);
     const int last_pos = block_max_int(local > 0.0 ? tid : -1, red);
     if (tid == 0) s_chunk = -1;
-    if (tid < kTileM) sprev[tid] = -1;
     __syncthreads();
     if (finite && local > 0.0 &&
         ((start <= tgt && tgt < end) || (tid == last_pos && tgt >= end))) {
@@ -347,53 +380,72 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
       s_chunk = found;
       s_before = before;
     }
-    const int mrow = b % kTileM;
-    if (tid == 0 && residual)
-      sprev[mrow] = clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1], V, nullptr);
     __syncthreads();
     const int cstar = s_chunk;
     if (cstar < 0) {
       if (tid == 0) flag(status, DSPARK_DEV_NONFINITE);
       y = 0;
     } else {
-      const int vt = cstar >> 2, q = cstar & 3;
-      if (tid < kWave) {
-        const int lane = tid, c = lane & 31, h = lane >> 5;
-        const int v0 = vt * kTileV;
-        f32x16_t acc[8];
-        if (residual) {
-          bias_tile<T>(W1, sprev, W2t, v0, V, rank, 8 * q, 8 * q + 8, acc);
+      // recompute the crossing chunk exactly as verify_final_stats did
+      const int vt = cstar / kChunksPerTile, q = cstar % kChunksPerTile;
+      const int v0 = vt * kTileV;
+      const int mrow = b % kTileM;
+      const int lane = tid & 63, c = lane & 31, h = lane >> 5;
+      const int c_lo = 16 * q, c_hi = 16 * q + 16;
+      const bool mine = tid < kWave && h == row_half(mrow) && c >= c_lo && c < c_hi;
+      const int vb = v0 + 4 * c;
+      const int prev = residual
+          ? clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1], V, nullptr)
+          : -1;
+      raw4_t<T> traw = raw4_t<T>{}, uraw = raw4_t<T>{};
+      if (mine && vb < V) {
+        traw = load4_raw(target + sk * V + vb);
+        if (residual) uraw = load4_raw(U + ((size_t)b * gamma + slot) * V + vb);
+      }
+      f32x16_t acc[kSub];
+      if (residual) {
+        if constexpr (bf) {
+          stage_w2_rows(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s, kChunk * q,
+                        kChunk);
+          bf16x8_t afrag[KS];
+          if (tid < kWave)
+            load_afrag<KS>(reinterpret_cast<const uint16_t*>(W1), c == mrow ? prev : -1, afrag);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+          if (tid < kWave) bias_tile_lds<KS>(afrag, w2s, c_lo, c_hi, acc);
+        } else {
+          if (tid < kWave)
+            bias_tile_f32(reinterpret_cast<const float*>(W1), c == mrow ? prev : -1,
+                          reinterpret_cast<const float*>(W2t), v0, V, rank, c_lo, c_hi, acc);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) acc[t] = f32x16_t{};
+      }
+      if (mine) {
+        const int jm = row_elem(mrow);
+        const float it = 1.f / Tb;
+        const float M = ws.rM[sk], LZ = ws.rLZ[sk];
+        float yt[4], yq[4] = {0.f, 0.f, 0.f, 0.f}, r[4], p[4];
+        float mq = 0.f, lzq = 0.f;
+        if (vb < V) {
+          unpack4(traw, yt);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) yt[t] *= it;
+          if (residual) {
+            unpack4(uraw, yq);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) yq[t] = (yq[t] + acc[t][jm]) * it;
+            mq = row_max[(size_t)b * gamma + slot];
+            lzq = row_logZ[(size_t)b * gamma + slot];
+          }
+          final_weights(yt, yq, M, LZ, mq, lzq, residual, r, p);
         } else {
 #pragma unroll
-          for (int t = 0; t < 8; ++t) acc[t] = f32x16_t{};
+          for (int t = 0; t < 4; ++t) { r[t] = 0.f; p[t] = 0.f; }
         }
-        const int hm = (mrow >> 2) & 1;
-        const int jm = 4 * (mrow >> 3) + (mrow & 3);
-        if (h == hm && c >= 8 * q && c < 8 * q + 8) {
-          const int vb = v0 + 8 * c;
-          const float it = 1.f / Tb;
-          const float M = ws.rM[sk], LZ = ws.rLZ[sk];
-          float yt[8], yq[8], r[8], p[8];
-          float mq = 0.f, lzq = 0.f;
-          if (vb < V) {
-            load8_f32(target + sk * V + vb, yt);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) yt[t] *= it;
-            if (residual) {
-              load8_f32(U + ((size_t)b * gamma + slot) * V + vb, yq);
-#pragma unroll
-              for (int t = 0; t < 8; ++t) yq[t] = (yq[t] + acc[t][jm]) * it;
-              mq = row_max[(size_t)b * gamma + slot];
-              lzq = row_logZ[(size_t)b * gamma + slot];
-            }
-            final_weights(yt, yq, M, LZ, mq, lzq, residual, r, p);
-          } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) { r[t] = 0.f; p[t] = 0.f; }
-          }
-#pragma unroll
-          for (int t = 0; t < 8; ++t) se[(c - 8 * q) * 8 + t] = use_p ? p[t] : r[t];
-        }
+        for (int t = 0; t < 4; ++t) se[(c - c_lo) * kSub + t] = use_p ? p[t] : r[t];
       }
       __syncthreads();
       if (tid == 0) {
@@ -407,7 +459,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
           if (e > 0.0 && rr < run) { pick = i; break; }
         }
         if (pick < 0) pick = lastp < 0 ? 0 : lastp;
-        s_pick = vt * kTileV + q * kChunk + pick;
+        s_pick = v0 + q * kChunk + pick;
       }
       __syncthreads();
       y = s_pick;
@@ -435,7 +487,7 @@ size_t verify_workspace_bytes(int B, int gamma, int V, int rank, int dtype) {
          2 * align256((size_t)B * gamma * 4) + 2 * align256((size_t)B * nC * 4);
 }
 
-template <typename T>
+template <typename T, int KS>
 static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target, const T* U,
                               const T* W1, const T* W2t, const int32_t* anchor,
                               const int32_t* tokens, const float* q_tok, const float* row_max,
@@ -445,24 +497,22 @@ static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target
                               hipStream_t stream) {
   VerifyWs ws = carve(wsp, B, gamma, V);
   {
-  TraceScope t0("verify_init_kernel", stream);
-  verify_init_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(B, ws.first_rej);
+    TraceScope t0("verify_init_kernel", stream);
+    verify_init_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(B, ws.first_rej);
   }
   {
-  TraceScope t1("verify_rows_kernel", stream);
-  verify_rows_kernel<T><<<dim3(B * (gamma + 1)), dim3(256), 0, stream>>>(
-      B, gamma, V, target, tokens, q_tok, temperature, uniforms, ell, ws, status);
+    TraceScope t1("verify_rows_kernel", stream);
+    verify_rows_kernel<T><<<dim3(B * (gamma + 1)), dim3(256), 0, stream>>>(
+        B, gamma, V, target, tokens, q_tok, temperature, uniforms, ell, ws, status);
   }
-  const int nRB = (B + kTileM - 1) / kTileM;
-  const int tasks = n_tiles(V) * nRB;
   {
-  TraceScope t2("verify_final_stats_kernel", stream);
-  verify_final_stats_kernel<T><<<dim3((tasks + 3) / 4), dim3(256), 0, stream>>>(
-      B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature, ell,
-      ws, status);
+    TraceScope t2("verify_final_stats_kernel", stream);
+    verify_final_stats_kernel<T, KS><<<dim3(n_tiles(V)), dim3(256), 0, stream>>>(
+        B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
+        ell, ws, status);
   }
   TraceScope t3("verify_finish_kernel", stream);
-  verify_finish_kernel<T><<<dim3(B), dim3(256), 0, stream>>>(
+  verify_finish_kernel<T, KS><<<dim3(B), dim3(256), 0, stream>>>(
       B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
       uniforms, ell, ws, out_tokens, n_accepted, ratio, status);
   return hipGetLastError();
@@ -474,17 +524,28 @@ hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const voi
                          const float* row_logZ, const float* temperature, const float* uniforms,
                          const int32_t* ell, int32_t* out_tokens, int32_t* n_accepted,
                          float* ratio, int32_t* status, void* ws, hipStream_t stream) {
-  if (dtype == DSPARK_BF16)
-    return verify_impl<uint16_t>(
-        B, gamma, V, rank, static_cast<const uint16_t*>(target), static_cast<const uint16_t*>(U),
-        static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), anchor, tokens, q_tok,
-        row_max, row_logZ, temperature, uniforms, ell, out_tokens, n_accepted, ratio, status, ws,
-        stream);
-  return verify_impl<float>(B, gamma, V, rank, static_cast<const float*>(target),
-                            static_cast<const float*>(U), static_cast<const float*>(W1),
-                            static_cast<const float*>(W2t), anchor, tokens, q_tok, row_max,
-                            row_logZ, temperature, uniforms, ell, out_tokens, n_accepted, ratio,
-                            status, ws, stream);
+  if (dtype == DSPARK_BF16) {
+    auto* tg = static_cast<const uint16_t*>(target);
+    auto* u = static_cast<const uint16_t*>(U);
+    auto* w1 = static_cast<const uint16_t*>(W1);
+    auto* w2 = static_cast<const uint16_t*>(W2t);
+#define DSPARK_VERIFY_KS(KS)                                                                  \
+  return verify_impl<uint16_t, KS>(B, gamma, V, rank, tg, u, w1, w2, anchor, tokens, q_tok,    \
+                                   row_max, row_logZ, temperature, uniforms, ell, out_tokens,  \
+                                   n_accepted, ratio, status, ws, stream)
+    switch (rank) {
+      case 32: DSPARK_VERIFY_KS(2);
+      case 64: DSPARK_VERIFY_KS(4);
+      case 128: DSPARK_VERIFY_KS(8);
+      default: DSPARK_VERIFY_KS(16);
+    }
+#undef DSPARK_VERIFY_KS
+  }
+  return verify_impl<float, 1>(B, gamma, V, rank, static_cast<const float*>(target),
+                               static_cast<const float*>(U), static_cast<const float*>(W1),
+                               static_cast<const float*>(W2t), anchor, tokens, q_tok, row_max,
+                               row_logZ, temperature, uniforms, ell, out_tokens, n_accepted, ratio,
+                               status, ws, stream);
 }
 
 }  // namespace dspark

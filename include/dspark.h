@@ -29,8 +29,9 @@
  *    W2t, hidden): DSPARK_BF16 (bit patterns, round-to-nearest-even) or
  *    DSPARK_F32.  Accumulation is fp32 (bf16 inputs use MFMA), cross-tile
  *    sums and cumulative sums are fp64.
- *  - Shapes: V % 8 == 0, rank % 32 == 0 with 32 <= rank <= 512,
- *    H % 8 == 0, 1 <= gamma <= 64, B >= 1.
+ *  - Shapes: V % 8 == 0; rank in {32, 64, 128, 256} for bf16 (the matrix-
+ *    core path stages 128 x rank tiles of W2t in LDS), any multiple of 32
+ *    in [32, 512] for fp32; H % 8 == 0; 1 <= gamma <= 64; B >= 1.
  *  - Positions are 0-based: draft position k (0..gamma-1) is the pages'
  *    x_{k+1}.
  *  - uniforms [B, gamma+1, 2] fp32 in [0,1): uniforms[b,k,0] draws draft
@@ -131,6 +132,9 @@ int dspark_confidence(int B, int gamma, int H, int V, int rank, int dtype,
  *     for each candidate in rank order: stop if Bt+1 >= sps_len or
  *       sps[Bt+1] <= 0; tau' = tau + a; Theta' = tau'*sps[Bt+1];
  *       admit iff Theta' > Theta (strict rise), else stop.
+ *     tau is the exact sum of R and the admitted survivals rounded once to
+ *     fp64 (double-double prefix sums on the device), so the result does
+ *     not depend on a summation order.
  *     ell[r] = number of admitted positions of request r (always a prefix)
  * in : conf [R,gamma] fp32 (NaN / out of [0,1] clamped and flagged);
  *      sps [sps_len] fp64, steps per second at target batch Bt (entry Bt)

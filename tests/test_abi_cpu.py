@@ -36,9 +36,9 @@ def test_status_strings_and_version(lib):
 
 
 def test_workspace_queries(lib):
-    # per-tile max + argmax and per-64-entry chunk sums, 256-byte aligned
-    nT = (151936 + 255) // 256
-    expect = 2 * ((128 * nT * 4 + 255) // 256 * 256) + (128 * nT * 4 * 4 + 255) // 256 * 256
+    # per-128-entry-tile max + argmax and per-64-entry chunk sums, 256-byte aligned
+    nT = (151936 + 127) // 128
+    expect = 2 * ((128 * nT * 4 + 255) // 256 * 256) + (128 * nT * 2 * 4 + 255) // 256 * 256
     assert dv.dspark_draft_block_workspace(128, 15, 151936, 256, 1) == expect
     assert dv.dspark_draft_block_workspace(128, 15, 151937, 256, 1) == 0  # invalid V
     assert dv.dspark_verify_workspace(4, 5, 1024, 32, 0) > 0
@@ -54,6 +54,7 @@ def test_host_validation_rejects_before_launch(lib):
     assert lib.dspark_draft_block(4, 5, 1024, 32, 9, *P, None, 0, None) == -2
     assert lib.dspark_draft_block(4, 5, 1020, 32, 0, *P, None, 0, None) == -1
     assert lib.dspark_draft_block(4, 5, 1024, 48, 0, *P, None, 0, None) == -1
+    assert lib.dspark_draft_block(4, 5, 1024, 96, 1, *P, None, 0, None) == -1  # bf16 rank
     fake = 4096  # aligned, never dereferenced: validation fails first
     assert lib.dspark_draft_block(4, 5, 1024, 32, 0, *([fake] * 11), fake, 16, None) == -4
     assert lib.dspark_draft_block(4, 5, 1024, 32, 0, *([fake + 8] + [fake] * 10), fake, 1 << 30,
