@@ -8,7 +8,8 @@ HBM.  Prints ONE JSON line.
                     [--no-cpu-baseline] [--cpu-requests N]
 
 value      = B * gamma / (time per step), drafted-and-verified positions/s
-roofline   = the dominant kernel (draft_stats_kernel): algorithmic bytes per
+roofline   = the draft kernel (pdraft_kernel, or draft_stats_kernel where the
+             per-position launches run): algorithmic bytes per
              launch / its mean duration, timed with per-launch HIP events in a
              second pass over the same K steps (events are kept out of the
              pass that gives `value`)
@@ -38,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--draft-path", type=int, default=0,
+                    help="dspark_set_draft_path value (0 = automatic)")
     ap.add_argument("--cpu-requests", type=int, default=0,
                     help="requests in the oracle sample (0 = sized for ~15 s)")
     return ap.parse_args()
@@ -54,14 +57,22 @@ def algorithmic_bytes(wl, ell, n_acc):
             + 4 * B * (g + 1) * 2 + 4 * B * g * 4 + 4 * B * (g + 1))
 
 
-def draft_stats_bytes(wl):
-    """Algorithmic bytes of one draft_stats_kernel launch (one draft position)."""
+def draft_kernel_bytes(wl, kernel):
+    """Algorithmic bytes of one launch of the draft kernel `kernel`.
+
+    pdraft_kernel (one launch per block of gamma positions): every U row, the
+    W2 factor once, the gathered W1 rows, the tile statistics written and the
+    per-position outputs.  draft_stats_kernel (one launch per position): that
+    position's U rows, its gathered W1 rows, W2 once per launch, its tile
+    statistics.
+    """
     e = 2 if wl.dtype == "bf16" else 4
-    nT = (wl.V + 127) // 128
-    return (e * wl.B * wl.V              # the position's U rows
-            + e * wl.B * wl.rank         # gathered W1 rows
-            + e * wl.rank * wl.V / wl.gamma  # W2 read once per step, shared by gamma launches
-            + 4 * wl.B * nT * 4)         # tile max/argmax + 2 chunk sums per tile written
+    nT = (wl.V + 63) // 64
+    B, g, V, r = wl.B, wl.gamma, wl.V, wl.rank
+    if kernel == "pdraft_kernel":
+        return (e * B * g * V + e * r * V + e * B * g * r + 3 * 4 * B * g * nT
+                + 4 * B * g * 4)
+    return e * B * V + e * B * r + e * r * V + 3 * 4 * B * nT
 
 
 def cpu_baseline(cfg, n_req):
@@ -110,6 +121,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dv.load()
+    dv.dspark_set_draft_path(args.draft_path)
     cfg = args.config
     spec = SPECS[cfg]
     t0 = time.perf_counter()
@@ -144,8 +156,9 @@ def main():
     dom = max(tr, key=lambda k: tr[k][1])
     kern_ms = {k: v[1] / v[0] for k, v in tr.items()}
     per_step_ms = {k: v[1] / args.steps for k, v in tr.items()}
-    stats_bytes = draft_stats_bytes(wl)
-    avg_s = kern_ms["draft_stats_kernel"] / 1e3
+    draft_kernel = "pdraft_kernel" if "pdraft_kernel" in kern_ms else "draft_stats_kernel"
+    stats_bytes = draft_kernel_bytes(wl, draft_kernel)
+    avg_s = kern_ms[draft_kernel] / 1e3
     achieved = stats_bytes / avg_s / 1e9
     bytes_step = algorithmic_bytes(wl, ell, n_acc)
 
@@ -166,7 +179,7 @@ def main():
                                f"rank={wl.rank} H={wl.H} {wl.dtype}",
                    "B": wl.B, "gamma": wl.gamma, "V": wl.V, "rank": wl.rank, "H": wl.H,
                    "scheduler": bool(spec.scheduler), "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "draft_stats_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": draft_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "bytes_per_launch": stats_bytes,
                      "mean_launch_us": avg_s * 1e6},

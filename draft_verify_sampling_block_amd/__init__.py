@@ -23,14 +23,15 @@ __all__ = [
     "DsparkError", "lib_path", "load", "dspark_draft_block", "dspark_confidence",
     "dspark_schedule", "dspark_verify", "dspark_draft_block_workspace",
     "dspark_verify_workspace", "dspark_schedule_workspace", "exported_names", "header_names",
-    "dspark_trace_enable", "dspark_trace_summary",
+    "dspark_trace_enable", "dspark_trace_summary", "dspark_set_draft_path",
     "DSPARK_F32", "DSPARK_BF16", "DEV_FLAGS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "dspark.h")
 DSPARK_F32, DSPARK_BF16 = 0, 1
-DEV_FLAGS = {1: "BAD_TOKEN", 2: "NONFINITE", 4: "DEGENERATE", 8: "BAD_ELL", 16: "BAD_CONF"}
+DEV_FLAGS = {1: "BAD_TOKEN", 2: "NONFINITE", 4: "DEGENERATE", 8: "BAD_ELL", 16: "BAD_CONF",
+             32: "TIMEOUT"}
 
 
 class DsparkError(RuntimeError):
@@ -61,6 +62,7 @@ _SIGS = {
     "dspark_verify": (_I, [_I] * 5 + [_P] * 15 + [_P, _P, _SZ, _P]),
     "dspark_trace_enable": (_I, [_I]),
     "dspark_trace_summary": (_I, [ctypes.c_char_p, _SZ]),
+    "dspark_set_draft_path": (_I, [_I]),
 }
 
 
@@ -128,6 +130,14 @@ def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
 
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def dspark_set_draft_path(path: int) -> int:
+    """0 automatic, 1 multi-launch, 2 persistent only; returns the old value."""
+    rc = load().dspark_set_draft_path(int(path))
+    if rc < 0:
+        _check(rc)
+    return rc
 
 
 def dspark_trace_enable(on: bool) -> None:

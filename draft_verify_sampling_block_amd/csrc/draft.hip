@@ -4,17 +4,23 @@
 // where prev is the token sampled at position k-1 (the anchor for k = 0);
 // positions are sampled left to right.  [weigao] part 2: rank-r factors.
 //
-// Per position k two launches:
-//   draft_stats_kernel   vocabulary-parallel: one work-group per 128-entry
-//                        vocabulary tile stages the tile's W2t rows in LDS
-//                        (DMA), and each wave takes 32-request blocks: bias
-//                        tile on the matrix cores, streamed base logits added,
-//                        per-tile max / argmax and per-64-entry-chunk sums of
-//                        exp(y - tile max) written out.
-//   draft_sample_kernel  request-parallel: combines the tile statistics in
-//                        fp64, finds the chunk where the cumulative mass
-//                        crosses u * Z, recomputes that one chunk
-//                        bit-identically, and picks the token.
+// Two implementations with identical results:
+//
+//  * persistent (bf16, rank <= 256, one work-group per compute unit, launched
+//    cooperatively so all work-groups are resident): each work-group owns a
+//    fixed set of 64-entry vocabulary tiles for the whole block; the W2t
+//    rows of those tiles stay resident (8 tiles in registers, one per wave,
+//    the rest in LDS) across all gamma positions, so W2 is read from memory
+//    once per call.  Per position: gather the W1 rows of the previous
+//    tokens into LDS, compute every (tile, 32-request block) on the matrix
+//    cores with the streamed base logits, publish per-tile statistics, then
+//    the work-group that owns request b draws token b as soon as every
+//    work-group has published (flags in memory, bounded spins), and
+//    publishes it for the next position.
+//
+//  * multi-launch (any dtype / fallback): per position one
+//    vocabulary-parallel launch (draft_stats_kernel) and one request-parallel
+//    launch (draft_sample_kernel) doing the same two steps.
 #include <type_traits>
 
 #include "dspark_common.hpp"
@@ -26,111 +32,321 @@ namespace dspark {
 template <typename T>
 constexpr bool kIsBf16 = std::is_same<T, uint16_t>::value;
 
-// Per-lane state of one 32-request block: A operand, streamed logits and
-// the lane's own row token / inverse temperature.
-template <typename T, int KS>
-struct BlockIn {
-  bf16x8_t afrag[KS];
-  raw4_t<T> up[16];
-  int tok;
-  float itc;
+// ---------------------------------------------------------------------------
+// Shared pieces
+// ---------------------------------------------------------------------------
+
+struct TileStats {
+  float* max;     // [B][nT] max over the tile of y' = z + bias (unscaled logits)
+  int32_t* arg;   // [B][nT] lowest vocabulary index attaining it (greedy rows)
+  float* sum;     // [B][nT] sum over the tile of exp((y' - max) / T)
 };
 
-template <typename T, int KS>
-__device__ inline void block_prefetch(BlockIn<T, KS>& in, int rb, int B, int gamma, int V, int k,
-                                      int vt, const T* __restrict__ U, const T* __restrict__ W1,
-                                      const int32_t* __restrict__ prev_src, int prev_stride,
-                                      const float* __restrict__ temperature, int32_t* status) {
-  const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
-  const int bc = rb * kTileM + c;
-  in.tok = -1;
-  in.itc = 0.f;
-  if (bc < B) {
-    in.tok = clamp_token(prev_src[(size_t)bc * prev_stride], V, h == 0 ? status : nullptr);
-    const float Tb = temperature[bc];
-    in.itc = (Tb > 0.f) ? 1.f / Tb : 0.f;
-  }
-  if constexpr (kIsBf16<T>) load_afrag<KS>(W1, in.tok, in.afrag);
-  const int vb = vt * kTileV + 4 * c;
+// inverse temperature of a request; 0 marks greedy
+__device__ inline float inv_temp(float T) { return (T > 0.f) ? 1.f / T : 0.f; }
+
+// Summand of the tile mass: exp((y' - m') / T) as 2^(y' ce - m' ce) with
+// ce = log2(e) / T and mc = m' ce.  The statistics pass and the sampler's
+// recompute evaluate exactly this expression.
+__device__ inline float tile_term(float yp, float ce, float mc) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(yp, ce, -mc));
+}
+
+// Epilogue of one block-tile for this lane's request b (column c): acc holds
+// y' = base logit + bias (-inf past V); computes the tile max / lowest
+// argmax / exp-sum, combined over the two half-waves, and the h = 0 lane
+// stores them with device-coherent stores.  `it` is the lane's inverse
+// temperature (0 = greedy); `any_greedy` is wave-uniform.
+__device__ inline void block_tile_epilogue(const f32x16_t acc[kSub], int b, int B, int vt,
+                                           int nT, float it, bool any_greedy,
+                                           const TileStats& ts) {
+  const int h = (threadIdx.x & 63) >> 5;
+  float mx = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int b = rb * kTileM + acc_row(j, h);
-    in.up[j] = (b < B && vb < V) ? load4_raw(U + ((size_t)b * gamma + k) * V + vb) : raw4_t<T>{};
+  for (int t = 0; t < kSub; ++t) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, acc[t][j]);
+  }
+  float lo, hi;
+  half_pair(mx, lo, hi);
+  mx = fmaxf(lo, hi);
+  int arg = 0x7fffffff;
+  if (any_greedy) {
+    int off = 0x7fffffff;   // lowest in-lane offset 32t + j attaining the max
+#pragma unroll
+    for (int t = kSub - 1; t >= 0; --t) {
+#pragma unroll
+      for (int j = 15; j >= 0; --j) off = (acc[t][j] == mx) ? 32 * t + j : off;
+    }
+    arg = off == 0x7fffffff ? off : vt * kTileV + 16 * h + off;
+    int alo, ahi;
+    half_pair(arg, alo, ahi);
+    arg = min(alo, ahi);
+  }
+  const float ce = it * kLog2e, mc = mx * ce;
+  float s = 0.f;
+#pragma unroll
+  for (int t = 0; t < kSub; ++t) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += tile_term(acc[t][j], ce, mc);
+  }
+  half_pair(s, lo, hi);
+  s = lo + hi;
+  if (b < B && h == 0) {
+    const size_t i = (size_t)b * nT + vt;
+    st_dev(ts.max + i, mx);
+    st_dev(ts.arg + i, arg);
+    st_dev(ts.sum + i, s);
   }
 }
+
+// Shared-memory state of the per-request sampler (block-wide).
+struct SampShared {
+  double red[8];
+  double before, scale;
+  int tile;
+  float se[kTileV];
+  __attribute__((aligned(16))) char arow[kMaxKSteps * 32];  // W1 row of the request (bf16)
+};
+// LDS the sampler needs besides SampShared: the crossing tile's W2t rows,
+// then a copy of the request's tile statistics
+constexpr int kSampScratchBytes = kLdsTileBytes + 2 * kMaxTiles * 4;
+
+// Draw draft token k of request b from the tile statistics (all threads of
+// the work-group call this).  `scratch` is kSampScratchBytes of LDS.
+// Writes tokens (device-coherent store) and q_tok/row_max/row_logZ.
+template <typename T, int KS>
+__device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, int prev,
+                               const T* __restrict__ U, const T* __restrict__ W1,
+                               const T* __restrict__ W2t, const float* __restrict__ temperature,
+                               const float* __restrict__ uniforms, const TileStats& ts,
+                               int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
+                               int32_t* status, char* scratch, SampShared& sh) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int nT = n_tiles(V);
+  float* cm = reinterpret_cast<float*>(scratch + kLdsTileBytes);  // tile maxima
+  float* cs = cm + kMaxTiles;                                      // tile sums
+  const float* tm = ts.max + (size_t)b * nT;
+  const float* tsum = ts.sum + (size_t)b * nT;
+  const float Tb = temperature[b];
+  const bool greedy = !(Tb > 0.f);
+  const size_t out = (size_t)b * gamma + k;
+
+  // all loads of the statistics are issued before any is used (work-groups
+  // of >= 256 threads: kMaxTiles / 256 per thread at most)
+  constexpr int kPer = kMaxTiles / 256;
+  float xm[kPer], xs[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int t = tid + i * nthr;
+    xm[i] = -INFINITY;
+    xs[i] = 0.f;
+    if (t < nT) {
+      xm[i] = ld_dev(tm + t);
+      xs[i] = ld_dev(tsum + t);
+    }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int t = tid + i * nthr;
+    if (t < nT) {
+      cm[t] = xm[i];
+      cs[t] = xs[i];
+      m = fmaxf(m, xm[i]);
+    }
+  }
+  m = block_max(m, sh.red);   // its barriers also publish cm / cs
+
+  if (greedy) {
+    int a = 0x7fffffff;
+    for (int t = tid; t < nT; t += nthr)
+      if (cm[t] == m) a = min(a, ld_dev(ts.arg + (size_t)b * nT + t));
+    a = block_min_int(a, sh.red);
+    if (tid == 0) {
+      if (!(m == m) || a < 0 || a >= V) {  // NaN logits leave no argmax
+        flag(status, DSPARK_DEV_NONFINITE);
+        a = 0;
+      }
+      st_dev(tokens + out, a);
+      q_tok[out] = 1.f;
+      row_max[out] = m;
+      row_logZ[out] = 0.f;
+    }
+    __syncthreads();
+    return;
+  }
+
+  // mass of tile t relative to the row max: cs[t] * 2^((cm[t] - m) ce),
+  // factor in fp32, accumulation in fp64 over each thread's contiguous range
+  const float scale = 1.f / Tb;
+  const float ce = scale * kLog2e;
+  const int per = (nT + nthr - 1) / nthr;
+  const int c0 = min(nT, tid * per), c1 = min(nT, c0 + per);
+  double local = 0.0;
+  for (int t = c0; t < c1; ++t)
+    local += (double)cs[t] * (double)__builtin_amdgcn_exp2f((cm[t] - m) * ce);
+  double start, end;
+  const double Z = block_scan_interval(local, sh.red, &start, &end);
+  const double u = (double)uniforms[((size_t)b * (gamma + 1) + k) * 2 + 0];
+  const double target = u * Z;
+  const bool finite = isfinite(m) && isfinite(Z) && Z > 0.0;
+  const int last_pos = block_max_int(local > 0.0 ? tid : -1, sh.red);
+
+  if (tid == 0) sh.tile = -1;
+  __syncthreads();
+  if (finite && local > 0.0 &&
+      ((start <= target && target < end) || (tid == last_pos && target >= end))) {
+    double run = start, before = start, lastb = start;
+    int found = -1, lastt = -1;
+    for (int t = c0; t < c1; ++t) {
+      const double st = (double)cs[t] * (double)__builtin_amdgcn_exp2f((cm[t] - m) * ce);
+      if (st > 0.0) { lastt = t; lastb = run; }
+      if (st > 0.0 && target < run + st) { found = t; before = run; break; }
+      run += st;
+    }
+    if (found < 0) { found = lastt; before = lastb; }
+    sh.tile = found;
+    sh.before = before;
+    sh.scale = (double)__builtin_amdgcn_exp2f((cm[found] - m) * ce);
+  }
+  __syncthreads();
+  const int vt = sh.tile;
+  const float ms = m * scale;    // row max of the scaled logits
+  if (!finite || vt < 0) {
+    if (tid == 0) {
+      flag(status, DSPARK_DEV_NONFINITE);
+      st_dev(tokens + out, 0);
+      q_tok[out] = 0.f;
+      row_max[out] = ms;
+      row_logZ[out] = (float)log(Z);
+    }
+    __syncthreads();
+    return;
+  }
+  const float mc = cm[vt] * ce;
+  __syncthreads();   // cm / cs are dead from here: the tile rows may land
+
+  // recompute the crossing tile exactly as the statistics pass did: same
+  // operands, request b in its own column b % 32, one sub-tile at a time
+  const int v0 = vt * kTileV;
+  const int mrow = b % kTileM;
+  const int lane = tid & 63, c = lane & 31, h = lane >> 5;
+  const bool mine = tid < kWave && c == mrow;
+  const int rem = V - (v0 + 16 * h);   // usable entries: j < rem - 32t
+  URow<T> ur;
+  load_urow<T>(ur, U + out * V, v0, V, mine, U);
+  if constexpr (kIsBf16<T>) {
+    stage_tile(W2t, v0, V, rank, scratch);
+    if (tid < 2 * KS)
+      *reinterpret_cast<uint4*>(sh.arow + 16 * tid) =
+          *reinterpret_cast<const uint4*>(W1 + (size_t)prev * rank + 8 * tid);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid < kWave) {
+      const bf16x8_t zero = bf16x8_t{};
+      auto bfrag = [&](int ks) {
+        const bf16x8_t f = *reinterpret_cast<const bf16x8_t*>(sh.arow + 16 * (2 * ks + h));
+        return mine ? f : zero;
+      };
+      f32x16_t acc[kSub];
+      init_acc<T>(ur, rem, acc);
+      bias_tile_ldsA<KS>(bfrag, scratch, acc);
+      if (mine) {
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) {
+          float* se = sh.se + 32 * t + 16 * h;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) se[j] = tile_term(acc[t][j], ce, mc);
+        }
+      }
+    }
+  } else {
+    if (tid < kWave) {
+      f32x16_t acc[kSub];
+      init_acc<T>(ur, rem, acc);
+      bias_tile_f32(reinterpret_cast<const float*>(W1), mine ? prev : -1,
+                    reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
+      if (mine) {
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) {
+          float* se = sh.se + 32 * t + 16 * h;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) se[j] = tile_term(acc[t][j], ce, mc);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const double r = (target - sh.before) / sh.scale;
+    double run = 0.0;
+    int pick = -1, lastp = -1;
+    for (int i = 0; i < kTileV; ++i) {
+      const double e = (double)sh.se[i];
+      if (e > 0.0) lastp = i;
+      run += e;
+      if (e > 0.0 && r < run) { pick = i; break; }
+    }
+    if (pick < 0) pick = lastp < 0 ? 0 : lastp;
+    st_dev(tokens + out, v0 + pick);
+    q_tok[out] = (float)((double)sh.se[pick] * sh.scale / Z);
+    row_max[out] = ms;
+    row_logZ[out] = (float)log(Z);
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Multi-launch path
+// ---------------------------------------------------------------------------
 
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void draft_stats_kernel(
     int B, int gamma, int V, int rank, int k, const T* __restrict__ U, const T* __restrict__ W1,
     const T* __restrict__ W2t, const int32_t* __restrict__ prev_src, int prev_stride,
-    const float* __restrict__ temperature, float* __restrict__ tile_max,
-    int32_t* __restrict__ tile_arg, float* __restrict__ chunk_sum, int32_t* status) {
+    const float* __restrict__ temperature, TileStats ts, int32_t* status) {
   __shared__ __attribute__((aligned(16))) char w2s[kIsBf16<T> ? kLdsTileBytes : 16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int nRB = (B + kTileM - 1) / kTileM;
-  const int nT = n_tiles(V), nC = n_chunks(V);
+  const int nT = n_tiles(V);
   const int vt = blockIdx.x, v0 = vt * kTileV;
 
-  if constexpr (kIsBf16<T>) stage_w2_rows(W2t, v0, V, rank, w2s, 0, kTileV);
-  BlockIn<T, KS> in;
+  if constexpr (kIsBf16<T>) stage_tile(W2t, v0, V, rank, w2s);
   int rb = wave;
-  if (rb < nRB)
-    block_prefetch<T, KS>(in, rb, B, gamma, V, k, vt, U, W1, prev_src, prev_stride, temperature,
-                          status);
+  bf16x8_t bfrag[KS];
+  URow<T> ur;
+  int tok = -1;
+  float it = 0.f;
+  auto setup = [&](int blk) {
+    const int b = blk * kTileM + c;
+    tok = -1;
+    it = 0.f;
+    if (b < B) {
+      tok = clamp_token(prev_src[(size_t)b * prev_stride], V, h == 0 ? status : nullptr);
+      it = inv_temp(temperature[b]);
+    }
+    if constexpr (kIsBf16<T>) load_bfrag<KS>(W1, tok, bfrag);
+    load_urow<T>(ur, U + ((size_t)b * gamma + k) * V, v0, V, b < B, U);
+  };
+  if (rb < nRB) setup(rb);
   if constexpr (kIsBf16<T>) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-
-  const int vb = v0 + 4 * c;
-  const bool vok = vb < V;
+  const int rem = V - (v0 + 16 * h);
   while (rb < nRB) {
     f32x16_t acc[kSub];
+    init_acc<T>(ur, rem, acc);
     if constexpr (kIsBf16<T>)
-      bias_tile_lds<KS>(in.afrag, w2s, 0, 32, acc);
+      bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
     else
-      bias_tile_f32(reinterpret_cast<const float*>(W1), in.tok, reinterpret_cast<const float*>(W2t),
-                    v0, V, rank, 0, 32, acc);
-    // does any row of this block sample greedily (needs the argmax)?
-    const bool any_greedy = __ballot((rb * kTileM + c < B) && !(in.itc > 0.f)) != 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int m = acc_row(j, h);
-      const int b = rb * kTileM + m;
-      const bool bok = b < B;
-      const float it = __shfl(in.itc, m, kWave);
-      const float scale = (it > 0.f) ? it : 1.f;
-      float y[4];
-      unpack4(in.up[j], y);
-#pragma unroll
-      for (int t = 0; t < kSub; ++t) y[t] = (bok && vok) ? (y[t] + acc[t][j]) * scale : -INFINITY;
-      float mx = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-      int arg = 0x7fffffff;
-      if (any_greedy) {
-#pragma unroll
-        for (int t = kSub - 1; t >= 0; --t)
-          if (y[t] == mx) arg = vb + t;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) arg = min(arg, __shfl_xor(arg, o, kWave));
-      }
-      float s = 0.f;
-#pragma unroll
-      for (int t = 0; t < kSub; ++t) s += __expf(y[t] - mx);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, kWave);
-      if (bok) {
-        if (c == 0) {
-          tile_max[(size_t)b * nT + vt] = mx;
-          tile_arg[(size_t)b * nT + vt] = arg;
-        }
-        if ((c & 15) == 0) chunk_sum[(size_t)b * nC + vt * kChunksPerTile + (c >> 4)] = s;
-      }
-    }
+      bias_tile_f32(reinterpret_cast<const float*>(W1), tok, reinterpret_cast<const float*>(W2t),
+                    v0, V, rank, acc);
+    const int b = rb * kTileM + c;
+    const bool any_greedy = __ballot((b < B) && !(it > 0.f)) != 0;
+    block_tile_epilogue(acc, b, B, vt, nT, it, any_greedy, ts);
     rb += 4;
-    if (rb < nRB)
-      block_prefetch<T, KS>(in, rb, B, gamma, V, k, vt, U, W1, prev_src, prev_stride,
-                            temperature, status);
+    if (rb < nRB) setup(rb);
   }
 }
 
@@ -138,190 +354,397 @@ template <typename T, int KS>
 __global__ __launch_bounds__(256) void draft_sample_kernel(
     int B, int gamma, int V, int rank, int k, const T* __restrict__ U, const T* __restrict__ W1,
     const T* __restrict__ W2t, const int32_t* __restrict__ prev_src, int prev_stride,
-    const float* __restrict__ temperature, const float* __restrict__ uniforms,
-    const float* __restrict__ tile_max, const int32_t* __restrict__ tile_arg,
-    const float* __restrict__ chunk_sum, int32_t* __restrict__ tokens, float* __restrict__ q_tok,
-    float* __restrict__ row_max, float* __restrict__ row_logZ, int32_t* status) {
-  __shared__ __attribute__((aligned(16))) char w2s[kIsBf16<T> ? kLdsTileBytes : 16];
-  __shared__ double red[8];
-  __shared__ int s_chunk;
-  __shared__ double s_before, s_scale;
-  __shared__ float se[kChunk];
-
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int nT = n_tiles(V), nC = n_chunks(V);
-  const float* tm = tile_max + (size_t)b * nT;
-  const float Tb = temperature[b];
-  const bool greedy = !(Tb > 0.f);
-  const size_t out = (size_t)b * gamma + k;
-
-  float m = -INFINITY;
-  for (int t = tid; t < nT; t += blockDim.x) m = fmaxf(m, tm[t]);
-  m = block_max(m, red);
-
-  if (greedy) {
-    int a = 0x7fffffff;
-    for (int t = tid; t < nT; t += blockDim.x)
-      if (tm[t] == m) a = min(a, tile_arg[(size_t)b * nT + t]);
-    a = block_min_int(a, red);
-    if (tid == 0) {
-      if (!(m == m) || a < 0 || a >= V) {  // NaN logits leave no argmax
-        flag(status, DSPARK_DEV_NONFINITE);
-        a = 0;
-      }
-      tokens[out] = a;
-      q_tok[out] = 1.f;
-      row_max[out] = m;
-      row_logZ[out] = 0.f;
-    }
-    return;
-  }
-
-  // fp64 mass of each thread's contiguous range of chunks
-  const int per = (nC + blockDim.x - 1) / blockDim.x;
-  const int c0 = min(nC, tid * per), c1 = min(nC, c0 + per);
-  const float* cs = chunk_sum + (size_t)b * nC;
-  const double md = (double)m;
-  double local = 0.0;
-  {
-    int tcur = -1;
-    double sc_t = 0.0;
-    for (int cc = c0; cc < c1; ++cc) {
-      const int t = cc / kChunksPerTile;
-      if (t != tcur) { tcur = t; sc_t = exp((double)tm[t] - md); }
-      local += (double)cs[cc] * sc_t;
-    }
-  }
-  double start, end;
-  const double Z = block_scan_interval(local, red, &start, &end);
-  const double u = (double)uniforms[((size_t)b * (gamma + 1) + k) * 2 + 0];
-  const double target = u * Z;
-  const bool finite = isfinite(m) && isfinite(Z) && Z > 0.0;
-  const int last_pos = block_max_int(local > 0.0 ? tid : -1, red);
-
-  if (tid == 0) s_chunk = -1;
-  __syncthreads();
-  if (finite && local > 0.0 &&
-      ((start <= target && target < end) || (tid == last_pos && target >= end))) {
-    double run = start;
-    int found = -1, lastc = -1;
-    double before = start, lastb = start;
-    int tcur = -1;
-    double sc_t = 0.0;
-    for (int cc = c0; cc < c1; ++cc) {
-      const int t = cc / kChunksPerTile;
-      if (t != tcur) { tcur = t; sc_t = exp((double)tm[t] - md); }
-      const double sc = (double)cs[cc] * sc_t;
-      if (sc > 0.0) { lastc = cc; lastb = run; }
-      if (sc > 0.0 && target < run + sc) { found = cc; before = run; break; }
-      run += sc;
-    }
-    if (found < 0) { found = lastc; before = lastb; }
-    s_chunk = found;
-    s_before = before;
-    s_scale = exp((double)tm[found / kChunksPerTile] - md);
-  }
-  __syncthreads();
-  const int cstar = s_chunk;
-  if (!finite || cstar < 0) {
-    if (tid == 0) {
-      flag(status, DSPARK_DEV_NONFINITE);
-      tokens[out] = 0;
-      q_tok[out] = 0.f;
-      row_max[out] = m;
-      row_logZ[out] = (float)log(Z);
-    }
-    return;
-  }
-
-  // recompute the crossing chunk exactly as draft_stats_kernel computed it
-  const int vt = cstar / kChunksPerTile, q = cstar % kChunksPerTile;
-  const int v0 = vt * kTileV;
-  const int mrow = b % kTileM;
+    const float* __restrict__ temperature, const float* __restrict__ uniforms, TileStats ts,
+    int32_t* __restrict__ tokens, float* __restrict__ q_tok, float* __restrict__ row_max,
+    float* __restrict__ row_logZ, int32_t* status) {
+  __shared__ __attribute__((aligned(16))) char scratch[kSampScratchBytes];
+  __shared__ SampShared sh;
+  const int b = blockIdx.x;
   const int prev = clamp_token(prev_src[(size_t)b * prev_stride], V, nullptr);
-  const int lane = tid & 63, c = lane & 31, h = lane >> 5;
-  const int c_lo = 16 * q, c_hi = 16 * q + 16;
-  const bool mine = tid < kWave && h == row_half(mrow) && c >= c_lo && c < c_hi;
-  const int vb = v0 + 4 * c;
-  raw4_t<T> uraw = raw4_t<T>{};
-  if (mine && vb < V) uraw = load4_raw(U + out * V + vb);
-  f32x16_t acc[kSub];
-  if constexpr (kIsBf16<T>) {
-    stage_w2_rows(W2t, v0, V, rank, w2s, kChunk * q, kChunk);
-    bf16x8_t afrag[KS];
-    if (tid < kWave) load_afrag<KS>(W1, c == mrow ? prev : -1, afrag);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid < kWave) bias_tile_lds<KS>(afrag, w2s, c_lo, c_hi, acc);
-  } else {
-    if (tid < kWave)
-      bias_tile_f32(reinterpret_cast<const float*>(W1), c == mrow ? prev : -1,
-                    reinterpret_cast<const float*>(W2t), v0, V, rank, c_lo, c_hi, acc);
-  }
-  if (mine) {
-    const int jm = row_elem(mrow);
-    const float scale = 1.f / Tb;
-    const float tmax = tm[vt];
-    float y[4];
-    unpack4(uraw, y);
-#pragma unroll
-    for (int t = 0; t < kSub; ++t) {
-      const float yy = (vb < V) ? (y[t] + acc[t][jm]) * scale : -INFINITY;
-      se[(c - c_lo) * kSub + t] = __expf(yy - tmax);
+  sample_request<T, KS>(b, k, B, gamma, V, rank, prev, U, W1, W2t, temperature, uniforms, ts,
+                        tokens, q_tok, row_max, row_logZ, status, scratch, sh);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent path (bf16)
+// ---------------------------------------------------------------------------
+
+constexpr int kPdRegTiles = 8;              // resident tiles in registers per group
+constexpr int kPdLdsTiles = 2;              // extra resident tiles in LDS
+constexpr int kPdMaxRows = 128;             // W1 rows gathered per chunk
+constexpr int kPdFlagStride = 32;           // 128-byte spacing of per-group flags
+constexpr int kPdMaxGroups = 4096;
+constexpr int kPdRowBytes = kPdMaxRows * kMaxKSteps * 2 * 16;   // 64 KB
+static_assert(kPdRowBytes >= kSampScratchBytes, "the sampler reuses the W1 row area");
+
+struct PdArgs {
+  int B, gamma, V, rank, P;
+  const uint16_t* U;
+  const uint16_t* W1;
+  const uint16_t* W2t;
+  const int32_t* anchor;
+  const float* temperature;
+  const float* uniforms;
+  int32_t* tokens;
+  float* q_tok;
+  float* row_max;
+  float* row_logZ;
+  int32_t* status;
+  TileStats ts;
+  uint32_t* stats_flag;  // [P * kPdFlagStride]: positions whose statistics group p published
+  uint32_t* tok_flag;    // [B]: positions whose token request b published
+  long long spin_cap;    // wall-clock ticks a wait may last
+};
+
+__device__ inline uint32_t ld_flag(const uint32_t* p) { return ld_dev(p); }
+__device__ inline void st_flag(uint32_t* p, uint32_t v) { st_dev(p, v); }
+
+// Wave 0 waits until flags[i*stride] >= want for all i < n; then the group
+// synchronises.  The wait is bounded: past `cap_ticks` of the device wall
+// clock it raises DSPARK_DEV_TIMEOUT and gives up, and any group that sees
+// that flag already raised gives up at once, so a kernel whose groups cannot
+// all make progress still drains.  All threads of the work-group call it.
+__device__ inline void wait_flags(const uint32_t* flags, int n, int stride, uint32_t want,
+                                  long long cap_ticks, int32_t* status) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const long long t0 = wall_clock64();
+    for (int it = 0;; ++it) {
+      bool ok = true;
+      for (int i = lane; i < n; i += kWave) ok &= ld_flag(flags + (size_t)i * stride) >= want;
+      if (__all(ok)) break;
+      if ((it & 15) == 15) {
+        const bool late = wall_clock64() - t0 > cap_ticks;
+        const bool gave_up = status && (ld_dev(status) & DSPARK_DEV_TIMEOUT);
+        if (late || gave_up) {
+          if (late && lane == 0) flag(status, DSPARK_DEV_TIMEOUT);
+          break;
+        }
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    const double r = (target - s_before) / s_scale;
-    double run = 0.0;
-    int pick = -1, lastp = -1;
-    for (int i = 0; i < kChunk; ++i) {
-      const double e = (double)se[i];
-      if (e > 0.0) lastp = i;
-      run += e;
-      if (e > 0.0 && r < run) { pick = i; break; }
+}
+
+// Every wave waits for its own stores to complete, then the group
+// synchronises; thread 0 may then raise a flag.
+__device__ inline void stores_done_group() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// NW waves per group; each wave holds R = kPdRegTiles / NW W2t tiles in
+// registers (NW = 8: two waves per SIMD, 128 registers of tile each at rank
+// 256; NW = 4: one wave per SIMD with two tiles, the tiles and the
+// accumulators split over the architectural and accumulation registers).
+template <int KS, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
+  constexpr int nq = 2 * KS;
+  constexpr int R = kPdRegTiles / NW;
+  __shared__ __attribute__((aligned(16))) char ldsL[kPdLdsTiles * kLdsTileBytes];
+  __shared__ __attribute__((aligned(16))) char ldsA[kPdRowBytes];
+  __shared__ int s_tok[kPdMaxRows];
+  __shared__ float s_it[kPdMaxRows];   // inverse temperatures of the chunk
+  __shared__ SampShared sh;
+
+  const int p = blockIdx.x, P = a.P;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5;
+  const int B = a.B, V = a.V, gamma = a.gamma;
+  const int nT = n_tiles(V);
+
+  // resident W2t tiles: register tile i of wave w is p + P (w + NW i);
+  // LDS tile i is p + P (kPdRegTiles + i)
+  bf16x8_t wreg[R][KS][kSub];
+#pragma unroll
+  for (int i = 0; i < R; ++i) load_wreg<KS>(a.W2t, p + P * (wave + NW * i), V, wreg[i]);
+  int nL = 0;
+  for (int i = 0; i < kPdLdsTiles; ++i) {
+    const int tl = p + P * (kPdRegTiles + i);
+    if (tl < nT) {
+      stage_tile(a.W2t, tl * kTileV, V, a.rank, ldsL + i * kLdsTileBytes);
+      ++nL;
     }
-    if (pick < 0) pick = lastp < 0 ? 0 : lastp;
-    const int x = v0 + q * kChunk + pick;
-    tokens[out] = x;
-    q_tok[out] = (float)((double)se[pick] * s_scale / Z);
-    row_max[out] = m;
-    row_logZ[out] = (float)log(Z);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Block-tasks of this wave for one position, in order: per chunk of up to
+  // kPdMaxRows requests, its register tiles x every block of the chunk, then
+  // its round-robin share (from `start`, step NW) of the (LDS tile, block)
+  // pairs.  Register tiles of a wave that lie inside the vocabulary form a
+  // prefix i < nreg; R <= 2 and kPdLdsTiles == 2 keep the index maths free
+  // of divisions.
+  static_assert(R <= 2 && kPdLdsTiles == 2, "task indexing assumes at most two of each");
+  const int nch = (B + kPdMaxRows - 1) / kPdMaxRows;
+  int nreg = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) nreg += (p + P * (wave + NW * i) < nT) ? 1 : 0;
+  auto chunk_blocks = [&](int ch) {
+    return (min(kPdMaxRows, B - ch * kPdMaxRows) + kTileM - 1) / kTileM;
+  };
+  auto chunk_tasks = [&](int ch, int start) {
+    const int nblk = chunk_blocks(ch);
+    const int nlds = nL * nblk;
+    return nreg * nblk + (start < nlds ? (nlds - start + NW - 1) / NW : 0);
+  };
+  // A ring of D prefetched tasks: base logits (they do not depend on the
+  // drafted tokens, so the first ones of a position are requested before
+  // its tokens are known) and the task's tile / block / W2t location
+  // (which: -1 - i = register tile i, >= 0 = LDS tile).  One slot ahead is
+  // enough at two waves per SIMD; one wave per SIMD keeps two.
+  constexpr int D = NW >= 8 ? 1 : 2;
+  struct Slot {
+    URow<uint16_t> u;
+    int tile, rb, which;
+  };
+  Slot ring[D];
+  int fch = 0, fidx = 0;   // next task to fetch: chunk, index in the chunk
+  auto fetch_next = [&](Slot& sl, int start, int k) {
+    if (fch >= nch) return;
+    const int nblk = chunk_blocks(fch);
+    const int rbase = fch * (kPdMaxRows / kTileM);
+    if (fidx < nreg * nblk) {
+      const int i = (R == 2 && fidx >= nblk) ? 1 : 0;
+      sl.rb = rbase + fidx - i * nblk;
+      sl.tile = p + P * (wave + NW * i);
+      sl.which = -1 - i;
+    } else {
+      const int li = start + (fidx - nreg * nblk) * NW;
+      const int which = li >= nblk ? 1 : 0;
+      sl.rb = rbase + li - which * nblk;
+      sl.tile = p + P * (kPdRegTiles + which);
+      sl.which = which;
+    }
+    const int b = sl.rb * kTileM + c;
+    load_urow<uint16_t>(sl.u, a.U + ((size_t)b * gamma + k) * V, sl.tile * kTileV, V, b < B,
+                        a.U);
+    if (++fidx == chunk_tasks(fch, start)) {
+      fidx = 0;
+      ++fch;
+      while (fch < nch && chunk_tasks(fch, start) == 0) ++fch;
+    }
+  };
+
+  for (int k = 0; k < gamma; ++k) {
+    const int start = (wave + k) % NW;   // rotate who takes the LDS extras
+    fch = 0;
+    fidx = 0;
+    while (fch < nch && chunk_tasks(fch, start) == 0) ++fch;
+#pragma unroll
+    for (int d = 0; d < D; ++d) fetch_next(ring[d], start, k);
+    if (k > 0) wait_flags(a.tok_flag, B, 1, (uint32_t)k, a.spin_cap, a.status);
+
+    // run the task in slot sl: start the accumulators at its base logits,
+    // refill the slot with the task D ahead, add the bias, reduce
+    auto run_task = [&](Slot& sl) {
+      const int tile = sl.tile, rb = sl.rb, which = sl.which;
+      const int b = rb * kTileM + c;
+      const int v0 = tile * kTileV;
+      const int lrow = (rb % (kPdMaxRows / kTileM)) * kTileM + c;   // row in the gathered chunk
+      f32x16_t acc[kSub];
+      if (v0 + kTileV <= V) {
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[t][j] = urow_at(sl.u, t, j);
+        }
+      } else {
+        init_acc<uint16_t>(sl.u, V - (v0 + 16 * h), acc);
+      }
+      fetch_next(sl, start, k);
+      // no global load below: a later load would make the in-order memory
+      // counter wait for the prefetch just issued
+      const float it = s_it[lrow];
+      auto bfrag = [&](int ks) { return lds_frag(ldsA, lrow, 2 * ks + h, nq); };
+      if (which >= 0) {
+        bias_tile_ldsA<KS>(bfrag, ldsL + which * kLdsTileBytes, acc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          if (which == -1 - i) bias_tile_regA<KS>(bfrag, wreg[i], acc);
+      }
+      const bool any_greedy = __ballot((b < B) && !(it > 0.f)) != 0;
+      block_tile_epilogue(acc, b, B, tile, nT, it, any_greedy, a.ts);
+    };
+
+    int g = 0;
+    for (int ch = 0; ch < nch; ++ch) {
+      const int r0 = ch * kPdMaxRows;
+      const int nrows = min(kPdMaxRows, B - r0);
+      const int nblk = chunk_blocks(ch);
+      for (int r = threadIdx.x; r < nblk * kTileM; r += blockDim.x) {
+        int t = 0;
+        float it = 0.f;
+        if (r < nrows) {
+          const int b = r0 + r;
+          t = (k == 0) ? a.anchor[b] : ld_dev(a.tokens + (size_t)b * gamma + k - 1);
+          t = clamp_token(t, V, k == 0 ? a.status : nullptr);
+          it = inv_temp(a.temperature[b]);
+        }
+        s_tok[r] = t;
+        s_it[r] = it;
+      }
+      __syncthreads();
+      stage_gather(a.W1, s_tok, a.rank, ldsA, nblk * kTileM);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const int gend = g + chunk_tasks(ch, start);
+      for (; g < gend; ++g) {
+        if (D == 1 || (g & 1) == 0)
+          run_task(ring[0]);
+        else
+          run_task(ring[D - 1]);
+      }
+      __syncthreads();  // the W1 row area is reused by the next chunk / sampler
+    }
+    // publish this group's statistics of position k
+    stores_done_group();
+    if (threadIdx.x == 0) st_flag(a.stats_flag + (size_t)p * kPdFlagStride, (uint32_t)(k + 1));
+
+    // draw the tokens of the requests this group owns
+    bool waited = false;
+    for (int b = p; b < B; b += P) {
+      if (!waited) {
+        wait_flags(a.stats_flag, P, kPdFlagStride, (uint32_t)(k + 1), a.spin_cap, a.status);
+        waited = true;
+      }
+      const int prev = clamp_token(
+          k == 0 ? a.anchor[b] : ld_dev(a.tokens + (size_t)b * gamma + k - 1), V, nullptr);
+      sample_request<uint16_t, KS>(b, k, B, gamma, V, a.rank, prev, a.U, a.W1, a.W2t,
+                                   a.temperature, a.uniforms, a.ts, a.tokens, a.q_tok,
+                                   a.row_max, a.row_logZ, a.status, ldsA, sh);
+      stores_done_group();
+      if (threadIdx.x == 0) st_flag(a.tok_flag + b, (uint32_t)(k + 1));
+    }
   }
 }
+
+__global__ void pdraft_reset_kernel(uint32_t* flags, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) flags[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+namespace {
+int g_draft_path = 0;  // 0 auto, 1 multi-launch, 2-4 persistent only (3: 8 waves, 4: 4 waves)
+
+struct DevInfo {
+  int cus = 0;
+  bool coop = false;
+  int wall_khz = 100000;  // rate of the device wall clock read by wall_clock64()
+};
+DevInfo dev_info() {
+  static thread_local int cached_dev = -1;
+  static thread_local DevInfo info;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DevInfo{};
+  if (dev != cached_dev) {
+    info = DevInfo{};
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      info.cus = v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess)
+      info.coop = v != 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) == hipSuccess && v > 0)
+      info.wall_khz = v;
+    cached_dev = dev;
+  }
+  return info;
+}
+}  // namespace
+
+void set_draft_path(int path) { g_draft_path = path; }
+int get_draft_path() { return g_draft_path; }
+
+static size_t stats_bytes(int B, int V) { return align256((size_t)B * n_tiles(V) * 4); }
 
 size_t draft_workspace_bytes(int B, int gamma, int V, int rank, int dtype) {
   (void)gamma; (void)rank; (void)dtype;
-  size_t nT = n_tiles(V), nC = n_chunks(V);
-  return align256((size_t)B * nT * 4) * 2 + align256((size_t)B * nC * 4);
+  const size_t flags = align256((size_t)kPdMaxGroups * kPdFlagStride * 4) + align256((size_t)B * 4);
+  return 3 * stats_bytes(B, V) + flags;
+}
+
+static TileStats carve_stats(void* ws, int B, int V) {
+  char* w = static_cast<char*>(ws);
+  TileStats ts;
+  ts.max = reinterpret_cast<float*>(w);
+  ts.arg = reinterpret_cast<int32_t*>(w + stats_bytes(B, V));
+  ts.sum = reinterpret_cast<float*>(w + 2 * stats_bytes(B, V));
+  return ts;
 }
 
 template <typename T, int KS>
-static hipError_t draft_impl(int B, int gamma, int V, int rank, const T* U, const T* W1,
-                             const T* W2t, const int32_t* anchor, const float* temperature,
-                             const float* uniforms, int32_t* tokens, float* q_tok, float* row_max,
-                             float* row_logZ, int32_t* status, void* ws, hipStream_t stream) {
-  const size_t nT = n_tiles(V);
-  char* w = static_cast<char*>(ws);
-  float* tile_max = reinterpret_cast<float*>(w);
-  int32_t* tile_arg = reinterpret_cast<int32_t*>(w + align256((size_t)B * nT * 4));
-  float* chunk_sum = reinterpret_cast<float*>(w + 2 * align256((size_t)B * nT * 4));
+static hipError_t draft_multi(int B, int gamma, int V, int rank, const T* U, const T* W1,
+                              const T* W2t, const int32_t* anchor, const float* temperature,
+                              const float* uniforms, int32_t* tokens, float* q_tok,
+                              float* row_max, float* row_logZ, int32_t* status, void* ws,
+                              hipStream_t stream) {
+  const TileStats ts = carve_stats(ws, B, V);
   const dim3 blk(256);
   for (int k = 0; k < gamma; ++k) {
     const int32_t* prev = (k == 0) ? anchor : tokens + (k - 1);
     const int stride = (k == 0) ? 1 : gamma;
     {
-      TraceScope ts("draft_stats_kernel", stream);
-      draft_stats_kernel<T, KS><<<dim3((unsigned)nT), blk, 0, stream>>>(
-          B, gamma, V, rank, k, U, W1, W2t, prev, stride, temperature, tile_max, tile_arg,
-          chunk_sum, status);
+      TraceScope t("draft_stats_kernel", stream);
+      draft_stats_kernel<T, KS><<<dim3((unsigned)n_tiles(V)), blk, 0, stream>>>(
+          B, gamma, V, rank, k, U, W1, W2t, prev, stride, temperature, ts, status);
     }
-    TraceScope ts("draft_sample_kernel", stream);
-    draft_sample_kernel<T, KS><<<dim3(B), blk, 0, stream>>>(
-        B, gamma, V, rank, k, U, W1, W2t, prev, stride, temperature, uniforms, tile_max, tile_arg,
-        chunk_sum, tokens, q_tok, row_max, row_logZ, status);
+    TraceScope t("draft_sample_kernel", stream);
+    draft_sample_kernel<T, KS><<<dim3(B), blk, 0, stream>>>(B, gamma, V, rank, k, U, W1, W2t,
+                                                           prev, stride, temperature, uniforms,
+                                                           ts, tokens, q_tok, row_max, row_logZ,
+                                                           status);
   }
   return hipGetLastError();
+}
+
+// Returns hipErrorNotSupported when the persistent kernel cannot run here.
+template <int KS>
+static hipError_t draft_persistent(int B, int gamma, int V, int rank, const uint16_t* U,
+                                   const uint16_t* W1, const uint16_t* W2t,
+                                   const int32_t* anchor, const float* temperature,
+                                   const float* uniforms, int32_t* tokens, float* q_tok,
+                                   float* row_max, float* row_logZ, int32_t* status, void* ws,
+                                   hipStream_t stream) {
+  const DevInfo di = dev_info();
+  const int P = di.cus;
+  if (!di.coop || P < 1 || P > kPdMaxGroups) return hipErrorNotSupported;
+  if ((long long)n_tiles(V) > (long long)P * (kPdRegTiles + kPdLdsTiles))
+    return hipErrorNotSupported;
+  // waves per group: 4 (two register tiles each) from rank 128 up, where
+  // one tile per wave leaves too few registers at two waves per SIMD; else 8
+  const int nw = g_draft_path == 3 ? 8 : g_draft_path == 4 ? 4 : (KS >= 8 ? 4 : 8);
+  const void* kern = nw == 8 ? reinterpret_cast<const void*>(pdraft_kernel<KS, 8>)
+                             : reinterpret_cast<const void*>(pdraft_kernel<KS, 4>);
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, nw * 64, 0) != hipSuccess ||
+      occ < 1)
+    return hipErrorNotSupported;
+  PdArgs a;
+  a.B = B; a.gamma = gamma; a.V = V; a.rank = rank; a.P = P;
+  a.U = U; a.W1 = W1; a.W2t = W2t; a.anchor = anchor; a.temperature = temperature;
+  a.uniforms = uniforms; a.tokens = tokens; a.q_tok = q_tok; a.row_max = row_max;
+  a.row_logZ = row_logZ; a.status = status;
+  a.ts = carve_stats(ws, B, V);
+  char* fl = static_cast<char*>(ws) + 3 * stats_bytes(B, V);
+  a.stats_flag = reinterpret_cast<uint32_t*>(fl);
+  a.tok_flag = reinterpret_cast<uint32_t*>(fl + align256((size_t)kPdMaxGroups * kPdFlagStride * 4));
+  a.spin_cap = 200LL * di.wall_khz;  // 0.2 s: reached only if a group never arrives
+  {
+    TraceScope t("pdraft_reset_kernel", stream);
+    const int nflags = P * kPdFlagStride;
+    pdraft_reset_kernel<<<dim3((nflags + 255) / 256), dim3(256), 0, stream>>>(a.stats_flag,
+                                                                              nflags);
+    pdraft_reset_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(a.tok_flag, B);
+  }
+  TraceScope t("pdraft_kernel", stream);
+  void* args[] = {&a};
+  return hipLaunchCooperativeKernel(kern, dim3(P), dim3(nw * 64), args, 0, stream);
 }
 
 hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U,
@@ -333,21 +756,30 @@ hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, cons
     auto* u = static_cast<const uint16_t*>(U);
     auto* w1 = static_cast<const uint16_t*>(W1);
     auto* w2 = static_cast<const uint16_t*>(W2t);
-#define DSPARK_DRAFT_KS(KS)                                                                   \
-  return draft_impl<uint16_t, KS>(B, gamma, V, rank, u, w1, w2, anchor, temperature, uniforms, \
-                                  tokens, q_tok, row_max, row_logZ, status, ws, stream)
+#define DSPARK_DRAFT_KS(KS)                                                                     \
+  {                                                                                             \
+    if (g_draft_path != 1) {                                                                    \
+      hipError_t e = draft_persistent<KS>(B, gamma, V, rank, u, w1, w2, anchor, temperature,    \
+                                          uniforms, tokens, q_tok, row_max, row_logZ, status,   \
+                                          ws, stream);                                          \
+      if (e != hipErrorNotSupported || g_draft_path >= 2) return e;                             \
+    }                                                                                           \
+    return draft_multi<uint16_t, KS>(B, gamma, V, rank, u, w1, w2, anchor, temperature,         \
+                                     uniforms, tokens, q_tok, row_max, row_logZ, status, ws,    \
+                                     stream);                                                   \
+  }
     switch (rank) {
-      case 32: DSPARK_DRAFT_KS(2);
-      case 64: DSPARK_DRAFT_KS(4);
-      case 128: DSPARK_DRAFT_KS(8);
-      default: DSPARK_DRAFT_KS(16);
+      case 32: DSPARK_DRAFT_KS(2)
+      case 64: DSPARK_DRAFT_KS(4)
+      case 128: DSPARK_DRAFT_KS(8)
+      default: DSPARK_DRAFT_KS(16)
     }
 #undef DSPARK_DRAFT_KS
   }
-  return draft_impl<float, 1>(B, gamma, V, rank, static_cast<const float*>(U),
-                              static_cast<const float*>(W1), static_cast<const float*>(W2t),
-                              anchor, temperature, uniforms, tokens, q_tok, row_max, row_logZ,
-                              status, ws, stream);
+  return draft_multi<float, 1>(B, gamma, V, rank, static_cast<const float*>(U),
+                               static_cast<const float*>(W1), static_cast<const float*>(W2t),
+                               anchor, temperature, uniforms, tokens, q_tok, row_max, row_logZ,
+                               status, ws, stream);
 }
 
 }  // namespace dspark

@@ -40,6 +40,8 @@ int check_dims(const char* fn, int B, int gamma, int V, int rank, int dtype) {
   if (B < 1) return fail(DSPARK_EINVAL, "%s: B=%d must be >= 1", fn, B);
   if (gamma < 1 || gamma > 64) return fail(DSPARK_EINVAL, "%s: gamma=%d outside [1,64]", fn, gamma);
   if (V < 8 || V % 8) return fail(DSPARK_EINVAL, "%s: V=%d must be a positive multiple of 8", fn, V);
+  if (V > dspark::kMaxVocab)
+    return fail(DSPARK_EUNSUPPORTED, "%s: V=%d exceeds %d", fn, V, dspark::kMaxVocab);
   if (dtype == DSPARK_BF16 && rank != 32 && rank != 64 && rank != 128 && rank != 256)
     return fail(DSPARK_EINVAL, "%s: bf16 rank=%d must be 32, 64, 128 or 256", fn, rank);
   if (rank < 32 || rank > 512 || rank % 32)
@@ -74,6 +76,14 @@ const char* dspark_status_str(int status) {
 const char* dspark_last_error(void) { return g_err; }
 
 const char* dspark_version(void) { return "libdspark 0.1 gfx950"; }
+
+int dspark_set_draft_path(int path) {
+  if (path < 0 || path > 4)
+    return fail(DSPARK_EINVAL, "dspark_set_draft_path: path %d is not in 0..4", path);
+  const int old = dspark::get_draft_path();
+  dspark::set_draft_path(path);
+  return old;
+}
 
 size_t dspark_draft_block_workspace(int B, int gamma, int V, int rank, int dtype) {
   if (check_dims("dspark_draft_block_workspace", B, gamma, V, rank, dtype) != DSPARK_OK) return 0;

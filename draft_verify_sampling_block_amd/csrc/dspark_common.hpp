@@ -2,49 +2,51 @@
 //
 // Tiling used by every vocabulary-streaming kernel
 // -------------------------------------------------
-// A wave owns a "wave tile" of 32 requests x 128 vocabulary entries.  The
-// Markov bias of the tile is one 32 x 128 x rank contraction on the bf16
-// matrix cores: v_mfma_f32_32x32x16_bf16, 4 output sub-tiles of 32 x 32,
-// rank/16 k-steps each.  Operand layout of that instruction (lane l, c =
-// l % 32, h = l / 32):
+// The vocabulary is cut into 64-entry tiles.  A "block-tile" is one tile x
+// 32 requests: its Markov bias is a 64 x 32 x rank contraction on the bf16
+// matrix cores, v_mfma_f32_32x32x16_bf16, as 2 output sub-tiles of 32 x 32
+// with rank/16 k-steps each.  Operand layout of that instruction (lane l,
+// c = l % 32, h = l / 32):
 //     A: row c,    k = 8h .. 8h+7 of the k-step      (8 bf16 per lane)
 //     B: column c, k = 8h .. 8h+7 of the k-step      (8 bf16 per lane)
 //     D: column c, rows 8*(j/4) + 4h + (j%4) for j = 0..15
-// Rows are requests (A = gathered W1 rows), columns are vocabulary entries
-// (B = W2t rows, which are k-contiguous).  Column c of sub-tile t is mapped
-// to vocabulary entry v0 + 4c + t, so after the contraction each lane holds,
-// for each of its 16 requests, 4 CONSECUTIVE vocabulary entries: the base
-// logits are read as one 8-byte load per (lane, request) and a half-wave
-// covers 256 contiguous bytes of a row.
+// Rows are vocabulary entries (A = W2t rows, k-contiguous) and columns are
+// requests (B = the W1 rows of the requests' previous tokens).  Matrix row
+// i of sub-tile t stands for vocabulary entry v0 + 32t + sub_row_vocab(i),
+// chosen so that accumulator element j of lane (c, h) is entry
+// v0 + 32t + 16h + j of request c: every lane ends up with 2 runs of 16
+// CONSECUTIVE vocabulary entries of ONE request.  The base logits are read
+// as 16-byte loads straight into that layout, the temperature is the
+// lane's own, and the per-tile reductions run inside the lane with one
+// exchange between the two half-waves.
 //
-// The W2t rows of a tile (128 x rank bf16, 64 KB at rank 256) are staged
-// once per work-group into LDS with global->LDS DMA loads and shared by the
-// work-group's 4 waves (one 32-request block each).  LDS rows keep their 16
-// byte k-chunks XOR-swizzled by (row/4) so that the 16 lanes of a matrix
-// operand read hit 16 distinct bank groups.
-//
-// A "chunk" is 64 consecutive vocabulary entries (lanes c = 16q..16q+15 of
-// a half-wave); 2 chunks make the 128-entry tile.  Sampling is two-level:
-// per-chunk partial sums are written by the streaming kernel, and the
-// per-request kernel scans them in fp64 and recomputes only the one chunk
-// where the cumulative sum crosses u * Z.
+// W2t tile rows staged in LDS are stored in matrix-row order (LDS row
+// 32t + i holds entry v0 + 32t + sub_row_vocab(i)) with their 16-byte
+// k-chunks XOR-swizzled per row, so that the 16 lanes of each quarter-wave,
+// which read 16 consecutive rows at one k-chunk, hit 16 distinct bank
+// groups.  The per-tile statistics (max, lowest argmax, sum of exp(y - max))
+// are the first level of the two-level inverse-CDF draw; the per-request
+// sampler scans them in fp64 and recomputes only the one tile where the
+// cumulative mass crosses u * Z, with the same instructions on the same
+// operands, hence bit for bit.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/dspark.h"
+#include "dspark_launch.hpp"
 
 namespace dspark {
 
 constexpr int kWave = 64;
-constexpr int kTileM = 32;        // requests per wave tile
-constexpr int kTileV = 128;       // vocabulary entries per tile
-constexpr int kSub = 4;           // 32-column matrix sub-tiles per tile
-constexpr int kChunk = 64;        // vocabulary entries per sampling chunk
-constexpr int kChunksPerTile = kTileV / kChunk;
+constexpr int kTileM = 32;        // requests per block
+constexpr int kTileV = 64;        // vocabulary entries per tile
+constexpr int kSub = 2;           // 32-column matrix sub-tiles per tile
 constexpr int kMaxKSteps = 16;    // rank <= 256
-constexpr int kLdsTileBytes = kTileV * kMaxKSteps * 2 * 16;   // 64 KB
+constexpr int kLdsTileBytes = kTileV * kMaxKSteps * 2 * 16;   // 32 KB
+constexpr int kMaxTiles = kMaxVocab / kTileV;     // 4096 (kMaxVocab: dspark_launch.hpp)
+constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -53,45 +55,59 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __host__ __device__ inline int n_tiles(int V) { return (V + kTileV - 1) / kTileV; }
-__host__ __device__ inline int n_chunks(int V) { return n_tiles(V) * kChunksPerTile; }
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// 4 consecutive elements -> fp32 (streamed, read-once: non-temporal)
-__device__ inline void load4_f32_stream(const uint16_t* p, float out[4]) {
-  u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-  out[0] = __uint_as_float(v.x << 16);
-  out[1] = __uint_as_float(v.x & 0xFFFF0000u);
-  out[2] = __uint_as_float(v.y << 16);
-  out[3] = __uint_as_float(v.y & 0xFFFF0000u);
-}
-__device__ inline void load4_f32_stream(const float* p, float out[4]) {
-  f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
-  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
-}
-// raw 4-element loads kept in registers until the epilogue (8 bytes for
-// bf16, 16 bytes for fp32)
-template <typename T> struct Raw4;
-template <> struct Raw4<uint16_t> { using type = u32x2_t; };
-template <> struct Raw4<float> { using type = u32x4_t; };
-template <typename T> using raw4_t = typename Raw4<T>::type;
+// This lane's base logits of one block-tile: for sub-tile t the 16
+// consecutive entries v0 + 32t + 16h + [0, 16), kept raw (16-byte loads,
+// streamed and read once: non-temporal) until the epilogue.
+template <typename T> struct URow;
+template <> struct URow<uint16_t> {
+  static constexpr int kLoads = 2;   // 8 bf16 per load
+  u32x4_t w[kSub][kLoads];
+};
+template <> struct URow<float> {
+  static constexpr int kLoads = 4;   // 4 fp32 per load
+  u32x4_t w[kSub][kLoads];
+};
 
-__device__ inline u32x4_t load4_raw(const float* p) {
-  f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
-  return __builtin_bit_cast(u32x4_t, v);
+// `row` is the start of a length-V row; `ok` false (or entries past V) give
+// zeros.  V % 8 == 0 keeps every 16-byte load wholly inside or outside; an
+// excluded load reads `safe` (any valid 16-byte-aligned address) instead,
+// so that no load is predicated.
+template <typename T>
+__device__ inline void load_urow(URow<T>& u, const T* __restrict__ row, int v0, int V, bool ok,
+                                 const T* __restrict__ safe) {
+  const int h = (threadIdx.x & 63) >> 5;
+  constexpr int per = 16 / (int)sizeof(T);
+  const int vb = v0 + 16 * h, rem = V - vb;
+#pragma unroll
+  for (int t = 0; t < kSub; ++t) {
+#pragma unroll
+    for (int q = 0; q < URow<T>::kLoads; ++q) {
+      const bool in = ok && (32 * t + q * per < rem);
+      const T* p = in ? row + vb + 32 * t + q * per : safe;
+      const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+      u.w[t][q] = in ? x : u32x4_t{};
+    }
+  }
 }
-__device__ inline u32x2_t load4_raw(const uint16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+__device__ inline float urow_at(const URow<uint16_t>& u, int t, int j) {
+  const uint32_t w = u.w[t][j >> 3][(j >> 1) & 3];
+  return (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
 }
-__device__ inline void unpack4(const u32x2_t& r, float out[4]) {
-  out[0] = __uint_as_float(r.x << 16);
-  out[1] = __uint_as_float(r.x & 0xFFFF0000u);
-  out[2] = __uint_as_float(r.y << 16);
-  out[3] = __uint_as_float(r.y & 0xFFFF0000u);
+__device__ inline float urow_at(const URow<float>& u, int t, int j) {
+  return __uint_as_float(u.w[t][j >> 2][j & 3]);
 }
-__device__ inline void unpack4(const u32x4_t& r, float out[4]) {
-  out[0] = __uint_as_float(r.x); out[1] = __uint_as_float(r.y);
-  out[2] = __uint_as_float(r.z); out[3] = __uint_as_float(r.w);
+// Start value of a block-tile accumulator: the base logits, -inf for the
+// entries at or past V.  `rem` = V - (v0 + 16h) for this lane.
+template <typename T>
+__device__ inline void init_acc(const URow<T>& u, int rem, f32x16_t acc[kSub]) {
+#pragma unroll
+  for (int t = 0; t < kSub; ++t) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[t][j] = (32 * t + j < rem) ? urow_at(u, t, j) : -INFINITY;
+  }
 }
 
 // 8 consecutive elements -> fp32 (bf16 path: one 16-byte load)
@@ -126,6 +142,34 @@ __device__ inline void load8_f32_stream(const float* p, float out[8]) {
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+// Loads and stores of data exchanged between work-groups of one running
+// kernel: relaxed atomics at device scope, so each access is coherent across
+// the chip's L2 slices without whole-cache write-backs or invalidations.
+// Ordering comes from the flag protocol around them (stores complete before
+// a flag is raised; loads issue after the flag is seen).
+template <typename X>
+__device__ inline X ld_dev(const X* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename X>
+__device__ inline void st_dev(X* p, X v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// lane l receives (x of lane l % 32, x of lane l % 32 + 32): the two
+// half-waves' values in the same order on every lane
+__device__ inline void half_pair(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ inline void half_pair(int x, int& lo, int& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  lo = (int)r[0];
+  hi = (int)r[1];
+}
+
 __device__ inline bf16x8_t load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
@@ -142,121 +186,183 @@ __device__ inline int clamp_token(int t, int V, int32_t* status) {
   return t;
 }
 
-// request row m(j) of accumulator element j for half-wave h (D layout above)
-__device__ inline int acc_row(int j, int h) { return 8 * (j >> 2) + 4 * h + (j & 3); }
-// accumulator element that holds request row m for half-wave (m/4)%2
-__device__ inline int row_half(int m) { return (m >> 2) & 1; }
-__device__ inline int row_elem(int m) { return 4 * (m >> 3) + (m & 3); }
+// vocabulary offset, within a 32-entry sub-tile, of matrix row i (the
+// inverse of: accumulator element j of half-wave h holds offset 16h + j)
+__host__ __device__ inline int sub_row_vocab(int i) {
+  return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+}
+// vocabulary offset within the tile of tile row r (r in [0, 64))
+__host__ __device__ inline int tile_row_vocab(int r) { return (r & 32) + sub_row_vocab(r & 31); }
 
 // ---------------------------------------------------------------------------
-// W2t tile in LDS: 128 rows (tile-local vocabulary index r) of rank bf16,
-// i.e. nq = rank/8 chunks of 16 bytes per row, chunk q stored at slot
-// q ^ swz(r).  Row r is read by lane column c = r/4 of sub-tile t = r%4.
+// Rows of rank bf16 in LDS (W2t tile rows, or gathered W1 rows): nq = rank/8
+// chunks of 16 bytes per row, chunk q stored at slot q ^ swz(r).  The XOR
+// key makes 16 consecutive rows read at one chunk land in 16 distinct
+// 16-byte bank groups for every nq in {4, 8, 16, 32}.
 // ---------------------------------------------------------------------------
-__device__ inline int lds_swz(int r, int nq) { return ((r >> 2) & 15) & (nq - 1); }
+__device__ inline int lds_swz(int r, int nq) {
+  return nq >= 16 ? (r & 15) : ((r / (16 / nq)) & (nq - 1));
+}
 __device__ inline int lds_off(int r, int q, int nq) { return (r * nq + (q ^ lds_swz(r, nq))) * 16; }
 
-// Issue DMA loads of tile rows [row_lo, row_lo + nrows) into `lds`; every
-// wave of the work-group takes part.  Rows past V read row V-1 (their
-// columns are masked later).  Completion: s_waitcnt + barrier by the caller.
-__device__ inline void stage_w2_rows(const uint16_t* __restrict__ W2t, int v0, int V, int rank,
-                                     char* lds, int row_lo, int nrows) {
+// DMA the 64 rows of W2t tile v0 into `lds` in matrix-row order: LDS row r
+// <- W2t row v0 + tile_row_vocab(r), clamped to V - 1 (rows past V are
+// never used: their logits are masked).  Every wave of the work-group takes
+// part.  Completion: s_waitcnt + barrier by the caller.
+__device__ inline void stage_tile(const uint16_t* __restrict__ W2t, int v0, int V, int rank,
+                                  char* lds) {
   const int nq = rank >> 3;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
-  const int nslots = nrows * nq;           // a multiple of 64 (nrows in {64,128}, nq >= 4)
-  const int s_lo = row_lo * nq;
+  const int nslots = kTileV * nq;          // a multiple of 64
   for (int g = wave; g * 64 < nslots; g += nwaves) {
-    const int s = s_lo + g * 64 + lane;
-    const int r = s / nq, p = s - (s / nq) * nq;
+    const int s = g * 64 + lane;
+    const int r = s / nq, p = s - r * nq;
     const int q = p ^ lds_swz(r, nq);
-    int v = v0 + r;
+    int v = v0 + tile_row_vocab(r);
     v = v < V ? v : V - 1;
-    const uint16_t* src = W2t + (size_t)v * rank + q * 8;
-    __builtin_amdgcn_global_load_lds(src, lds + (size_t)(s_lo + g * 64) * 16, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(W2t + (size_t)v * rank + q * 8,
+                                     lds + (size_t)(g * 64) * 16, 16, 0, 0);
   }
 }
 
-// Markov bias of one wave tile with B read from the LDS tile.
-//   acc[t][j] = sum_k W1[prev(m(j))][k] * W2t[v0 + 4c + t][k]
-// `afrag` holds this lane's A operand for every k-step (its row c =
-// request c of the block, zeros for an empty row).  Lanes whose column c lies
-// outside [col_lo, col_hi) feed zeros for B: this recomputes a single chunk
-// bit-identically (each output element depends only on its own A row and B
-// column, and the k-step order is fixed).  All 64 lanes must call it.
-template <int KS>
-__device__ inline void bias_tile_lds(const bf16x8_t afrag[KS], const char* lds, int col_lo,
-                                     int col_hi, f32x16_t acc[kSub]) {
+// DMA gathered rows: LDS row r <- src row ids[r]; nrows rows (nrows * nq a
+// multiple of 64).
+__device__ inline void stage_gather(const uint16_t* __restrict__ src, const int* ids, int rank,
+                                    char* lds, int nrows) {
+  const int nq = rank >> 3;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int nslots = nrows * nq;
+  for (int g = wave; g * 64 < nslots; g += nwaves) {
+    const int s = g * 64 + lane;
+    const int r = s / nq, p = s - r * nq;
+    const int q = p ^ lds_swz(r, nq);
+    __builtin_amdgcn_global_load_lds(src + (size_t)ids[r] * rank + q * 8,
+                                     lds + (size_t)(g * 64) * 16, 16, 0, 0);
+  }
+}
+
+__device__ inline bf16x8_t lds_frag(const char* lds, int r, int q, int nq) {
+  return *reinterpret_cast<const bf16x8_t*>(lds + lds_off(r, q, nq));
+}
+
+// Markov bias of one block-tile with the W2t tile (A) read from LDS and the
+// request operand (B) given per k-step by `bfrag`, accumulated onto acc:
+//   acc[t][j] += sum_k W2t[v0 + 32t + 16h + j][k] * Wrow_c[k]
+// (k-steps in ascending order) where Wrow_c is the W1 row fed by the lanes
+// of column c.  The callers start acc at the base logits (init_acc), so the
+// result is the biased logit itself.  Each output element depends only on
+// its own A row, its own B column, its own start value and the fixed k-step
+// order, so feeding zeros to the other columns recomputes one request's
+// values bit for bit.  All 64 lanes must call it.
+template <int KS, typename BF>
+__device__ inline void bias_tile_ldsA(BF&& bfrag, const char* ldsA, f32x16_t acc[kSub]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 31, h = lane >> 5;
   constexpr int nq = 2 * KS;
-  const bool col_ok = (c >= col_lo) && (c < col_hi);
-  const bf16x8_t zero = bf16x8_t{};
+  bf16x8_t acur[kSub], anext[kSub];
 #pragma unroll
-  for (int t = 0; t < kSub; ++t) acc[t] = f32x16_t{};
-  // B fragments double-buffered: the LDS reads of k-step ks+1 are issued
-  // before the matrix instructions of k-step ks; the scheduling barrier
-  // keeps the compiler from hoisting further reads (register pressure)
-  bf16x8_t bcur[kSub], bnext[kSub];
-#pragma unroll
-  for (int t = 0; t < kSub; ++t) {
-    bcur[t] = *reinterpret_cast<const bf16x8_t*>(lds + lds_off(4 * c + t, h, nq));
-    bcur[t] = col_ok ? bcur[t] : zero;
-  }
+  for (int t = 0; t < kSub; ++t) acur[t] = lds_frag(ldsA, 32 * t + c, h, nq);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (ks + 1 < KS) {
 #pragma unroll
-      for (int t = 0; t < kSub; ++t) {
-        bnext[t] = *reinterpret_cast<const bf16x8_t*>(lds + lds_off(4 * c + t, 2 * (ks + 1) + h, nq));
-        bnext[t] = col_ok ? bnext[t] : zero;
-      }
+      for (int t = 0; t < kSub; ++t) anext[t] = lds_frag(ldsA, 32 * t + c, 2 * (ks + 1) + h, nq);
     }
+    const bf16x8_t bv = bfrag(ks);
 #pragma unroll
     for (int t = 0; t < kSub; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[ks], bcur[t], acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[t], bv, acc[t], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < kSub; ++t) bcur[t] = bnext[t];
+    for (int t = 0; t < kSub; ++t) acur[t] = anext[t];
   }
 }
 
-// this lane's A operand (row c = request `tok` or empty) for all k-steps
-template <int KS>
-__device__ inline void load_afrag(const uint16_t* __restrict__ W1, int tok, bf16x8_t afrag[KS]) {
-  const int h = (threadIdx.x & 63) >> 5;
-  const bf16x8_t zero = bf16x8_t{};
-  const uint16_t* arow = W1 + (size_t)(tok >= 0 ? tok : 0) * (16 * KS) + 8 * h;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    afrag[ks] = load_bf16x8(arow + 16 * ks);
-    afrag[ks] = tok >= 0 ? afrag[ks] : zero;
-  }
-}
-
-// fp32 inputs: plain FMA dot products (k ascending) in the same layout.
-// `tok` is this lane's A row (request c of the block, -1 = empty); the rows
-// of the lane's outputs are fetched from the owning lanes.  All 64 lanes.
-__device__ inline void bias_tile_f32(const float* __restrict__ W1, int tok,
-                                     const float* __restrict__ W2t, int v0, int V, int rank,
-                                     int col_lo, int col_hi, f32x16_t acc[kSub]) {
+// Sub-tile t alone of the same contraction (the identical instruction chain
+// that bias_tile_ldsA runs for acc[t]).
+template <int KS, typename BF>
+__device__ inline void bias_subtile_ldsA(BF&& bfrag, const char* ldsA, int t, f32x16_t& acc) {
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 31, h = lane >> 5;
-  const bool col_ok = (c >= col_lo) && (c < col_hi);
-  int prow[16];
+  constexpr int nq = 2 * KS;
+  bf16x8_t acur = lds_frag(ldsA, 32 * t + c, h, nq), anext;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) prow[j] = __shfl(tok, acc_row(j, h), kWave);
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) anext = lds_frag(ldsA, 32 * t + c, 2 * (ks + 1) + h, nq);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur, bfrag(ks), acc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    acur = anext;
+  }
+}
+
+// The same contraction with the W2t tile held in registers (see load_wreg).
+template <int KS, typename BF>
+__device__ inline void bias_tile_regA(BF&& bfrag, const bf16x8_t (&wreg)[KS][kSub],
+                                      f32x16_t acc[kSub]) {
+  bf16x8_t bcur = bfrag(0), bnext;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) bnext = bfrag(ks + 1);
+#pragma unroll
+    for (int t = 0; t < kSub; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wreg[ks][t], bcur, acc[t], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // keep later operand reads from being hoisted
+    bcur = bnext;
+  }
+}
+
+// This lane's A operand of W2t tile `vt` for every k-step (zeros past V, or
+// for a tile index >= nT).
+template <int KS>
+__device__ inline void load_wreg(const uint16_t* __restrict__ W2t, int vt, int V,
+                                 bf16x8_t (&wreg)[KS][kSub]) {
+  const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
+  const bf16x8_t zero = bf16x8_t{};
 #pragma unroll
   for (int t = 0; t < kSub; ++t) {
-    const int v = v0 + 4 * c + t;
-    const bool vok = col_ok && v < V;
-    const float* brow = W2t + (size_t)(vok ? v : 0) * rank;
+    int v = vt * kTileV + 32 * t + sub_row_vocab(c);
+    const bool vok = v < V;
+    v = vok ? v : 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t f = load_bf16x8(W2t + (size_t)v * (16 * KS) + 16 * ks + 8 * h);
+      wreg[ks][t] = vok ? f : zero;
+    }
+  }
+}
+
+// this lane's B operand (the W1 row of token `tok`, or zeros for tok < 0)
+// for all k-steps, straight from global memory
+template <int KS>
+__device__ inline void load_bfrag(const uint16_t* __restrict__ W1, int tok, bf16x8_t bfrag[KS]) {
+  const int h = (threadIdx.x & 63) >> 5;
+  const bf16x8_t zero = bf16x8_t{};
+  const uint16_t* row = W1 + (size_t)(tok >= 0 ? tok : 0) * (16 * KS) + 8 * h;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bfrag[ks] = load_bf16x8(row + 16 * ks);
+    bfrag[ks] = tok >= 0 ? bfrag[ks] : zero;
+  }
+}
+
+// fp32 inputs: plain FMA dot products (k ascending) in the same layout,
+// accumulated onto acc.  `tok` is the W1 row of this lane's request column
+// (-1 = nothing added).
+__device__ inline void bias_tile_f32(const float* __restrict__ W1, int tok,
+                                     const float* __restrict__ W2t, int v0, int V, int rank,
+                                     f32x16_t acc[kSub]) {
+  const int h = (threadIdx.x & 63) >> 5;
+  const float* arow = W1 + (size_t)(tok >= 0 ? tok : 0) * rank;
+#pragma unroll
+  for (int t = 0; t < kSub; ++t) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int p = prow[j];
-      float s = 0.f;
-      if (vok && p >= 0) {
-        const float* arow = W1 + (size_t)p * rank;
+      const int v = v0 + 32 * t + 16 * h + j;
+      float s = acc[t][j];
+      if (tok >= 0 && v < V) {
+        const float* brow = W2t + (size_t)v * rank;
         for (int i = 0; i < rank; ++i) s = fmaf(arow[i], brow[i], s);
       }
       acc[t][j] = s;

@@ -9,7 +9,14 @@ namespace dspark {
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
+constexpr int kMaxVocab = 262144;   // largest vocabulary the kernels take
+
 size_t draft_workspace_bytes(int B, int gamma, int V, int rank, int dtype);
+// 0 = automatic (persistent kernel when possible), 1 = multi-launch only,
+// 2 = persistent only (fails with hipErrorNotSupported where it cannot run),
+// 3 / 4 = persistent only with 8 / 4 waves per work-group
+void set_draft_path(int path);
+int get_draft_path();
 hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U,
                               const void* W1, const void* W2t, const int32_t* anchor,
                               const float* temperature, const float* uniforms, int32_t* tokens,

@@ -42,7 +42,7 @@ struct VerifyWs {
 
 VerifyWs carve(void* ws, int B, int gamma, int V) {
   char* p = static_cast<char*>(ws);
-  const size_t nC = n_chunks(V);
+  const size_t nC = n_tiles(V);
   VerifyWs w;
   w.first_rej = reinterpret_cast<int32_t*>(p); p += align256((size_t)B * 4);
   w.rM = reinterpret_cast<float*>(p); p += align256((size_t)B * (gamma + 1) * 4);
@@ -163,18 +163,14 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
 }
 
 // per-element residual / bonus weight; identical expression in both kernels
-__device__ inline void final_weights(const float yt[4], const float yq[4], float M, float LZ,
-                                     float mq, float lzq, bool residual, float r[4],
-                                     float p[4]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    p[t] = __expf(yt[t] - M - LZ);
-    if (residual) {
-      const float q = __expf(yq[t] - mq - lzq);
-      r[t] = fmaxf(0.f, p[t] - q);
-    } else {
-      r[t] = p[t];
-    }
+__device__ inline void final_weight(float yt, float yq, float M, float LZ, float mq, float lzq,
+                                    bool residual, float& r, float& p) {
+  p = __expf(yt - M - LZ);
+  if (residual) {
+    const float q = __expf(yq - mq - lzq);
+    r = fmaxf(0.f, p - q);
+  } else {
+    r = p;
   }
 }
 
@@ -202,6 +198,7 @@ __device__ inline FinalRow final_row(int b, int B, int gamma, int V, const int32
   return f;
 }
 
+// one work-group per 64-entry tile; waves take 32-request blocks
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void verify_final_stats_kernel(
     int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
@@ -214,43 +211,30 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int nRB = (B + kTileM - 1) / kTileM;
-  const int nC = n_chunks(V);
+  const int nT = n_tiles(V);
   const int vt = blockIdx.x, v0 = vt * kTileV;
-  const int vb = v0 + 4 * c;
-  const bool vok = vb < V;
 
   // does any request of the batch need the q recompute (a residual draw)?
   int any = 0;
   for (int b = threadIdx.x; b < B; b += blockDim.x)
     any |= final_row(b, B, gamma, V, ell, temperature, anchor, tokens, ws).mode == 1;
   const bool any_res = __syncthreads_or(any) != 0;
-  if (bf && any_res) stage_w2_rows(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s, 0,
-                                   kTileV);
+  if (bf && any_res) stage_tile(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s);
 
   for (int rb = wave; rb < nRB || (rb == wave); rb += 4) {
-    // one pass per 32-request block; the first pass of every wave also
-    // joins the barrier that publishes the LDS tile
+    // one pass per 32-request block (lane column c = request b); the first
+    // pass of every wave also joins the barrier that publishes the LDS tile
     const bool live = rb < nRB;
-    const FinalRow mine = final_row(live ? rb * kTileM + c : B, B, gamma, V, ell, temperature,
-                                    anchor, tokens, ws);
-    bf16x8_t afrag[KS];
-    if constexpr (bf) load_afrag<KS>(reinterpret_cast<const uint16_t*>(W1),
-                                     mine.mode == 1 ? mine.prev : -1, afrag);
-    raw4_t<T> tp[16], up[16];
-    int mode_j[16], slot_j[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int m = acc_row(j, h);
-      mode_j[j] = __shfl(mine.mode, m, kWave);
-      slot_j[j] = __shfl(mine.slot, m, kWave);
-      const int b = rb * kTileM + m;
-      tp[j] = raw4_t<T>{};
-      up[j] = raw4_t<T>{};
-      if (live && vok && mode_j[j] != 0)
-        tp[j] = load4_raw(target + ((size_t)b * (gamma + 1) + slot_j[j]) * V + vb);
-      if (live && vok && mode_j[j] == 1)
-        up[j] = load4_raw(U + ((size_t)b * gamma + slot_j[j]) * V + vb);
-    }
+    const int b = rb * kTileM + c;
+    const FinalRow mine = final_row(live ? b : B, B, gamma, V, ell, temperature, anchor, tokens,
+                                    ws);
+    bf16x8_t bfrag[KS];
+    if constexpr (bf) load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1),
+                                     mine.mode == 1 ? mine.prev : -1, bfrag);
+    URow<T> tp, up;
+    load_urow<T>(tp, target + ((size_t)b * (gamma + 1) + mine.slot) * V, v0, V, mine.mode != 0,
+                 target);
+    load_urow<T>(up, U + ((size_t)b * gamma + mine.slot) * V, v0, V, mine.mode == 1, U);
     if (rb == wave) {
       if (bf && any_res) __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -258,55 +242,47 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
     if (!live) break;
     const bool blk_res = __ballot(mine.mode == 1) != 0;
     f32x16_t acc[kSub];
+    init_acc<T>(up, V - (v0 + 16 * h), acc);   // q logits start at the base logits
     if (blk_res) {
       if constexpr (bf)
-        bias_tile_lds<KS>(afrag, w2s, 0, 32, acc);
+        bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
       else
         bias_tile_f32(reinterpret_cast<const float*>(W1), mine.mode == 1 ? mine.prev : -1,
-                      reinterpret_cast<const float*>(W2t), v0, V, rank, 0, 32, acc);
-    } else {
-#pragma unroll
-      for (int t = 0; t < kSub; ++t) acc[t] = f32x16_t{};
+                      reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
     }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int m = acc_row(j, h);
-      const int b = rb * kTileM + m;
-      const int mode = mode_j[j];
-      if (b >= B || mode == 0) continue;  // uniform across the half-wave
-      const int slot = slot_j[j];
+    float sr = 0.f, sp = 0.f;
+    if (mine.mode != 0) {
       const float it = 1.f / temperature[b];
-      const size_t sk = (size_t)b * (gamma + 1) + slot;
+      const size_t sk = (size_t)b * (gamma + 1) + mine.slot;
       const float M = ws.rM[sk], LZ = ws.rLZ[sk];
-      float yt[4], yq[4] = {0.f, 0.f, 0.f, 0.f}, r[4], p[4];
-      float mq = 0.f, lzq = 0.f;
-      if (vok) {
-        unpack4(tp[j], yt);
+      const bool res = mine.mode == 1;
+      const float mq = res ? row_max[(size_t)b * gamma + mine.slot] : 0.f;
+      const float lzq = res ? row_logZ[(size_t)b * gamma + mine.slot] : 0.f;
+      const int rem = V - (v0 + 16 * h);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) yt[t] *= it;
-        if (mode == 1) {
-          unpack4(up[j], yq);
+      for (int t = 0; t < kSub; ++t) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) yq[t] = (yq[t] + acc[t][j]) * it;
-          mq = row_max[(size_t)b * gamma + slot];
-          lzq = row_logZ[(size_t)b * gamma + slot];
+        for (int j = 0; j < 16; ++j) {
+          if (32 * t + j < rem) {
+            const float yt = urow_at(tp, t, j) * it;
+            const float yq = res ? acc[t][j] * it : 0.f;
+            float r, p;
+            final_weight(yt, yq, M, LZ, mq, lzq, res, r, p);
+            sr += r;
+            sp += p;
+          }
         }
-        final_weights(yt, yq, M, LZ, mq, lzq, mode == 1, r, p);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) { r[t] = 0.f; p[t] = 0.f; }
       }
-      float sr = r[0] + r[1] + r[2] + r[3], sp = p[0] + p[1] + p[2] + p[3];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        sr += __shfl_xor(sr, o, kWave);
-        sp += __shfl_xor(sp, o, kWave);
-      }
-      if ((c & 15) == 0) {
-        const size_t ci = (size_t)b * nC + vt * kChunksPerTile + (c >> 4);
-        ws.fchunk[ci] = sr;
-        ws.pchunk[ci] = sp;
-      }
+    }
+    float lo, hi;
+    half_pair(sr, lo, hi);
+    sr = lo + hi;
+    half_pair(sp, lo, hi);
+    sp = lo + hi;
+    if (mine.mode != 0 && h == 0) {
+      const size_t ci = (size_t)b * nT + vt;
+      ws.fchunk[ci] = sr;
+      ws.pchunk[ci] = sp;
     }
   }
 }
@@ -323,12 +299,12 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
   constexpr bool bf = sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) char w2s[bf ? kLdsTileBytes : 16];
   __shared__ double red[8];
-  __shared__ int s_chunk, s_pick;
+  __shared__ int s_tile, s_pick;
   __shared__ double s_before;
-  __shared__ float se[kChunk];
+  __shared__ float se[kTileV];
 
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int nC = n_chunks(V);
+  const int nT = n_tiles(V);
   const int L = clamp_ell(ell, b, gamma, nullptr);
   const int j = ws.first_rej[b];
   const bool residual = j < L;
@@ -342,11 +318,11 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
   if (greedy) {
     y = ws.rArg[sk];
   } else {
-    // residual chunk sums; fall back to p when the residual has no mass
-    const float* fc = ws.fchunk + (size_t)b * nC;
-    const float* pc = ws.pchunk + (size_t)b * nC;
-    const int per = (nC + blockDim.x - 1) / blockDim.x;
-    const int c0 = min(nC, tid * per), c1 = min(nC, c0 + per);
+    // residual tile sums; fall back to p when the residual has no mass
+    const float* fc = ws.fchunk + (size_t)b * nT;
+    const float* pc = ws.pchunk + (size_t)b * nT;
+    const int per = (nT + blockDim.x - 1) / blockDim.x;
+    const int c0 = min(nT, tid * per), c1 = min(nT, c0 + per);
     double local = 0.0;
     for (int cc = c0; cc < c1; ++cc) local += (double)fc[cc];
     double start, end;
@@ -364,7 +340,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
     const double tgt = u * S;
     const bool finite = S > 0.0 && isfinite(S);
     const int last_pos = block_max_int(local > 0.0 ? tid : -1, red);
-    if (tid == 0) s_chunk = -1;
+    if (tid == 0) s_tile = -1;
     __syncthreads();
     if (finite && local > 0.0 &&
         ((start <= tgt && tgt < end) || (tid == last_pos && tgt >= end))) {
@@ -377,89 +353,78 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
         run += sc;
       }
       if (found < 0) { found = lastc; before = lastb; }
-      s_chunk = found;
+      s_tile = found;
       s_before = before;
     }
     __syncthreads();
-    const int cstar = s_chunk;
-    if (cstar < 0) {
+    const int vt = s_tile;
+    if (vt < 0) {
       if (tid == 0) flag(status, DSPARK_DEV_NONFINITE);
       y = 0;
     } else {
-      // recompute the crossing chunk exactly as verify_final_stats did
-      const int vt = cstar / kChunksPerTile, q = cstar % kChunksPerTile;
+      // recompute the crossing tile exactly as verify_final_stats did:
+      // same operands, request b in its own column b % 32
       const int v0 = vt * kTileV;
       const int mrow = b % kTileM;
       const int lane = tid & 63, c = lane & 31, h = lane >> 5;
-      const int c_lo = 16 * q, c_hi = 16 * q + 16;
-      const bool mine = tid < kWave && h == row_half(mrow) && c >= c_lo && c < c_hi;
-      const int vb = v0 + 4 * c;
+      const bool mine = tid < kWave && c == mrow;
       const int prev = residual
           ? clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1], V, nullptr)
           : -1;
-      raw4_t<T> traw = raw4_t<T>{}, uraw = raw4_t<T>{};
-      if (mine && vb < V) {
-        traw = load4_raw(target + sk * V + vb);
-        if (residual) uraw = load4_raw(U + ((size_t)b * gamma + slot) * V + vb);
-      }
+      URow<T> tr, ur;
+      load_urow<T>(tr, target + sk * V, v0, V, mine, target);
+      load_urow<T>(ur, U + ((size_t)b * gamma + slot) * V, v0, V, mine && residual, U);
       f32x16_t acc[kSub];
+      init_acc<T>(ur, V - (v0 + 16 * h), acc);
       if (residual) {
         if constexpr (bf) {
-          stage_w2_rows(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s, kChunk * q,
-                        kChunk);
-          bf16x8_t afrag[KS];
+          stage_tile(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s);
+          bf16x8_t bfrag[KS];
           if (tid < kWave)
-            load_afrag<KS>(reinterpret_cast<const uint16_t*>(W1), c == mrow ? prev : -1, afrag);
+            load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), mine ? prev : -1, bfrag);
           __builtin_amdgcn_s_waitcnt(0);
           __syncthreads();
-          if (tid < kWave) bias_tile_lds<KS>(afrag, w2s, c_lo, c_hi, acc);
+          if (tid < kWave) bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
         } else {
           if (tid < kWave)
-            bias_tile_f32(reinterpret_cast<const float*>(W1), c == mrow ? prev : -1,
-                          reinterpret_cast<const float*>(W2t), v0, V, rank, c_lo, c_hi, acc);
+            bias_tile_f32(reinterpret_cast<const float*>(W1), mine ? prev : -1,
+                          reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
         }
-      } else {
-#pragma unroll
-        for (int t = 0; t < kSub; ++t) acc[t] = f32x16_t{};
       }
       if (mine) {
-        const int jm = row_elem(mrow);
         const float it = 1.f / Tb;
         const float M = ws.rM[sk], LZ = ws.rLZ[sk];
-        float yt[4], yq[4] = {0.f, 0.f, 0.f, 0.f}, r[4], p[4];
-        float mq = 0.f, lzq = 0.f;
-        if (vb < V) {
-          unpack4(traw, yt);
+        const float mq = residual ? row_max[(size_t)b * gamma + slot] : 0.f;
+        const float lzq = residual ? row_logZ[(size_t)b * gamma + slot] : 0.f;
+        const int rem = V - (v0 + 16 * h);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) yt[t] *= it;
-          if (residual) {
-            unpack4(uraw, yq);
+        for (int t = 0; t < kSub; ++t) {
+          float* so = se + 32 * t + 16 * h;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) yq[t] = (yq[t] + acc[t][jm]) * it;
-            mq = row_max[(size_t)b * gamma + slot];
-            lzq = row_logZ[(size_t)b * gamma + slot];
+          for (int jj = 0; jj < 16; ++jj) {
+            float r = 0.f, p = 0.f;
+            if (32 * t + jj < rem) {
+              const float yt = urow_at(tr, t, jj) * it;
+              const float yq = residual ? acc[t][jj] * it : 0.f;
+              final_weight(yt, yq, M, LZ, mq, lzq, residual, r, p);
+            }
+            so[jj] = use_p ? p : r;
           }
-          final_weights(yt, yq, M, LZ, mq, lzq, residual, r, p);
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) { r[t] = 0.f; p[t] = 0.f; }
         }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) se[(c - c_lo) * kSub + t] = use_p ? p[t] : r[t];
       }
       __syncthreads();
       if (tid == 0) {
         const double rr = tgt - s_before;
         double run = 0.0;
         int pick = -1, lastp = -1;
-        for (int i = 0; i < kChunk; ++i) {
+        for (int i = 0; i < kTileV; ++i) {
           const double e = (double)se[i];
           if (e > 0.0) lastp = i;
           run += e;
           if (e > 0.0 && rr < run) { pick = i; break; }
         }
         if (pick < 0) pick = lastp < 0 ? 0 : lastp;
-        s_pick = v0 + q * kChunk + pick;
+        s_pick = v0 + pick;
       }
       __syncthreads();
       y = s_pick;
@@ -482,7 +447,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
 
 size_t verify_workspace_bytes(int B, int gamma, int V, int rank, int dtype) {
   (void)rank; (void)dtype;
-  const size_t nC = n_chunks(V);
+  const size_t nC = n_tiles(V);
   return align256((size_t)B * 4) + 3 * align256((size_t)B * (gamma + 1) * 4) +
          2 * align256((size_t)B * gamma * 4) + 2 * align256((size_t)B * nC * 4);
 }

@@ -29,9 +29,10 @@
  *    W2t, hidden): DSPARK_BF16 (bit patterns, round-to-nearest-even) or
  *    DSPARK_F32.  Accumulation is fp32 (bf16 inputs use MFMA), cross-tile
  *    sums and cumulative sums are fp64.
- *  - Shapes: V % 8 == 0; rank in {32, 64, 128, 256} for bf16 (the matrix-
- *    core path stages 128 x rank tiles of W2t in LDS), any multiple of 32
- *    in [32, 512] for fp32; H % 8 == 0; 1 <= gamma <= 64; B >= 1.
+ *  - Shapes: V % 8 == 0 and V <= 262144 (larger: DSPARK_EUNSUPPORTED);
+ *    rank in {32, 64, 128, 256} for bf16 (the matrix-core path keeps
+ *    64 x rank tiles of W2t in LDS and registers), any multiple of 32 in
+ *    [32, 512] for fp32; H % 8 == 0; 1 <= gamma <= 64; B >= 1.
  *  - Positions are 0-based: draft position k (0..gamma-1) is the pages'
  *    x_{k+1}.
  *  - uniforms [B, gamma+1, 2] fp32 in [0,1): uniforms[b,k,0] draws draft
@@ -72,6 +73,8 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 #define DSPARK_DEV_DEGENERATE  4  /* residual had no mass; drew from p instead  */
 #define DSPARK_DEV_BAD_ELL     8  /* ell outside [0,gamma]; clamped             */
 #define DSPARK_DEV_BAD_CONF   16  /* confidence NaN or outside [0,1]; clamped   */
+#define DSPARK_DEV_TIMEOUT    32  /* a cross-work-group wait gave up; results of
+                                     the call are undefined (never expected)   */
 
 const char* dspark_status_str(int status);
 const char* dspark_last_error(void);
@@ -190,6 +193,21 @@ int dspark_verify(int B, int gamma, int V, int rank, int dtype,
  * ---------------------------------------------------------------------- */
 int dspark_trace_enable(int on);
 int dspark_trace_summary(char* buf, size_t len);
+
+/* ------------------------------------------------------------------------
+ * Drafting implementation choice (process-wide; for tests and benchmarks).
+ * 0 = automatic (default): the persistent single-launch kernel for bf16
+ *     inputs when the device supports cooperative launch and the vocabulary
+ *     fits its resident tiles, else one launch pair per position;
+ * 1 = always one launch pair per position;
+ * 2 = persistent only: dspark_draft_block returns DSPARK_EHIP where it
+ *     cannot run;
+ * 3, 4 = persistent only, with 8 (one register-resident W2t tile each) or
+ *     4 (two each) waves per work-group; 2 picks 4 from rank 128 up, else 8.
+ * All settings return identical results.
+ * Returns the previous setting, or DSPARK_EINVAL for another value.
+ * ---------------------------------------------------------------------- */
+int dspark_set_draft_path(int path);
 
 #ifdef __cplusplus
 }

@@ -36,9 +36,11 @@ def test_status_strings_and_version(lib):
 
 
 def test_workspace_queries(lib):
-    # per-128-entry-tile max + argmax and per-64-entry chunk sums, 256-byte aligned
-    nT = (151936 + 127) // 128
-    expect = 2 * ((128 * nT * 4 + 255) // 256 * 256) + (128 * nT * 2 * 4 + 255) // 256 * 256
+    # per-64-entry-tile max, argmax and exp-sum, then the persistent kernel's
+    # flag words (4096 groups x 128 bytes, one word per request), 256-byte aligned
+    a256 = lambda n: (n + 255) // 256 * 256
+    nT = (151936 + 63) // 64
+    expect = 3 * a256(128 * nT * 4) + a256(4096 * 32 * 4) + a256(128 * 4)
     assert dv.dspark_draft_block_workspace(128, 15, 151936, 256, 1) == expect
     assert dv.dspark_draft_block_workspace(128, 15, 151937, 256, 1) == 0  # invalid V
     assert dv.dspark_verify_workspace(4, 5, 1024, 32, 0) > 0

@@ -171,6 +171,49 @@ def test_full_size_configs(cfg):
     print(f"config {cfg}: mean ell {ell.mean():.2f}, mean accepted {n.mean():.2f}", flush=True)
 
 
+PATH_CASES = {
+    "bf16-ragged-V1000-B40": lambda: SMALL["bf16-ragged-V1000-B40"](),
+    "bf16-greedy-mix-T0.7": lambda: SMALL["bf16-greedy-mix-T0.7"](),
+    "bf16-strong-bias": lambda: SMALL["bf16-strong-bias"](),
+    "bf16-B300-rank128-V5000": lambda: make_custom(300, 3, 5000, 128, 16, "bf16", "mixture",
+                                                   seed=9, temperature=0.8, greedy_frac=0.2),
+    "config 1 full size": lambda: make_config(1),
+}
+
+
+@pytest.mark.parametrize("name", list(PATH_CASES))
+def test_draft_paths_agree(name):
+    """The persistent kernel (8 and 4 waves per work-group) and the
+    per-position launches give the same bits."""
+    import draft_verify_sampling_block_amd as dv
+    from draft_verify_sampling_block_amd.step import upload
+    wl = PATH_CASES[name]()
+    d = upload(wl, "cuda", scheduler=False)
+    res = {}
+    for path in (1, 3, 4):
+        _say(f"{name}: draft path {path}")
+        old = dv.dspark_set_draft_path(path)
+        try:
+            st = torch.zeros((1,), dtype=torch.int32, device="cuda")
+            out = dv.dspark_draft_block(d.U, d.W1, d.W2t, d.anchor, d.temperature, d.uniforms,
+                                        status=st)
+            torch.cuda.synchronize()
+        finally:
+            dv.dspark_set_draft_path(old)
+        res[path] = [out[k].cpu().numpy() for k in ("tokens", "q_tok", "row_max", "row_logZ")]
+        res[path].append(int(st.item()))
+    for path in (3, 4):
+        for i, key in enumerate(("tokens", "q_tok", "row_max", "row_logZ")):
+            assert np.array_equal(res[1][i], res[path][i]), (path, key)
+    assert all(res[p][4] == 0 for p in res), {p: res[p][4] for p in res}
+    B, g = wl.B, wl.gamma
+    rows = None
+    if B * g > 200:
+        rng = np.random.default_rng(7)
+        rows = [(int(i) // g, int(i) % g) for i in rng.choice(B * g, 40, replace=False)]
+    print(check_draft(wl, f64(wl.W1), f64(wl.W2t), *res[1][:4], rows=rows), flush=True)
+
+
 def test_repeat_is_deterministic():
     _say("determinism")
     wl = SMALL["bf16-ragged-V1000-B40"]()
