@@ -37,10 +37,15 @@ constexpr bool kIsBf16 = std::is_same<T, uint16_t>::value;
 // ---------------------------------------------------------------------------
 
 struct TileStats {
-  float* max;     // [B][nT] max over the tile of y' = z + bias (unscaled logits)
-  int32_t* arg;   // [B][nT] lowest vocabulary index attaining it (greedy rows)
-  float* sum;     // [B][nT] sum over the tile of exp((y' - max) / T)
+  uint64_t* ms;   // [B][nT] (max, sum) as two fp32: max over the tile of y' = z + bias
+                  // (unscaled logits), sum over the tile of exp((y' - max) / T)
+  int32_t* arg;   // [B][nT] lowest vocabulary index attaining the max (greedy rows only)
 };
+__device__ inline uint64_t pack_ms(float mx, float s) {
+  return (uint64_t)__float_as_uint(mx) | ((uint64_t)__float_as_uint(s) << 32);
+}
+__device__ inline float ms_max(uint64_t v) { return __uint_as_float((uint32_t)v); }
+__device__ inline float ms_sum(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
 
 // inverse temperature of a request; 0 marks greedy
 __device__ inline float inv_temp(float T) { return (T > 0.f) ? 1.f / T : 0.f; }
@@ -52,14 +57,17 @@ __device__ inline float tile_term(float yp, float ce, float mc) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(yp, ce, -mc));
 }
 
-// Epilogue of one block-tile for this lane's request b (column c): acc holds
-// y' = base logit + bias (-inf past V); computes the tile max / lowest
-// argmax / exp-sum, combined over the two half-waves, and the h = 0 lane
-// stores them with device-coherent stores.  `it` is the lane's inverse
-// temperature (0 = greedy); `any_greedy` is wave-uniform.
-__device__ inline void block_tile_epilogue(const f32x16_t acc[kSub], int b, int B, int vt,
-                                           int nT, float it, bool any_greedy,
-                                           const TileStats& ts) {
+// Reduction of one block-tile for this lane's request (column c): acc holds
+// y' = base logit + bias (-inf past V); gives the tile max, lowest argmax
+// (when `any_greedy`, which is wave-uniform) and exp-sum, combined over the
+// two half-waves so both lanes of the request hold them.  `it` is the lane's
+// inverse temperature (0 = greedy).
+struct TileStat {
+  float mx, s;
+  int arg;
+};
+__device__ inline TileStat tile_reduce(const f32x16_t acc[kSub], int vt, float it,
+                                       bool any_greedy) {
   const int h = (threadIdx.x & 63) >> 5;
   float mx = -INFINITY;
 #pragma unroll
@@ -91,13 +99,16 @@ __device__ inline void block_tile_epilogue(const f32x16_t acc[kSub], int b, int 
     for (int j = 0; j < 16; ++j) s += tile_term(acc[t][j], ce, mc);
   }
   half_pair(s, lo, hi);
-  s = lo + hi;
-  if (b < B && h == 0) {
-    const size_t i = (size_t)b * nT + vt;
-    st_dev(ts.max + i, mx);
-    st_dev(ts.arg + i, arg);
-    st_dev(ts.sum + i, s);
-  }
+  return TileStat{mx, lo + hi, arg};
+}
+
+// store the statistics of request b (< B) for tile vt (device-coherent);
+// the argmax only for a greedy request (inverse temperature `it` 0)
+__device__ inline void store_tile_stat(const TileStats& ts, int b, int nT, int vt,
+                                       const TileStat& st, float it) {
+  const size_t i = (size_t)b * nT + vt;
+  st_dev(ts.ms + i, pack_ms(st.mx, st.s));
+  if (!(it > 0.f)) st_dev(ts.arg + i, st.arg);
 }
 
 // Shared-memory state of the per-request sampler (block-wide).
@@ -115,26 +126,36 @@ constexpr int kSampScratchBytes = kLdsTileBytes + 2 * kMaxTiles * 4;
 // Draw draft token k of request b from the tile statistics (all threads of
 // the work-group call this).  `scratch` is kSampScratchBytes of LDS.
 // Writes tokens (device-coherent store) and q_tok/row_max/row_logZ.
-template <typename T, int KS>
+template <typename T, int KS, int NTHR>
 __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, int prev,
                                const T* __restrict__ U, const T* __restrict__ W1,
                                const T* __restrict__ W2t, const float* __restrict__ temperature,
                                const float* __restrict__ uniforms, const TileStats& ts,
                                int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
-                               int32_t* status, char* scratch, SampShared& sh) {
-  const int tid = threadIdx.x, nthr = blockDim.x;
+                               int32_t* status, char* scratch, SampShared& sh,
+                               uint32_t* tok_flag) {
+  static_assert(NTHR >= 256, "the statistics loads assume >= 256 threads");
+  // thread 0: the token, published first (flag word (k + 1) << 24 | token
+  // when tok_flag is given, so that waiting work-groups read it with the
+  // flag itself), then the other outputs
+  auto emit = [&](int tok, float q, float rmax, float rlz) {
+    if (tok_flag) st_dev(tok_flag + b, ((uint32_t)(k + 1) << 24) | (uint32_t)tok);
+    tokens[(size_t)b * gamma + k] = tok;
+    q_tok[(size_t)b * gamma + k] = q;
+    row_max[(size_t)b * gamma + k] = rmax;
+    row_logZ[(size_t)b * gamma + k] = rlz;
+  };
+  const int tid = threadIdx.x, nthr = NTHR;
   const int nT = n_tiles(V);
   float* cm = reinterpret_cast<float*>(scratch + kLdsTileBytes);  // tile maxima
   float* cs = cm + kMaxTiles;                                      // tile sums
-  const float* tm = ts.max + (size_t)b * nT;
-  const float* tsum = ts.sum + (size_t)b * nT;
+  const uint64_t* tms = ts.ms + (size_t)b * nT;
   const float Tb = temperature[b];
   const bool greedy = !(Tb > 0.f);
   const size_t out = (size_t)b * gamma + k;
 
-  // all loads of the statistics are issued before any is used (work-groups
-  // of >= 256 threads: kMaxTiles / 256 per thread at most)
-  constexpr int kPer = kMaxTiles / 256;
+  // all loads of the statistics are issued before any is used
+  constexpr int kPer = kMaxTiles / NTHR;
   float xm[kPer], xs[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -142,8 +163,9 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
     xm[i] = -INFINITY;
     xs[i] = 0.f;
     if (t < nT) {
-      xm[i] = ld_dev(tm + t);
-      xs[i] = ld_dev(tsum + t);
+      const uint64_t v = ld_dev(tms + t);
+      xm[i] = ms_max(v);
+      xs[i] = ms_sum(v);
     }
   }
   float m = -INFINITY;
@@ -168,10 +190,7 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
         flag(status, DSPARK_DEV_NONFINITE);
         a = 0;
       }
-      st_dev(tokens + out, a);
-      q_tok[out] = 1.f;
-      row_max[out] = m;
-      row_logZ[out] = 0.f;
+      emit(a, 1.f, m, 0.f);
     }
     __syncthreads();
     return;
@@ -216,10 +235,7 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
   if (!finite || vt < 0) {
     if (tid == 0) {
       flag(status, DSPARK_DEV_NONFINITE);
-      st_dev(tokens + out, 0);
-      q_tok[out] = 0.f;
-      row_max[out] = ms;
-      row_logZ[out] = (float)log(Z);
+      emit(0, 0.f, ms, (float)log(Z));
     }
     __syncthreads();
     return;
@@ -249,15 +265,19 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
         const bf16x8_t f = *reinterpret_cast<const bf16x8_t*>(sh.arow + 16 * (2 * ks + h));
         return mine ? f : zero;
       };
-      f32x16_t acc[kSub];
-      init_acc<T>(ur, rem, acc);
-      bias_tile_ldsA<KS>(bfrag, scratch, acc);
-      if (mine) {
+      // one sub-tile at a time; the clobber keeps the operand reads of the
+      // second pass from being merged with the first (fewer live registers)
 #pragma unroll
-        for (int t = 0; t < kSub; ++t) {
+      for (int t = 0; t < kSub; ++t) {
+        f32x16_t acc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = (32 * t + j < rem) ? urow_at(ur, t, j) : -INFINITY;
+        asm volatile("" ::: "memory");
+        bias_subtile_ldsA<KS>(bfrag, scratch, t, acc);
+        if (mine) {
           float* se = sh.se + 32 * t + 16 * h;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) se[j] = tile_term(acc[t][j], ce, mc);
+          for (int j = 0; j < 16; ++j) se[j] = tile_term(acc[j], ce, mc);
         }
       }
     }
@@ -278,21 +298,23 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
     }
   }
   __syncthreads();
-  if (tid == 0) {
+  // inverse CDF inside the tile on wave 0: lane i holds entry i; prefix
+  // sums over the wave, the first entry whose running mass exceeds r wins
+  // (the last positive one if rounding leaves r past the total)
+  if (tid < kWave) {
     const double r = (target - sh.before) / sh.scale;
-    double run = 0.0;
-    int pick = -1, lastp = -1;
-    for (int i = 0; i < kTileV; ++i) {
-      const double e = (double)sh.se[i];
-      if (e > 0.0) lastp = i;
-      run += e;
-      if (e > 0.0 && r < run) { pick = i; break; }
+    const double e = (double)sh.se[tid];
+    double incl = e;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const double n = __shfl_up(incl, o, kWave);
+      if (tid >= o) incl += n;
     }
-    if (pick < 0) pick = lastp < 0 ? 0 : lastp;
-    st_dev(tokens + out, v0 + pick);
-    q_tok[out] = (float)((double)sh.se[pick] * sh.scale / Z);
-    row_max[out] = ms;
-    row_logZ[out] = (float)log(Z);
+    const unsigned long long hit = __ballot(e > 0.0 && r < incl);
+    const unsigned long long pos = __ballot(e > 0.0);
+    const int pick = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
+    if (tid == 0)
+      emit(v0 + pick, (float)((double)sh.se[pick] * sh.scale / Z), ms, (float)log(Z));
   }
   __syncthreads();
 }
@@ -344,7 +366,8 @@ __global__ __launch_bounds__(256) void draft_stats_kernel(
                     v0, V, rank, acc);
     const int b = rb * kTileM + c;
     const bool any_greedy = __ballot((b < B) && !(it > 0.f)) != 0;
-    block_tile_epilogue(acc, b, B, vt, nT, it, any_greedy, ts);
+    const TileStat st = tile_reduce(acc, vt, it, any_greedy);
+    if (b < B && h == 0) store_tile_stat(ts, b, nT, vt, st, it);
     rb += 4;
     if (rb < nRB) setup(rb);
   }
@@ -361,8 +384,8 @@ __global__ __launch_bounds__(256) void draft_sample_kernel(
   __shared__ SampShared sh;
   const int b = blockIdx.x;
   const int prev = clamp_token(prev_src[(size_t)b * prev_stride], V, nullptr);
-  sample_request<T, KS>(b, k, B, gamma, V, rank, prev, U, W1, W2t, temperature, uniforms, ts,
-                        tokens, q_tok, row_max, row_logZ, status, scratch, sh);
+  sample_request<T, KS, 256>(b, k, B, gamma, V, rank, prev, U, W1, W2t, temperature, uniforms,
+                             ts, tokens, q_tok, row_max, row_logZ, status, scratch, sh, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -374,7 +397,7 @@ constexpr int kPdLdsTiles = 2;              // extra resident tiles in LDS
 constexpr int kPdMaxRows = 128;             // W1 rows gathered per chunk
 constexpr int kPdFlagStride = 32;           // 128-byte spacing of per-group flags
 constexpr int kPdMaxGroups = 4096;
-constexpr int kPdRowBytes = kPdMaxRows * kMaxKSteps * 2 * 16;   // 64 KB
+constexpr int kPdRowBytes = kPdMaxRows * (2 * kMaxKSteps + 1) * 16;   // 66 KB (padded rows)
 static_assert(kPdRowBytes >= kSampScratchBytes, "the sampler reuses the W1 row area");
 
 struct PdArgs {
@@ -392,7 +415,7 @@ struct PdArgs {
   int32_t* status;
   TileStats ts;
   uint32_t* stats_flag;  // [P * kPdFlagStride]: positions whose statistics group p published
-  uint32_t* tok_flag;    // [B]: positions whose token request b published
+  uint32_t* tok_flag;    // [B]: ((k + 1) << 24) | token k of request b, once drawn
   long long spin_cap;    // wall-clock ticks a wait may last
 };
 
@@ -400,18 +423,24 @@ __device__ inline uint32_t ld_flag(const uint32_t* p) { return ld_dev(p); }
 __device__ inline void st_flag(uint32_t* p, uint32_t v) { st_dev(p, v); }
 
 // Wave 0 waits until flags[i*stride] >= want for all i < n; then the group
-// synchronises.  The wait is bounded: past `cap_ticks` of the device wall
-// clock it raises DSPARK_DEV_TIMEOUT and gives up, and any group that sees
-// that flag already raised gives up at once, so a kernel whose groups cannot
-// all make progress still drains.  All threads of the work-group call it.
+// synchronises.  With `low` given (n <= kPdMaxRows), the low 24 bits of each
+// flag as finally read are left in low[i].  The wait is bounded: past
+// `cap_ticks` of the device wall clock it raises DSPARK_DEV_TIMEOUT and gives
+// up, and any group that sees that flag already raised gives up at once, so a
+// kernel whose groups cannot all make progress still drains.  All threads of
+// the work-group call it.
 __device__ inline void wait_flags(const uint32_t* flags, int n, int stride, uint32_t want,
-                                  long long cap_ticks, int32_t* status) {
+                                  long long cap_ticks, int32_t* status, int* low = nullptr) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     const long long t0 = wall_clock64();
     for (int it = 0;; ++it) {
       bool ok = true;
-      for (int i = lane; i < n; i += kWave) ok &= ld_flag(flags + (size_t)i * stride) >= want;
+      for (int i = lane; i < n; i += kWave) {
+        const uint32_t v = ld_flag(flags + (size_t)i * stride);
+        ok &= v >= want;
+        if (low) low[i] = (int)(v & 0xFFFFFFu);
+      }
       if (__all(ok)) break;
       if ((it & 15) == 15) {
         const bool late = wall_clock64() - t0 > cap_ticks;
@@ -446,10 +475,17 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
   __shared__ __attribute__((aligned(16))) char ldsA[kPdRowBytes];
   __shared__ int s_tok[kPdMaxRows];
   __shared__ float s_it[kPdMaxRows];   // inverse temperatures of the chunk
+  // statistics of the chunk's block-tasks, per resident tile slot (register
+  // tile i of wave w: slot w + NW i; LDS tile i: slot kPdRegTiles + i) and
+  // chunk row; written to memory once the chunk is done
+  constexpr int kSlots = kPdRegTiles + kPdLdsTiles;
+  __shared__ float s_mx[kSlots][kPdMaxRows], s_sum[kSlots][kPdMaxRows];
+  __shared__ int s_arg[kSlots][kPdMaxRows];
   __shared__ SampShared sh;
 
   const int p = blockIdx.x, P = a.P;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int B = a.B, V = a.V, gamma = a.gamma;
   const int nT = n_tiles(V);
@@ -534,7 +570,12 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
     while (fch < nch && chunk_tasks(fch, start) == 0) ++fch;
 #pragma unroll
     for (int d = 0; d < D; ++d) fetch_next(ring[d], start, k);
-    if (k > 0) wait_flags(a.tok_flag, B, 1, (uint32_t)k, a.spin_cap, a.status);
+    // tokens of position k - 1: flag words (k << 24) | token; with one chunk
+    // the wait leaves them in s_tok directly
+    const bool tok_in_lds = k > 0 && nch == 1;
+    if (k > 0)
+      wait_flags(a.tok_flag, B, 1, (uint32_t)k << 24, a.spin_cap, a.status,
+                 tok_in_lds ? s_tok : nullptr);
 
     // run the task in slot sl: start the accumulators at its base logits,
     // refill the slot with the task D ahead, add the bias, reduce
@@ -566,11 +607,30 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
           if (which == -1 - i) bias_tile_regA<KS>(bfrag, wreg[i], acc);
       }
       const bool any_greedy = __ballot((b < B) && !(it > 0.f)) != 0;
-      block_tile_epilogue(acc, b, B, tile, nT, it, any_greedy, a.ts);
+      const TileStat st = tile_reduce(acc, tile, it, any_greedy);
+      if (h == 0) {
+        const int slot = which >= 0 ? kPdRegTiles + which : wave + NW * (-1 - which);
+        s_mx[slot][lrow] = st.mx;
+        s_sum[slot][lrow] = st.s;
+        s_arg[slot][lrow] = st.arg;
+      }
+    };
+    // write the finished chunk's statistics (all waves done: caller synced)
+    auto flush = [&](int chd) {
+      const int r0 = chd * kPdMaxRows;
+      const int nrows = min(kPdMaxRows, B - r0);
+      for (int e = threadIdx.x; e < kSlots * kPdMaxRows; e += blockDim.x) {
+        const int slot = e % kSlots, row = e / kSlots;
+        const int tile = p + P * slot;
+        if (row < nrows && tile < nT)
+          store_tile_stat(a.ts, r0 + row, nT, tile,
+                          TileStat{s_mx[slot][row], s_sum[slot][row], s_arg[slot][row]},
+                          s_it[row]);
+      }
     };
 
-    int g = 0;
-    for (int ch = 0; ch < nch; ++ch) {
+    // stage chunk ch: its previous tokens' W1 rows and inverse temperatures
+    auto load_chunk = [&](int ch) {
       const int r0 = ch * kPdMaxRows;
       const int nrows = min(kPdMaxRows, B - r0);
       const int nblk = chunk_blocks(ch);
@@ -579,7 +639,8 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
         float it = 0.f;
         if (r < nrows) {
           const int b = r0 + r;
-          t = (k == 0) ? a.anchor[b] : ld_dev(a.tokens + (size_t)b * gamma + k - 1);
+          t = (k == 0) ? a.anchor[b]
+                       : tok_in_lds ? s_tok[r] : (int)(ld_dev(a.tok_flag + b) & 0xFFFFFFu);
           t = clamp_token(t, V, k == 0 ? a.status : nullptr);
           it = inv_temp(a.temperature[b]);
         }
@@ -590,15 +651,49 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
       stage_gather(a.W1, s_tok, a.rank, ldsA, nblk * kTileM);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      const int gend = g + chunk_tasks(ch, start);
-      for (; g < gend; ++g) {
-        if (D == 1 || (g & 1) == 0)
-          run_task(ring[0]);
-        else
-          run_task(ring[D - 1]);
+    };
+    // Every wave stages every chunk in order (the barriers match), switching
+    // chunk whenever its next task lies in the following one.  The task loop
+    // is unrolled by the ring depth so each slot stays in fixed registers
+    // and its loads stay in flight until the slot's task runs.
+    int ch = -1, chunk_end = 0, g = 0;
+    auto enter = [&]() {
+      while (g == chunk_end && ch + 1 < nch) {
+        if (ch >= 0) {
+          __syncthreads();  // chunk ch done: the row area and statistics are reused
+          flush(ch);
+        }
+        ++ch;
+        load_chunk(ch);
+        chunk_end += chunk_tasks(ch, start);
       }
-      __syncthreads();  // the W1 row area is reused by the next chunk / sampler
+    };
+    const int ntot = [&] {
+      int n = 0;
+      for (int cc = 0; cc < nch; ++cc) n += chunk_tasks(cc, start);
+      return n;
+    }();
+    while (g < ntot) {
+      enter();
+      run_task(ring[0]);
+      ++g;
+      if constexpr (D == 2) {
+        if (g >= ntot) break;
+        enter();
+        run_task(ring[1]);
+        ++g;
+      }
     }
+    while (ch + 1 < nch) {   // chunks after this wave's last task
+      if (ch >= 0) {
+        __syncthreads();
+        flush(ch);
+      }
+      ++ch;
+      load_chunk(ch);
+    }
+    __syncthreads();  // the W1 row area is reused by the sampler
+    flush(ch);
     // publish this group's statistics of position k
     stores_done_group();
     if (threadIdx.x == 0) st_flag(a.stats_flag + (size_t)p * kPdFlagStride, (uint32_t)(k + 1));
@@ -611,12 +706,11 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
         waited = true;
       }
       const int prev = clamp_token(
-          k == 0 ? a.anchor[b] : ld_dev(a.tokens + (size_t)b * gamma + k - 1), V, nullptr);
-      sample_request<uint16_t, KS>(b, k, B, gamma, V, a.rank, prev, a.U, a.W1, a.W2t,
-                                   a.temperature, a.uniforms, a.ts, a.tokens, a.q_tok,
-                                   a.row_max, a.row_logZ, a.status, ldsA, sh);
-      stores_done_group();
-      if (threadIdx.x == 0) st_flag(a.tok_flag + b, (uint32_t)(k + 1));
+          k == 0 ? a.anchor[b] : (int)(ld_dev(a.tok_flag + b) & 0xFFFFFFu), V, nullptr);
+      sample_request<uint16_t, KS, NW * 64>(b, k, B, gamma, V, a.rank, prev, a.U, a.W1, a.W2t,
+                                            a.temperature, a.uniforms, a.ts, a.tokens, a.q_tok,
+                                            a.row_max, a.row_logZ, a.status, ldsA, sh,
+                                            a.tok_flag);
     }
   }
 }
@@ -672,9 +766,8 @@ size_t draft_workspace_bytes(int B, int gamma, int V, int rank, int dtype) {
 static TileStats carve_stats(void* ws, int B, int V) {
   char* w = static_cast<char*>(ws);
   TileStats ts;
-  ts.max = reinterpret_cast<float*>(w);
-  ts.arg = reinterpret_cast<int32_t*>(w + stats_bytes(B, V));
-  ts.sum = reinterpret_cast<float*>(w + 2 * stats_bytes(B, V));
+  ts.ms = reinterpret_cast<uint64_t*>(w);                          // 2 x stats_bytes
+  ts.arg = reinterpret_cast<int32_t*>(w + 2 * stats_bytes(B, V));
   return ts;
 }
 
@@ -716,9 +809,10 @@ static hipError_t draft_persistent(int B, int gamma, int V, int rank, const uint
   if (!di.coop || P < 1 || P > kPdMaxGroups) return hipErrorNotSupported;
   if ((long long)n_tiles(V) > (long long)P * (kPdRegTiles + kPdLdsTiles))
     return hipErrorNotSupported;
-  // waves per group: 4 (two register tiles each) from rank 128 up, where
-  // one tile per wave leaves too few registers at two waves per SIMD; else 8
-  const int nw = g_draft_path == 3 ? 8 : g_draft_path == 4 ? 4 : (KS >= 8 ? 4 : 8);
+  // waves per group: 8 (one register tile each, two waves per SIMD, which
+  // overlap one wave's reductions with the other's matrix instructions)
+  // unless 4 (two tiles each) are asked for
+  const int nw = g_draft_path == 4 ? 4 : 8;
   const void* kern = nw == 8 ? reinterpret_cast<const void*>(pdraft_kernel<KS, 8>)
                              : reinterpret_cast<const void*>(pdraft_kernel<KS, 4>);
   int occ = 0;

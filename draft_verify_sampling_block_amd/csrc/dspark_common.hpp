@@ -21,10 +21,9 @@
 // exchange between the two half-waves.
 //
 // W2t tile rows staged in LDS are stored in matrix-row order (LDS row
-// 32t + i holds entry v0 + 32t + sub_row_vocab(i)) with their 16-byte
-// k-chunks XOR-swizzled per row, so that the 16 lanes of each quarter-wave,
-// which read 16 consecutive rows at one k-chunk, hit 16 distinct bank
-// groups.  The per-tile statistics (max, lowest argmax, sum of exp(y - max))
+// 32t + i holds entry v0 + 32t + sub_row_vocab(i)), each row padded by one
+// 16-byte chunk, so that the 16 lanes of each quarter-wave, which read 16
+// consecutive rows at one k-chunk, hit 16 distinct bank groups.  The per-tile statistics (max, lowest argmax, sum of exp(y - max))
 // are the first level of the two-level inverse-CDF draw; the per-request
 // sampler scans them in fp64 and recomputes only the one tile where the
 // cumulative mass crosses u * Z, with the same instructions on the same
@@ -44,7 +43,7 @@ constexpr int kTileM = 32;        // requests per block
 constexpr int kTileV = 64;        // vocabulary entries per tile
 constexpr int kSub = 2;           // 32-column matrix sub-tiles per tile
 constexpr int kMaxKSteps = 16;    // rank <= 256
-constexpr int kLdsTileBytes = kTileV * kMaxKSteps * 2 * 16;   // 32 KB
+constexpr int kLdsTileBytes = kTileV * (2 * kMaxKSteps + 1) * 16;   // 33 KB (padded rows)
 constexpr int kMaxTiles = kMaxVocab / kTileV;     // 4096 (kMaxVocab: dspark_launch.hpp)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -71,10 +70,13 @@ template <> struct URow<float> {
   u32x4_t w[kSub][kLoads];
 };
 
-// `row` is the start of a length-V row; `ok` false (or entries past V) give
-// zeros.  V % 8 == 0 keeps every 16-byte load wholly inside or outside; an
-// excluded load reads `safe` (any valid 16-byte-aligned address) instead,
-// so that no load is predicated.
+// `row` is the start of a length-V row.  A load that `ok` false or the end
+// of the row excludes reads `safe` (any valid 16-byte-aligned address)
+// instead, so no load is predicated; its values are meaningless and every
+// caller discards them (entries past V start at -inf in init_acc, lanes of
+// absent requests are never stored).  Nothing selects on the loaded values
+// here, so the loads stay in flight until their first real use.  V % 8 == 0
+// keeps every 16-byte load wholly inside or outside the row.
 template <typename T>
 __device__ inline void load_urow(URow<T>& u, const T* __restrict__ row, int v0, int V, bool ok,
                                  const T* __restrict__ safe) {
@@ -87,8 +89,7 @@ __device__ inline void load_urow(URow<T>& u, const T* __restrict__ row, int v0, 
     for (int q = 0; q < URow<T>::kLoads; ++q) {
       const bool in = ok && (32 * t + q * per < rem);
       const T* p = in ? row + vb + 32 * t + q * per : safe;
-      const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-      u.w[t][q] = in ? x : u32x4_t{};
+      u.w[t][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
     }
   }
 }
@@ -196,51 +197,50 @@ __host__ __device__ inline int tile_row_vocab(int r) { return (r & 32) + sub_row
 
 // ---------------------------------------------------------------------------
 // Rows of rank bf16 in LDS (W2t tile rows, or gathered W1 rows): nq = rank/8
-// chunks of 16 bytes per row, chunk q stored at slot q ^ swz(r).  The XOR
-// key makes 16 consecutive rows read at one chunk land in 16 distinct
-// 16-byte bank groups for every nq in {4, 8, 16, 32}.
+// chunks of 16 bytes per row plus one pad chunk, so a row takes nq + 1
+// chunks.  nq + 1 is odd, so 16 consecutive rows read at one chunk land in
+// 16 distinct 16-byte bank groups, and chunk q of row r sits at the fixed
+// offset (r (nq + 1) + q) 16: a k-step's operand address is the row base
+// plus an immediate.
 // ---------------------------------------------------------------------------
-__device__ inline int lds_swz(int r, int nq) {
-  return nq >= 16 ? (r & 15) : ((r / (16 / nq)) & (nq - 1));
-}
-__device__ inline int lds_off(int r, int q, int nq) { return (r * nq + (q ^ lds_swz(r, nq))) * 16; }
+__host__ __device__ constexpr int lds_row_bytes(int nq) { return (nq + 1) * 16; }
+__device__ inline int lds_off(int r, int q, int nq) { return r * lds_row_bytes(nq) + q * 16; }
 
-// DMA the 64 rows of W2t tile v0 into `lds` in matrix-row order: LDS row r
-// <- W2t row v0 + tile_row_vocab(r), clamped to V - 1 (rows past V are
-// never used: their logits are masked).  Every wave of the work-group takes
-// part.  Completion: s_waitcnt + barrier by the caller.
+// DMA nrows rows into `lds` (row r <- src row row_of(r)); the pad chunk of
+// each row is filled with the row's chunk 0.  Every wave of the work-group
+// takes part.  Completion: s_waitcnt + barrier by the caller.
+template <typename RowOf>
+__device__ inline void stage_rows_lds(const uint16_t* __restrict__ src, int rank, char* lds,
+                                      int nrows, RowOf&& row_of) {
+  const int nq = rank >> 3, nc = nq + 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int nslots = nrows * nc;
+  for (int g = wave; g * 64 < nslots; g += nwaves) {
+    const int s = g * 64 + lane;
+    if (s < nslots) {
+      const int r = s / nc, q = s - r * nc;
+      __builtin_amdgcn_global_load_lds(src + (size_t)row_of(r) * rank + (q < nq ? q : 0) * 8,
+                                       lds + (size_t)(g * 64) * 16, 16, 0, 0);
+    }
+  }
+}
+
+// The 64 rows of W2t tile v0 in matrix-row order: LDS row r <- W2t row
+// v0 + tile_row_vocab(r), clamped to V - 1 (rows past V are never used:
+// their logits start at -inf).
 __device__ inline void stage_tile(const uint16_t* __restrict__ W2t, int v0, int V, int rank,
                                   char* lds) {
-  const int nq = rank >> 3;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  const int nslots = kTileV * nq;          // a multiple of 64
-  for (int g = wave; g * 64 < nslots; g += nwaves) {
-    const int s = g * 64 + lane;
-    const int r = s / nq, p = s - r * nq;
-    const int q = p ^ lds_swz(r, nq);
-    int v = v0 + tile_row_vocab(r);
-    v = v < V ? v : V - 1;
-    __builtin_amdgcn_global_load_lds(W2t + (size_t)v * rank + q * 8,
-                                     lds + (size_t)(g * 64) * 16, 16, 0, 0);
-  }
+  stage_rows_lds(W2t, rank, lds, kTileV, [&](int r) {
+    const int v = v0 + tile_row_vocab(r);
+    return v < V ? v : V - 1;
+  });
 }
 
-// DMA gathered rows: LDS row r <- src row ids[r]; nrows rows (nrows * nq a
-// multiple of 64).
+// Gathered rows: LDS row r <- src row ids[r] (ids in LDS or memory).
 __device__ inline void stage_gather(const uint16_t* __restrict__ src, const int* ids, int rank,
                                     char* lds, int nrows) {
-  const int nq = rank >> 3;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
-  const int nslots = nrows * nq;
-  for (int g = wave; g * 64 < nslots; g += nwaves) {
-    const int s = g * 64 + lane;
-    const int r = s / nq, p = s - r * nq;
-    const int q = p ^ lds_swz(r, nq);
-    __builtin_amdgcn_global_load_lds(src + (size_t)ids[r] * rank + q * 8,
-                                     lds + (size_t)(g * 64) * 16, 16, 0, 0);
-  }
+  stage_rows_lds(src, rank, lds, nrows, [&](int r) { return ids[r]; });
 }
 
 __device__ inline bf16x8_t lds_frag(const char* lds, int r, int q, int nq) {

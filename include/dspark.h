@@ -203,7 +203,7 @@ int dspark_trace_summary(char* buf, size_t len);
  * 2 = persistent only: dspark_draft_block returns DSPARK_EHIP where it
  *     cannot run;
  * 3, 4 = persistent only, with 8 (one register-resident W2t tile each) or
- *     4 (two each) waves per work-group; 2 picks 4 from rank 128 up, else 8.
+ *     4 (two each) waves per work-group; 2 picks 8.
  * All settings return identical results.
  * Returns the previous setting, or DSPARK_EINVAL for another value.
  * ---------------------------------------------------------------------- */
