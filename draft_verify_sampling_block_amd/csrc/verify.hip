@@ -38,6 +38,8 @@ struct VerifyWs {
   int32_t* wacc;       // [B][gamma]
   float* fchunk;       // [B][nC] residual (or bonus p) chunk sums
   float* pchunk;       // [B][nC] p chunk sums of the residual slot (fallback)
+  int4* plan;          // [B] final draw of the request: (mode, slot, prev, -)
+  int32_t* any_res;    // [1] nonzero when some request draws from a residual
 };
 
 VerifyWs carve(void* ws, int B, int gamma, int V) {
@@ -52,6 +54,8 @@ VerifyWs carve(void* ws, int B, int gamma, int V) {
   w.wacc = reinterpret_cast<int32_t*>(p); p += align256((size_t)B * gamma * 4);
   w.fchunk = reinterpret_cast<float*>(p); p += align256((size_t)B * nC * 4);
   w.pchunk = reinterpret_cast<float*>(p); p += align256((size_t)B * nC * 4);
+  w.plan = reinterpret_cast<int4*>(p); p += align256((size_t)B * 16);
+  w.any_res = reinterpret_cast<int32_t*>(p); p += 256;
   return w;
 }
 
@@ -68,9 +72,10 @@ __device__ inline float inv_temp(float T) { return (T > 0.f) ? 1.f / T : 0.f; }
 
 }  // namespace
 
-__global__ void verify_init_kernel(int B, int32_t* first_rej) {
+__global__ void verify_init_kernel(int B, int32_t* first_rej, int32_t* any_res) {
   int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < B) first_rej[b] = 0x7fffffff;
+  if (b == 0) *any_res = 0;
 }
 
 template <typename T>
@@ -97,35 +102,57 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
   const float scale = greedy ? 1.f : it;
   const T* row = target + ((size_t)b * (gamma + 1) + k) * V;
 
+  // each thread: groups of kU chunks of 8 consecutive entries, all loads of a
+  // group in flight together; running max and exp-sum in fp32 (the sum is
+  // rescaled when the max grows), combined across threads in fp64
+  constexpr int kU = 4;
   float m = -INFINITY;
-  double s = 0.0;
+  float s32 = 0.f;
   int arg = 0x7fffffff;
-  for (int i = 8 * tid; i < V; i += 8 * 256) {
-    float y[8];
-    load8_f32_stream(row + i, y);
-    float gm = y[0] * scale;
+  const int stride = 8 * 256;
+  for (int base = 8 * tid; base < V; base += kU * stride) {
+    float y[kU][8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      y[t] *= scale;
-      gm = fmaxf(gm, y[t]);
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * stride;
+      if (i < V) {
+        load8_f32_stream(row + i, y[u]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) y[u][t] = -INFINITY;
+      }
+    }
+    float gm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        y[u][t] *= scale;
+        gm = fmaxf(gm, y[u][t]);
+      }
     }
     if (gm > m) {
       if (greedy) {
 #pragma unroll
-        for (int t = 7; t >= 0; --t)
-          if (y[t] == gm) arg = i + t;
-      } else if (s > 0.0) {
-        s *= exp((double)m - (double)gm);
+        for (int u = kU - 1; u >= 0; --u) {
+#pragma unroll
+          for (int t = 7; t >= 0; --t)
+            if (y[u][t] == gm) arg = base + u * stride + t;
+        }
+      } else if (s32 > 0.f) {
+        s32 *= __expf(m - gm);
       }
       m = gm;
     }
     if (!greedy) {
-      float g = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) g += __expf(y[t] - m);
-      s += (double)g;
+      for (int u = 0; u < kU; ++u) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) s32 += __expf(y[u][t] - m);
+      }
     }
   }
+  const double s = (double)s32;
   const float M = block_max(m, red);
   int a = 0x7fffffff;
   if (greedy) a = (m == M) ? arg : 0x7fffffff;
@@ -198,6 +225,18 @@ __device__ inline FinalRow final_row(int b, int B, int gamma, int V, const int32
   return f;
 }
 
+// the final draw of every request, once the first rejections are known
+__global__ void verify_plan_kernel(int B, int gamma, int V, const int32_t* __restrict__ ell,
+                                   const float* __restrict__ temperature,
+                                   const int32_t* __restrict__ anchor,
+                                   const int32_t* __restrict__ tokens, VerifyWs ws) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const FinalRow f = final_row(b, B, gamma, V, ell, temperature, anchor, tokens, ws);
+  ws.plan[b] = make_int4(f.mode, f.slot, f.prev, 0);
+  if (f.mode == 1) atomicOr(ws.any_res, 1);
+}
+
 // one work-group per 64-entry tile; waves take 32-request blocks
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void verify_final_stats_kernel(
@@ -215,10 +254,7 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
   const int vt = blockIdx.x, v0 = vt * kTileV;
 
   // does any request of the batch need the q recompute (a residual draw)?
-  int any = 0;
-  for (int b = threadIdx.x; b < B; b += blockDim.x)
-    any |= final_row(b, B, gamma, V, ell, temperature, anchor, tokens, ws).mode == 1;
-  const bool any_res = __syncthreads_or(any) != 0;
+  const bool any_res = *ws.any_res != 0;
   if (bf && any_res) stage_tile(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s);
 
   for (int rb = wave; rb < nRB || (rb == wave); rb += 4) {
@@ -226,8 +262,11 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
     // pass of every wave also joins the barrier that publishes the LDS tile
     const bool live = rb < nRB;
     const int b = rb * kTileM + c;
-    const FinalRow mine = final_row(live ? b : B, B, gamma, V, ell, temperature, anchor, tokens,
-                                    ws);
+    FinalRow mine{0, 0, -1};
+    if (live && b < B) {
+      const int4 pl = ws.plan[b];
+      mine = FinalRow{pl.x, pl.y, pl.z};
+    }
     bf16x8_t bfrag[KS];
     if constexpr (bf) load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1),
                                      mine.mode == 1 ? mine.prev : -1, bfrag);
@@ -449,7 +488,8 @@ size_t verify_workspace_bytes(int B, int gamma, int V, int rank, int dtype) {
   (void)rank; (void)dtype;
   const size_t nC = n_tiles(V);
   return align256((size_t)B * 4) + 3 * align256((size_t)B * (gamma + 1) * 4) +
-         2 * align256((size_t)B * gamma * 4) + 2 * align256((size_t)B * nC * 4);
+         2 * align256((size_t)B * gamma * 4) + 2 * align256((size_t)B * nC * 4) +
+         align256((size_t)B * 16) + 256;
 }
 
 template <typename T, int KS>
@@ -463,12 +503,19 @@ static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target
   VerifyWs ws = carve(wsp, B, gamma, V);
   {
     TraceScope t0("verify_init_kernel", stream);
-    verify_init_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(B, ws.first_rej);
+    verify_init_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(B, ws.first_rej,
+                                                                        ws.any_res);
   }
   {
     TraceScope t1("verify_rows_kernel", stream);
     verify_rows_kernel<T><<<dim3(B * (gamma + 1)), dim3(256), 0, stream>>>(
         B, gamma, V, target, tokens, q_tok, temperature, uniforms, ell, ws, status);
+  }
+  {
+    TraceScope tp("verify_plan_kernel", stream);
+    verify_plan_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(B, gamma, V, ell,
+                                                                        temperature, anchor,
+                                                                        tokens, ws);
   }
   {
     TraceScope t2("verify_final_stats_kernel", stream);
