@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 5 times "
+                         "(a reference for hardware byte counters), and exit")
     ap.add_argument("--draft-path", type=int, default=0,
                     help="dspark_set_draft_path value (0 = automatic)")
     ap.add_argument("--cpu-requests", type=int, default=0,
@@ -120,6 +123,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_mb:
+        n = args.copy_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+        return
     dv.load()
     dv.dspark_set_draft_path(args.draft_path)
     cfg = args.config

@@ -490,14 +490,20 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
   const int B = a.B, V = a.V, gamma = a.gamma;
   const int nT = n_tiles(V);
 
-  // resident W2t tiles: register tile i of wave w is p + P (w + NW i);
-  // LDS tile i is p + P (kPdRegTiles + i)
+  // Resident W2t tiles: group p owns the contiguous tiles [tbase, tbase +
+  // tcount) (the first nT % P groups one more), so that its statistics of a
+  // request form one contiguous run.  Tile slot s is tile tbase + s:
+  // register tile i of wave w is slot w + NW i, LDS tile i slot
+  // kPdRegTiles + i; slots >= tcount are empty.
+  const int tcount = nT / P + (p < nT % P ? 1 : 0);
+  const int tbase = p * (nT / P) + min(p, nT % P);
+  auto slot_tile = [&](int slot) { return slot < tcount ? tbase + slot : nT; };  // nT: none
   bf16x8_t wreg[R][KS][kSub];
 #pragma unroll
-  for (int i = 0; i < R; ++i) load_wreg<KS>(a.W2t, p + P * (wave + NW * i), V, wreg[i]);
+  for (int i = 0; i < R; ++i) load_wreg<KS>(a.W2t, slot_tile(wave + NW * i), V, wreg[i]);
   int nL = 0;
   for (int i = 0; i < kPdLdsTiles; ++i) {
-    const int tl = p + P * (kPdRegTiles + i);
+    const int tl = slot_tile(kPdRegTiles + i);
     if (tl < nT) {
       stage_tile(a.W2t, tl * kTileV, V, a.rank, ldsL + i * kLdsTileBytes);
       ++nL;
@@ -516,7 +522,7 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
   const int nch = (B + kPdMaxRows - 1) / kPdMaxRows;
   int nreg = 0;
 #pragma unroll
-  for (int i = 0; i < R; ++i) nreg += (p + P * (wave + NW * i) < nT) ? 1 : 0;
+  for (int i = 0; i < R; ++i) nreg += (slot_tile(wave + NW * i) < nT) ? 1 : 0;
   auto chunk_blocks = [&](int ch) {
     return (min(kPdMaxRows, B - ch * kPdMaxRows) + kTileM - 1) / kTileM;
   };
@@ -544,13 +550,13 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
     if (fidx < nreg * nblk) {
       const int i = (R == 2 && fidx >= nblk) ? 1 : 0;
       sl.rb = rbase + fidx - i * nblk;
-      sl.tile = p + P * (wave + NW * i);
+      sl.tile = slot_tile(wave + NW * i);
       sl.which = -1 - i;
     } else {
       const int li = start + (fidx - nreg * nblk) * NW;
       const int which = li >= nblk ? 1 : 0;
       sl.rb = rbase + li - which * nblk;
-      sl.tile = p + P * (kPdRegTiles + which);
+      sl.tile = slot_tile(kPdRegTiles + which);
       sl.which = which;
     }
     const int b = sl.rb * kTileM + c;
@@ -621,7 +627,7 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
       const int nrows = min(kPdMaxRows, B - r0);
       for (int e = threadIdx.x; e < kSlots * kPdMaxRows; e += blockDim.x) {
         const int slot = e % kSlots, row = e / kSlots;
-        const int tile = p + P * slot;
+        const int tile = slot_tile(slot);
         if (row < nrows && tile < nT)
           store_tile_stat(a.ts, r0 + row, nT, tile,
                           TileStat{s_mx[slot][row], s_sum[slot][row], s_arg[slot][row]},
