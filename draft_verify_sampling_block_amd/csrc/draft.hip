@@ -118,6 +118,7 @@ struct SampShared {
   int tile;
   float se[kTileV];
   __attribute__((aligned(16))) char arow[kMaxKSteps * 32];  // W1 row of the request (bf16)
+  __attribute__((aligned(16))) char useg[kTileV * 4];        // base logits of the crossing tile
 };
 // LDS the sampler needs besides SampShared: the crossing tile's W2t rows,
 // then a copy of the request's tile statistics
@@ -147,43 +148,33 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
   };
   const int tid = threadIdx.x, nthr = NTHR;
   const int nT = n_tiles(V);
-  float* cm = reinterpret_cast<float*>(scratch + kLdsTileBytes);  // tile maxima
-  float* cs = cm + kMaxTiles;                                      // tile sums
-  const uint64_t* tms = ts.ms + (size_t)b * nT;
+  // the request's packed tile statistics, copied to LDS (device-coherent
+  // reads); the row starts `shift` entries into the copy when it is not
+  // 16-byte aligned
+  const uint64_t* cms;
+  {
+    const size_t first = (size_t)b * nT;
+    const int shift = (int)(first & 1);
+    cms = reinterpret_cast<const uint64_t*>(scratch + kLdsTileBytes) + shift;
+    dma_copy<true>(ts.ms + (first - shift), scratch + kLdsTileBytes, (nT + shift + 1) / 2);
+  }
+  auto cm = [&](int t) { return ms_max(cms[t]); };
+  auto cs = [&](int t) { return ms_sum(cms[t]); };
   const float Tb = temperature[b];
+  const double u = (double)uniforms[((size_t)b * (gamma + 1) + k) * 2 + 0];
   const bool greedy = !(Tb > 0.f);
   const size_t out = (size_t)b * gamma + k;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  // all loads of the statistics are issued before any is used
-  constexpr int kPer = kMaxTiles / NTHR;
-  float xm[kPer], xs[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int t = tid + i * nthr;
-    xm[i] = -INFINITY;
-    xs[i] = 0.f;
-    if (t < nT) {
-      const uint64_t v = ld_dev(tms + t);
-      xm[i] = ms_max(v);
-      xs[i] = ms_sum(v);
-    }
-  }
   float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int t = tid + i * nthr;
-    if (t < nT) {
-      cm[t] = xm[i];
-      cs[t] = xs[i];
-      m = fmaxf(m, xm[i]);
-    }
-  }
-  m = block_max(m, sh.red);   // its barriers also publish cm / cs
+  for (int t = tid; t < nT; t += nthr) m = fmaxf(m, cm(t));
+  m = block_max(m, sh.red);
 
   if (greedy) {
     int a = 0x7fffffff;
     for (int t = tid; t < nT; t += nthr)
-      if (cm[t] == m) a = min(a, ld_dev(ts.arg + (size_t)b * nT + t));
+      if (cm(t) == m) a = min(a, ld_dev(ts.arg + (size_t)b * nT + t));
     a = block_min_int(a, sh.red);
     if (tid == 0) {
       if (!(m == m) || a < 0 || a >= V) {  // NaN logits leave no argmax
@@ -204,22 +195,22 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
   const int c0 = min(nT, tid * per), c1 = min(nT, c0 + per);
   double local = 0.0;
   for (int t = c0; t < c1; ++t)
-    local += (double)cs[t] * (double)__builtin_amdgcn_exp2f((cm[t] - m) * ce);
+    local += (double)cs(t) * (double)__builtin_amdgcn_exp2f((cm(t) - m) * ce);
   double start, end;
   const double Z = block_scan_interval(local, sh.red, &start, &end);
-  const double u = (double)uniforms[((size_t)b * (gamma + 1) + k) * 2 + 0];
-  const double target = u * Z;
+  // u * Z can round up to Z: the target is kept below Z, so exactly one
+  // thread's interval [start, end) holds it (the intervals tile [0, Z))
+  double target = u * Z;
+  if (!(target < Z)) target = nextafter(Z, 0.0);
   const bool finite = isfinite(m) && isfinite(Z) && Z > 0.0;
-  const int last_pos = block_max_int(local > 0.0 ? tid : -1, sh.red);
 
   if (tid == 0) sh.tile = -1;
   __syncthreads();
-  if (finite && local > 0.0 &&
-      ((start <= target && target < end) || (tid == last_pos && target >= end))) {
+  if (finite && local > 0.0 && start <= target && target < end) {
     double run = start, before = start, lastb = start;
     int found = -1, lastt = -1;
     for (int t = c0; t < c1; ++t) {
-      const double st = (double)cs[t] * (double)__builtin_amdgcn_exp2f((cm[t] - m) * ce);
+      const double st = (double)cs(t) * (double)__builtin_amdgcn_exp2f((cm(t) - m) * ce);
       if (st > 0.0) { lastt = t; lastb = run; }
       if (st > 0.0 && target < run + st) { found = t; before = run; break; }
       run += st;
@@ -227,7 +218,7 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
     if (found < 0) { found = lastt; before = lastb; }
     sh.tile = found;
     sh.before = before;
-    sh.scale = (double)__builtin_amdgcn_exp2f((cm[found] - m) * ce);
+    sh.scale = (double)__builtin_amdgcn_exp2f((cm(found) - m) * ce);
   }
   __syncthreads();
   const int vt = sh.tile;
@@ -235,13 +226,13 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
   if (!finite || vt < 0) {
     if (tid == 0) {
       flag(status, DSPARK_DEV_NONFINITE);
-      emit(0, 0.f, ms, (float)log(Z));
+      emit(0, 0.f, ms, __logf((float)Z));
     }
     __syncthreads();
     return;
   }
-  const float mc = cm[vt] * ce;
-  __syncthreads();   // cm / cs are dead from here: the tile rows may land
+  const float mc = cm(vt) * ce;
+  __syncthreads();   // the statistics copy is dead from here: the tile rows may land
 
   // recompute the crossing tile exactly as the statistics pass did: same
   // operands, request b in its own column b % 32, one sub-tile at a time
@@ -250,15 +241,14 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
   const int lane = tid & 63, c = lane & 31, h = lane >> 5;
   const bool mine = tid < kWave && c == mrow;
   const int rem = V - (v0 + 16 * h);   // usable entries: j < rem - 32t
-  URow<T> ur;
-  load_urow<T>(ur, U + out * V, v0, V, mine, U);
   if constexpr (kIsBf16<T>) {
+    // tile rows, the request's W1 row and base logits of the tile: all by DMA
     stage_tile(W2t, v0, V, rank, scratch);
-    if (tid < 2 * KS)
-      *reinterpret_cast<uint4*>(sh.arow + 16 * tid) =
-          *reinterpret_cast<const uint4*>(W1 + (size_t)prev * rank + 8 * tid);
+    dma_copy<false>(W1 + (size_t)prev * rank, sh.arow, rank / 8);
+    dma_copy<false>(U + out * V + v0, sh.useg, min(kTileV, V - v0) / 8);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    const uint16_t* useg = reinterpret_cast<const uint16_t*>(sh.useg) + 16 * h;
     if (tid < kWave) {
       const bf16x8_t zero = bf16x8_t{};
       auto bfrag = [&](int ks) {
@@ -271,7 +261,8 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
       for (int t = 0; t < kSub; ++t) {
         f32x16_t acc;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[j] = (32 * t + j < rem) ? urow_at(ur, t, j) : -INFINITY;
+        for (int j = 0; j < 16; ++j)
+          acc[j] = (32 * t + j < rem) ? bf16_to_f32(useg[32 * t + j]) : -INFINITY;
         asm volatile("" ::: "memory");
         bias_subtile_ldsA<KS>(bfrag, scratch, t, acc);
         if (mine) {
@@ -282,6 +273,8 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
       }
     }
   } else {
+    URow<T> ur;
+    load_urow<T>(ur, U + out * V, v0, V, mine, U);
     if (tid < kWave) {
       f32x16_t acc[kSub];
       init_acc<T>(ur, rem, acc);
@@ -314,7 +307,7 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
     const unsigned long long pos = __ballot(e > 0.0);
     const int pick = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
     if (tid == 0)
-      emit(v0 + pick, (float)((double)sh.se[pick] * sh.scale / Z), ms, (float)log(Z));
+      emit(v0 + pick, (float)((double)sh.se[pick] * sh.scale / Z), ms, __logf((float)Z));
   }
   __syncthreads();
 }
@@ -569,13 +562,19 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
     }
   };
 
-  for (int k = 0; k < gamma; ++k) {
-    const int start = (wave + k) % NW;   // rotate who takes the LDS extras
+  // put the first D tasks of position kk in flight
+  auto prime = [&](int kk) {
+    const int st = (wave + kk) % NW;
     fch = 0;
     fidx = 0;
-    while (fch < nch && chunk_tasks(fch, start) == 0) ++fch;
+    while (fch < nch && chunk_tasks(fch, st) == 0) ++fch;
 #pragma unroll
-    for (int d = 0; d < D; ++d) fetch_next(ring[d], start, k);
+    for (int d = 0; d < D; ++d) fetch_next(ring[d], st, kk);
+  };
+
+  for (int k = 0; k < gamma; ++k) {
+    const int start = (wave + k) % NW;   // rotate who takes the LDS extras
+    prime(k);
     // tokens of position k - 1: flag words (k << 24) | token; with one chunk
     // the wait leaves them in s_tok directly
     const bool tok_in_lds = k > 0 && nch == 1;

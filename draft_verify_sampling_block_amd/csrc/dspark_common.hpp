@@ -243,6 +243,23 @@ __device__ inline void stage_gather(const uint16_t* __restrict__ src, const int*
   stage_rows_lds(src, rank, lds, nrows, [&](int r) { return ids[r]; });
 }
 
+// DMA nchunks consecutive 16-byte chunks from src (16-byte aligned) to
+// lds; every wave of the work-group takes part.  kCoherent reads at device
+// scope (data written by other work-groups of the running kernel).
+// Completion: s_waitcnt + barrier by the caller.
+template <bool kCoherent>
+__device__ inline void dma_copy(const void* src, char* lds, int nchunks) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const char* s = static_cast<const char*>(src);
+  for (int g = wave; g * 64 < nchunks; g += nwaves) {
+    const int ch = g * 64 + lane;
+    if (ch < nchunks)
+      __builtin_amdgcn_global_load_lds(s + (size_t)ch * 16, lds + (size_t)(g * 64) * 16, 16, 0,
+                                       kCoherent ? 16 : 0);
+  }
+}
+
 __device__ inline bf16x8_t lds_frag(const char* lds, int r, int q, int nq) {
   return *reinterpret_cast<const bf16x8_t*>(lds + lds_off(r, q, nq));
 }
