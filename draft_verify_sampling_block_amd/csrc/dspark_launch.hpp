@@ -29,6 +29,7 @@ hipError_t launch_confidence(int B, int gamma, int H, int V, int rank, int dtype
                              int32_t* status, hipStream_t stream);
 
 constexpr int kScheduleMaxKeys = 8192;
+constexpr int kScheduleMergeKeys = 4096;   // candidates sorted by merging runs
 size_t schedule_workspace_bytes(int R, int gamma);
 hipError_t launch_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
                            int32_t* ell, int32_t* order, double* stats, int32_t* status,

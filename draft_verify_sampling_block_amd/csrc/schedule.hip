@@ -8,11 +8,14 @@
 // admission of position j independent of later positions' confidences.
 //
 // Layout: 1024 threads, keys (fp64 survival) and flat ids in LDS (<= 8192
-// keys = 96 KB).  Steps:
+// keys = 96 KB), padded to a power of two >= 1024.  Steps:
 //   1. per-request cumulative product, left to right in fp64 (one thread per
 //      request; bit-identical to a sequential product);
-//   2. bitonic sort by (a desc, flat id asc) -- a total order, so the order
-//      is exact;
+//   2. order by (a desc, flat id asc) -- a total order, so the order is
+//      exact: a request's survivals never increase along its positions, so
+//      the R runs of gamma are merged pairwise (log2 R levels, binary
+//      searches); beyond the merge buffer a bitonic sort with the keys in
+//      registers (shuffles within a wave, LDS for strides 64..512);
 //   3. tau_n = R + sum of the first n ranked survivals, computed as a
 //      double-double prefix scan and rounded once (the exact sum up to
 //      ~1e-30 relative; independent of association);
@@ -44,6 +47,153 @@ __device__ inline dd shfl_up_dd(dd v, int o) {
   return dd{__shfl_up(v.hi, o, kWave), __shfl_up(v.lo, o, kWave)};
 }
 
+// rank order of candidates: survival descending, then flat id ascending
+__device__ inline bool rank_before(double ka, int ia, double kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Bitonic sort of the P = 1024 E keys in key[] / idx[] (LDS) into rank
+// order, 1024 threads.  Thread t holds elements t + 1024 e in registers;
+// compare-exchange partners at distance >= 1024 sit in the same thread,
+// below 64 in the same wave (exchanged by shuffles), and in between they
+// meet through LDS.  Every element keeps the rank-first of itself and its
+// partner when (it is the lower of the pair) == (its run sorts in rank
+// order), else the rank-second.
+template <int E>
+__device__ void bitonic_sort(double* key, int* idx) {
+  const int tid = threadIdx.x;
+  constexpr int P = 1024 * E;
+  double k[E];
+  int id[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    k[e] = key[tid + 1024 * e];
+    id[e] = idx[tid + 1024 * e];
+  }
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 1024) {
+        const int es = stride >> 10;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int f = e ^ es;
+          if (f > e) {
+            const int i = tid + 1024 * e;
+            const bool up = (i & size) == 0;
+            const bool first_is_hi = rank_before(k[f], id[f], k[e], id[e]);
+            if (first_is_hi == up) {
+              const double tk = k[e]; k[e] = k[f]; k[f] = tk;
+              const int ti = id[e]; id[e] = id[f]; id[f] = ti;
+            }
+          }
+        }
+      } else {
+        double ko[E];
+        int io[E];
+        if (stride >= 64) {
+          __syncthreads();   // earlier readers are done with the arrays
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            key[tid + 1024 * e] = k[e];
+            idx[tid + 1024 * e] = id[e];
+          }
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            ko[e] = key[(tid + 1024 * e) ^ stride];
+            io[e] = idx[(tid + 1024 * e) ^ stride];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            ko[e] = __shfl_xor(k[e], stride, kWave);
+            io[e] = __shfl_xor(id[e], stride, kWave);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = tid + 1024 * e;
+          const bool up = (i & size) == 0;
+          const bool lower = (i & stride) == 0;
+          const bool mine_first = rank_before(k[e], id[e], ko[e], io[e]);
+          const bool keep_first = (up == lower);
+          if (mine_first != keep_first) {
+            k[e] = ko[e];
+            id[e] = io[e];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    key[tid + 1024 * e] = k[e];
+    idx[tid + 1024 * e] = id[e];
+  }
+  __syncthreads();
+}
+
+// Merge sort of N keys whose consecutive runs of length L0 are already in
+// rank order (each request's survivals never increase along its positions,
+// and equal ones keep ascending flat ids): each level merges pairs of runs;
+// an element's place is its index in its run plus the number of elements of
+// the partner run ranked before it (a binary search).  The order is total,
+// so the places form a permutation.  Returns the buffer holding the result.
+// EPT elements per thread (N <= 1024 EPT); their searches advance in
+// lockstep so the LDS latencies overlap.
+template <int EPT>
+__device__ int merge_runs(double* k0, int* i0, double* k1, int* i1, int N, int L0) {
+  const int tid = threadIdx.x;
+  int cur = 0;
+  for (int L = L0; L < N; L <<= 1) {
+    const double* ks = cur ? k1 : k0;
+    const int* is = cur ? i1 : i0;
+    double* kd = cur ? k0 : k1;
+    int* id = cur ? i0 : i1;
+    int steps = 0;
+    while ((1 << steps) <= L) ++steps;   // searches over at most L entries
+    double kx[EPT];
+    int ix[EPT], lo[EPT], hi[EPT], ps[EPT], dst[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = tid + 1024 * u;
+      lo[u] = hi[u] = ps[u] = dst[u] = 0;
+      kx[u] = 0.0;
+      ix[u] = 0;
+      if (e < N) {
+        const int q = e / L, i = e - q * L;
+        ps[u] = (q ^ 1) * L;
+        lo[u] = ps[u];
+        hi[u] = max(ps[u], min(ps[u] + L, N));
+        dst[u] = (q & ~1) * L + i;
+        kx[u] = ks[e];
+        ix[u] = is[e];
+      }
+    }
+    for (int st = 0; st < steps; ++st) {
+#pragma unroll
+      for (int u = 0; u < EPT; ++u) {
+        if (lo[u] < hi[u]) {
+          const int mid = (lo[u] + hi[u]) >> 1;
+          if (rank_before(ks[mid], is[mid], kx[u], ix[u])) lo[u] = mid + 1;
+          else hi[u] = mid;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      if (tid + 1024 * u < N) {
+        kd[dst[u] + (lo[u] - ps[u])] = kx[u];
+        id[dst[u] + (lo[u] - ps[u])] = ix[u];
+      }
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  return cur;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
@@ -53,15 +203,19 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
                                                         int32_t* __restrict__ order,
                                                         double* __restrict__ stats,
                                                         int32_t* status) {
-  __shared__ double key[kScheduleMaxKeys];
-  __shared__ int idx[kScheduleMaxKeys];
+  __shared__ double key_a[kScheduleMaxKeys];
+  __shared__ int idx_a[kScheduleMaxKeys];
+  __shared__ double key_b[kScheduleMergeKeys];   // merge ping-pong partner
+  __shared__ int idx_b[kScheduleMergeKeys];
+  double* key = key_a;
+  int* idx = idx_a;
   __shared__ double wsum_hi[16], wsum_lo[16];
   __shared__ int s_first_fail;
   __shared__ double s_tau, s_theta;
 
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x, nthr = blockDim.x;   // 1024
   const int N = R * gamma;
-  int P = 1;
+  int P = 1024;
   while (P < N) P <<= 1;
 
   // 1. survival products
@@ -89,22 +243,22 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
   if (tid == 0) s_first_fail = N;
   __syncthreads();
 
-  // 2. bitonic sort: position p precedes q iff (key desc, idx asc)
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < (P >> 1); t += nthr) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;  // this sub-sequence sorts in rank order
-        const double kl = key[lo], kh = key[hi];
-        const int il = idx[lo], ih = idx[hi];
-        const bool hi_first = (kh > kl) || (kh == kl && ih < il);
-        if (hi_first == up) {
-          key[lo] = kh; key[hi] = kl;
-          idx[lo] = ih; idx[hi] = il;
-        }
-      }
-      __syncthreads();
+  // 2. rank order (survival desc, flat id asc): merge the per-request runs,
+  //    or a bitonic sort beyond the merge buffer
+  if (N <= kScheduleMergeKeys) {
+    const int moved = N <= 1024   ? merge_runs<1>(key_a, idx_a, key_b, idx_b, N, gamma)
+                      : N <= 2048 ? merge_runs<2>(key_a, idx_a, key_b, idx_b, N, gamma)
+                                  : merge_runs<4>(key_a, idx_a, key_b, idx_b, N, gamma);
+    if (moved) {
+      key = key_b;
+      idx = idx_b;
+    }
+  } else {
+    switch (P) {
+      case 1024: bitonic_sort<1>(key, idx); break;
+      case 2048: bitonic_sort<2>(key, idx); break;
+      case 4096: bitonic_sort<4>(key, idx); break;
+      default: bitonic_sort<8>(key, idx); break;
     }
   }
 

@@ -118,11 +118,14 @@ def test_verify_extreme_lengths(ell_value):
     print(rep, flush=True)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(8))
 def test_schedule_random_confidences(seed):
+    # sizes on both sides of 4096 candidates (run merging below, bitonic
+    # sort above), runs of one position, and one request
     import draft_verify_sampling_block_amd as dv
     rng = np.random.default_rng(seed)
-    R, gamma = [(1, 1), (3, 64), (128, 15), (512, 7), (1000, 8), (8192, 1)][seed]
+    R, gamma = [(1, 1), (3, 64), (128, 15), (512, 7), (1000, 8), (8192, 1), (4096, 1),
+                (273, 15)][seed]
     _say(f"schedule R={R} gamma={gamma}")
     c = rng.uniform(0.0, 1.0, (R, gamma)).astype(np.float32)
     c[rng.random((R, gamma)) < 0.1] = 1.0           # ties in survival
