@@ -64,18 +64,55 @@ def draft_kernel_bytes(wl, kernel):
     """Algorithmic bytes of one launch of the draft kernel `kernel`.
 
     pdraft_kernel (one launch per block of gamma positions): every U row, the
-    W2 factor once, the gathered W1 rows, the tile statistics written and the
-    per-position outputs.  draft_stats_kernel (one launch per position): that
-    position's U rows, its gathered W1 rows, W2 once per launch, its tile
-    statistics.
+    W2 factor once, the gathered W1 rows, the per-(request, position, tile)
+    statistics written (packed max and sum, plus the argmax of greedy rows)
+    and the per-position outputs.  draft_stats_kernel (one launch per
+    position): that position's U rows, its W1 rows, W2 once per launch, its
+    tile statistics.
     """
+    import numpy as np
     e = 2 if wl.dtype == "bf16" else 4
     nT = (wl.V + 63) // 64
     B, g, V, r = wl.B, wl.gamma, wl.V, wl.rank
+    greedy = int(np.sum(~(np.asarray(wl.temperature) > 0)))
+    stats = 8 * B * nT + 4 * greedy * nT          # per position
     if kernel == "pdraft_kernel":
-        return (e * B * g * V + e * r * V + e * B * g * r + 3 * 4 * B * g * nT
-                + 4 * B * g * 4)
-    return e * B * V + e * B * r + e * r * V + 3 * 4 * B * nT
+        return e * B * g * V + e * r * V + e * B * g * r + g * stats + 4 * B * g * 4
+    return e * B * V + e * B * r + e * r * V + stats
+
+
+KERNEL_SOURCES = ["draft_verify_sampling_block_amd/csrc/draft.hip",
+                  "draft_verify_sampling_block_amd/csrc/dspark_common.hpp",
+                  "draft_verify_sampling_block_amd/csrc/dspark_launch.hpp"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel, cfg):
+    """HBM bytes per launch of `kernel` from the recorded rocprofv3 counters
+    (profiles/<kernel>-config<cfg>.counters.txt), scaled by the plain-copy
+    calibration recorded with them; None when absent or when the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}-config{cfg}.counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    return (float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
+            + float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])) * 1024.0
 
 
 def cpu_baseline(cfg, n_req):
@@ -193,7 +230,8 @@ def main():
                    "scheduler": bool(spec.scheduler), "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": draft_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_launch": stats_bytes,
+                     "traffic": counter_traffic(draft_kernel, cfg),
+                     "bytes_per_launch": stats_bytes,
                      "mean_launch_us": avg_s * 1e6},
         "step": {"bytes_alg": bytes_step, "hbm_gbs": bytes_step / (ms / 1e3) / 1e9,
                  "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
