@@ -255,20 +255,22 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
         const bf16x8_t f = *reinterpret_cast<const bf16x8_t*>(sh.arow + 16 * (2 * ks + h));
         return mine ? f : zero;
       };
-      // one sub-tile at a time; the clobber keeps the operand reads of the
-      // second pass from being merged with the first (fewer live registers)
+      // both sub-tiles' chains interleaved, operands double-buffered: the
+      // same instruction sequence per accumulator as the statistics pass
+      f32x16_t acc[kSub];
 #pragma unroll
       for (int t = 0; t < kSub; ++t) {
-        f32x16_t acc;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          acc[j] = (32 * t + j < rem) ? bf16_to_f32(useg[32 * t + j]) : -INFINITY;
-        asm volatile("" ::: "memory");
-        bias_subtile_ldsA<KS>(bfrag, scratch, t, acc);
-        if (mine) {
+          acc[t][j] = (32 * t + j < rem) ? bf16_to_f32(useg[32 * t + j]) : -INFINITY;
+      }
+      bias_tile_ldsA<KS>(bfrag, scratch, acc);
+      if (mine) {
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) {
           float* se = sh.se + 32 * t + 16 * h;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) se[j] = tile_term(acc[j], ce, mc);
+          for (int j = 0; j < 16; ++j) se[j] = tile_term(acc[t][j], ce, mc);
         }
       }
     }
