@@ -538,22 +538,38 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
   };
   Slot ring[D];
   int fch = 0, fidx = 0;   // next task to fetch: chunk, index in the chunk
-  auto fetch_next = [&](Slot& sl, int start, int k) {
-    if (fch >= nch) return;
-    const int nblk = chunk_blocks(fch);
-    const int rbase = fch * (kPdMaxRows / kTileM);
-    if (fidx < nreg * nblk) {
-      const int i = (R == 2 && fidx >= nblk) ? 1 : 0;
-      sl.rb = rbase + fidx - i * nblk;
-      sl.tile = slot_tile(wave + NW * i);
-      sl.which = -1 - i;
+  // tile / request block / A source of task fi of chunk ch
+  auto task_at = [&](int ch, int fi, int start, int& tile, int& rb, int& which) {
+    const int nblk = chunk_blocks(ch);
+    const int rbase = ch * (kPdMaxRows / kTileM);
+    if (fi < nreg * nblk) {
+      const int i = (R == 2 && fi >= nblk) ? 1 : 0;
+      rb = rbase + fi - i * nblk;
+      tile = slot_tile(wave + NW * i);
+      which = -1 - i;
     } else {
-      const int li = start + (fidx - nreg * nblk) * NW;
-      const int which = li >= nblk ? 1 : 0;
-      sl.rb = rbase + li - which * nblk;
-      sl.tile = slot_tile(kPdRegTiles + which);
-      sl.which = which;
+      const int li = start + (fi - nreg * nblk) * NW;
+      const int w = li >= nblk ? 1 : 0;
+      rb = rbase + li - w * nblk;
+      tile = slot_tile(kPdRegTiles + w);
+      which = w;
     }
+  };
+  // Past the last task the slot still issues its loads (of a safe
+  // address): a fixed count of loads per task lets the in-order memory
+  // counter wait for exactly the slot it needs, not for every later one.
+  auto fetch_next = [&](Slot& sl, int start, int k) {
+    if (fch >= nch) {
+#pragma unroll
+      for (int t = 0; t < kSub; ++t) {
+#pragma unroll
+        for (int q = 0; q < URow<uint16_t>::kLoads; ++q)   // four distinct 16-byte words
+          sl.u.w[t][q] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_t*>(a.W2t) + t * URow<uint16_t>::kLoads + q);
+      }
+      return;
+    }
+    task_at(fch, fidx, start, sl.tile, sl.rb, sl.which);
     const int b = sl.rb * kTileM + c;
     load_urow<uint16_t>(sl.u, a.U + ((size_t)b * gamma + k) * V, sl.tile * kTileV, V, b < B,
                         a.U);
@@ -591,35 +607,50 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
       const int b = rb * kTileM + c;
       const int v0 = tile * kTileV;
       const int lrow = (rb % (kPdMaxRows / kTileM)) * kTileM + c;   // row in the gathered chunk
-      f32x16_t acc[kSub];
-      if (v0 + kTileV <= V) {
-#pragma unroll
-        for (int t = 0; t < kSub; ++t) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) acc[t][j] = urow_at(sl.u, t, j);
-        }
-      } else {
-        init_acc<uint16_t>(sl.u, V - (v0 + 16 * h), acc);
-      }
-      fetch_next(sl, start, k);
-      // no global load below: a later load would make the in-order memory
-      // counter wait for the prefetch just issued
       const float it = s_it[lrow];
+      const bool any_greedy = __ballot((b < B) && !(it > 0.f)) != 0;
       auto bfrag = [&](int ks) { return lds_frag(ldsA, lrow, 2 * ks + h, nq); };
+      // Each A source runs its own start / contraction / reduction, so the
+      // accumulators of one never meet those of the other at a merge point
+      // (which would cost register copies and a second accumulator set).
+      auto finish = [&](f32x16_t (&acc)[kSub], int slot) {
+        const TileStat st = tile_reduce(acc, tile, it, any_greedy);
+        if (h == 0) {
+          s_mx[slot][lrow] = st.mx;
+          s_sum[slot][lrow] = st.s;
+          s_arg[slot][lrow] = st.arg;
+        }
+      };
+      // start the accumulators at the base logits, then refill the slot
+      // (no global load after that: a later load would make the in-order
+      // memory counter wait for the prefetch just issued)
+      auto start_acc = [&](f32x16_t (&acc)[kSub]) {
+        if (v0 + kTileV <= V) {
+#pragma unroll
+          for (int t = 0; t < kSub; ++t) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[t][j] = urow_at(sl.u, t, j);
+          }
+        } else {
+          init_acc<uint16_t>(sl.u, V - (v0 + 16 * h), acc);
+        }
+        fetch_next(sl, start, k);
+      };
       if (which >= 0) {
+        f32x16_t acc[kSub];
+        start_acc(acc);
         bias_tile_ldsA<KS>(bfrag, ldsL + which * kLdsTileBytes, acc);
+        finish(acc, kPdRegTiles + which);
       } else {
 #pragma unroll
-        for (int i = 0; i < R; ++i)
-          if (which == -1 - i) bias_tile_regA<KS>(bfrag, wreg[i], acc);
-      }
-      const bool any_greedy = __ballot((b < B) && !(it > 0.f)) != 0;
-      const TileStat st = tile_reduce(acc, tile, it, any_greedy);
-      if (h == 0) {
-        const int slot = which >= 0 ? kPdRegTiles + which : wave + NW * (-1 - which);
-        s_mx[slot][lrow] = st.mx;
-        s_sum[slot][lrow] = st.s;
-        s_arg[slot][lrow] = st.arg;
+        for (int i = 0; i < R; ++i) {
+          if (which == -1 - i) {
+            f32x16_t acc[kSub];
+            start_acc(acc);
+            bias_tile_regA<KS>(bfrag, wreg[i], acc);
+            finish(acc, wave + NW * i);
+          }
+        }
       }
     };
     // write the finished chunk's statistics (all waves done: caller synced)
@@ -681,13 +712,11 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
       return n;
     }();
     while (g < ntot) {
-      enter();
-      run_task(ring[0]);
-      ++g;
-      if constexpr (D == 2) {
-        if (g >= ntot) break;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (d > 0 && g >= ntot) break;
         enter();
-        run_task(ring[1]);
+        run_task(ring[d]);
         ++g;
       }
     }
