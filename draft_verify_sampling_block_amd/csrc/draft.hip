@@ -751,9 +751,11 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
   }
 }
 
-__global__ void pdraft_reset_kernel(uint32_t* flags, int n) {
+// zero the statistics flags [0, n0) and the token flags [0, n1)
+__global__ void pdraft_reset_kernel(uint32_t* f0, int n0, uint32_t* f1, int n1) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) flags[i] = 0u;
+  if (i < n0) f0[i] = 0u;
+  if (i < n1) f1[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -789,6 +791,7 @@ DevInfo dev_info() {
 }  // namespace
 
 void set_draft_path(int path) { g_draft_path = path; }
+int device_cu_count() { return dev_info().cus; }
 int get_draft_path() { return g_draft_path; }
 
 static size_t stats_bytes(int B, int V) { return align256((size_t)B * n_tiles(V) * 4); }
@@ -868,9 +871,9 @@ static hipError_t draft_persistent(int B, int gamma, int V, int rank, const uint
   {
     TraceScope t("pdraft_reset_kernel", stream);
     const int nflags = P * kPdFlagStride;
-    pdraft_reset_kernel<<<dim3((nflags + 255) / 256), dim3(256), 0, stream>>>(a.stats_flag,
-                                                                              nflags);
-    pdraft_reset_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(a.tok_flag, B);
+    const int n = nflags > B ? nflags : B;
+    pdraft_reset_kernel<<<dim3((n + 255) / 256), dim3(256), 0, stream>>>(a.stats_flag, nflags,
+                                                                         a.tok_flag, B);
   }
   TraceScope t("pdraft_kernel", stream);
   void* args[] = {&a};

@@ -17,6 +17,8 @@ size_t draft_workspace_bytes(int B, int gamma, int V, int rank, int dtype);
 // 3 / 4 = persistent only with 8 / 4 waves per work-group
 void set_draft_path(int path);
 int get_draft_path();
+// compute units of the current device (cached per device)
+int device_cu_count();
 hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U,
                               const void* W1, const void* W2t, const int32_t* anchor,
                               const float* temperature, const float* uniforms, int32_t* tokens,

@@ -21,6 +21,9 @@
 //   verify_finish_kernel  per request: fp64 scan of the chunk sums, exact
 //                         recompute of the crossing chunk, the drawn token,
 //                         and the outputs.
+#include <algorithm>
+#include <type_traits>
+
 #include "dspark_common.hpp"
 #include "dspark_launch.hpp"
 #include "trace.hpp"
@@ -105,19 +108,23 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
   // each thread: groups of kU chunks of 8 consecutive entries, all loads of a
   // group in flight together; running max and exp-sum in fp32 (the sum is
   // rescaled when the max grows), combined across threads in fp64
-  constexpr int kU = 4;
+  constexpr int kU = 8;
   float m = -INFINITY;
   float s32 = 0.f;
   int arg = 0x7fffffff;
   const int stride = 8 * 256;
   for (int base = 8 * tid; base < V; base += kU * stride) {
+    // the loads are unconditional (chunks past the row re-read chunk 0 and
+    // are masked afterwards) so that all kU are in flight together
     float y[kU][8];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = base + u * stride;
-      if (i < V) {
-        load8_f32_stream(row + i, y[u]);
-      } else {
+      load8_f32_stream(row + (i < V ? i : 0), y[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (base + u * stride >= V) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) y[u][t] = -INFINITY;
       }
@@ -237,6 +244,100 @@ __global__ void verify_plan_kernel(int B, int gamma, int V, const int32_t* __res
   if (f.mode == 1) atomicOr(ws.any_res, 1);
 }
 
+// Per-request constants of the final weights (mode 0: nothing to sum).
+struct FinalParams {
+  int mode;
+  float it, M, LZ, mq, lzq;
+};
+__device__ inline FinalParams final_params(const FinalRow& mine, int b, int gamma,
+                                           const float* __restrict__ row_max,
+                                           const float* __restrict__ row_logZ,
+                                           const float* __restrict__ temperature,
+                                           const VerifyWs& ws) {
+  FinalParams f{mine.mode, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (mine.mode != 0) {
+    f.it = 1.f / temperature[b];
+    const size_t sk = (size_t)b * (gamma + 1) + mine.slot;
+    f.M = ws.rM[sk];
+    f.LZ = ws.rLZ[sk];
+    if (mine.mode == 1) {
+      f.mq = row_max[(size_t)b * gamma + mine.slot];
+      f.lzq = row_logZ[(size_t)b * gamma + mine.slot];
+    }
+  }
+  return f;
+}
+// Residual and p mass of one 32-entry sub-tile for the lane's request: the
+// lane's 16 entries (target logits yt, q logits yq; `rem` usable entries of
+// the lane) summed in order, then the two half-waves' sums added.
+__device__ inline void subtile_sums(const FinalParams& f, const float (&yt)[16],
+                                    const f32x16_t& yq, int rem, float& sr, float& sp) {
+  sr = 0.f;
+  sp = 0.f;
+  if (f.mode != 0) {
+    const bool res = f.mode == 1;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < rem) {
+        float r, p;
+        final_weight(yt[j] * f.it, res ? yq[j] * f.it : 0.f, f.M, f.LZ, f.mq, f.lzq, res, r, p);
+        sr += r;
+        sp += p;
+      }
+    }
+  }
+  float lo, hi;
+  half_pair(sr, lo, hi);
+  sr = lo + hi;
+  half_pair(sp, lo, hi);
+  sp = lo + hi;
+}
+
+// One (64-entry tile, 32-request block) task of the final statistics for
+// the lane's request b (column c): the q logits of residual requests start
+// at the base logits and get the Markov bias on the matrix cores (A = the
+// W2t tile in LDS, B = the W1 rows of the previous tokens), then the
+// residual and p masses of the tile are summed per request.  All 64 lanes
+// call it; tp holds the lane's target entries and acc starts at its base
+// logits (init_acc).
+template <typename T, int KS>
+__device__ inline void final_task(const FinalRow& mine, int b, int vt, int V, int gamma, int nT,
+                                  int rank, const URow<T>& tp, f32x16_t (&acc)[kSub],
+                                  const bf16x8_t (&bfrag)[KS], const char* w2s,
+                                  const T* __restrict__ W1, const T* __restrict__ W2t,
+                                  const float* __restrict__ row_max,
+                                  const float* __restrict__ row_logZ,
+                                  const float* __restrict__ temperature, const VerifyWs& ws) {
+  constexpr bool bf = sizeof(T) == 2;
+  const int h = (threadIdx.x & 63) >> 5;
+  const int v0 = vt * kTileV;
+  const bool blk_res = __ballot(mine.mode == 1) != 0;
+  if (blk_res) {
+    if constexpr (bf)
+      bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
+    else
+      bias_tile_f32(reinterpret_cast<const float*>(W1), mine.mode == 1 ? mine.prev : -1,
+                    reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
+  }
+  float sr = 0.f, sp = 0.f;
+  const FinalParams fp = final_params(mine, b, gamma, row_max, row_logZ, temperature, ws);
+#pragma unroll
+  for (int t = 0; t < kSub; ++t) {
+    float yt[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) yt[j] = urow_at(tp, t, j);
+    float r, p;
+    subtile_sums(fp, yt, acc[t], V - (v0 + 32 * t + 16 * h), r, p);
+    sr += r;
+    sp += p;
+  }
+  if (mine.mode != 0 && h == 0) {
+    const size_t ci = (size_t)b * nT + vt;
+    ws.fchunk[ci] = sr;
+    ws.pchunk[ci] = sp;
+  }
+}
+
 // one work-group per 64-entry tile; waves take 32-request blocks
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void verify_final_stats_kernel(
@@ -279,51 +380,195 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
       __syncthreads();
     }
     if (!live) break;
-    const bool blk_res = __ballot(mine.mode == 1) != 0;
     f32x16_t acc[kSub];
     init_acc<T>(up, V - (v0 + 16 * h), acc);   // q logits start at the base logits
-    if (blk_res) {
-      if constexpr (bf)
-        bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
-      else
-        bias_tile_f32(reinterpret_cast<const float*>(W1), mine.mode == 1 ? mine.prev : -1,
-                      reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
+    final_task<T, KS>(mine, b, vt, V, gamma, nT, rank, tp, acc, bfrag, w2s, W1, W2t, row_max,
+                      row_logZ, temperature, ws);
+  }
+}
+
+// The same statistics in tile-loop form (bf16, at most kVtMaxRows
+// requests): one work-group of 8 waves per compute unit.  Work-group p owns
+// the contiguous tiles [tbase, tbase + tcount) and walks them one by one;
+// wave w computes sub-tile w % 2 of 32-request block w / 2 (A = the W2t tile
+// in LDS, B = the gathered W1 rows of the previous tokens in LDS), so each
+// element is computed exactly as verify_final_stats_kernel computes it and
+// the sub-tile sums are combined in the same order.  The next tile's W2t
+// rows are loaded into registers while the current one is processed and
+// written to the other LDS buffer; the chunk sums collect in LDS and are
+// written out every kVtOutTiles tiles.
+constexpr int kVtWaves = 8;
+constexpr int kVtMaxRows = 4 * kTileM;
+constexpr int kVtOutTiles = 16;
+template <int KS>
+__global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
+    int B, int gamma, int V, int rank, const uint16_t* __restrict__ target,
+    const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W2t, const int32_t* __restrict__ anchor,
+    const int32_t* __restrict__ tokens, const float* __restrict__ row_max,
+    const float* __restrict__ row_logZ, const float* __restrict__ temperature,
+    const int32_t* __restrict__ ell, VerifyWs ws) {
+  constexpr int nq = 2 * KS, nc = nq + 1;
+  constexpr int kRowB = nc * 16;                 // bytes of one padded LDS row
+  constexpr int kThr = kVtWaves * 64;
+  constexpr int kChunks = kTileV * nq;           // 16-byte chunks of one tile
+  constexpr int kPer = (kChunks + kThr - 1) / kThr;
+  __shared__ __attribute__((aligned(16))) char w2s[2][kTileV * kRowB];
+  __shared__ __attribute__((aligned(16))) char w1s[kVtMaxRows * kRowB];
+  __shared__ float s_part[2][kSub][kVtMaxRows][2];
+  __shared__ float s_out[2][kVtOutTiles][kVtMaxRows];
+  __shared__ int s_prev[kVtMaxRows];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 31, h = lane >> 5;
+  const int t = wave & 1, rb = wave >> 1;
+  const int P = gridDim.x, p = blockIdx.x;
+  const int nT = n_tiles(V);
+  const int tcount = nT / P + (p < nT % P ? 1 : 0);
+  const int tbase = p * (nT / P) + min(p, nT % P);
+  const bool any_res = *ws.any_res != 0;
+
+  // plans and the W1 rows of the residual requests' previous tokens
+  for (int r = tid; r < kVtMaxRows; r += kThr) {
+    int prev = 0;
+    if (r < B) {
+      const FinalRow f = final_row(r, B, gamma, V, ell, temperature, anchor, tokens, ws);
+      if (f.mode == 1) prev = f.prev;
     }
-    float sr = 0.f, sp = 0.f;
-    if (mine.mode != 0) {
-      const float it = 1.f / temperature[b];
-      const size_t sk = (size_t)b * (gamma + 1) + mine.slot;
-      const float M = ws.rM[sk], LZ = ws.rLZ[sk];
-      const bool res = mine.mode == 1;
-      const float mq = res ? row_max[(size_t)b * gamma + mine.slot] : 0.f;
-      const float lzq = res ? row_logZ[(size_t)b * gamma + mine.slot] : 0.f;
-      const int rem = V - (v0 + 16 * h);
+    s_prev[r] = prev;
+  }
+  __syncthreads();
+  if (any_res) stage_gather(W1, s_prev, rank, w1s, kVtMaxRows);
+
+  // tile vt's rows in the stage_tile image: row r <- W2t row v0 +
+  // tile_row_vocab(r) (clamped); thread chunks (r, q < nq), the pad chunk
+  // written from chunk 0.  Two register stages: tile i + 1 waits in one
+  // while tile i + 2 loads into the other.
+  u32x4_t stA[kPer], stB[kPer];
+  auto load_tile = [&](u32x4_t (&st)[kPer], int vt) {
 #pragma unroll
-      for (int t = 0; t < kSub; ++t) {
+    for (int j = 0; j < kPer; ++j) {
+      const int s = min(tid + kThr * j, kChunks - 1);
+      const int r = s / nq, q = s - r * nq;
+      const int v = min(vt * kTileV + tile_row_vocab(r), V - 1);
+      st[j] = *reinterpret_cast<const u32x4_t*>(W2t + (size_t)v * rank + q * 8);
+    }
+  };
+  auto write_tile = [&](const u32x4_t (&st)[kPer], int buf) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          if (32 * t + j < rem) {
-            const float yt = urow_at(tp, t, j) * it;
-            const float yq = res ? acc[t][j] * it : 0.f;
-            float r, p;
-            final_weight(yt, yq, M, LZ, mq, lzq, res, r, p);
-            sr += r;
-            sp += p;
-          }
-        }
+    for (int j = 0; j < kPer; ++j) {
+      const int s = tid + kThr * j;
+      const int r = s / nq, q = s - r * nq;
+      if (kChunks % kThr == 0 || s < kChunks) {
+        *reinterpret_cast<u32x4_t*>(w2s[buf] + r * kRowB + q * 16) = st[j];
+        if (q == 0) *reinterpret_cast<u32x4_t*>(w2s[buf] + r * kRowB + nq * 16) = st[j];
       }
     }
-    float lo, hi;
-    half_pair(sr, lo, hi);
-    sr = lo + hi;
-    half_pair(sp, lo, hi);
-    sp = lo + hi;
-    if (mine.mode != 0 && h == 0) {
-      const size_t ci = (size_t)b * nT + vt;
-      ws.fchunk[ci] = sr;
-      ws.pchunk[ci] = sp;
-    }
+  };
+  // every load below is issued unconditionally (safe or clamped addresses
+  // where there is nothing to read): with a fixed count of loads per step
+  // the in-order memory counter waits for exactly the data it needs
+  const int tlast = tbase + tcount - 1;
+  if (any_res) {
+    load_tile(stA, tbase);
+    write_tile(stA, 0);
   }
+  __builtin_amdgcn_s_waitcnt(0);   // the gathered rows have landed
+  __syncthreads();
+
+  // this wave's request column: plan, weights' constants, entries of the
+  // next tile requested one tile ahead (before the tile rows two ahead, so
+  // that waiting for them leaves those in flight)
+  const int b = rb * kTileM + c;
+  const bool active = rb * kTileM < B;
+  FinalRow mine{0, 0, -1};
+  if (active && b < B) mine = final_row(b, B, gamma, V, ell, temperature, anchor, tokens, ws);
+  const FinalParams fpar = final_params(mine, b, gamma, row_max, row_logZ, temperature, ws);
+  const bool blk_res = any_res && __ballot(mine.mode == 1) != 0;
+  const uint16_t* trow = target + ((size_t)b * (gamma + 1) + mine.slot) * V;
+  const uint16_t* urow = U + ((size_t)b * gamma + mine.slot) * V;
+  // two slice sets, like the tile stages: step i reads one and fills the
+  // other, so no loaded register is ever copied (a copy would wait for it)
+  u32x4_t tqA[2], uqA[2], tqB[2], uqB[2];
+  auto fetch = [&](u32x4_t (&tq)[2], u32x4_t (&uq)[2], int vt) {
+    const int e0 = vt * kTileV + 32 * t + 16 * h;   // the lane's first entry
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bool in = vt <= tlast && e0 + 8 * q < V;
+      tq[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+          in && mine.mode != 0 ? trow + e0 + 8 * q : target));
+      uq[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+          in && mine.mode == 1 ? urow + e0 + 8 * q : U));
+    }
+  };
+
+  auto flush = [&](int first, int n) {   // s_out rows of tiles [first, first + n)
+    for (int e = tid; e < n * kVtMaxRows; e += kThr) {
+      const int r = e / n, i = e - r * n;
+      if (r < B) {
+        const size_t ci = (size_t)r * nT + tbase + first + i;
+        ws.fchunk[ci] = s_out[0][(first + i) % kVtOutTiles][r];
+        ws.pchunk[ci] = s_out[1][(first + i) % kVtOutTiles][r];
+      }
+    }
+  };
+  // the tile walk, with (kRes) or without the bias on the matrix cores
+  auto walk = [&](auto res_tag) {
+    constexpr bool kRes = decltype(res_tag)::value;
+    fetch(tqA, uqA, tbase);
+    if constexpr (kRes) load_tile(stB, min(tbase + 1, tlast));
+    // tile i from LDS buffer i & 1; `next` holds tile i + 1, `after`
+    // receives tile i + 2
+    auto step = [&](int i, const u32x4_t (&next)[kPer], u32x4_t (&after)[kPer],
+                    const u32x4_t (&tq)[2], const u32x4_t (&uq)[2], u32x4_t (&tq1)[2],
+                    u32x4_t (&uq1)[2]) {
+      const int vt = tbase + i;
+      f32x16_t acc;
+      float yt[16];
+      const int rem = V - (vt * kTileV + 32 * t + 16 * h);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t wu = uq[j >> 3][(j >> 1) & 3], wt = tq[j >> 3][(j >> 1) & 3];
+        const float fu = (j & 1) ? __uint_as_float(wu & 0xFFFF0000u) : __uint_as_float(wu << 16);
+        yt[j] = (j & 1) ? __uint_as_float(wt & 0xFFFF0000u) : __uint_as_float(wt << 16);
+        acc[j] = j < rem ? fu : -INFINITY;   // q logits start at the base logits
+      }
+      fetch(tq1, uq1, vt + 1);
+      if constexpr (kRes) load_tile(after, min(vt + 2, tlast));
+      if (active) {
+        if (kRes && blk_res)
+          bias_subtile_ldsA<KS>([&](int ks) { return lds_frag(w1s, b, 2 * ks + h, nq); },
+                                w2s[i & 1], t, acc);
+        float sr, sp;
+        subtile_sums(fpar, yt, acc, rem, sr, sp);
+        if (h == 0) {
+          s_part[i & 1][t][b][0] = sr;
+          s_part[i & 1][t][b][1] = sp;
+        }
+      }
+      if constexpr (kRes) {
+        if (i + 1 < tcount) write_tile(next, (i + 1) & 1);
+      }
+      __syncthreads();
+      // the tile's chunk sums: sub-tile 0 + sub-tile 1, as in final_task
+      if (tid < kVtMaxRows) {
+        s_out[0][i % kVtOutTiles][tid] = s_part[i & 1][0][tid][0] + s_part[i & 1][1][tid][0];
+        s_out[1][i % kVtOutTiles][tid] = s_part[i & 1][0][tid][1] + s_part[i & 1][1][tid][1];
+      }
+      if ((i + 1) % kVtOutTiles == 0 || i + 1 == tcount) {
+        __syncthreads();
+        const int first = i - i % kVtOutTiles;
+        flush(first, i + 1 - first);
+        __syncthreads();
+      }
+    };
+    for (int i = 0; i < tcount; i += 2) {
+      step(i, stB, stA, tqA, uqA, tqB, uqB);
+      if (i + 1 < tcount) step(i + 1, stA, stB, tqB, uqB, tqA, uqA);
+    }
+  };
+  if (any_res) walk(std::true_type{});
+  else walk(std::false_type{});
 }
 
 template <typename T, int KS>
@@ -517,7 +762,20 @@ static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target
                                                                         temperature, anchor,
                                                                         tokens, ws);
   }
-  {
+  // bf16 with at most 128 requests: the tile-loop form
+  bool tiles = false;
+  if constexpr (sizeof(T) == 2) {
+    const int cus = device_cu_count();
+    if (B <= kVtMaxRows && cus > 0) {
+      const int P = std::min(cus, n_tiles(V));
+      TraceScope t2("verify_tile_stats_kernel", stream);
+      verify_tile_stats_kernel<KS><<<dim3(P), dim3(kVtWaves * 64), 0, stream>>>(
+          B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
+          ell, ws);
+      tiles = true;
+    }
+  }
+  if (!tiles) {
     TraceScope t2("verify_final_stats_kernel", stream);
     verify_final_stats_kernel<T, KS><<<dim3(n_tiles(V)), dim3(256), 0, stream>>>(
         B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
