@@ -6,18 +6,15 @@
 // verified tokens pass, one bonus token is drawn from the next target slot.
 //
 // Launches:
-//   verify_init_kernel    first_reject[b] = +inf
 //   verify_rows_kernel    one work-group per (slot k, request b), k-major, for
 //                         k <= ell[b]: target-row max / argmax / log-sum-exp,
-//                         p(x_k), ratio and accept test.  A row is skipped
-//                         once an earlier slot of the same request has
-//                         rejected (rows are claimed in slot order, so late
-//                         slots are mostly skipped: "row-lazy" without a
-//                         sequential dependency).
-//   verify_final_stats    vocabulary-parallel wave tiles (as in drafting):
-//                         per-chunk sums of the residual max(0, p_j - q_j)
-//                         (q_j recomputed bit-identically on the matrix
-//                         cores) or of the bonus slot's p.
+//                         p(x_k), ratio and the accept flag; the first
+//                         rejected slot is read off the flags afterwards.
+//   verify_tile_stats     (bf16, B <= 128) or verify_init + verify_plan +
+//   / verify_final_stats  verify_final_stats: vocabulary-parallel tiles (as
+//                         in drafting): per-chunk sums of the residual
+//                         max(0, p_j - q_j) (q_j recomputed bit-identically
+//                         on the matrix cores) or of the bonus slot's p.
 //   verify_finish_kernel  per request: fp64 scan of the chunk sums, exact
 //                         recompute of the crossing chunk, the drawn token,
 //                         and the outputs.
@@ -33,7 +30,6 @@ namespace dspark {
 namespace {
 
 struct VerifyWs {
-  int32_t* first_rej;  // [B]
   float* rM;           // [B][gamma+1] target row max of y = t/T (max t when greedy)
   float* rLZ;          // [B][gamma+1] log sum exp(y - max)
   int32_t* rArg;       // [B][gamma+1] lowest argmax
@@ -49,7 +45,6 @@ VerifyWs carve(void* ws, int B, int gamma, int V) {
   char* p = static_cast<char*>(ws);
   const size_t nC = n_tiles(V);
   VerifyWs w;
-  w.first_rej = reinterpret_cast<int32_t*>(p); p += align256((size_t)B * 4);
   w.rM = reinterpret_cast<float*>(p); p += align256((size_t)B * (gamma + 1) * 4);
   w.rLZ = reinterpret_cast<float*>(p); p += align256((size_t)B * (gamma + 1) * 4);
   w.rArg = reinterpret_cast<int32_t*>(p); p += align256((size_t)B * (gamma + 1) * 4);
@@ -73,12 +68,19 @@ __device__ inline int clamp_ell(const int32_t* ell, int b, int gamma, int32_t* s
 
 __device__ inline float inv_temp(float T) { return (T > 0.f) ? 1.f / T : 0.f; }
 
+// first rejected slot of request b among its L verified slots (L when all
+// pass), from the accept flags verify_rows_kernel wrote for every k < L
+__device__ inline int first_reject(const VerifyWs& ws, int b, int gamma, int L) {
+  const int32_t* acc = ws.wacc + (size_t)b * gamma;
+  for (int k = 0; k < L; ++k)
+    if (acc[k] == 0) return k;
+  return L;
+}
+
 }  // namespace
 
-__global__ void verify_init_kernel(int B, int32_t* first_rej, int32_t* any_res) {
-  int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < B) first_rej[b] = 0x7fffffff;
-  if (b == 0) *any_res = 0;
+__global__ void verify_init_kernel(int32_t* any_res) {
+  if (threadIdx.x == 0) *any_res = 0;
 }
 
 template <typename T>
@@ -88,17 +90,10 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
     const float* __restrict__ uniforms, const int32_t* __restrict__ ell, VerifyWs ws,
     int32_t* status) {
   __shared__ double red[8];
-  __shared__ int s_skip;
   const int k = blockIdx.x / B, b = blockIdx.x % B;
   const int tid = threadIdx.x;
   const int L = clamp_ell(ell, b, gamma, tid == 0 ? status : nullptr);
   if (k > L) return;  // uniform: every thread reads the same ell[b]
-  // skip the row if an earlier slot of this request already rejected; one
-  // thread reads the flag so the whole work-group takes the same branch
-  if (tid == 0)
-    s_skip = __hip_atomic_load(&ws.first_rej[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < k;
-  __syncthreads();
-  if (s_skip) return;
 
   const float it = inv_temp(temperature[b]);
   const bool greedy = !(it > 0.f);
@@ -191,7 +186,6 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
       const bool accept = u * q < p;
       ws.wratio[bk] = p / q;
       ws.wacc[bk] = accept ? 1 : 0;
-      if (!accept) atomicMin(&ws.first_rej[b], k);
     }
   }
 }
@@ -219,8 +213,8 @@ __device__ inline FinalRow final_row(int b, int B, int gamma, int V, const int32
   FinalRow f{0, 0, -1};
   if (b >= B) return f;
   const int L = clamp_ell(ell, b, gamma, nullptr);
-  const int j = ws.first_rej[b];
   if (!(temperature[b] > 0.f)) return f;
+  const int j = first_reject(ws, b, gamma, L);
   if (j < L) {
     f.mode = 1;
     f.slot = j;
@@ -418,6 +412,7 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
   __shared__ float s_part[2][kSub][kVtMaxRows][2];
   __shared__ float s_out[2][kVtOutTiles][kVtMaxRows];
   __shared__ int s_prev[kVtMaxRows];
+  __shared__ int s_any;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c = lane & 31, h = lane >> 5;
@@ -426,18 +421,22 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
   const int nT = n_tiles(V);
   const int tcount = nT / P + (p < nT % P ? 1 : 0);
   const int tbase = p * (nT / P) + min(p, nT % P);
-  const bool any_res = *ws.any_res != 0;
-
   // plans and the W1 rows of the residual requests' previous tokens
+  if (tid == 0) s_any = 0;
+  __syncthreads();
   for (int r = tid; r < kVtMaxRows; r += kThr) {
     int prev = 0;
     if (r < B) {
       const FinalRow f = final_row(r, B, gamma, V, ell, temperature, anchor, tokens, ws);
-      if (f.mode == 1) prev = f.prev;
+      if (f.mode == 1) {
+        prev = f.prev;
+        s_any = 1;
+      }
     }
     s_prev[r] = prev;
   }
   __syncthreads();
+  const bool any_res = s_any != 0;   // some request of the batch draws from a residual
   if (any_res) stage_gather(W1, s_prev, rank, w1s, kVtMaxRows);
 
   // tile vt's rows in the stage_tile image: row r <- W2t row v0 +
@@ -590,7 +589,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
   const int b = blockIdx.x, tid = threadIdx.x;
   const int nT = n_tiles(V);
   const int L = clamp_ell(ell, b, gamma, nullptr);
-  const int j = ws.first_rej[b];
+  const int j = first_reject(ws, b, gamma, L);
   const bool residual = j < L;
   const int slot = residual ? j : L;
   const int n = residual ? j : L;
@@ -732,7 +731,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
 size_t verify_workspace_bytes(int B, int gamma, int V, int rank, int dtype) {
   (void)rank; (void)dtype;
   const size_t nC = n_tiles(V);
-  return align256((size_t)B * 4) + 3 * align256((size_t)B * (gamma + 1) * 4) +
+  return 3 * align256((size_t)B * (gamma + 1) * 4) +
          2 * align256((size_t)B * gamma * 4) + 2 * align256((size_t)B * nC * 4) +
          align256((size_t)B * 16) + 256;
 }
@@ -747,21 +746,11 @@ static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target
                               hipStream_t stream) {
   VerifyWs ws = carve(wsp, B, gamma, V);
   {
-    TraceScope t0("verify_init_kernel", stream);
-    verify_init_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(B, ws.first_rej,
-                                                                        ws.any_res);
-  }
-  {
     TraceScope t1("verify_rows_kernel", stream);
     verify_rows_kernel<T><<<dim3(B * (gamma + 1)), dim3(256), 0, stream>>>(
         B, gamma, V, target, tokens, q_tok, temperature, uniforms, ell, ws, status);
   }
-  {
-    TraceScope tp("verify_plan_kernel", stream);
-    verify_plan_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(B, gamma, V, ell,
-                                                                        temperature, anchor,
-                                                                        tokens, ws);
-  }
+
   // bf16 with at most 128 requests: the tile-loop form
   bool tiles = false;
   if constexpr (sizeof(T) == 2) {
@@ -776,6 +765,16 @@ static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target
     }
   }
   if (!tiles) {
+    {
+      TraceScope t0("verify_init_kernel", stream);
+      verify_init_kernel<<<dim3(1), dim3(64), 0, stream>>>(ws.any_res);
+    }
+    {
+      TraceScope tp("verify_plan_kernel", stream);
+      verify_plan_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(B, gamma, V, ell,
+                                                                          temperature, anchor,
+                                                                          tokens, ws);
+    }
     TraceScope t2("verify_final_stats_kernel", stream);
     verify_final_stats_kernel<T, KS><<<dim3(n_tiles(V)), dim3(256), 0, stream>>>(
         B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
