@@ -30,6 +30,9 @@ namespace dspark {
 
 namespace {
 
+// candidates per thread of the 1024-thread group (kScheduleMaxKeys / 1024)
+constexpr int kSchedPer = kScheduleMaxKeys / 1024;
+
 struct dd {
   double hi, lo;
 };
@@ -218,29 +221,44 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
   int P = 1024;
   while (P < N) P <<= 1;
 
-  // 1. survival products
+  // 1. survival products: the confidences are read by the whole group at
+  //    once (clamped into [0, 1], a bad value flagged), then each request's
+  //    running product is taken in LDS
+  for (int i = tid; i < N; i += nthr) {
+    float c = conf[i];
+    if (!(c >= 0.f)) {  // negative or NaN
+      flag(status, DSPARK_DEV_BAD_CONF);
+      c = 0.f;
+    } else if (c > 1.f) {
+      flag(status, DSPARK_DEV_BAD_CONF);
+      c = 1.f;
+    }
+    key[i] = (double)c;
+    idx[i] = i;
+  }
+  __syncthreads();
   for (int r = tid; r < R; r += nthr) {
     double acc = 1.0;
     for (int j = 0; j < gamma; ++j) {
-      float c = conf[(size_t)r * gamma + j];
-      if (!(c >= 0.f)) {  // negative or NaN
-        flag(status, DSPARK_DEV_BAD_CONF);
-        c = 0.f;
-      } else if (c > 1.f) {
-        flag(status, DSPARK_DEV_BAD_CONF);
-        c = 1.f;
-      }
-      acc = acc * (double)c;
+      acc = acc * key[r * gamma + j];
       key[r * gamma + j] = acc;
-      idx[r * gamma + j] = r * gamma + j;
     }
-    ell[r] = 0;
   }
   for (int i = N + tid; i < P; i += nthr) {
     key[i] = -1.0;
     idx[i] = 0x7fffffff;
   }
   if (tid == 0) s_first_fail = N;
+  // the SPS entries this thread's admission tests read (R + n for n in its
+  // block and one past it), requested now and used after the ranking
+  const int per = (N + nthr - 1) / nthr;
+  const int c0 = min(N, tid * per), c1 = min(N, c0 + per);
+  double spv[kSchedPer + 1];
+#pragma unroll
+  for (int u = 0; u <= kSchedPer; ++u) {
+    const int i = R + c0 + u;
+    spv[u] = (u <= per && i < sps_len) ? sps[i] : 0.0;
+  }
   __syncthreads();
 
   // 2. rank order (survival desc, flat id asc): merge the per-request runs,
@@ -264,8 +282,6 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
 
   // 3. double-double prefix sums over ranked survivals, in thread-contiguous
   //    blocks of `per` candidates
-  const int per = (N + nthr - 1) / nthr;
-  const int c0 = min(N, tid * per), c1 = min(N, c0 + per);
   dd local{0.0, 0.0};
   for (int i = c0; i < c1; ++i) local = dd_add(local, dd{key[i], 0.0});
   const int lane = tid & 63, wave = tid >> 6;
@@ -285,17 +301,20 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
 
   // 4. admission test of each candidate n in this thread's block
   int fail = N;
-  for (int n = c0; n < c1; ++n) {
+#pragma unroll
+  for (int u = 0; u < kSchedPer; ++u) {
+    const int n = c0 + u;
+    if (n >= c1 || fail != N) break;
     const double tau_n = run.hi + run.lo;
     run = dd_add(run, dd{key[n], 0.0});
     const double tau_n1 = run.hi + run.lo;
-    const int nb = R + n + 1;
-    bool ok = nb < sps_len && sps[nb] > 0.0;
+    const int nb = R + n + 1;   // SPS at nb is spv[u + 1], at nb - 1 spv[u]
+    bool ok = nb < sps_len && spv[u + 1] > 0.0;
     if (ok) {
-      const double theta_n = tau_n * sps[nb - 1];
-      ok = tau_n1 * sps[nb] > theta_n;
+      const double theta_n = tau_n * spv[u];
+      ok = tau_n1 * spv[u + 1] > theta_n;
     }
-    if (!ok) { fail = n; break; }
+    if (!ok) fail = n;
   }
   // first failing candidate overall
   fail = block_min_int(fail, reinterpret_cast<double*>(wsum_hi));
@@ -304,21 +323,35 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
   // or the start value when nothing is admitted)
   if (tid == 0 && nadm == 0) {
     s_tau = (double)R;
-    s_theta = R < sps_len ? (double)R * sps[R] : 0.0;
+    s_theta = R < sps_len ? (double)R * spv[0] : 0.0;   // thread 0: spv[0] = SPS[R]
   }
   if (nadm > 0 && nadm - 1 >= c0 && nadm - 1 < c1) {
     dd r2 = dd_add(base, excl);
     for (int n = c0; n < nadm; ++n) r2 = dd_add(r2, dd{key[n], 0.0});
     const double tau = r2.hi + r2.lo;
+    double sp_last = 0.0;   // SPS[R + nadm] = spv[nadm - c0]
+#pragma unroll
+    for (int u = 0; u <= kSchedPer; ++u)
+      if (u == nadm - c0) sp_last = spv[u];
     s_tau = tau;
-    s_theta = tau * sps[R + nadm];
+    s_theta = tau * sp_last;
   }
   __syncthreads();
 
-  // 5. outputs
+  // 5. outputs: the ranked order, and ell[r] = the admitted candidates of
+  //    request r, which are a prefix of its positions (its survival never
+  //    rises with j and ties keep the flat order), read off their ranks
+  int* rank = reinterpret_cast<int*>(key);   // the keys are no longer read
   for (int i = tid; i < N; i += nthr) {
-    if (order) order[i] = idx[i];
-    if (i < nadm) atomicAdd(&ell[idx[i] / gamma], 1);
+    const int id = idx[i];
+    if (order) order[i] = id;
+    rank[id] = i;
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += nthr) {
+    int L = 0;
+    while (L < gamma && rank[r * gamma + L] < nadm) ++L;
+    ell[r] = L;
   }
   if (tid == 0 && stats) {
     stats[0] = (double)nadm;
