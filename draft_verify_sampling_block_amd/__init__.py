@@ -4,7 +4,8 @@ Argument marshalling only: every step of the sampling path runs in the
 library's kernels.  torch supplies device memory and the current stream.
 The functions carry the C entry points' names:
 
-    dspark_draft_block, dspark_confidence, dspark_schedule, dspark_verify
+    dspark_draft_block, dspark_confidence, dspark_schedule, dspark_verify,
+    dspark_schedule_capacity, dspark_schedule_threshold
 
 If ``libdspark.so`` is missing the import still succeeds (so the CPU test
 suite can run), but every entry point raises ``DsparkError``; nothing falls
@@ -21,7 +22,8 @@ import torch
 
 __all__ = [
     "DsparkError", "lib_path", "load", "dspark_draft_block", "dspark_confidence",
-    "dspark_schedule", "dspark_verify", "dspark_draft_block_workspace",
+    "dspark_schedule", "dspark_schedule_capacity", "dspark_schedule_threshold", "dspark_verify",
+    "dspark_draft_block_workspace",
     "dspark_verify_workspace", "dspark_schedule_workspace", "exported_names", "header_names",
     "dspark_trace_enable", "dspark_trace_summary", "dspark_set_draft_path",
     "DSPARK_F32", "DSPARK_BF16", "DEV_FLAGS",
@@ -58,6 +60,9 @@ _SIGS = {
     "dspark_confidence": (_I, [_I] * 6 + [_P] * 5 + [ctypes.c_float, _P, _P, _P]),
     "dspark_schedule_workspace": (_SZ, [_I, _I]),
     "dspark_schedule": (_I, [_I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dspark_schedule_capacity": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dspark_schedule_threshold": (_I, [_I, _I, _P, ctypes.c_double, _P, _P, _P, _P, _P, _SZ,
+                                       _P]),
     "dspark_verify_workspace": (_SZ, [_I, _I, _I, _I, _I]),
     "dspark_verify": (_I, [_I] * 5 + [_P] * 15 + [_P, _P, _SZ, _P]),
     "dspark_trace_enable": (_I, [_I]),
@@ -233,6 +238,45 @@ def dspark_schedule(conf, sps, *, ell=None, order=None, stats=None, status=None,
     _check(lib.dspark_schedule(R, gamma, _ptr(conf), _ptr(sps), int(sps.numel()), _ptr(ell),
                                _ptr(order), _ptr(stats), _ptr(status), _ptr(ws),
                                0 if ws is None else ws.numel(), _stream()))
+    return ell, order, stats
+
+
+def _schedule_outputs(conf, ell, order, stats, want_order):
+    R, gamma = conf.shape
+    dev = conf.device
+    _need(conf, "conf", torch.float32)
+    ell = ell if ell is not None else torch.empty((R,), dtype=torch.int32, device=dev)
+    if order is None and want_order:
+        order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
+    stats = stats if stats is not None else torch.empty((3,), dtype=torch.float64, device=dev)
+    need = dspark_schedule_workspace(R, gamma)
+    ws = _workspace(need, dev) if need else None
+    return R, gamma, ell, order, stats, ws
+
+
+def dspark_schedule_capacity(conf, capacity, *, ell=None, order=None, stats=None, status=None,
+                             want_order=True):
+    """Top-K scheduler (two-step barrier); capacity: fp64 device tensor whose first
+    element is K (e.g. stats of an earlier dspark_schedule).  Returns (ell, order, stats)."""
+    lib = load()
+    R, gamma, ell, order, stats, ws = _schedule_outputs(conf, ell, order, stats, want_order)
+    if not (isinstance(capacity, torch.Tensor) and capacity.dtype == torch.float64
+            and capacity.device == conf.device and capacity.numel() >= 1):
+        raise DsparkError(-1, "capacity must be a float64 tensor on the device of conf")
+    _check(lib.dspark_schedule_capacity(R, gamma, _ptr(conf), _ptr(capacity), _ptr(ell),
+                                        _ptr(order), _ptr(stats), _ptr(status), _ptr(ws),
+                                        0 if ws is None else ws.numel(), _stream()))
+    return ell, order, stats
+
+
+def dspark_schedule_threshold(conf, threshold, *, ell=None, order=None, stats=None, status=None,
+                              want_order=True):
+    """Fixed survival threshold scheduler.  Returns (ell, order, stats)."""
+    lib = load()
+    R, gamma, ell, order, stats, ws = _schedule_outputs(conf, ell, order, stats, want_order)
+    _check(lib.dspark_schedule_threshold(R, gamma, _ptr(conf), ctypes.c_double(threshold),
+                                         _ptr(ell), _ptr(order), _ptr(stats), _ptr(status),
+                                         _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
     return ell, order, stats
 
 

@@ -7,6 +7,7 @@
 
 #include "../../include/dspark.h"
 #include "dspark_launch.hpp"
+#include "schedule_launch.hpp"
 
 namespace {
 
@@ -130,23 +131,63 @@ size_t dspark_schedule_workspace(int R, int gamma) {
   return dspark::schedule_workspace_bytes(R, gamma);
 }
 
-int dspark_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
-                    int32_t* ell, int32_t* order, double* stats, int32_t* status,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "dspark_schedule";
+namespace {
+// checks shared by the three scheduler entry points
+int check_schedule(const char* fn, int R, int gamma, const float* conf, int32_t* ell,
+                   int32_t* order, double* stats, int32_t* status, void* workspace,
+                   size_t workspace_bytes) {
   if (R < 1) return fail(DSPARK_EINVAL, "%s: R=%d must be >= 1", fn, R);
   if (gamma < 1 || gamma > 64) return fail(DSPARK_EINVAL, "%s: gamma=%d outside [1,64]", fn, gamma);
   if ((long long)R * gamma > dspark::kScheduleMaxKeys)
     return fail(DSPARK_EUNSUPPORTED, "%s: R*gamma=%lld exceeds %d candidates", fn,
                 (long long)R * gamma, dspark::kScheduleMaxKeys);
-  if (sps_len < 1) return fail(DSPARK_EINVAL, "%s: sps_len=%d must be >= 1", fn, sps_len);
-  REQUIRE_PTR(conf); REQUIRE_PTR(sps); REQUIRE_PTR(ell); OPT_PTR(order); OPT_PTR(stats);
-  OPT_PTR(status);
+  REQUIRE_PTR(conf); REQUIRE_PTR(ell); OPT_PTR(order); OPT_PTR(stats); OPT_PTR(status);
   const size_t need = dspark::schedule_workspace_bytes(R, gamma);
   if (need && (!workspace || workspace_bytes < need))
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
-  return hip_status(fn, dspark::launch_schedule(R, gamma, conf, sps, sps_len, ell, order, stats,
-                                                status, workspace, stream));
+  return DSPARK_OK;
+}
+}  // namespace
+
+int dspark_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
+                    int32_t* ell, int32_t* order, double* stats, int32_t* status,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dspark_schedule";
+  int rc = check_schedule(fn, R, gamma, conf, ell, order, stats, status, workspace,
+                          workspace_bytes);
+  if (rc) return rc;
+  if (sps_len < 1) return fail(DSPARK_EINVAL, "%s: sps_len=%d must be >= 1", fn, sps_len);
+  REQUIRE_PTR(sps);
+  return hip_status(fn, dspark::launch_schedule(R, gamma, conf, sps, sps_len, dspark::kSchedTheta,
+                                                0.0, nullptr, ell, order, stats, status,
+                                                workspace, stream));
+}
+
+int dspark_schedule_capacity(int R, int gamma, const float* conf, const double* capacity,
+                             int32_t* ell, int32_t* order, double* stats, int32_t* status,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dspark_schedule_capacity";
+  int rc = check_schedule(fn, R, gamma, conf, ell, order, stats, status, workspace,
+                          workspace_bytes);
+  if (rc) return rc;
+  if (!capacity) return fail(DSPARK_EINVAL, "%s: 'capacity' is NULL", fn);
+  if (reinterpret_cast<uintptr_t>(capacity) & 7u)
+    return fail(DSPARK_EALIGN, "%s: 'capacity' is not 8-byte aligned", fn);
+  return hip_status(fn, dspark::launch_schedule(R, gamma, conf, nullptr, 0,
+                                                dspark::kSchedCapacity, 0.0, capacity, ell,
+                                                order, stats, status, workspace, stream));
+}
+
+int dspark_schedule_threshold(int R, int gamma, const float* conf, double threshold,
+                              int32_t* ell, int32_t* order, double* stats, int32_t* status,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dspark_schedule_threshold";
+  int rc = check_schedule(fn, R, gamma, conf, ell, order, stats, status, workspace,
+                          workspace_bytes);
+  if (rc) return rc;
+  return hip_status(fn, dspark::launch_schedule(R, gamma, conf, nullptr, 0,
+                                                dspark::kSchedThreshold, threshold, nullptr,
+                                                ell, order, stats, status, workspace, stream));
 }
 
 size_t dspark_verify_workspace(int B, int gamma, int V, int rank, int dtype) {

@@ -33,9 +33,6 @@ hipError_t launch_confidence(int B, int gamma, int H, int V, int rank, int dtype
 constexpr int kScheduleMaxKeys = 8192;
 constexpr int kScheduleMergeKeys = 4096;   // candidates sorted by merging runs
 size_t schedule_workspace_bytes(int R, int gamma);
-hipError_t launch_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
-                           int32_t* ell, int32_t* order, double* stats, int32_t* status,
-                           void* ws, hipStream_t stream);
 
 size_t verify_workspace_bytes(int B, int gamma, int V, int rank, int dtype);
 hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const void* target,

@@ -22,8 +22,16 @@
 //   4. candidate n is admitted iff Bt+1 is inside the table, SPS > 0 there,
 //      and tau_{n+1} * SPS[R+n+1] > tau_n * SPS[R+n]; the number admitted is
 //      the first n that fails (block min-reduction) -- no sequential loop.
+//
+// Two further stop rules share steps 1-3 and admit a prefix of the same
+// ranking: capacity ([billytse] 7, [weigao] part 4 asynchronous scheduling:
+// the batch size K is fixed from older predictions, the current candidates
+// are still ranked by their latest survival; the first K are taken) and
+// threshold ([billytse] 8 threshold sweep: every candidate whose survival is
+// at least the threshold).
 #include "dspark_common.hpp"
 #include "dspark_launch.hpp"
+#include "schedule_launch.hpp"
 #include "trace.hpp"
 
 namespace dspark {
@@ -202,7 +210,9 @@ __device__ int merge_runs(double* k0, int* i0, double* k1, int* i1, int N, int L
 __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
                                                         const float* __restrict__ conf,
                                                         const double* __restrict__ sps,
-                                                        int sps_len, int32_t* __restrict__ ell,
+                                                        int sps_len, int mode, double thr,
+                                                        const double* __restrict__ cap,
+                                                        int32_t* __restrict__ ell,
                                                         int32_t* __restrict__ order,
                                                         double* __restrict__ stats,
                                                         int32_t* status) {
@@ -213,7 +223,6 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
   double* key = key_a;
   int* idx = idx_a;
   __shared__ double wsum_hi[16], wsum_lo[16];
-  __shared__ int s_first_fail;
   __shared__ double s_tau, s_theta;
 
   const int tid = threadIdx.x, nthr = blockDim.x;   // 1024
@@ -248,7 +257,6 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
     key[i] = -1.0;
     idx[i] = 0x7fffffff;
   }
-  if (tid == 0) s_first_fail = N;
   // the SPS entries this thread's admission tests read (R + n for n in its
   // block and one past it), requested now and used after the ranking
   const int per = (N + nthr - 1) / nthr;
@@ -257,7 +265,13 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
 #pragma unroll
   for (int u = 0; u <= kSchedPer; ++u) {
     const int i = R + c0 + u;
-    spv[u] = (u <= per && i < sps_len) ? sps[i] : 0.0;
+    spv[u] = (mode == kSchedTheta && u <= per && i < sps_len) ? sps[i] : 0.0;
+  }
+  // capacity: K floored and clamped to [0, N]; NaN or below 1 takes nothing
+  int kcap = 0;
+  if (mode == kSchedCapacity) {
+    const double K = cap[0];
+    kcap = K >= 1.0 ? (K >= (double)N ? N : (int)floor(K)) : 0;
   }
   __syncthreads();
 
@@ -301,20 +315,32 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
 
   // 4. admission test of each candidate n in this thread's block
   int fail = N;
-#pragma unroll
-  for (int u = 0; u < kSchedPer; ++u) {
-    const int n = c0 + u;
-    if (n >= c1 || fail != N) break;
-    const double tau_n = run.hi + run.lo;
-    run = dd_add(run, dd{key[n], 0.0});
-    const double tau_n1 = run.hi + run.lo;
-    const int nb = R + n + 1;   // SPS at nb is spv[u + 1], at nb - 1 spv[u]
-    bool ok = nb < sps_len && spv[u + 1] > 0.0;
-    if (ok) {
-      const double theta_n = tau_n * spv[u];
-      ok = tau_n1 * spv[u + 1] > theta_n;
+  if (mode == kSchedCapacity) {
+    fail = kcap;
+  } else if (mode == kSchedThreshold) {
+    // survivals are ranked descending: the first one below the threshold
+    for (int n = c0; n < c1; ++n) {
+      if (!(key[n] >= thr)) {
+        fail = n;
+        break;
+      }
     }
-    if (!ok) fail = n;
+  } else {
+#pragma unroll
+    for (int u = 0; u < kSchedPer; ++u) {
+      const int n = c0 + u;
+      if (n >= c1 || fail != N) break;
+      const double tau_n = run.hi + run.lo;
+      run = dd_add(run, dd{key[n], 0.0});
+      const double tau_n1 = run.hi + run.lo;
+      const int nb = R + n + 1;   // SPS at nb is spv[u + 1], at nb - 1 spv[u]
+      bool ok = nb < sps_len && spv[u + 1] > 0.0;
+      if (ok) {
+        const double theta_n = tau_n * spv[u];
+        ok = tau_n1 * spv[u + 1] > theta_n;
+      }
+      if (!ok) fail = n;
+    }
   }
   // first failing candidate overall
   fail = block_min_int(fail, reinterpret_cast<double*>(wsum_hi));
@@ -324,6 +350,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
   if (tid == 0 && nadm == 0) {
     s_tau = (double)R;
     s_theta = R < sps_len ? (double)R * spv[0] : 0.0;   // thread 0: spv[0] = SPS[R]
+    if (mode != kSchedTheta) s_theta = __builtin_nan("");
   }
   if (nadm > 0 && nadm - 1 >= c0 && nadm - 1 < c1) {
     dd r2 = dd_add(base, excl);
@@ -334,7 +361,7 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
     for (int u = 0; u <= kSchedPer; ++u)
       if (u == nadm - c0) sp_last = spv[u];
     s_tau = tau;
-    s_theta = tau * sp_last;
+    s_theta = mode == kSchedTheta ? tau * sp_last : __builtin_nan("");
   }
   __syncthreads();
 
@@ -366,12 +393,14 @@ size_t schedule_workspace_bytes(int R, int gamma) {
 }
 
 hipError_t launch_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
-                           int32_t* ell, int32_t* order, double* stats, int32_t* status,
-                           void* ws, hipStream_t stream) {
+                           int mode, double threshold, const double* capacity, int32_t* ell,
+                           int32_t* order, double* stats, int32_t* status, void* ws,
+                           hipStream_t stream) {
   (void)ws;
   TraceScope ts("schedule_kernel", stream);
-  schedule_kernel<<<dim3(1), dim3(1024), 0, stream>>>(R, gamma, conf, sps, sps_len, ell, order,
-                                                      stats, status);
+  schedule_kernel<<<dim3(1), dim3(1024), 0, stream>>>(R, gamma, conf, sps, sps_len, mode,
+                                                      threshold, capacity, ell, order, stats,
+                                                      status);
   return hipGetLastError();
 }
 

@@ -47,7 +47,7 @@ int trace_begin(const char* name, hipStream_t stream) {
   std::lock_guard<std::mutex> lk(g_mu);
   Rec r{name, get_event(), get_event()};
   if (!r.a || !r.b) return -1;
-  hipEventRecord(r.a, stream);
+  if (hipEventRecord(r.a, stream) != hipSuccess) return -1;
   g_recs.push_back(r);
   return (int)g_recs.size() - 1;
 }
@@ -55,7 +55,8 @@ int trace_begin(const char* name, hipStream_t stream) {
 void trace_end(int slot, hipStream_t stream) {
   if (slot < 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (slot < (int)g_recs.size()) hipEventRecord(g_recs[slot].b, stream);
+  // a failed record makes dspark_trace_summary report DSPARK_EHIP
+  if (slot < (int)g_recs.size()) (void)hipEventRecord(g_recs[slot].b, stream);
 }
 
 }  // namespace dspark

@@ -153,6 +153,43 @@ int dspark_schedule(int R, int gamma, const float* conf,
                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * dspark_schedule_capacity: the two-step causal barrier ([billytse] 7;
+ * [weigao] part 4, asynchronous scheduling).  The size of the next target
+ * batch is fixed beforehand from older predictions; the current candidates
+ * are still ranked by their latest survival, and the first K are verified:
+ *     a[r,j] and the rank order exactly as dspark_schedule
+ *     K = floor(*capacity) clamped to [0, R*gamma]; NaN or < 1 gives 0
+ *     ell[r] = number of request r's candidates among the first K ranked
+ *     (always a prefix; whether (r,j) is taken never reads conf[r, j+1..])
+ * in : conf [R,gamma] fp32 (clamped and flagged as in dspark_schedule);
+ *      capacity: DEVICE pointer to one fp64, read when the kernel runs (for
+ *      example stats[0] written by a dspark_schedule call of an earlier
+ *      step, so the chain needs no host round trip); 8-byte aligned
+ * out: ell [R] int32; order [R*gamma] int32 (or NULL); stats [3] fp64
+ *      {n_admitted, tau, NaN} (or NULL), tau as in dspark_schedule
+ * workspace: dspark_schedule_workspace(R, gamma) bytes (currently 0).
+ * ---------------------------------------------------------------------- */
+int dspark_schedule_capacity(int R, int gamma, const float* conf,
+                             const double* capacity,
+                             int32_t* ell, int32_t* order, double* stats,
+                             int32_t* status, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dspark_schedule_threshold: fixed confidence threshold ([billytse] 8,
+ * threshold sweep; [xhh] scheduler Q&A contrasts it with the load-dependent
+ * rule).  Candidate (r,j) is verified iff a[r,j] >= threshold (fp64
+ * comparison of the fp64 survival); a NaN threshold verifies nothing.
+ * Survival never rises along a request, so ell[r] counts a prefix.
+ * in/out and workspace as dspark_schedule_capacity; stats {n, tau, NaN}.
+ * ---------------------------------------------------------------------- */
+int dspark_schedule_threshold(int R, int gamma, const float* conf,
+                              double threshold,
+                              int32_t* ell, int32_t* order, double* stats,
+                              int32_t* status, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * dspark_verify: lossless speculative rejection sampling ([billytse] 1;
  * [xhh] acceptance-rule Q&A).
  * For request b with verify length L = ell[b] (0..gamma):

@@ -48,6 +48,8 @@ __all__ = [
     "confidence",
     "survival",
     "schedule",
+    "schedule_capacity",
+    "schedule_threshold",
     "target_probs",
     "verify",
 ]
@@ -306,6 +308,75 @@ def schedule(c, sps):
             break
     return dict(ell=ell, order=np.asarray(order, dtype=np.int64), n_admitted=n,
                 tau=tau, theta=theta, a=a)
+
+
+def _ranked(a):
+    """Flat ids of every candidate by survival descending, flat id ascending."""
+    flat = a.reshape(-1)
+    return flat, sorted(range(flat.size), key=lambda i: (-flat[i], i))
+
+
+def _admit_prefix(a, order, n):
+    """ell and tau when the first n ranked candidates are verified."""
+    R, gamma = a.shape
+    flat = a.reshape(-1)
+    ell = np.zeros(R, dtype=np.int64)
+    exact = Fraction(R)
+    for i in order[:n]:
+        ell[i // gamma] += 1
+        exact += Fraction(float(flat[i]))
+    return ell, float(exact)
+
+
+def schedule_capacity(c, capacity):
+    """Verify the top-K candidates, K fixed beforehand (two-step barrier).
+
+    [billytse] 7 and [weigao] part 4 (asynchronous scheduling): the size of
+    the next target batch is decided from the predictions of two steps
+    earlier, so it is known before the current drafts exist; the current
+    candidates are still ranked by their latest cumulative confidence, and
+    the old information only fixes how many of them (K) are taken.  Whether
+    candidate (r, j) is taken then depends only on how many candidates rank
+    ahead of it, none of which is a later position of request r.
+
+    capacity: K as a real number (the count an earlier Theta-greedy admitted,
+    for example); it is floored and clamped to [0, R*gamma]; NaN or negative
+    means 0.  Returns the fields of ``schedule`` with theta = NaN (no SPS
+    table is involved).
+    """
+    a = survival(c)
+    R, gamma = a.shape
+    _, order = _ranked(a)
+    K = float(capacity)
+    n = 0 if not (K >= 1.0) else int(min(np.floor(K), R * gamma))
+    ell, tau = _admit_prefix(a, order, n)
+    return dict(ell=ell, order=np.asarray(order, dtype=np.int64), n_admitted=n, tau=tau,
+                theta=float("nan"), a=a)
+
+
+def schedule_threshold(c, threshold):
+    """Verify every candidate whose survival is at least a fixed threshold.
+
+    [billytse] 8 (offline threshold sweep on confidence) and [xhh] scheduler
+    Q&A (a fixed threshold, unlike the Theta rule, does not follow the
+    load): candidate (r, j) is verified iff a[r, j] >= threshold.  Survival
+    never rises along a request's positions, so each request's verified set
+    is a prefix, and the decision for (r, j) reads only c[r, :j+1].
+    A NaN threshold verifies nothing.  Returns the fields of ``schedule``
+    with theta = NaN.
+    """
+    a = survival(c)
+    R, gamma = a.shape
+    flat, order = _ranked(a)
+    thr = float(threshold)
+    n = 0
+    for i in order:
+        if not (flat[i] >= thr):
+            break
+        n += 1
+    ell, tau = _admit_prefix(a, order, n)
+    return dict(ell=ell, order=np.asarray(order, dtype=np.int64), n_admitted=n, tau=tau,
+                theta=float("nan"), a=a)
 
 
 # ----------------------------------------------------------------------------

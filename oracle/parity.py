@@ -84,6 +84,20 @@ def check_schedule(conf, sps, ell, order, stats):
     return dict(n_admitted=s["n_admitted"], mean_ell=float(np.mean(s["ell"])))
 
 
+def check_schedule_mode(conf, mode, arg, ell, order, stats):
+    """Capacity (arg = K) or threshold (arg = survival threshold) scheduler:
+    ell, order and the admitted count bit-exact, tau to 1e-12, Theta NaN."""
+    c = conf.astype(np.float64)
+    s = O.schedule_capacity(c, arg) if mode == "capacity" else O.schedule_threshold(c, arg)
+    _req(np.array_equal(np.asarray(order, dtype=np.int64), s["order"]), "scheduler order differs")
+    _req(np.array_equal(np.asarray(ell, dtype=np.int64), s["ell"]),
+         f"ell differs at {np.nonzero(np.asarray(ell) != s['ell'])[0][:8]}")
+    _req(int(round(stats[0])) == s["n_admitted"], f"n_admitted {stats[0]} vs {s['n_admitted']}")
+    _req(abs(stats[1] - s["tau"]) <= 1e-12 * abs(s["tau"]), f"tau {stats[1]} vs {s['tau']}")
+    _req(np.isnan(stats[2]), f"theta {stats[2]} should be NaN")
+    return dict(n_admitted=s["n_admitted"], mean_ell=float(np.mean(s["ell"])))
+
+
 def check_verify(wl, W1_64, W2t_64, tokens, ell, out_tokens, n_accepted, ratio, requests=None):
     B, gamma = tokens.shape
     reqs = list(range(B)) if requests is None else list(requests)
