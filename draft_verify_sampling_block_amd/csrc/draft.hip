@@ -462,7 +462,9 @@ __device__ inline void stores_done_group() {
 // registers (NW = 8: two waves per SIMD, 128 registers of tile each at rank
 // 256; NW = 4: one wave per SIMD with two tiles, the tiles and the
 // accumulators split over the architectural and accumulation registers).
-template <int KS, int NW>
+// PF: the groups that draw no token warm the caches with the next
+// position's base logits while the owners draw.
+template <int KS, int NW, bool PF>
 __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
   constexpr int nq = 2 * KS;
   constexpr int R = kPdRegTiles / NW;
@@ -477,6 +479,8 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
   __shared__ float s_mx[kSlots][kPdMaxRows], s_sum[kSlots][kPdMaxRows];
   __shared__ int s_arg[kSlots][kPdMaxRows];
   __shared__ SampShared sh;
+  // sink of the cache-warming loads (never read)
+  __shared__ uint32_t s_pf[1];
 
   const int p = blockIdx.x, P = a.P;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -734,6 +738,52 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
     stores_done_group();
     if (threadIdx.x == 0) st_flag(a.stats_flag + (size_t)p * kPdFlagStride, (uint32_t)(k + 1));
 
+    // Groups that draw no token are idle until the tokens of position k
+    // arrive: they touch the next position's base logits (one dword per
+    // 32 bytes, DMA'd into LDS the group never reads) of their own tiles and
+    // of an owner group's tiles, so those rows sit in the caches (the
+    // Infinity Cache, and the L2 of the XCD both groups run on) when the
+    // tasks of position k + 1 stream them.  Wave 0 keeps polling flags.
+    if constexpr (PF) {
+      const int nown = min(B, P);
+      if (k + 1 < gamma && p >= nown && wave > 0) {
+        const int other = p - nown;     // owner group covered by this one, if any
+        const int nsl = (other < nown) ? 2 : 1;
+        constexpr int kSeg = 16;        // bf16 entries per 32-byte segment
+        auto slice = [&](int sl, int& v0, int& v1) {
+          const int q = sl == 0 ? p : other;
+          const int tc = nT / P + (q < nT % P ? 1 : 0);
+          const int tb = q * (nT / P) + min(q, nT % P);
+          v0 = tb * kTileV;
+          v1 = min(V, (tb + tc) * kTileV);
+        };
+        int s0a, s0b, s1a = 0, s1b = 0;
+        slice(0, s0a, s0b);
+        if (nsl == 2) slice(1, s1a, s1b);
+        const int n0 = (s0b - s0a + kSeg - 1) / kSeg, n1 = (s1b - s1a + kSeg - 1) / kSeg;
+        const int per_req = n0 + n1;
+        const int total = per_req * B;
+        // eight loads in flight per lane per round; their XOR is kept only
+        // so that the loads are issued (and the wave waits for them here,
+        // while wave 0 is still polling)
+        constexpr int kPfU = 8;
+        uint32_t x = 0;
+        for (int g0 = (wave - 1) * 64; g0 < total; g0 += (NW - 1) * 64 * kPfU) {
+          uint32_t w[kPfU];
+#pragma unroll
+          for (int u = 0; u < kPfU; ++u) {
+            const int g = min(g0 + u * (NW - 1) * 64 + lane, total - 1);
+            const int b = g / per_req, j = g - b * per_req;
+            const int v = j < n0 ? s0a + j * kSeg : s1a + (j - n0) * kSeg;
+            w[u] = *reinterpret_cast<const uint32_t*>(a.U + ((size_t)b * gamma + k + 1) * V + v);
+          }
+#pragma unroll
+          for (int u = 0; u < kPfU; ++u) x ^= w[u];
+        }
+        if (x == 0x7fc00001u) s_pf[0] = x;   // practically never true
+      }
+    }
+
     // draw the tokens of the requests this group owns
     bool waited = false;
     for (int b = p; b < B; b += P) {
@@ -852,8 +902,8 @@ static hipError_t draft_persistent(int B, int gamma, int V, int rank, const uint
   // overlap one wave's reductions with the other's matrix instructions)
   // unless 4 (two tiles each) are asked for
   const int nw = g_draft_path == 4 ? 4 : 8;
-  const void* kern = nw == 8 ? reinterpret_cast<const void*>(pdraft_kernel<KS, 8>)
-                             : reinterpret_cast<const void*>(pdraft_kernel<KS, 4>);
+  const void* kern = nw == 8 ? reinterpret_cast<const void*>(pdraft_kernel<KS, 8, true>)
+                             : reinterpret_cast<const void*>(pdraft_kernel<KS, 4, false>);
   int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, nw * 64, 0) != hipSuccess ||
       occ < 1)
