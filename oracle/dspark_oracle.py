@@ -34,6 +34,7 @@ exhaustive enumeration; no function here is "parity unpinned".
 
 from __future__ import annotations
 
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -52,6 +53,7 @@ __all__ = [
     "schedule_threshold",
     "target_probs",
     "verify",
+    "tv_label",
 ]
 
 
@@ -485,3 +487,44 @@ def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell
     return dict(out_tokens=out, n_accepted=n_acc, ratio=ratio, final_lo=f_lo,
                 final_hi=f_hi, final_margin=f_margin, degenerate=degenerate,
                 final_cdf=final_cdf)
+
+
+# ----------------------------------------------------------------------------
+# (5) acceptance label: total variation between draft and target
+# ----------------------------------------------------------------------------
+
+def tv_label(target, U, W1, W2t, anchor, tokens, temperature, rows=None):
+    """Per-position acceptance label from the total variation distance.
+
+    [weigao] part 3 (the confidence head's training target) and [billytse]
+    5.1: c*_k = 1 - 0.5 * ||p^d_k - p^t_k||_1, the draft distribution of
+    position k against the target distribution of the same position; the
+    total variation equals one minus the probability that the
+    accept-or-resample test keeps the drafted token ([billytse] 1).
+
+    The draft distribution is the one the token was sampled from: softmax of
+    (U[b, k] + W1[prev] W2) / T with prev the anchor (k = 0) or the drafted
+    token k - 1; the target distribution is softmax(target[b, k] / T).  A
+    greedy request (T <= 0) has one-hot q at its drafted token (the argmax
+    it drew) and one-hot p at the target's lowest-index argmax, so its label
+    is 1 when they agree, else 0.
+
+    rows: optional list of (b, k) to compute (others are NaN).
+    Returns dict(tv [B, gamma], label [B, gamma]).
+    """
+    B, gamma, V = np.asarray(U).shape
+    U = f64(U)
+    target = f64(target)
+    tv = np.full((B, gamma), np.nan)
+    todo = [(b, k) for b in range(B) for k in range(gamma)] if rows is None else rows
+    for b, k in todo:
+        T = float(temperature[b])
+        x = int(tokens[b, k])
+        if not (T > 0.0):
+            tv[b, k] = 0.0 if int(np.argmax(target[b, k])) == x else 1.0
+            continue
+        prev = int(anchor[b]) if k == 0 else int(tokens[b, k - 1])
+        q = _draft_probs(U[b, k] + markov_bias(W1, W2t, prev), T)
+        p = target_probs(target[b, k], T)
+        tv[b, k] = 0.5 * math.fsum(np.abs(p - q))
+    return dict(tv=tv, label=1.0 - tv)
