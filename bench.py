@@ -115,6 +115,63 @@ def counter_traffic(kernel, cfg):
             + float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])) * 1024.0
 
 
+def tv_label_bytes(wl):
+    """Algorithmic bytes of one dspark_tv_label call: every drafted
+    position's base-logit and target rows once, W2 once, the W1 rows of the
+    previous tokens, the draft row statistics, temperatures and the labels."""
+    e = 2 if wl.dtype == "bf16" else 4
+    B, g, V, r = wl.B, wl.gamma, wl.V, wl.rank
+    return e * V * 2 * B * g + e * r * V + e * B * g * r + 4 * B * g * 4 + 4 * B
+
+
+def next_rows(st, wl, reps):
+    """Time the scheduler stop-rule variants and the acceptance-label kernels
+    on this step's confidences and drafts (events on the launch stream)."""
+    import torch
+
+    import draft_verify_sampling_block_amd as dv
+
+    d = st.d
+    B, g = wl.B, wl.gamma
+    dev = d.U.device
+    ell = torch.empty((B,), dtype=torch.int32, device=dev)
+    order = torch.empty((B * g,), dtype=torch.int32, device=dev)
+    stats = torch.empty((3,), dtype=torch.float64, device=dev)
+    cap = torch.tensor([float(B * g) / 2.0], dtype=torch.float64, device=dev)
+    tv = torch.empty((B, g), dtype=torch.float32, device=dev)
+    label = torch.empty((B, g), dtype=torch.float32, device=dev)
+    dt = dv.DSPARK_BF16 if wl.dtype == "bf16" else dv.DSPARK_F32
+    ws = torch.empty(max(256, dv.dspark_tv_label_workspace(B, g, wl.V, wl.rank, dt)),
+                     dtype=torch.uint8, device=dev)
+    calls = {
+        "schedule_capacity": lambda: dv.dspark_schedule_capacity(st.conf, cap, ell=ell,
+                                                                 order=order, stats=stats),
+        "schedule_threshold": lambda: dv.dspark_schedule_threshold(st.conf, 0.5, ell=ell,
+                                                                   order=order, stats=stats),
+        "tv_label": lambda: dv.dspark_tv_label(d.target, d.U, d.W1, d.W2t, d.anchor, st.tokens,
+                                               st.row_max, st.row_logZ, d.temperature, tv=tv,
+                                               label=label, workspace=ws),
+    }
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        out[name] = {"us_per_call": us}
+    nb = tv_label_bytes(wl)
+    gbs = nb / (out["tv_label"]["us_per_call"] / 1e6) / 1e9
+    out["tv_label"].update({"bytes_alg": nb, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                            "mean_label": float(label.mean().item())})
+    return out
+
+
 def cpu_baseline(cfg, n_req):
     import numpy as np
 
@@ -240,6 +297,7 @@ def main():
                  "kernel_ms_per_step": {k: round(v, 5) for k, v in per_step_ms.items()},
                  "device_status": status},
     }
+    out["next_rows"] = next_rows(st, wl, max(3, args.steps // 2))
     if not args.no_cpu_baseline:
         n_req = args.cpu_requests or {0: 4, 1: 32, 2: 128, 3: 128, 4: 256}[cfg]
         out["cpu_baseline"] = cpu_baseline(cfg, n_req)

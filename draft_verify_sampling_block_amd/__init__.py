@@ -5,7 +5,7 @@ library's kernels.  torch supplies device memory and the current stream.
 The functions carry the C entry points' names:
 
     dspark_draft_block, dspark_confidence, dspark_schedule, dspark_verify,
-    dspark_schedule_capacity, dspark_schedule_threshold
+    dspark_schedule_capacity, dspark_schedule_threshold, dspark_tv_label
 
 If ``libdspark.so`` is missing the import still succeeds (so the CPU test
 suite can run), but every entry point raises ``DsparkError``; nothing falls
@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "DsparkError", "lib_path", "load", "dspark_draft_block", "dspark_confidence",
     "dspark_schedule", "dspark_schedule_capacity", "dspark_schedule_threshold", "dspark_verify",
-    "dspark_draft_block_workspace",
+    "dspark_tv_label", "dspark_tv_label_workspace", "dspark_draft_block_workspace",
     "dspark_verify_workspace", "dspark_schedule_workspace", "exported_names", "header_names",
     "dspark_trace_enable", "dspark_trace_summary", "dspark_set_draft_path",
     "DSPARK_F32", "DSPARK_BF16", "DEV_FLAGS",
@@ -64,6 +64,8 @@ _SIGS = {
     "dspark_schedule_threshold": (_I, [_I, _I, _P, ctypes.c_double, _P, _P, _P, _P, _P, _SZ,
                                        _P]),
     "dspark_verify_workspace": (_SZ, [_I, _I, _I, _I, _I]),
+    "dspark_tv_label_workspace": (_SZ, [_I, _I, _I, _I, _I]),
+    "dspark_tv_label": (_I, [_I] * 5 + [_P] * 12 + [_P, _SZ, _P]),
     "dspark_verify": (_I, [_I] * 5 + [_P] * 15 + [_P, _P, _SZ, _P]),
     "dspark_trace_enable": (_I, [_I]),
     "dspark_trace_summary": (_I, [ctypes.c_char_p, _SZ]),
@@ -308,3 +310,33 @@ def dspark_verify(target, U, W1, W2t, anchor, tokens, q_tok, row_max, row_logZ, 
                              _ptr(n_accepted), _ptr(ratio), _ptr(status), _ptr(ws), ws.numel(),
                              _stream()))
     return out_tokens, n_accepted, ratio
+
+
+def dspark_tv_label_workspace(B, gamma, V, rank, dtype) -> int:
+    return int(load().dspark_tv_label_workspace(B, gamma, V, rank, dtype))
+
+
+def dspark_tv_label(target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature, *,
+                    tv=None, label=None, status=None, workspace=None, want_label=True):
+    """Acceptance label 1 - TV(draft, target) per drafted position; returns (tv, label)."""
+    lib = load()
+    B, gamma, V = U.shape
+    rank = W1.shape[1]
+    dt = _dtype_code(U)
+    dev = U.device
+    _need(target, "target", U.dtype, (B, gamma + 1, V)); _need(U, "U")
+    _need(W1, "W1", U.dtype, (V, rank)); _need(W2t, "W2t", U.dtype, (V, rank))
+    for name, t, dtp in (("anchor", anchor, torch.int32), ("tokens", tokens, torch.int32),
+                         ("row_max", row_max, torch.float32), ("row_logZ", row_logZ, torch.float32),
+                         ("temperature", temperature, torch.float32)):
+        _need(t, name, dtp)
+    tv = tv if tv is not None else torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    if label is None and want_label:
+        label = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    need = dspark_tv_label_workspace(B, gamma, V, rank, dt)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.dspark_tv_label(B, gamma, V, rank, dt, _ptr(target), _ptr(U), _ptr(W1), _ptr(W2t),
+                               _ptr(anchor), _ptr(tokens), _ptr(row_max), _ptr(row_logZ),
+                               _ptr(temperature), _ptr(tv), _ptr(label), _ptr(status), _ptr(ws),
+                               ws.numel(), _stream()))
+    return tv, label

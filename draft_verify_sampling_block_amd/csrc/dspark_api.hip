@@ -8,6 +8,7 @@
 #include "../../include/dspark.h"
 #include "dspark_launch.hpp"
 #include "schedule_launch.hpp"
+#include "tv_launch.hpp"
 
 namespace {
 
@@ -220,3 +221,29 @@ int dspark_verify(int B, int gamma, int V, int rank, int dtype, const void* targ
 }
 
 }  // extern "C"
+
+size_t dspark_tv_label_workspace(int B, int gamma, int V, int rank, int dtype) {
+  if (check_dims("dspark_tv_label_workspace", B, gamma, V, rank, dtype) != DSPARK_OK) return 0;
+  return dspark::tv_workspace_bytes(B, gamma, V);
+}
+
+int dspark_tv_label(int B, int gamma, int V, int rank, int dtype, const void* target,
+                    const void* U, const void* W1, const void* W2t, const int32_t* anchor,
+                    const int32_t* tokens, const float* row_max, const float* row_logZ,
+                    const float* temperature, float* tv, float* label, int32_t* status,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "dspark_tv_label";
+  int rc = check_dims(fn, B, gamma, V, rank, dtype);
+  if (rc) return rc;
+  REQUIRE_PTR(target); REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2t); REQUIRE_PTR(anchor);
+  REQUIRE_PTR(tokens); REQUIRE_PTR(row_max); REQUIRE_PTR(row_logZ); REQUIRE_PTR(temperature);
+  REQUIRE_PTR(tv); OPT_PTR(label); OPT_PTR(status);
+  const size_t need = dspark::tv_workspace_bytes(B, gamma, V);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
+  return hip_status(fn, dspark::launch_tv_label(B, gamma, V, rank, dtype, target, U, W1, W2t,
+                                                anchor, tokens, row_max, row_logZ, temperature,
+                                                tv, label, status, workspace, stream));
+}

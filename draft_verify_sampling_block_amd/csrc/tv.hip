@@ -1,0 +1,234 @@
+// dspark_tv_label kernels: per drafted position, the total variation between
+// the draft and target distributions and the acceptance label 1 - TV.
+//
+// [weigao] part 3 (the confidence head's training target) and [billytse]
+// 5.1: c*_k = 1 - 0.5 * ||p^d_k - p^t_k||_1, which equals the probability
+// that the accept-or-resample test keeps drafted token k.  The draft
+// distribution of position k is softmax((U[b,k] + W1[prev] W2) / T) with
+// prev the anchor or drafted token k-1 (the distribution token k was drawn
+// from); the target one is softmax(target[b,k] / T).  Greedy requests
+// (T <= 0): one-hot q at the drafted token, one-hot p at the target's
+// lowest-index argmax, label 1 when they agree.
+//
+// Launches:
+//   tv_rows_kernel    one work-group per (request, position): target-row
+//                     max / log-sum-exp / argmax (shared row_stats).
+//   tv_tile_kernel    one work-group per 64-entry vocabulary tile, waves over
+//                     (32-request block, position) tasks: the draft logits
+//                     are recomputed exactly as the draft computed them (base
+//                     logits + Markov bias on the matrix cores, W2t tile in
+//                     LDS) and normalised with the draft's stored row max and
+//                     log-sum-exp; each request's |p - q| over the tile goes
+//                     to a per-(row, tile) partial.
+//   tv_finish_kernel  one wave per row: fp64 sum of the partials.
+#include "dspark_common.hpp"
+#include "dspark_launch.hpp"
+#include "row_stats.hpp"
+#include "trace.hpp"
+#include "tv_launch.hpp"
+
+namespace dspark {
+
+namespace {
+
+struct TvWs {
+  float* M;       // [B*gamma] target row max of t/T (max t when greedy)
+  float* LZ;      // [B*gamma] log sum exp(t/T - M)
+  int32_t* arg;   // [B*gamma] lowest argmax of the target row
+  float* part;    // [B*gamma][nT] sum over the tile of |p - q|
+};
+
+TvWs carve_tv(void* ws, int B, int gamma, int V) {
+  char* p = static_cast<char*>(ws);
+  const size_t rows = (size_t)B * gamma;
+  TvWs w;
+  w.M = reinterpret_cast<float*>(p); p += align256(rows * 4);
+  w.LZ = reinterpret_cast<float*>(p); p += align256(rows * 4);
+  w.arg = reinterpret_cast<int32_t*>(p); p += align256(rows * 4);
+  w.part = reinterpret_cast<float*>(p);
+  return w;
+}
+
+__device__ inline float tv_inv_temp(float T) { return (T > 0.f) ? 1.f / T : 0.f; }
+
+}  // namespace
+
+template <typename T>
+__global__ __launch_bounds__(256) void tv_rows_kernel(int B, int gamma, int V,
+                                                      const T* __restrict__ target,
+                                                      const float* __restrict__ temperature,
+                                                      TvWs ws, int32_t* status) {
+  __shared__ double red[8];
+  const int row = blockIdx.x;   // b * gamma + k
+  const int b = row / gamma, k = row - b * gamma;
+  const float it = tv_inv_temp(temperature[b]);
+  const bool greedy = !(it > 0.f);
+  const RowStats rs = row_stats<T>(target + ((size_t)b * (gamma + 1) + k) * V, V,
+                                   greedy ? 1.f : it, greedy, red);
+  if (threadIdx.x == 0) {
+    const bool fin = (rs.M == rs.M) && rs.M > -INFINITY && rs.M < INFINITY &&
+                     (greedy || (rs.Z > 0.0 && rs.Z < INFINITY));
+    if (!fin) flag(status, DSPARK_DEV_NONFINITE);
+    ws.M[row] = rs.M;
+    ws.LZ[row] = greedy ? 0.f : (float)log(rs.Z);
+    ws.arg[row] = (rs.arg >= 0 && rs.arg < V) ? rs.arg : 0;
+  }
+}
+
+// One work-group (4 waves) per tile vt; task t = (request block t / gamma,
+// position t % gamma).  Lane column c is request b of the block; h picks the
+// lane's 16-entry halves, as in the draft's block-tiles.
+template <typename T, int KS>
+__global__ __launch_bounds__(256) void tv_tile_kernel(
+    int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
+    const T* __restrict__ W1, const T* __restrict__ W2t, const int32_t* __restrict__ anchor,
+    const int32_t* __restrict__ tokens, const float* __restrict__ row_max,
+    const float* __restrict__ row_logZ, const float* __restrict__ temperature, TvWs ws) {
+  constexpr bool bf = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) char w2s[bf ? kLdsTileBytes : 16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5;
+  const int nRB = (B + kTileM - 1) / kTileM;
+  const int nT = n_tiles(V);
+  const int vt = blockIdx.x, v0 = vt * kTileV;
+  const int ntask = nRB * gamma;
+
+  if constexpr (bf) stage_tile(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s);
+
+  for (int t = wave; t < ntask || t == wave; t += 4) {
+    // the first pass of every wave also joins the barrier that publishes
+    // the LDS tile
+    const bool live = t < ntask;
+    const int rb = live ? t / gamma : 0, k = live ? t - rb * gamma : 0;
+    const int b = rb * kTileM + c;
+    const bool in = live && b < B;
+    const float it = in ? tv_inv_temp(temperature[b]) : 0.f;
+    const bool sampled = in && it > 0.f;   // greedy rows need no stream
+    int prev = -1;
+    if (sampled)
+      prev = clamp_token(k == 0 ? anchor[b] : tokens[(size_t)b * gamma + k - 1], V, nullptr);
+    bf16x8_t bfrag[bf ? KS : 1];
+    if constexpr (bf) load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), prev, bfrag);
+    URow<T> tp, up;
+    load_urow<T>(tp, target + ((size_t)b * (gamma + 1) + k) * V, v0, V, sampled, target);
+    load_urow<T>(up, U + ((size_t)b * gamma + k) * V, v0, V, sampled, U);
+    if (t == wave) {
+      if constexpr (bf) __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (!live) break;
+    f32x16_t acc[kSub];
+    init_acc<T>(up, V - (v0 + 16 * h), acc);   // draft logits start at the base logits
+    if (__ballot(sampled) != 0) {
+      if constexpr (bf)
+        bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
+      else
+        bias_tile_f32(reinterpret_cast<const float*>(W1), prev,
+                      reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
+    }
+    float s = 0.f;
+    if (sampled) {
+      const size_t row = (size_t)b * gamma + k;
+      const float M = ws.M[row], LZ = ws.LZ[row];
+      const float mq = row_max[row], lzq = row_logZ[row];
+#pragma unroll
+      for (int st = 0; st < kSub; ++st) {
+        const int rem = V - (v0 + 32 * st + 16 * h);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (j < rem) {
+            const float p = __expf(urow_at(tp, st, j) * it - M - LZ);
+            const float q = __expf(acc[st][j] * it - mq - lzq);
+            s += fabsf(p - q);
+          }
+        }
+      }
+    }
+    float lo, hi;
+    half_pair(s, lo, hi);
+    if (sampled && h == 0) ws.part[((size_t)b * gamma + k) * nT + vt] = lo + hi;
+  }
+}
+
+__global__ __launch_bounds__(256) void tv_finish_kernel(int B, int gamma, int V,
+                                                        const int32_t* __restrict__ tokens,
+                                                        const float* __restrict__ temperature,
+                                                        TvWs ws, float* __restrict__ tv,
+                                                        float* __restrict__ label) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= B * gamma) return;   // wave-uniform
+  const int b = row / gamma;
+  const int nT = n_tiles(V);
+  float d;
+  if (!(temperature[b] > 0.f)) {
+    d = (tokens[row] == ws.arg[row]) ? 0.f : 1.f;
+  } else {
+    double acc = 0.0;
+    for (int t = lane; t < nT; t += kWave) acc += (double)ws.part[(size_t)row * nT + t];
+    acc = wave_sum(acc);
+    d = (float)(0.5 * acc);
+  }
+  if (lane == 0) {
+    tv[row] = d;
+    if (label) label[row] = 1.f - d;
+  }
+}
+
+size_t tv_workspace_bytes(int B, int gamma, int V) {
+  const size_t rows = (size_t)B * gamma;
+  return 3 * align256(rows * 4) + align256(rows * (size_t)n_tiles(V) * 4);
+}
+
+template <typename T, int KS>
+static hipError_t tv_impl(int B, int gamma, int V, int rank, const T* target, const T* U,
+                          const T* W1, const T* W2t, const int32_t* anchor, const int32_t* tokens,
+                          const float* row_max, const float* row_logZ, const float* temperature,
+                          float* tv, float* label, int32_t* status, void* wsp,
+                          hipStream_t stream) {
+  const TvWs ws = carve_tv(wsp, B, gamma, V);
+  {
+    TraceScope t1("tv_rows_kernel", stream);
+    tv_rows_kernel<T><<<dim3(B * gamma), dim3(256), 0, stream>>>(B, gamma, V, target,
+                                                                 temperature, ws, status);
+  }
+  {
+    TraceScope t2("tv_tile_kernel", stream);
+    tv_tile_kernel<T, KS><<<dim3(n_tiles(V)), dim3(256), 0, stream>>>(
+        B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
+        ws);
+  }
+  TraceScope t3("tv_finish_kernel", stream);
+  tv_finish_kernel<<<dim3((B * gamma + 3) / 4), dim3(256), 0, stream>>>(B, gamma, V, tokens,
+                                                                         temperature, ws, tv,
+                                                                         label);
+  return hipGetLastError();
+}
+
+hipError_t launch_tv_label(int B, int gamma, int V, int rank, int dtype, const void* target,
+                           const void* U, const void* W1, const void* W2t,
+                           const int32_t* anchor, const int32_t* tokens, const float* row_max,
+                           const float* row_logZ, const float* temperature, float* tv,
+                           float* label, int32_t* status, void* ws, hipStream_t stream) {
+  if (dtype == DSPARK_BF16) {
+    auto* tg = static_cast<const uint16_t*>(target);
+    auto* u = static_cast<const uint16_t*>(U);
+    auto* w1 = static_cast<const uint16_t*>(W1);
+    auto* w2 = static_cast<const uint16_t*>(W2t);
+#define DSPARK_TV_KS(KS)                                                                    \
+  return tv_impl<uint16_t, KS>(B, gamma, V, rank, tg, u, w1, w2, anchor, tokens, row_max,    \
+                               row_logZ, temperature, tv, label, status, ws, stream)
+    switch (rank) {
+      case 32: DSPARK_TV_KS(2);
+      case 64: DSPARK_TV_KS(4);
+      case 128: DSPARK_TV_KS(8);
+      default: DSPARK_TV_KS(16);
+    }
+#undef DSPARK_TV_KS
+  }
+  return tv_impl<float, 1>(B, gamma, V, rank, static_cast<const float*>(target),
+                           static_cast<const float*>(U), static_cast<const float*>(W1),
+                           static_cast<const float*>(W2t), anchor, tokens, row_max, row_logZ,
+                           temperature, tv, label, status, ws, stream);
+}
+
+}  // namespace dspark

@@ -23,6 +23,7 @@
 
 #include "dspark_common.hpp"
 #include "dspark_launch.hpp"
+#include "row_stats.hpp"
 #include "trace.hpp"
 
 namespace dspark {
@@ -100,67 +101,10 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
   const float scale = greedy ? 1.f : it;
   const T* row = target + ((size_t)b * (gamma + 1) + k) * V;
 
-  // each thread: groups of kU chunks of 8 consecutive entries, all loads of a
-  // group in flight together; running max and exp-sum in fp32 (the sum is
-  // rescaled when the max grows), combined across threads in fp64
-  constexpr int kU = 8;
-  float m = -INFINITY;
-  float s32 = 0.f;
-  int arg = 0x7fffffff;
-  const int stride = 8 * 256;
-  for (int base = 8 * tid; base < V; base += kU * stride) {
-    // the loads are unconditional (chunks past the row re-read chunk 0 and
-    // are masked afterwards) so that all kU are in flight together
-    float y[kU][8];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int i = base + u * stride;
-      load8_f32_stream(row + (i < V ? i : 0), y[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (base + u * stride >= V) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) y[u][t] = -INFINITY;
-      }
-    }
-    float gm = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        y[u][t] *= scale;
-        gm = fmaxf(gm, y[u][t]);
-      }
-    }
-    if (gm > m) {
-      if (greedy) {
-#pragma unroll
-        for (int u = kU - 1; u >= 0; --u) {
-#pragma unroll
-          for (int t = 7; t >= 0; --t)
-            if (y[u][t] == gm) arg = base + u * stride + t;
-        }
-      } else if (s32 > 0.f) {
-        s32 *= __expf(m - gm);
-      }
-      m = gm;
-    }
-    if (!greedy) {
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) s32 += __expf(y[u][t] - m);
-      }
-    }
-  }
-  const double s = (double)s32;
-  const float M = block_max(m, red);
-  int a = 0x7fffffff;
-  if (greedy) a = (m == M) ? arg : 0x7fffffff;
-  a = block_min_int(a, red);
-  double mine = (!greedy && m > -INFINITY) ? s * exp((double)m - (double)M) : 0.0;
-  const double Zt = block_sum(mine, red);
+  const RowStats rs = row_stats<T>(row, V, scale, greedy, red);
+  const float M = rs.M;
+  const double Zt = rs.Z;
+  const int a = rs.arg;
 
   if (tid == 0) {
     const size_t sk = (size_t)b * (gamma + 1) + k;

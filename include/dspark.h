@@ -220,6 +220,37 @@ int dspark_verify(int B, int gamma, int V, int rank, int dtype,
                   hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * dspark_tv_label: the confidence head's training label per drafted
+ * position ([weigao] part 3; [billytse] 5.1):
+ *     tv[b,k]    = 0.5 * sum_v |p_k(v) - q_k(v)|
+ *     label[b,k] = 1 - tv[b,k]  (= the probability that the acceptance test
+ *                                 of dspark_verify keeps drafted token k)
+ *   q_k = softmax((U[b,k] + W1[prev] W2t^T) / T), prev = anchor[b] (k = 0)
+ *         or tokens[b,k-1]: the distribution dspark_draft_block drew token k
+ *         from, recomputed bit-identically and normalised with its row_max /
+ *         row_logZ outputs;
+ *   p_k = softmax(target[b,k] / T) (target slots 0..gamma-1; the bonus slot
+ *         is not read);
+ *   greedy requests (T <= 0): tv = 0 if tokens[b,k] is the target row's
+ *         lowest-index argmax, else 1.
+ * Sums: per element fp32, per 64-entry tile fp32, across tiles fp64.
+ * in : target [B,gamma+1,V], U [B,gamma,V], W1, W2t [V,rank] (dtype);
+ *      anchor [B], tokens [B,gamma] int32; row_max, row_logZ [B,gamma] fp32
+ *      (dspark_draft_block outputs); temperature [B]
+ * out: tv [B,gamma] fp32; label [B,gamma] fp32 (or NULL)
+ * workspace: dspark_tv_label_workspace(...) bytes (B*gamma*(3 + ceil(V/64))
+ *      fp32 words, each part 256-byte aligned).
+ * ---------------------------------------------------------------------- */
+size_t dspark_tv_label_workspace(int B, int gamma, int V, int rank, int dtype);
+int dspark_tv_label(int B, int gamma, int V, int rank, int dtype,
+                    const void* target, const void* U, const void* W1, const void* W2t,
+                    const int32_t* anchor, const int32_t* tokens,
+                    const float* row_max, const float* row_logZ,
+                    const float* temperature, float* tv, float* label,
+                    int32_t* status, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Optional per-kernel timing (not on the sampling path).
  * dspark_trace_enable(1) clears earlier records and brackets every later
  * kernel launch by a pair of hipEvents on its stream; (0) stops recording.

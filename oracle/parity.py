@@ -137,3 +137,22 @@ def check_verify(wl, W1_64, W2t_64, tokens, ell, out_tokens, n_accepted, ratio, 
         _req(lo - BAND <= uf <= cdf[y_g] + BAND, f"final token of {b}: interval far from u")
         rep["final_band"] += 1
     return rep
+
+
+def check_tv(wl, W1_64, W2t_64, tokens, tv, label, rows=None):
+    """Acceptance labels: tv and 1 - tv against the oracle on the GPU's own
+    drafted tokens; continuous tolerance, greedy rows exact."""
+    B, gamma = tokens.shape
+    todo = [(b, k) for b in range(B) for k in range(gamma)] if rows is None else list(rows)
+    ref = O.tv_label(wl.target, wl.U, W1_64, W2t_64, wl.anchor, tokens, wl.temperature, rows=todo)
+    worst = 0.0
+    for b, k in todo:
+        r = ref["tv"][b, k]
+        _req(close(tv[b, k], r), f"tv ({b},{k}): {tv[b, k]} vs {r}")
+        if label is not None:
+            _req(close(label[b, k], 1.0 - r), f"label ({b},{k}): {label[b, k]} vs {1.0 - r}")
+        if not (float(wl.temperature[b]) > 0.0):
+            _req(float(tv[b, k]) == r, f"greedy tv ({b},{k}): {tv[b, k]} vs {r}")
+        worst = max(worst, abs(float(tv[b, k]) - r))
+    return dict(rows=len(todo), max_abs=worst, mean_label=float(np.mean(1.0 - np.array(
+        [ref["tv"][b, k] for b, k in todo]))))
