@@ -366,24 +366,35 @@ __device__ inline void load_bfrag(const uint16_t* __restrict__ W1, int tok, bf16
 
 // fp32 inputs: plain FMA dot products (k ascending) in the same layout,
 // accumulated onto acc.  `tok` is the W1 row of this lane's request column
-// (-1 = nothing added).
+// (-1 = nothing added).  16-byte loads; the 16 entries' chains of one
+// sub-tile advance together (each still k ascending, one fma per k).
 __device__ inline void bias_tile_f32(const float* __restrict__ W1, int tok,
                                      const float* __restrict__ W2t, int v0, int V, int rank,
                                      f32x16_t acc[kSub]) {
+  if (tok < 0) return;
   const int h = (threadIdx.x & 63) >> 5;
-  const float* arow = W1 + (size_t)(tok >= 0 ? tok : 0) * rank;
+  const float* arow = W1 + (size_t)tok * rank;
 #pragma unroll
   for (int t = 0; t < kSub; ++t) {
+    const int vb = v0 + 32 * t + 16 * h;
+    float s[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int v = v0 + 32 * t + 16 * h + j;
-      float s = acc[t][j];
-      if (tok >= 0 && v < V) {
-        const float* brow = W2t + (size_t)v * rank;
-        for (int i = 0; i < rank; ++i) s = fmaf(arow[i], brow[i], s);
+    for (int j = 0; j < 16; ++j) s[j] = acc[t][j];
+    for (int i = 0; i < rank; i += 4) {
+      const f32x4_t a4 = *reinterpret_cast<const f32x4_t*>(arow + i);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int v = vb + j < V ? vb + j : 0;   // rows past V: computed, not kept
+        const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(W2t + (size_t)v * rank + i);
+        s[j] = fmaf(a4.x, b4.x, s[j]);
+        s[j] = fmaf(a4.y, b4.y, s[j]);
+        s[j] = fmaf(a4.z, b4.z, s[j]);
+        s[j] = fmaf(a4.w, b4.w, s[j]);
       }
-      acc[t][j] = s;
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (vb + j < V) acc[t][j] = s[j];
   }
 }
 
