@@ -14,6 +14,9 @@ roofline   = the draft kernel (pdraft_kernel, or draft_stats_kernel where the
              second pass over the same K steps (events are kept out of the
              pass that gives `value`)
 cpu_baseline = the fp64 oracle on a bounded sample of the same workload
+next_rows  = per-call times of the scheduler stop-rule variants (capacity,
+             threshold) and of the acceptance-label kernels on the last
+             step's confidences and drafts (outside `value`)
 """
 
 from __future__ import annotations
@@ -50,7 +53,10 @@ def parse():
 
 
 def algorithmic_bytes(wl, ell, n_acc):
-    """Bytes the step must move, each input read once."""
+    """Bytes the step must move, each input read once: every base-logit row,
+    the target rows up to each request's first reject (or its bonus slot), the
+    base-logit row again at a reject (the q recompute), W2 once, the hidden
+    states and gathered W1 rows, uniforms and outputs."""
     e = 2 if wl.dtype == "bf16" else 4
     B, g, V, r, H = wl.B, wl.gamma, wl.V, wl.rank, wl.H
     rejected = (n_acc < ell)
