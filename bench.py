@@ -14,6 +14,9 @@ roofline   = the draft kernel (pdraft_kernel, or draft_stats_kernel where the
              second pass over the same K steps (events are kept out of the
              pass that gives `value`)
 cpu_baseline = the fp64 oracle on a bounded sample of the same workload
+roofline.measured_read_ceiling_gbs = a plain streaming read (torch per-row
+             sums over 4 GiB) timed in the same run; the fractions of it sit beside the
+             fractions of the published 8 TB/s
 next_rows  = per-call times of the scheduler stop-rule variants (capacity,
              threshold) and of the acceptance-label kernels on the last
              step's confidences and drafts (outside `value`)
@@ -178,6 +181,30 @@ def next_rows(st, wl, reps):
     return out
 
 
+def read_ceiling_gbs(nbytes=4 << 30, reps=5):
+    """Achievable streaming-read rate of this GPU: per-row sums (torch) over a
+    4 GiB fp32 tensor viewed as 1024 rows of 1 Mi entries, best of `reps` timed
+    runs.  (One reduction to a single value is slower: it measured ~4.0 TB/s
+    against ~5.6 TB/s for the per-row form.)"""
+    import torch
+
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda").view(-1, 1 << 20)
+    x.sum(dim=1)
+    torch.cuda.synchronize()
+    best = float("inf")
+    stream = torch.cuda.current_stream()
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        x.sum(dim=1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1e3)
+    del x
+    torch.cuda.empty_cache()
+    return nbytes / best / 1e9
+
+
 def cpu_baseline(cfg, n_req):
     import numpy as np
 
@@ -312,6 +339,10 @@ def main():
                  "device_status": status},
     }
     out["next_rows"] = next_rows(st, wl, max(3, args.steps // 2))
+    ceil = read_ceiling_gbs()
+    out["roofline"]["measured_read_ceiling_gbs"] = ceil
+    out["roofline"]["frac_of_measured_ceiling"] = achieved / ceil
+    out["step"]["hbm_frac_of_measured_ceiling"] = bytes_step / (ms / 1e3) / 1e9 / ceil
     if not args.no_cpu_baseline:
         n_req = args.cpu_requests or {0: 4, 1: 32, 2: 128, 3: 128, 4: 256}[cfg]
         out["cpu_baseline"] = cpu_baseline(cfg, n_req)
