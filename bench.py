@@ -124,6 +124,24 @@ def counter_traffic(kernel, cfg):
             + float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])) * 1024.0
 
 
+def kernel_bytes(wl, ell, n_acc):
+    """Algorithmic bytes per launch of the step's streaming kernels, from the
+    realised verify lengths: verify_rows_kernel reads the target rows of every
+    slot up to each request's verify length (bonus slot included); the verify
+    statistics read each sampled request's final slot row, the base-logit row
+    of each rejecting request and W2 once; the confidence head reads the
+    hidden states and the gathered W1 rows."""
+    import numpy as np
+    e = 2 if wl.dtype == "bf16" else 4
+    B, g, V, r, H = wl.B, wl.gamma, wl.V, wl.rank, wl.H
+    sampled = np.asarray(wl.temperature) > 0
+    rejected = (n_acc < ell) & sampled
+    stats = e * V * (int(sampled.sum()) + int(rejected.sum())) + e * r * V
+    return {"verify_rows_kernel": e * V * int((np.asarray(ell) + 1).sum()),
+            "verify_tile_stats_kernel": stats, "verify_final_stats_kernel": stats,
+            "confidence_kernel": e * B * g * (H + r) + 4 * B * g}
+
+
 def tv_label_bytes(wl):
     """Algorithmic bytes of one dspark_tv_label call: every drafted
     position's base-logit and target rows once, W2 once, the W1 rows of the
@@ -335,6 +353,10 @@ def main():
                  "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                  "mean_ell": float(ell.mean()), "mean_accepted": float(n_acc.mean()),
                  "dominant_kernel": dom,
+                 "kernel_gbs": {k: {"bytes_alg": nb, "gbs": nb / (kern_ms[k] / 1e3) / 1e9,
+                                    "frac": nb / (kern_ms[k] / 1e3) / 1e9 / HBM_PEAK_GBS}
+                                for k, nb in kernel_bytes(wl, ell, n_acc).items()
+                                if k in kern_ms},
                  "kernel_ms_per_step": {k: round(v, 5) for k, v in per_step_ms.items()},
                  "device_status": status},
     }

@@ -60,3 +60,14 @@ def test_counter_traffic_follows_the_source_hash(monkeypatch, tmp_path):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "f" * 64)
     assert bench.counter_traffic("pdraft_kernel", 3) is None
     assert bench.counter_traffic("pdraft_kernel", 4) is None   # nothing recorded
+
+
+def test_kernel_bytes_per_launch():
+    wl = make_custom(3, 4, 64, 32, 16, "bf16", "gaussian", seed=0, temperature=1.0)
+    ell = np.array([4, 2, 0])
+    n_acc = np.array([4, 1, 0])
+    kb = bench.kernel_bytes(wl, ell, n_acc)
+    assert kb["verify_rows_kernel"] == 2 * 64 * (5 + 3 + 1)
+    # three sampled final rows, one rejecting request's base-logit row, W2 once
+    assert kb["verify_tile_stats_kernel"] == 2 * 64 * (3 + 1) + 2 * 32 * 64
+    assert kb["confidence_kernel"] == 2 * 3 * 4 * (16 + 32) + 4 * 3 * 4
