@@ -75,7 +75,17 @@ SMALL = {
     "bf16-one-request-one-position-V8": lambda: make_custom(1, 1, 8, 32, 8, "bf16", "gaussian",
                                                             seed=5, sps_kind="linear:4"),
     "bf16-fixed-ell-gamma": lambda: make_custom(37, 5, 1536, 64, 16, "bf16", "mixture", seed=6),
+    "bf16-temperature-extremes": lambda: _with_temperatures(
+        make_custom(45, 5, 3000, 64, 32, "bf16", "mixture", seed=11, sps_kind="linear:230",
+                    calibrated=True), [0.05, 0.3, 1.0, 4.0, 0.0]),
 }
+
+
+def _with_temperatures(wl, cycle):
+    """Per-request temperatures cycling through `cycle` (very sharp, very
+    flat and greedy requests in one batch)."""
+    wl.temperature[:] = np.resize(np.asarray(cycle, dtype=np.float32), wl.B)
+    return wl
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -178,6 +188,7 @@ PATH_CASES = {
     "bf16-ragged-V1000-B40": lambda: SMALL["bf16-ragged-V1000-B40"](),
     "bf16-greedy-mix-T0.7": lambda: SMALL["bf16-greedy-mix-T0.7"](),
     "bf16-strong-bias": lambda: SMALL["bf16-strong-bias"](),
+    "bf16-temperature-extremes": lambda: SMALL["bf16-temperature-extremes"](),
     "bf16-B300-rank128-V5000": lambda: make_custom(300, 3, 5000, 128, 16, "bf16", "mixture",
                                                    seed=9, temperature=0.8, greedy_frac=0.2),
     "config 1 full size": lambda: make_config(1),

@@ -43,7 +43,14 @@ CASES = {
                                                    w_std=0.3),
     "bf16-one-request-one-position-V8": lambda: make_custom(1, 1, 8, 32, 8, "bf16", "gaussian",
                                                             seed=5),
+    "bf16-temperature-extremes": lambda: _with_temperatures(
+        make_custom(45, 5, 3000, 64, 32, "bf16", "mixture", seed=11), [0.05, 0.3, 1.0, 4.0, 0.0]),
 }
+
+
+def _with_temperatures(wl, cycle):
+    wl.temperature[:] = np.resize(np.asarray(cycle, dtype=np.float32), wl.B)
+    return wl
 
 
 def _run(wl):
