@@ -75,6 +75,11 @@ SMALL = {
     "bf16-one-request-one-position-V8": lambda: make_custom(1, 1, 8, 32, 8, "bf16", "gaussian",
                                                             seed=5, sps_kind="linear:4"),
     "bf16-fixed-ell-gamma": lambda: make_custom(37, 5, 1536, 64, 16, "bf16", "mixture", seed=6),
+    # the library's largest block and vocabulary (4096 tiles: more than the
+    # persistent kernel keeps on chip, so the per-position launches run)
+    "bf16-max-gamma64-V262144": lambda: make_custom(2, 64, 262144, 32, 64, "bf16", "mixture",
+                                                    seed=12, sps_kind="linear:300",
+                                                    calibrated=True),
     "bf16-temperature-extremes": lambda: _with_temperatures(
         make_custom(45, 5, 3000, 64, 32, "bf16", "mixture", seed=11, sps_kind="linear:230",
                     calibrated=True), [0.05, 0.3, 1.0, 4.0, 0.0]),
