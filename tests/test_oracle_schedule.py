@@ -157,3 +157,31 @@ def test_tau_is_exact_sum_rounded_once():
     s = O.schedule(np.full((2, 3), 0.1), np.full(30, 5.0))
     exact = Fraction(2) + sum(Fraction(float(x)) for x in a.reshape(-1))
     assert s["tau"] == float(exact)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_verify_length_falls_as_load_rises(seed):
+    # [xhh] scheduler note / [billytse] 6: the admission bar rises with load.
+    # With SPS(B) = c (1 - s B), admitting candidate n needs
+    # a (1 - s (Bt + 1)) > tau s, harder for every candidate as s grows, so
+    # no request's verify length can grow with the slope; and more requests
+    # (a larger starting batch) shorten the same requests' prefixes.
+    rng = np.random.default_rng(700 + seed)
+    R, gamma = 48, 8
+    c = rng.uniform(0.4, 1.0, (R, gamma))
+    n = 4096
+    prev = None
+    for s in [0.0, 1e-4, 5e-4, 2e-3, 8e-3, 3e-2]:
+        sps = 2400.0 * (1.0 - s * np.arange(n))
+        sps[sps <= 0] = 0.0
+        ell = O.schedule(c, sps)["ell"]
+        if prev is not None:
+            assert np.all(ell <= prev)
+        prev = ell
+    assert prev.sum() < R * gamma   # the steepest table really cuts
+    # the same 48 requests inside a batch of 4 x 48 requests: no longer prefixes
+    sps = 2400.0 * (1.0 - 5e-4 * np.arange(n))
+    alone = O.schedule(c, sps)["ell"]
+    crowd = O.schedule(np.concatenate([c] + [rng.uniform(0.4, 1.0, (R, gamma))
+                                             for _ in range(3)]), sps)["ell"][:R]
+    assert np.all(crowd <= alone) and crowd.sum() < alone.sum()
