@@ -225,7 +225,8 @@ def dspark_confidence(hidden, W1, anchor, tokens, w, bias=0.0, *, conf=None, sta
     return conf
 
 
-def dspark_schedule(conf, sps, *, ell=None, order=None, stats=None, status=None, want_order=True):
+def dspark_schedule(conf, sps, *, ell=None, order=None, stats=None, status=None, want_order=True,
+                    workspace=None):
     """Prefix scheduler; conf [R,gamma] fp32, sps fp64 table; returns (ell, order, stats)."""
     lib = load()
     R, gamma = conf.shape
@@ -236,14 +237,14 @@ def dspark_schedule(conf, sps, *, ell=None, order=None, stats=None, status=None,
         order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
     stats = stats if stats is not None else torch.empty((3,), dtype=torch.float64, device=dev)
     need = dspark_schedule_workspace(R, gamma)
-    ws = _workspace(need, dev) if need else None
+    ws = _workspace(need, dev, workspace) if need else None
     _check(lib.dspark_schedule(R, gamma, _ptr(conf), _ptr(sps), int(sps.numel()), _ptr(ell),
                                _ptr(order), _ptr(stats), _ptr(status), _ptr(ws),
                                0 if ws is None else ws.numel(), _stream()))
     return ell, order, stats
 
 
-def _schedule_outputs(conf, ell, order, stats, want_order):
+def _schedule_outputs(conf, ell, order, stats, want_order, workspace=None):
     R, gamma = conf.shape
     dev = conf.device
     _need(conf, "conf", torch.float32)
@@ -252,16 +253,17 @@ def _schedule_outputs(conf, ell, order, stats, want_order):
         order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
     stats = stats if stats is not None else torch.empty((3,), dtype=torch.float64, device=dev)
     need = dspark_schedule_workspace(R, gamma)
-    ws = _workspace(need, dev) if need else None
+    ws = _workspace(need, dev, workspace) if need else None
     return R, gamma, ell, order, stats, ws
 
 
 def dspark_schedule_capacity(conf, capacity, *, ell=None, order=None, stats=None, status=None,
-                             want_order=True):
+                             want_order=True, workspace=None):
     """Top-K scheduler (two-step barrier); capacity: fp64 device tensor whose first
     element is K (e.g. stats of an earlier dspark_schedule).  Returns (ell, order, stats)."""
     lib = load()
-    R, gamma, ell, order, stats, ws = _schedule_outputs(conf, ell, order, stats, want_order)
+    R, gamma, ell, order, stats, ws = _schedule_outputs(conf, ell, order, stats, want_order,
+                                                        workspace)
     if not (isinstance(capacity, torch.Tensor) and capacity.dtype == torch.float64
             and capacity.device == conf.device and capacity.numel() >= 1):
         raise DsparkError(-1, "capacity must be a float64 tensor on the device of conf")
@@ -272,10 +274,11 @@ def dspark_schedule_capacity(conf, capacity, *, ell=None, order=None, stats=None
 
 
 def dspark_schedule_threshold(conf, threshold, *, ell=None, order=None, stats=None, status=None,
-                              want_order=True):
+                              want_order=True, workspace=None):
     """Fixed survival threshold scheduler.  Returns (ell, order, stats)."""
     lib = load()
-    R, gamma, ell, order, stats, ws = _schedule_outputs(conf, ell, order, stats, want_order)
+    R, gamma, ell, order, stats, ws = _schedule_outputs(conf, ell, order, stats, want_order,
+                                                        workspace)
     _check(lib.dspark_schedule_threshold(R, gamma, _ptr(conf), ctypes.c_double(threshold),
                                          _ptr(ell), _ptr(order), _ptr(stats), _ptr(status),
                                          _ptr(ws), 0 if ws is None else ws.numel(), _stream()))

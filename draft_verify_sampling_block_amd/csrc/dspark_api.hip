@@ -146,6 +146,8 @@ int check_schedule(const char* fn, int R, int gamma, const float* conf, int32_t*
   const size_t need = dspark::schedule_workspace_bytes(R, gamma);
   if (need && (!workspace || workspace_bytes < need))
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+  if (need && !aligned16(workspace))
+    return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
   return DSPARK_OK;
 }
 }  // namespace
@@ -154,11 +156,11 @@ int dspark_schedule(int R, int gamma, const float* conf, const double* sps, int 
                     int32_t* ell, int32_t* order, double* stats, int32_t* status,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "dspark_schedule";
+  if (sps_len < 1) return fail(DSPARK_EINVAL, "%s: sps_len=%d must be >= 1", fn, sps_len);
+  REQUIRE_PTR(sps);
   int rc = check_schedule(fn, R, gamma, conf, ell, order, stats, status, workspace,
                           workspace_bytes);
   if (rc) return rc;
-  if (sps_len < 1) return fail(DSPARK_EINVAL, "%s: sps_len=%d must be >= 1", fn, sps_len);
-  REQUIRE_PTR(sps);
   return hip_status(fn, dspark::launch_schedule(R, gamma, conf, sps, sps_len, dspark::kSchedTheta,
                                                 0.0, nullptr, ell, order, stats, status,
                                                 workspace, stream));

@@ -31,7 +31,7 @@ hipError_t launch_confidence(int B, int gamma, int H, int V, int rank, int dtype
                              int32_t* status, hipStream_t stream);
 
 constexpr int kScheduleMaxKeys = 8192;
-constexpr int kScheduleMergeKeys = 4096;   // candidates sorted by merging runs
+constexpr int kScheduleMergeKeys = 4096;   // candidates ranked by run searches
 size_t schedule_workspace_bytes(int R, int gamma);
 
 size_t verify_workspace_bytes(int B, int gamma, int V, int rank, int dtype);

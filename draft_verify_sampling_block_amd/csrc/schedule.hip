@@ -13,9 +13,10 @@
 //      request; bit-identical to a sequential product);
 //   2. order by (a desc, flat id asc) -- a total order, so the order is
 //      exact: a request's survivals never increase along its positions, so
-//      the R runs of gamma are merged pairwise (log2 R levels, binary
-//      searches); beyond the merge buffer a bitonic sort with the keys in
-//      registers (shuffles within a wave, LDS for strides 64..512);
+//      a candidate's rank is the sum over the R runs of one binary search
+//      each (schedule_rank_kernel, many compute units, up to 4096
+//      candidates); beyond that a bitonic sort with the keys in registers
+//      (shuffles within a wave, LDS for strides 64..512);
 //   3. tau_n = R + sum of the first n ranked survivals, computed as a
 //      double-double prefix scan and rounded once (the exact sum up to
 //      ~1e-30 relative; independent of association);
@@ -145,67 +146,88 @@ __device__ void bitonic_sort(double* key, int* idx) {
   __syncthreads();
 }
 
-// Merge sort of N keys whose consecutive runs of length L0 are already in
-// rank order (each request's survivals never increase along its positions,
-// and equal ones keep ascending flat ids): each level merges pairs of runs;
-// an element's place is its index in its run plus the number of elements of
-// the partner run ranked before it (a binary search).  The order is total,
-// so the places form a permutation.  Returns the buffer holding the result.
-// EPT elements per thread (N <= 1024 EPT); their searches advance in
-// lockstep so the LDS latencies overlap.
-template <int EPT>
-__device__ int merge_runs(double* k0, int* i0, double* k1, int* i1, int N, int L0) {
-  const int tid = threadIdx.x;
-  int cur = 0;
-  for (int L = L0; L < N; L <<= 1) {
-    const double* ks = cur ? k1 : k0;
-    const int* is = cur ? i1 : i0;
-    double* kd = cur ? k0 : k1;
-    int* id = cur ? i0 : i1;
-    int steps = 0;
-    while ((1 << steps) <= L) ++steps;   // searches over at most L entries
-    double kx[EPT];
-    int ix[EPT], lo[EPT], hi[EPT], ps[EPT], dst[EPT];
+}  // namespace
+
+// Survival of every candidate, exactly as schedule_kernel forms it: the
+// confidence clamped into [0, 1] (flagging is left to schedule_kernel), then
+// each request's running product left to right in fp64.
+__device__ inline void survival_keys(int R, int gamma, const float* __restrict__ conf,
+                                     double* key) {
+  const int N = R * gamma;
+  // eight loads per thread in flight at a time (indices clamped into the
+  // array), then the stores
+  constexpr int kU = 8;
+  const int nt = blockDim.x, t = threadIdx.x;
+  for (int i0 = 0; i0 < N; i0 += kU * nt) {
+    float c[kU];
 #pragma unroll
-    for (int u = 0; u < EPT; ++u) {
-      const int e = tid + 1024 * u;
-      lo[u] = hi[u] = ps[u] = dst[u] = 0;
-      kx[u] = 0.0;
-      ix[u] = 0;
-      if (e < N) {
-        const int q = e / L, i = e - q * L;
-        ps[u] = (q ^ 1) * L;
-        lo[u] = ps[u];
-        hi[u] = max(ps[u], min(ps[u] + L, N));
-        dst[u] = (q & ~1) * L + i;
-        kx[u] = ks[e];
-        ix[u] = is[e];
-      }
+    for (int u = 0; u < kU; ++u) c[u] = conf[min(i0 + u * nt + t, N - 1)];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u * nt + t;
+      if (i < N) key[i] = (double)((c[u] >= 0.f) ? fminf(c[u], 1.f) : 0.f);   // NaN -> 0
+    }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    double acc = 1.0;
+    for (int j = 0; j < gamma; ++j) {
+      acc = acc * key[r * gamma + j];
+      key[r * gamma + j] = acc;
+    }
+  }
+  __syncthreads();
+}
+
+// Rank of every candidate in the order (survival desc, flat id asc), for
+// up to kScheduleMergeKeys candidates, spread over compute units: a
+// candidate's rank is the number of entries ranked ahead of it in every
+// request's run.  A run is already in rank order (a request's survival never
+// rises along its positions and equal ones keep ascending flat ids), so each
+// run's count is one binary search.  kRankSplit lanes share a candidate,
+// each searching every kRankSplit-th run with kRankRuns searches advancing
+// together, and their counts are added by shuffles.  The order is total, so
+// the ranks are a permutation of [0, N).
+constexpr int kRankRuns = 16;
+constexpr int kRankSplit = 8;
+constexpr int kRankThreads = 256;   // kRankThreads / kRankSplit candidates per group
+__global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(
+    int R, int gamma, const float* __restrict__ conf, int32_t* __restrict__ rank_out) {
+  __shared__ double key[kScheduleMergeKeys];
+  survival_keys(R, gamma, conf, key);
+  const int N = R * gamma;
+  const int i = blockIdx.x * (kRankThreads / kRankSplit) + threadIdx.x / kRankSplit;
+  const int part = threadIdx.x % kRankSplit;
+  const int ic = min(i, N - 1);   // lanes past N search too, then drop their count
+  const double ki = key[ic];
+  int steps = 0;
+  while ((1 << steps) <= gamma) ++steps;   // searches over gamma entries
+  int rank = 0;
+  for (int r0 = part; r0 < R; r0 += kRankRuns * kRankSplit) {
+    int lo[kRankRuns], hi[kRankRuns];
+#pragma unroll
+    for (int u = 0; u < kRankRuns; ++u) {
+      lo[u] = 0;
+      hi[u] = r0 + u * kRankSplit < R ? gamma : 0;
     }
     for (int st = 0; st < steps; ++st) {
 #pragma unroll
-      for (int u = 0; u < EPT; ++u) {
+      for (int u = 0; u < kRankRuns; ++u) {
         if (lo[u] < hi[u]) {
           const int mid = (lo[u] + hi[u]) >> 1;
-          if (rank_before(ks[mid], is[mid], kx[u], ix[u])) lo[u] = mid + 1;
+          const int f = (r0 + u * kRankSplit) * gamma + mid;
+          if (rank_before(key[f], f, ki, ic)) lo[u] = mid + 1;
           else hi[u] = mid;
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < EPT; ++u) {
-      if (tid + 1024 * u < N) {
-        kd[dst[u] + (lo[u] - ps[u])] = kx[u];
-        id[dst[u] + (lo[u] - ps[u])] = ix[u];
-      }
-    }
-    __syncthreads();
-    cur ^= 1;
+    for (int u = 0; u < kRankRuns; ++u) rank += lo[u];
   }
-  return cur;
+#pragma unroll
+  for (int o = 1; o < kRankSplit; o <<= 1) rank += __shfl_xor(rank, o, kWave);
+  if (part == 0 && i < N) rank_out[i] = rank;
 }
-
-}  // namespace
 
 __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
                                                         const float* __restrict__ conf,
@@ -215,10 +237,11 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
                                                         int32_t* __restrict__ ell,
                                                         int32_t* __restrict__ order,
                                                         double* __restrict__ stats,
+                                                        const int32_t* __restrict__ ranks,
                                                         int32_t* status) {
   __shared__ double key_a[kScheduleMaxKeys];
   __shared__ int idx_a[kScheduleMaxKeys];
-  __shared__ double key_b[kScheduleMergeKeys];   // merge ping-pong partner
+  __shared__ double key_b[kScheduleMergeKeys];   // candidates placed by rank
   __shared__ int idx_b[kScheduleMergeKeys];
   double* key = key_a;
   int* idx = idx_a;
@@ -275,16 +298,17 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
   }
   __syncthreads();
 
-  // 2. rank order (survival desc, flat id asc): merge the per-request runs,
-  //    or a bitonic sort beyond the merge buffer
-  if (N <= kScheduleMergeKeys) {
-    const int moved = N <= 1024   ? merge_runs<1>(key_a, idx_a, key_b, idx_b, N, gamma)
-                      : N <= 2048 ? merge_runs<2>(key_a, idx_a, key_b, idx_b, N, gamma)
-                                  : merge_runs<4>(key_a, idx_a, key_b, idx_b, N, gamma);
-    if (moved) {
-      key = key_b;
-      idx = idx_b;
+  // 2. rank order (survival desc, flat id asc): placed by the ranks
+  //    schedule_rank_kernel computed, or (beyond its buffer) a bitonic sort
+  if (ranks) {
+    for (int i = tid; i < N; i += nthr) {
+      const int q = ranks[i];
+      key_b[q] = key_a[i];
+      idx_b[q] = i;
     }
+    key = key_b;
+    idx = idx_b;
+    __syncthreads();
   } else {
     switch (P) {
       case 1024: bitonic_sort<1>(key, idx); break;
@@ -387,20 +411,29 @@ __global__ __launch_bounds__(1024) void schedule_kernel(int R, int gamma,
   }
 }
 
+// the candidates' ranks (int32) when schedule_rank_kernel runs
 size_t schedule_workspace_bytes(int R, int gamma) {
-  (void)R; (void)gamma;
-  return 0;
+  const long long N = (long long)R * gamma;
+  return N <= kScheduleMergeKeys ? align256((size_t)N * 4) : 0;
 }
 
 hipError_t launch_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
                            int mode, double threshold, const double* capacity, int32_t* ell,
                            int32_t* order, double* stats, int32_t* status, void* ws,
                            hipStream_t stream) {
-  (void)ws;
+  const int N = R * gamma;
+  int32_t* ranks = nullptr;
+  if (N <= kScheduleMergeKeys) {
+    ranks = static_cast<int32_t*>(ws);
+    TraceScope tr("schedule_rank_kernel", stream);
+    constexpr int kPerGroup = kRankThreads / kRankSplit;
+    schedule_rank_kernel<<<dim3((N + kPerGroup - 1) / kPerGroup), dim3(kRankThreads), 0,
+                           stream>>>(R, gamma, conf, ranks);
+  }
   TraceScope ts("schedule_kernel", stream);
   schedule_kernel<<<dim3(1), dim3(1024), 0, stream>>>(R, gamma, conf, sps, sps_len, mode,
                                                       threshold, capacity, ell, order, stats,
-                                                      status);
+                                                      ranks, status);
   return hipGetLastError();
 }
 

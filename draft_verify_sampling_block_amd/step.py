@@ -84,6 +84,9 @@ class Step:
                                     dtype=torch.uint8, device=dev)
         self.ws_verify = torch.empty(max(256, dspark_verify_workspace(B, g, d.V, d.rank, dt)),
                                      dtype=torch.uint8, device=dev)
+        from . import dspark_schedule_workspace
+        self.ws_sched = torch.empty(max(256, dspark_schedule_workspace(B, g)), dtype=torch.uint8,
+                                    device=dev)
 
     def run(self):
         d = self.d
@@ -94,7 +97,7 @@ class Step:
                           status=self.status)
         if d.sps is not None:
             dspark_schedule(self.conf, d.sps, ell=self.ell, order=self.order, stats=self.stats,
-                            status=self.status)
+                            status=self.status, workspace=self.ws_sched)
             ell = self.ell
         else:
             ell = d.fixed_ell

@@ -143,7 +143,9 @@ int dspark_confidence(int B, int gamma, int H, int V, int rank, int dtype,
  *      sps [sps_len] fp64, steps per second at target batch Bt (entry Bt)
  * out: ell [R] int32; order [R*gamma] int32 flat ids in rank order (or
  *      NULL); stats [3] fp64 {n_admitted, tau, Theta} (or NULL)
- * Supports R*gamma <= 8192 (one work-group; the keys live in LDS).
+ * Supports R*gamma <= 8192 (the keys live in one work-group's LDS).
+ * workspace: dspark_schedule_workspace(R, gamma) bytes (the candidates'
+ * ranks, int32, for R*gamma <= 4096; 0 beyond), 16-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t dspark_schedule_workspace(int R, int gamma);
 int dspark_schedule(int R, int gamma, const float* conf,
@@ -167,7 +169,7 @@ int dspark_schedule(int R, int gamma, const float* conf,
  *      step, so the chain needs no host round trip); 8-byte aligned
  * out: ell [R] int32; order [R*gamma] int32 (or NULL); stats [3] fp64
  *      {n_admitted, tau, NaN} (or NULL), tau as in dspark_schedule
- * workspace: dspark_schedule_workspace(R, gamma) bytes (currently 0).
+ * workspace: dspark_schedule_workspace(R, gamma) bytes, as dspark_schedule.
  * ---------------------------------------------------------------------- */
 int dspark_schedule_capacity(int R, int gamma, const float* conf,
                              const double* capacity,

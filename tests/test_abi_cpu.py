@@ -44,7 +44,10 @@ def test_workspace_queries(lib):
     assert dv.dspark_draft_block_workspace(128, 15, 151936, 256, 1) == expect
     assert dv.dspark_draft_block_workspace(128, 15, 151937, 256, 1) == 0  # invalid V
     assert dv.dspark_verify_workspace(4, 5, 1024, 32, 0) > 0
-    assert dv.dspark_schedule_workspace(512, 7) == 0
+    # the candidates' ranks (int32, 256-byte aligned) up to 4096 candidates; none beyond
+    assert dv.dspark_schedule_workspace(512, 7) == 512 * 7 * 4
+    assert dv.dspark_schedule_workspace(3, 5) == 256
+    assert dv.dspark_schedule_workspace(1000, 8) == 0
 
 
 def test_host_validation_rejects_before_launch(lib):

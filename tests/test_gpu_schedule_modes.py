@@ -119,7 +119,9 @@ def test_abi_rejects_bad_capacity_pointer():
     lib = dv.load()
     x = torch.zeros(64, dtype=torch.float32, device="cuda")
     p = x.data_ptr()
-    assert lib.dspark_schedule_capacity(4, 5, p, None, p, p, p, None, None, 0, None) == -1
-    assert lib.dspark_schedule_capacity(4, 5, p, p + 4, p, p, p, None, None, 0, None) == -3
+    big = 1 << 20
+    assert lib.dspark_schedule_capacity(4, 5, p, None, p, p, p, None, p, big, None) == -1
+    assert lib.dspark_schedule_capacity(4, 5, p, p + 4, p, p, p, None, p, big, None) == -3
+    assert lib.dspark_schedule_capacity(4, 5, p, p, p, p, p, None, None, 0, None) == -4
     assert lib.dspark_schedule_capacity(9000, 1, p, p, p, p, p, None, None, 0, None) == -5
     assert lib.dspark_schedule_threshold(0, 5, p, 0.5, p, p, p, None, None, 0, None) == -1
