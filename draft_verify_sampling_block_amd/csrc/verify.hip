@@ -329,15 +329,23 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
 // requests): one work-group of 8 waves per compute unit.  Work-group p owns
 // the contiguous tiles [tbase, tbase + tcount) and walks them one by one;
 // wave w computes sub-tile w % 2 of 32-request block w / 2 (A = the W2t tile
-// in LDS, B = the gathered W1 rows of the previous tokens in LDS), so each
-// element is computed exactly as verify_final_stats_kernel computes it and
-// the sub-tile sums are combined in the same order.  The next tile's W2t
-// rows are loaded into registers while the current one is processed and
+// in LDS, B = the W1 row of the lane's previous token, held in registers),
+// so each element is computed exactly as verify_final_stats_kernel computes
+// it and the sub-tile sums are combined in the same order.  The next tile's
+// W2t rows are loaded into registers while the current one is processed and
 // written to the other LDS buffer; the chunk sums collect in LDS and are
 // written out every kVtOutTiles tiles.
+//
+// The target and base-logit entries a wave needs (32 rows x 64 bytes per
+// tile) are loaded 16 rows per instruction, four lanes to a row's 64 bytes,
+// and passed through a per-wave LDS area to the lanes of the matrix layout
+// (lane = request, 32 bytes each).  A load whose lanes each touch another
+// row (32 rows per instruction) moves about two thirds as many bytes per
+// second on this chip at the same occupancy.
 constexpr int kVtWaves = 8;
 constexpr int kVtMaxRows = 4 * kTileM;
 constexpr int kVtOutTiles = 16;
+constexpr int kVtStageRow = 80;   // 64 bytes of one row's entries + 16 of padding
 template <int KS>
 __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
     int B, int gamma, int V, int rank, const uint16_t* __restrict__ target,
@@ -352,10 +360,11 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
   constexpr int kChunks = kTileV * nq;           // 16-byte chunks of one tile
   constexpr int kPer = (kChunks + kThr - 1) / kThr;
   __shared__ __attribute__((aligned(16))) char w2s[2][kTileV * kRowB];
-  __shared__ __attribute__((aligned(16))) char w1s[kVtMaxRows * kRowB];
+  // per wave: [target | base logits][32 rows][kVtStageRow]
+  __shared__ __attribute__((aligned(16))) char s_stage[kVtWaves][2][kTileM][kVtStageRow];
   __shared__ float s_part[2][kSub][kVtMaxRows][2];
   __shared__ float s_out[2][kVtOutTiles][kVtMaxRows];
-  __shared__ int s_prev[kVtMaxRows];
+  __shared__ int s_mode[kVtMaxRows], s_slot[kVtMaxRows];
   __shared__ int s_any;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -365,23 +374,18 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
   const int nT = n_tiles(V);
   const int tcount = nT / P + (p < nT % P ? 1 : 0);
   const int tbase = p * (nT / P) + min(p, nT % P);
-  // plans and the W1 rows of the residual requests' previous tokens
+  // every request's plan (the rows the waves load for one another)
   if (tid == 0) s_any = 0;
   __syncthreads();
   for (int r = tid; r < kVtMaxRows; r += kThr) {
-    int prev = 0;
-    if (r < B) {
-      const FinalRow f = final_row(r, B, gamma, V, ell, temperature, anchor, tokens, ws);
-      if (f.mode == 1) {
-        prev = f.prev;
-        s_any = 1;
-      }
-    }
-    s_prev[r] = prev;
+    FinalRow f{0, 0, -1};
+    if (r < B) f = final_row(r, B, gamma, V, ell, temperature, anchor, tokens, ws);
+    if (f.mode == 1) s_any = 1;
+    s_mode[r] = f.mode;
+    s_slot[r] = f.slot;
   }
   __syncthreads();
   const bool any_res = s_any != 0;   // some request of the batch draws from a residual
-  if (any_res) stage_gather(W1, s_prev, rank, w1s, kVtMaxRows);
 
   // tile vt's rows in the stage_tile image: row r <- W2t row v0 +
   // tile_row_vocab(r) (clamped); thread chunks (r, q < nq), the pad chunk
@@ -416,33 +420,66 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
     load_tile(stA, tbase);
     write_tile(stA, 0);
   }
-  __builtin_amdgcn_s_waitcnt(0);   // the gathered rows have landed
-  __syncthreads();
 
-  // this wave's request column: plan, weights' constants, entries of the
-  // next tile requested one tile ahead (before the tile rows two ahead, so
-  // that waiting for them leaves those in flight)
+  // this wave's request column: plan, weights' constants, the W1 row of
+  // the previous token (zero unless the request draws from a residual)
   const int b = rb * kTileM + c;
   const bool active = rb * kTileM < B;
   FinalRow mine{0, 0, -1};
   if (active && b < B) mine = final_row(b, B, gamma, V, ell, temperature, anchor, tokens, ws);
   const FinalParams fpar = final_params(mine, b, gamma, row_max, row_logZ, temperature, ws);
   const bool blk_res = any_res && __ballot(mine.mode == 1) != 0;
-  const uint16_t* trow = target + ((size_t)b * (gamma + 1) + mine.slot) * V;
-  const uint16_t* urow = U + ((size_t)b * gamma + mine.slot) * V;
-  // two slice sets, like the tile stages: step i reads one and fills the
-  // other, so no loaded register is ever copied (a copy would wait for it)
-  u32x4_t tqA[2], uqA[2], tqB[2], uqB[2];
-  auto fetch = [&](u32x4_t (&tq)[2], u32x4_t (&uq)[2], int vt) {
-    const int e0 = vt * kTileV + 32 * t + 16 * h;   // the lane's first entry
+  bf16x8_t bfrag[KS];
+  load_bfrag<KS>(W1, (any_res && mine.mode == 1) ? mine.prev : -1, bfrag);
+  __builtin_amdgcn_s_waitcnt(0);   // the first W2t tile has landed
+  __syncthreads();
+
+  // The rows this lane loads for its wave: block rows 16 g + lane / 4
+  // (g = 0, 1), 16 bytes at entry 32 t + 8 (lane % 4) of the tile.
+  const int lr = lane >> 2, lq = lane & 3;
+  const uint16_t* lt[2];
+  const uint16_t* lu[2];
+  bool lt_on[2], lu_on[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int r = rb * kTileM + 16 * g + lr;
+    const bool own = active && r < B;
+    const int md = own ? s_mode[r] : 0;
+    const int sl = own ? s_slot[r] : 0;
+    lt_on[g] = md != 0;
+    lu_on[g] = md == 1;
+    lt[g] = target + ((size_t)(own ? r : 0) * (gamma + 1) + sl) * V;
+    lu[g] = U + ((size_t)(own ? r : 0) * gamma + sl) * V;
+  }
+  // two register sets, like the tile stages: step i stages one and fills
+  // the other, so no loaded register is ever copied (a copy would wait for
+  // it).  Set element j: j / 2 = target or base logits, j % 2 = g.
+  u32x4_t ldA[4], ldB[4];
+  auto fetch = [&](u32x4_t (&ld)[4], int vt) {
+    const int e = vt * kTileV + 32 * t + 8 * lq;
+    const bool in = vt <= tlast && e < V;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      ld[g] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(in && lt_on[g] ? lt[g] + e : target));
+      ld[2 + g] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(in && lu_on[g] ? lu[g] + e : U));
+    }
+  };
+  // registers -> this wave's LDS area -> the matrix layout: lane (c, h)
+  // takes entries 32 t + 16 h + [0, 16) of request row c
+  char (*stg)[kTileM][kVtStageRow] = s_stage[wave];
+  auto restage = [&](const u32x4_t (&ld)[4], u32x4_t (&tq)[2], u32x4_t (&uq)[2]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4_t*>(&stg[j >> 1][16 * (j & 1) + lr][16 * lq]) = ld[j];
+    asm volatile("" ::: "memory");   // the wave's LDS accesses stay in this order
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const bool in = vt <= tlast && e0 + 8 * q < V;
-      tq[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-          in && mine.mode != 0 ? trow + e0 + 8 * q : target));
-      uq[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-          in && mine.mode == 1 ? urow + e0 + 8 * q : U));
+      tq[q] = *reinterpret_cast<const u32x4_t*>(&stg[0][c][16 * (2 * h + q)]);
+      uq[q] = *reinterpret_cast<const u32x4_t*>(&stg[1][c][16 * (2 * h + q)]);
     }
+    asm volatile("" ::: "memory");
   };
 
   auto flush = [&](int first, int n) {   // s_out rows of tiles [first, first + n)
@@ -458,14 +495,16 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
   // the tile walk, with (kRes) or without the bias on the matrix cores
   auto walk = [&](auto res_tag) {
     constexpr bool kRes = decltype(res_tag)::value;
-    fetch(tqA, uqA, tbase);
+    fetch(ldA, tbase);
     if constexpr (kRes) load_tile(stB, min(tbase + 1, tlast));
     // tile i from LDS buffer i & 1; `next` holds tile i + 1, `after`
-    // receives tile i + 2
+    // receives tile i + 2; `ld` holds tile i's entries, `ld1` receives
+    // tile i + 1's
     auto step = [&](int i, const u32x4_t (&next)[kPer], u32x4_t (&after)[kPer],
-                    const u32x4_t (&tq)[2], const u32x4_t (&uq)[2], u32x4_t (&tq1)[2],
-                    u32x4_t (&uq1)[2]) {
+                    const u32x4_t (&ld)[4], u32x4_t (&ld1)[4]) {
       const int vt = tbase + i;
+      u32x4_t tq[2], uq[2];
+      restage(ld, tq, uq);
       f32x16_t acc;
       float yt[16];
       const int rem = V - (vt * kTileV + 32 * t + 16 * h);
@@ -476,12 +515,11 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
         yt[j] = (j & 1) ? __uint_as_float(wt & 0xFFFF0000u) : __uint_as_float(wt << 16);
         acc[j] = j < rem ? fu : -INFINITY;   // q logits start at the base logits
       }
-      fetch(tq1, uq1, vt + 1);
+      fetch(ld1, vt + 1);
       if constexpr (kRes) load_tile(after, min(vt + 2, tlast));
       if (active) {
         if (kRes && blk_res)
-          bias_subtile_ldsA<KS>([&](int ks) { return lds_frag(w1s, b, 2 * ks + h, nq); },
-                                w2s[i & 1], t, acc);
+          bias_subtile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s[i & 1], t, acc);
         float sr, sp;
         subtile_sums(fpar, yt, acc, rem, sr, sp);
         if (h == 0) {
@@ -506,8 +544,8 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
       }
     };
     for (int i = 0; i < tcount; i += 2) {
-      step(i, stB, stA, tqA, uqA, tqB, uqB);
-      if (i + 1 < tcount) step(i + 1, stA, stB, tqB, uqB, tqA, uqA);
+      step(i, stB, stA, ldA, ldB);
+      if (i + 1 < tcount) step(i + 1, stA, stB, ldB, ldA);
     }
   };
   if (any_res) walk(std::true_type{});
