@@ -78,6 +78,14 @@ __global__ __launch_bounds__(256) void tv_rows_kernel(int B, int gamma, int V,
 // One work-group (4 waves) per tile vt; task t = (request block t / gamma,
 // position t % gamma).  Lane column c is request b of the block; h picks the
 // lane's 16-entry halves, as in the draft's block-tiles.
+//
+// bf16: a wave loads its task's 32 target rows and 32 base-logit rows of the
+// tile as whole 128-byte rows (8 rows per instruction) one task ahead, with
+// the lane's temperature and previous token, and passes the entries to the
+// matrix layout through its own 4 KB of LDS (16-byte pieces swizzled by row).
+// A load whose lanes each take a piece of another row (32 rows per
+// instruction) moves about half as many bytes per second on this chip.
+constexpr int kTvStageBytes = kTileM * 128;
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void tv_tile_kernel(
     int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
@@ -86,6 +94,7 @@ __global__ __launch_bounds__(256) void tv_tile_kernel(
     const float* __restrict__ row_logZ, const float* __restrict__ temperature, TvWs ws) {
   constexpr bool bf = sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) char w2s[bf ? kLdsTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) char s_stg[bf ? 4 : 1][bf ? kTvStageBytes : 16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int nRB = (B + kTileM - 1) / kTileM;
@@ -95,37 +104,10 @@ __global__ __launch_bounds__(256) void tv_tile_kernel(
 
   if constexpr (bf) stage_tile(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s);
 
-  for (int t = wave; t < ntask || t == wave; t += 4) {
-    // the first pass of every wave also joins the barrier that publishes
-    // the LDS tile
-    const bool live = t < ntask;
-    const int rb = live ? t / gamma : 0, k = live ? t - rb * gamma : 0;
-    const int b = rb * kTileM + c;
-    const bool in = live && b < B;
-    const float it = in ? tv_inv_temp(temperature[b]) : 0.f;
-    const bool sampled = in && it > 0.f;   // greedy rows need no stream
-    int prev = -1;
-    if (sampled)
-      prev = clamp_token(k == 0 ? anchor[b] : tokens[(size_t)b * gamma + k - 1], V, nullptr);
-    bf16x8_t bfrag[bf ? KS : 1];
-    if constexpr (bf) load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), prev, bfrag);
-    URow<T> tp, up;
-    load_urow<T>(tp, target + ((size_t)b * (gamma + 1) + k) * V, v0, V, sampled, target);
-    load_urow<T>(up, U + ((size_t)b * gamma + k) * V, v0, V, sampled, U);
-    if (t == wave) {
-      if constexpr (bf) __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
-    if (!live) break;
-    f32x16_t acc[kSub];
-    init_acc<T>(up, V - (v0 + 16 * h), acc);   // draft logits start at the base logits
-    if (__ballot(sampled) != 0) {
-      if constexpr (bf)
-        bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
-      else
-        bias_tile_f32(reinterpret_cast<const float*>(W1), prev,
-                      reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
-    }
+  // the label partial of the lane's request over this tile (acc: its draft
+  // logits, tp: its target entries)
+  auto finish_task = [&](int b, int k, float it, bool sampled, const URow<T>& tp,
+                         const f32x16_t (&acc)[kSub]) {
     float s = 0.f;
     if (sampled) {
       const size_t row = (size_t)b * gamma + k;
@@ -147,6 +129,116 @@ __global__ __launch_bounds__(256) void tv_tile_kernel(
     float lo, hi;
     half_pair(s, lo, hi);
     if (sampled && h == 0) ws.part[((size_t)b * gamma + k) * nT + vt] = lo + hi;
+  };
+
+  if constexpr (bf) {
+    const uint16_t* tg = reinterpret_cast<const uint16_t*>(target);
+    const uint16_t* ub = reinterpret_cast<const uint16_t*>(U);
+    const int lr = lane >> 3, lp = lane & 7;   // loads: block row 8 j + lr, piece lp
+    char* stg = s_stg[wave];
+    // task tt's rows: u32x4 j < 4 target, j >= 4 base logits, row 8 (j % 4) + lr
+    auto fetch = [&](u32x4_t (&ld)[8], int tt) {
+      const bool lv = tt < ntask;
+      const int rb = lv ? tt / gamma : 0, k = lv ? tt - rb * gamma : 0;
+      const int e = v0 + 8 * lp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = rb * kTileM + 8 * j + lr;
+        const bool on = lv && r < B && e < V;
+        ld[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+            on ? tg + ((size_t)r * (gamma + 1) + k) * V + e : tg));
+        ld[4 + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+            on ? ub + ((size_t)r * gamma + k) * V + e : ub));
+      }
+    };
+    // the lane's request of task tt: temperature and previous token
+    auto head = [&](int tt, float& temp, int& tok) {
+      temp = 0.f;
+      tok = 0;
+      if (tt < ntask) {
+        const int rb = tt / gamma, k = tt - rb * gamma;
+        const int b = rb * kTileM + c;
+        if (b < B) {
+          temp = temperature[b];
+          tok = k == 0 ? anchor[b] : tokens[(size_t)b * gamma + k - 1];
+        }
+      }
+    };
+    // registers -> LDS (row r's piece q at q ^ (r % 8)) -> lane (c, h):
+    // sub-tile st, load q of URow = piece 4 st + 2 h + q of row c
+    auto restage = [&](const u32x4_t (&ld)[8], URow<uint16_t>& tp, URow<uint16_t>& up) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<u32x4_t*>(stg + (8 * j + lr) * 128 + 16 * (lp ^ lr)) = ld[4 * a + j];
+        asm volatile("" ::: "memory");   // the wave's LDS accesses stay in this order
+        URow<uint16_t>& dst = a == 0 ? tp : up;
+#pragma unroll
+        for (int st = 0; st < kSub; ++st) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int pc = 4 * st + 2 * h + q;
+            dst.w[st][q] =
+                *reinterpret_cast<const u32x4_t*>(stg + c * 128 + 16 * (pc ^ (c & 7)));
+          }
+        }
+        asm volatile("" ::: "memory");
+      }
+    };
+
+    u32x4_t ld[8];
+    float temp_n;
+    int tok_n;
+    head(wave, temp_n, tok_n);
+    fetch(ld, wave);
+    for (int t = wave; t < ntask || t == wave; t += 4) {
+      // the first pass of every wave also joins the barrier that publishes
+      // the LDS tile
+      const bool live = t < ntask;
+      const int rb = live ? t / gamma : 0, k = live ? t - rb * gamma : 0;
+      const int b = rb * kTileM + c;
+      const bool in = live && b < B;
+      const float it = in ? tv_inv_temp(temp_n) : 0.f;
+      const bool sampled = in && it > 0.f;   // greedy rows need no stream
+      const int prev = sampled ? clamp_token(tok_n, V, nullptr) : -1;
+      bf16x8_t bfrag[KS];
+      load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), prev, bfrag);
+      URow<uint16_t> tp, up;
+      restage(ld, tp, up);
+      head(t + 4, temp_n, tok_n);
+      fetch(ld, t + 4);
+      if (t == wave) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      if (!live) break;
+      f32x16_t acc[kSub];
+      init_acc<uint16_t>(up, V - (v0 + 16 * h), acc);   // draft logits start at the base logits
+      if (__ballot(sampled) != 0)
+        bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
+      finish_task(b, k, it, sampled, tp, acc);
+    }
+  } else {
+    for (int t = wave; t < ntask; t += 4) {
+      const int rb = t / gamma, k = t - rb * gamma;
+      const int b = rb * kTileM + c;
+      const bool in = b < B;
+      const float it = in ? tv_inv_temp(temperature[b]) : 0.f;
+      const bool sampled = in && it > 0.f;
+      int prev = -1;
+      if (sampled)
+        prev = clamp_token(k == 0 ? anchor[b] : tokens[(size_t)b * gamma + k - 1], V, nullptr);
+      URow<T> tp, up;
+      load_urow<T>(tp, target + ((size_t)b * (gamma + 1) + k) * V, v0, V, sampled, target);
+      load_urow<T>(up, U + ((size_t)b * gamma + k) * V, v0, V, sampled, U);
+      f32x16_t acc[kSub];
+      init_acc<T>(up, V - (v0 + 16 * h), acc);
+      if (__ballot(sampled) != 0)
+        bias_tile_f32(reinterpret_cast<const float*>(W1), prev,
+                      reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
+      finish_task(b, k, it, sampled, tp, acc);
+    }
   }
 }
 
