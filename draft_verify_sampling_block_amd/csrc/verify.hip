@@ -286,6 +286,7 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
     const int32_t* __restrict__ ell, VerifyWs ws, int32_t* status) {
   constexpr bool bf = sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) char w2s[bf ? kLdsTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) char s_stg[bf ? 4 : 1][bf ? kTileM * 128 : 16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int nRB = (B + kTileM - 1) / kTileM;
@@ -296,32 +297,119 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
   const bool any_res = *ws.any_res != 0;
   if (bf && any_res) stage_tile(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s);
 
-  for (int rb = wave; rb < nRB || (rb == wave); rb += 4) {
-    // one pass per 32-request block (lane column c = request b); the first
-    // pass of every wave also joins the barrier that publishes the LDS tile
-    const bool live = rb < nRB;
-    const int b = rb * kTileM + c;
-    FinalRow mine{0, 0, -1};
-    if (live && b < B) {
-      const int4 pl = ws.plan[b];
-      mine = FinalRow{pl.x, pl.y, pl.z};
+  auto plan_of = [&](int r) {   // the final-draw plan of request r (mode 0 past the batch)
+    FinalRow f{0, 0, -1};
+    if (r < B) {
+      const int4 pl = ws.plan[r];
+      f = FinalRow{pl.x, pl.y, pl.z};
     }
-    bf16x8_t bfrag[KS];
-    if constexpr (bf) load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1),
-                                     mine.mode == 1 ? mine.prev : -1, bfrag);
-    URow<T> tp, up;
-    load_urow<T>(tp, target + ((size_t)b * (gamma + 1) + mine.slot) * V, v0, V, mine.mode != 0,
-                 target);
-    load_urow<T>(up, U + ((size_t)b * gamma + mine.slot) * V, v0, V, mine.mode == 1, U);
-    if (rb == wave) {
-      if (bf && any_res) __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+    return f;
+  };
+
+  if constexpr (bf) {
+    // One pass per 32-request block rb (lane column c = request b), one
+    // block ahead: the block's target and base-logit rows of the tile are
+    // loaded as whole 128-byte rows (load j: block row 8 (j % 4) + lane / 8,
+    // entries 8 (lane % 8) + [0, 8)), with the plans they need requested one
+    // block earlier still, and passed to the matrix layout through the
+    // wave's 4 KB of LDS (16-byte pieces swizzled by row).  A load whose
+    // lanes each take 16 bytes of another row (32 rows per instruction)
+    // moves about half as many bytes per second on this chip.
+    const uint16_t* tg = reinterpret_cast<const uint16_t*>(target);
+    const uint16_t* ub = reinterpret_cast<const uint16_t*>(U);
+    const int lr = lane >> 3, lp = lane & 7;
+    char* stg = s_stg[wave];
+    struct Plans {
+      FinalRow mine;      // the lane's request
+      int2 rows[4];       // (mode, slot) of the rows the lane loads
+    };
+    auto plans = [&](int rb, Plans& pl) {
+      pl.mine = plan_of(rb < nRB ? rb * kTileM + c : B);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const FinalRow f = plan_of(rb < nRB ? rb * kTileM + 8 * j + lr : B);
+        pl.rows[j] = make_int2(f.mode, f.slot);
+      }
+    };
+    auto fetch = [&](u32x4_t (&ld)[8], int rb, const Plans& pl) {
+      const int e = v0 + 8 * lp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = rb * kTileM + 8 * j + lr;
+        const int md = pl.rows[j].x, sl = pl.rows[j].y;   // mode 0 for rows past the batch
+        const bool in = e < V;
+        ld[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+            in && md != 0 ? tg + ((size_t)r * (gamma + 1) + sl) * V + e : tg));
+        ld[4 + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+            in && md == 1 ? ub + ((size_t)r * gamma + sl) * V + e : ub));
+      }
+    };
+    // registers -> LDS (row r's piece q at q ^ (r % 8)) -> lane (c, h):
+    // sub-tile st, load q of URow = piece 4 st + 2 h + q of row c
+    auto restage = [&](const u32x4_t (&ld)[8], URow<uint16_t>& tp, URow<uint16_t>& up) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<u32x4_t*>(stg + (8 * j + lr) * 128 + 16 * (lp ^ lr)) = ld[4 * a + j];
+        asm volatile("" ::: "memory");   // the wave's LDS accesses stay in this order
+        URow<uint16_t>& dst = a == 0 ? tp : up;
+#pragma unroll
+        for (int st = 0; st < kSub; ++st) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int pc = 4 * st + 2 * h + q;
+            dst.w[st][q] =
+                *reinterpret_cast<const u32x4_t*>(stg + c * 128 + 16 * (pc ^ (c & 7)));
+          }
+        }
+        asm volatile("" ::: "memory");
+      }
+    };
+
+    Plans pl, pl_next;
+    plans(wave, pl);
+    u32x4_t ld[8];
+    fetch(ld, wave, pl);
+    plans(wave + 4, pl_next);
+    for (int rb = wave; rb < nRB || (rb == wave); rb += 4) {
+      // the first pass of every wave also joins the barrier that publishes
+      // the LDS tile
+      const bool live = rb < nRB;
+      const int b = rb * kTileM + c;
+      const FinalRow mine = pl.mine;
+      bf16x8_t bfrag[KS];
+      load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), mine.mode == 1 ? mine.prev : -1,
+                     bfrag);
+      URow<uint16_t> tp, up;
+      restage(ld, tp, up);
+      fetch(ld, rb + 4, pl_next);
+      pl = pl_next;
+      plans(rb + 8, pl_next);
+      if (rb == wave) {
+        if (any_res) __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      if (!live) break;
+      f32x16_t acc[kSub];
+      init_acc<uint16_t>(up, V - (v0 + 16 * h), acc);   // q logits start at the base logits
+      final_task<T, KS>(mine, b, vt, V, gamma, nT, rank, tp, acc, bfrag, w2s, W1, W2t, row_max,
+                        row_logZ, temperature, ws);
     }
-    if (!live) break;
-    f32x16_t acc[kSub];
-    init_acc<T>(up, V - (v0 + 16 * h), acc);   // q logits start at the base logits
-    final_task<T, KS>(mine, b, vt, V, gamma, nT, rank, tp, acc, bfrag, w2s, W1, W2t, row_max,
-                      row_logZ, temperature, ws);
+  } else {
+    for (int rb = wave; rb < nRB; rb += 4) {
+      const int b = rb * kTileM + c;
+      const FinalRow mine = plan_of(b);
+      bf16x8_t bfrag[KS];   // unused: fp32 adds the bias with plain FMAs
+      URow<T> tp, up;
+      load_urow<T>(tp, target + ((size_t)b * (gamma + 1) + mine.slot) * V, v0, V,
+                   mine.mode != 0, target);
+      load_urow<T>(up, U + ((size_t)b * gamma + mine.slot) * V, v0, V, mine.mode == 1, U);
+      f32x16_t acc[kSub];
+      init_acc<T>(up, V - (v0 + 16 * h), acc);   // q logits start at the base logits
+      final_task<T, KS>(mine, b, vt, V, gamma, nT, rank, tp, acc, bfrag, w2s, W1, W2t, row_max,
+                        row_logZ, temperature, ws);
+    }
   }
 }
 
