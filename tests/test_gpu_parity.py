@@ -83,6 +83,15 @@ SMALL = {
     "bf16-temperature-extremes": lambda: _with_temperatures(
         make_custom(45, 5, 3000, 64, 32, "bf16", "mixture", seed=11, sps_kind="linear:230",
                     calibrated=True), [0.05, 0.3, 1.0, 4.0, 0.0]),
+    # batch sizes at the edges of the verify statistics kernels' forms:
+    # 97 = three full 32-request blocks and one row (tile loop), 129 = four
+    # full blocks and one row (the per-tile fallback), ragged vocabularies
+    "bf16-B97-V2000-tile-loop-edge": lambda: make_custom(97, 3, 2000, 64, 16, "bf16", "mixture",
+                                                         seed=13, sps_kind="linear:300",
+                                                         calibrated=True),
+    "bf16-B129-V1800-fallback-edge": lambda: make_custom(129, 3, 1800, 64, 16, "bf16",
+                                                         "mixture", seed=14,
+                                                         sps_kind="linear:400", calibrated=True),
 }
 
 

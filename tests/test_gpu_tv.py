@@ -45,6 +45,9 @@ CASES = {
                                                             seed=5),
     "bf16-temperature-extremes": lambda: _with_temperatures(
         make_custom(45, 5, 3000, 64, 32, "bf16", "mixture", seed=11), [0.05, 0.3, 1.0, 4.0, 0.0]),
+    # 97 requests = three full 32-request blocks and one row, ragged tiles
+    "bf16-B97-V2000-partial-block": lambda: _with_temperatures(
+        make_custom(97, 3, 2000, 64, 16, "bf16", "mixture", seed=13), [1.0, 0.6, 0.0, 1.3]),
 }
 
 
