@@ -80,14 +80,15 @@ __global__ __launch_bounds__(256) void tv_rows_kernel(int B, int gamma, int V,
 // lane's 16-entry halves, as in the draft's block-tiles.
 //
 // bf16: a wave loads its task's 32 target rows and 32 base-logit rows of the
-// tile as whole 128-byte rows (8 rows per instruction) one task ahead, with
+// tile as whole 128-byte rows (8 rows per instruction) two tasks ahead, with
 // the lane's temperature and previous token, and passes the entries to the
 // matrix layout through its own 4 KB of LDS (16-byte pieces swizzled by row).
 // A load whose lanes each take a piece of another row (32 rows per
 // instruction) moves about half as many bytes per second on this chip.
 constexpr int kTvStageBytes = kTileM * 128;
+// (two work-groups per compute unit: two waves per SIMD)
 template <typename T, int KS>
-__global__ __launch_bounds__(256) void tv_tile_kernel(
+__global__ __launch_bounds__(256, 2) void tv_tile_kernel(
     int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
     const T* __restrict__ W1, const T* __restrict__ W2t, const int32_t* __restrict__ anchor,
     const int32_t* __restrict__ tokens, const float* __restrict__ row_max,
@@ -187,12 +188,10 @@ __global__ __launch_bounds__(256) void tv_tile_kernel(
       }
     };
 
-    u32x4_t ld[8];
-    float temp_n;
-    int tok_n;
-    head(wave, temp_n, tok_n);
-    fetch(ld, wave);
-    for (int t = wave; t < ntask || t == wave; t += 4) {
+    // task t of this wave: its entries in ld, its temperature and previous
+    // token in temp_n / tok_n; those of task t + 8 are requested in their
+    // place (two tasks in flight per wave).  False once the wave is done.
+    auto task = [&](int t, u32x4_t (&ld)[8], float& temp_n, int& tok_n) {
       // the first pass of every wave also joins the barrier that publishes
       // the LDS tile
       const bool live = t < ntask;
@@ -206,18 +205,30 @@ __global__ __launch_bounds__(256) void tv_tile_kernel(
       load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), prev, bfrag);
       URow<uint16_t> tp, up;
       restage(ld, tp, up);
-      head(t + 4, temp_n, tok_n);
-      fetch(ld, t + 4);
+      head(t + 8, temp_n, tok_n);
+      fetch(ld, t + 8);
       if (t == wave) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
-      if (!live) break;
+      if (!live) return false;
       f32x16_t acc[kSub];
       init_acc<uint16_t>(up, V - (v0 + 16 * h), acc);   // draft logits start at the base logits
       if (__ballot(sampled) != 0)
         bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
       finish_task(b, k, it, sampled, tp, acc);
+      return true;
+    };
+    u32x4_t ldA[8], ldB[8];
+    float tA, tB;
+    int kA, kB;
+    head(wave, tA, kA);
+    fetch(ldA, wave);
+    head(wave + 4, tB, kB);
+    fetch(ldB, wave + 4);
+    for (int t = wave;; t += 8) {
+      if (!task(t, ldA, tA, kA)) break;
+      if (!task(t + 4, ldB, tB, kB)) break;
     }
   } else {
     for (int t = wave; t < ntask; t += 4) {
