@@ -71,10 +71,18 @@ __device__ inline float inv_temp(float T) { return (T > 0.f) ? 1.f / T : 0.f; }
 
 // first rejected slot of request b among its L verified slots (L when all
 // pass), from the accept flags verify_rows_kernel wrote for every k < L
+// The flags are requested eight at a time (independent loads, indices
+// clamped to L - 1), so a row costs one memory round trip per eight slots.
 __device__ inline int first_reject(const VerifyWs& ws, int b, int gamma, int L) {
   const int32_t* acc = ws.wacc + (size_t)b * gamma;
-  for (int k = 0; k < L; ++k)
-    if (acc[k] == 0) return k;
+  for (int k0 = 0; k0 < L; k0 += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = acc[min(k0 + u, L - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k0 + u < L && v[u] == 0) return k0 + u;
+  }
   return L;
 }
 
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
   __shared__ __attribute__((aligned(16))) char s_stage[kVtWaves][2][kTileM][kVtStageRow];
   __shared__ float s_part[2][kSub][kVtMaxRows][2];
   __shared__ float s_out[2][kVtOutTiles][kVtMaxRows];
-  __shared__ int s_mode[kVtMaxRows], s_slot[kVtMaxRows];
+  __shared__ int s_mode[kVtMaxRows], s_slot[kVtMaxRows], s_prv[kVtMaxRows];
   __shared__ int s_any;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -471,6 +479,7 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
     if (f.mode == 1) s_any = 1;
     s_mode[r] = f.mode;
     s_slot[r] = f.slot;
+    s_prv[r] = f.prev;
   }
   __syncthreads();
   const bool any_res = s_any != 0;   // some request of the batch draws from a residual
@@ -504,23 +513,9 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
   // where there is nothing to read): with a fixed count of loads per step
   // the in-order memory counter waits for exactly the data it needs
   const int tlast = tbase + tcount - 1;
-  if (any_res) {
-    load_tile(stA, tbase);
-    write_tile(stA, 0);
-  }
-
-  // this wave's request column: plan, weights' constants, the W1 row of
-  // the previous token (zero unless the request draws from a residual)
+  // this wave's request column
   const int b = rb * kTileM + c;
   const bool active = rb * kTileM < B;
-  FinalRow mine{0, 0, -1};
-  if (active && b < B) mine = final_row(b, B, gamma, V, ell, temperature, anchor, tokens, ws);
-  const FinalParams fpar = final_params(mine, b, gamma, row_max, row_logZ, temperature, ws);
-  const bool blk_res = any_res && __ballot(mine.mode == 1) != 0;
-  bf16x8_t bfrag[KS];
-  load_bfrag<KS>(W1, (any_res && mine.mode == 1) ? mine.prev : -1, bfrag);
-  __builtin_amdgcn_s_waitcnt(0);   // the first W2t tile has landed
-  __syncthreads();
 
   // The rows this lane loads for its wave: block rows 16 g + lane / 4
   // (g = 0, 1), 16 bytes at entry 32 t + 8 (lane % 4) of the tile.
@@ -554,6 +549,24 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
           reinterpret_cast<const u32x4_t*>(in && lu_on[g] ? lu[g] + e : U));
     }
   };
+  // the first tile's entries, W2t rows and W1 fragments requested together
+  fetch(ldA, tbase);
+  if (any_res) {
+    load_tile(stA, tbase);
+    write_tile(stA, 0);
+  }
+
+  // plan, weights' constants, the W1 row of the previous token (zero
+  // unless the request draws from a residual)
+  FinalRow mine{0, 0, -1};
+  if (active && b < B) mine = FinalRow{s_mode[b], s_slot[b], s_prv[b]};
+  const FinalParams fpar = final_params(mine, b, gamma, row_max, row_logZ, temperature, ws);
+  const bool blk_res = any_res && __ballot(mine.mode == 1) != 0;
+  bf16x8_t bfrag[KS];
+  load_bfrag<KS>(W1, (any_res && mine.mode == 1) ? mine.prev : -1, bfrag);
+  __builtin_amdgcn_s_waitcnt(0);   // the first tile's operands have landed
+  __syncthreads();
+
   // registers -> this wave's LDS area -> the matrix layout: lane (c, h)
   // takes entries 32 t + 16 h + [0, 16) of request row c
   char (*stg)[kTileM][kVtStageRow] = s_stage[wave];
@@ -583,7 +596,6 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
   // the tile walk, with (kRes) or without the bias on the matrix cores
   auto walk = [&](auto res_tag) {
     constexpr bool kRes = decltype(res_tag)::value;
-    fetch(ldA, tbase);
     if constexpr (kRes) load_tile(stB, min(tbase + 1, tlast));
     // tile i from LDS buffer i & 1; `next` holds tile i + 1, `after`
     // receives tile i + 2; `ld` holds tile i's entries, `ld1` receives
