@@ -263,8 +263,8 @@ def cpu_baseline(cfg, n_req):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the sampling path "
-              "has no multi-GPU mode in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the sampling path "
+              "has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -27,7 +27,7 @@ def _gpu():
 CASES = {
     "bf16-ragged-V1000-B40": lambda: make_custom(40, 4, 1000, 64, 32, "bf16", "mixture", seed=1,
                                                  sps_kind="linear:200", calibrated=True),
-    "config 3 full size": lambda: make_config(3),
+    "long-proposal B=128 gamma=15 V=151936 full size": lambda: make_config(3),
 }
 
 

@@ -14,11 +14,18 @@ import numpy as np
 import pytest
 import torch
 
-from gen import make_config, make_custom
+from gen import SPECS, make_config, make_custom
 from oracle import f64
 from oracle.parity import check_confidence, check_draft, check_schedule, check_verify
 
 pytestmark = pytest.mark.gpu
+
+
+def _workload(i):
+    """A workload's name and sizes (for progress lines)."""
+    sp = SPECS[i]
+    return f"{sp.name} B={sp.B} gamma={sp.gamma} V={sp.V} rank={sp.rank} {sp.dtype}"
+
 
 
 def _say(msg):
@@ -174,9 +181,9 @@ FULL_DRAFT_ROWS = 40
 FULL_VERIFY_REQ = 20
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
-def test_full_size_configs(cfg):
-    _say(f"config {cfg} full size")
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4], ids=lambda i: SPECS[i].name)
+def test_full_size_workloads(cfg):
+    _say(f"{_workload(cfg)} full size")
     wl = make_config(cfg)
     out = run_step(wl)
     rng = np.random.default_rng(100 + cfg)
@@ -195,7 +202,7 @@ def test_full_size_configs(cfg):
         assert np.array_equal(out["out_tokens"][b, : n[b]], out["tokens"][b, : n[b]])
         assert 0 <= out["out_tokens"][b, n[b]] < wl.V
     assert np.all((out["tokens"] >= 0) & (out["tokens"] < wl.V))
-    print(f"config {cfg}: mean ell {ell.mean():.2f}, mean accepted {n.mean():.2f}", flush=True)
+    print(f"{_workload(cfg)}: mean ell {ell.mean():.2f}, mean accepted {n.mean():.2f}", flush=True)
 
 
 PATH_CASES = {
@@ -205,7 +212,7 @@ PATH_CASES = {
     "bf16-temperature-extremes": lambda: SMALL["bf16-temperature-extremes"](),
     "bf16-B300-rank128-V5000": lambda: make_custom(300, 3, 5000, 128, 16, "bf16", "mixture",
                                                    seed=9, temperature=0.8, greedy_frac=0.2),
-    "config 1 full size": lambda: make_config(1),
+    "qwen3-4b-block7 B=32 gamma=7 V=151936 full size": lambda: make_config(1),
 }
 
 

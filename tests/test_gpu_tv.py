@@ -13,11 +13,18 @@ import numpy as np
 import pytest
 import torch
 
-from gen import make_config, make_custom
+from gen import SPECS, make_config, make_custom
 from oracle import f64
 from oracle.parity import check_tv
 
 pytestmark = pytest.mark.gpu
+
+
+def _workload(i):
+    """A workload's name and sizes (for progress lines)."""
+    sp = SPECS[i]
+    return f"{sp.name} B={sp.B} gamma={sp.gamma} V={sp.V} rank={sp.rank} {sp.dtype}"
+
 
 
 def _say(msg):
@@ -80,9 +87,9 @@ def test_tv_label_small(name):
     assert np.all((tv >= -1e-6) & (tv <= 1 + 1e-6))
 
 
-@pytest.mark.parametrize("cfg", [1, 3])
+@pytest.mark.parametrize("cfg", [1, 3], ids=lambda i: SPECS[i].name)
 def test_tv_label_full_size(cfg):
-    _say(f"tv config {cfg}")
+    _say(f"label {_workload(cfg)}")
     wl = make_config(cfg)
     tokens, tv, label, status = _run(wl)
     assert status == 0, status
