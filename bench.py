@@ -255,7 +255,7 @@ def cpu_baseline(cfg, n_req):
     dt = (time.perf_counter() - t0) / reps
     return {"value": n_req * wl.gamma / dt, "unit": "positions/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"first {n_req} of {wl.spec.B} requests of config {cfg} "
+            "sample": f"first {n_req} of {wl.spec.B} requests of {wl.spec.name} "
                       f"({n_req * wl.gamma} positions; scheduler over the sample), "
                       f"{reps} passes, {dt:.1f} s each"}
 
@@ -291,7 +291,7 @@ def main():
     spec = SPECS[cfg]
     t0 = time.perf_counter()
     wl = make_config(cfg)
-    print(f"[bench] generated config {cfg} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
+    print(f"[bench] generated {spec.name} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
           flush=True)
     st = Step(upload(wl, "cuda"))
     for _ in range(args.warmup):
@@ -340,7 +340,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded; shapes and logit mixtures of the pages' workloads)",
-        "config": {"workload": f"config {cfg} {spec.name}: B={wl.B} gamma={wl.gamma} V={wl.V} "
+        "config": {"workload": f"{spec.name}: B={wl.B} gamma={wl.gamma} V={wl.V} "
                                f"rank={wl.rank} H={wl.H} {wl.dtype}",
                    "B": wl.B, "gamma": wl.gamma, "V": wl.V, "rank": wl.rank, "H": wl.H,
                    "scheduler": bool(spec.scheduler), "parallelism": "single GPU"},
