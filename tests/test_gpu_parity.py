@@ -149,6 +149,27 @@ def test_verify_extreme_lengths(ell_value):
     print(rep, flush=True)
 
 
+def test_verify_rejections_past_eight_slots():
+    """A 20-slot block verified in full with the target equal to the base
+    logits (the Markov bias alone separates p and q): first rejections fall
+    on both sides of slot 8, where the accept-flag scan reads its second
+    group of eight flags, and one request accepts every slot."""
+    _say("verify-long-block")
+    from draft_verify_sampling_block_amd.step import Step, upload
+    wl = make_custom(24, 20, 1024, 32, 16, "bf16", "mixture", seed=16, w_std=0.3)
+    wl.target[:, :wl.gamma] = wl.U
+    d = upload(wl, "cuda", scheduler=False)
+    d.fixed_ell = torch.full((wl.B,), wl.gamma, dtype=torch.int32, device="cuda")
+    st = Step(d).run()
+    torch.cuda.synchronize()
+    h = lambda t: t.cpu().numpy()
+    rep = check_verify(wl, f64(wl.W1), f64(wl.W2t), h(st.tokens), h(d.fixed_ell), h(st.out_tokens),
+                       h(st.n_accepted), h(st.ratio))
+    n = h(st.n_accepted)
+    assert np.any(n < 8) and np.any((n > 8) & (n < wl.gamma)) and np.any(n == wl.gamma), n
+    print(rep, flush=True)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_schedule_random_confidences(seed):
     # sizes on both sides of 4096 candidates (run merging below, bitonic
