@@ -114,14 +114,19 @@ __global__ __launch_bounds__(256, 2) void tv_tile_kernel(
       const size_t row = (size_t)b * gamma + k;
       const float M = ws.M[row], LZ = ws.LZ[row];
       const float mq = row_max[row], lzq = row_logZ[row];
+      // exp(y / T - M - log Z) as 2^(y (log2 e / T) - (M + log Z) log2 e):
+      // one fused multiply-add and the hardware base-2 exponential per term
+      constexpr float kLog2e = 1.4426950408889634f;
+      const float a = it * kLog2e;
+      const float cp = (M + LZ) * kLog2e, cq = (mq + lzq) * kLog2e;
 #pragma unroll
       for (int st = 0; st < kSub; ++st) {
         const int rem = V - (v0 + 32 * st + 16 * h);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           if (j < rem) {
-            const float p = __expf(urow_at(tp, st, j) * it - M - LZ);
-            const float q = __expf(acc[st][j] * it - mq - lzq);
+            const float p = __builtin_amdgcn_exp2f(fmaf(urow_at(tp, st, j), a, -cp));
+            const float q = __builtin_amdgcn_exp2f(fmaf(acc[st][j], a, -cq));
             s += fabsf(p - q);
           }
         }
