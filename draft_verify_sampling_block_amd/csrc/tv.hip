@@ -84,7 +84,9 @@ __global__ __launch_bounds__(256) void tv_rows_kernel(int B, int gamma, int V,
 // the lane's temperature and previous token, and passes the entries to the
 // matrix layout through its own 4 KB of LDS (16-byte pieces swizzled by row).
 // A load whose lanes each take a piece of another row (32 rows per
-// instruction) moves about half as many bytes per second on this chip.
+// instruction) moves about half as many bytes per second on this chip.  The
+// rows of greedy requests are read too (their temperatures are not known
+// when the loads issue; their lanes discard them).
 constexpr int kTvStageBytes = kTileM * 128;
 // (two work-groups per compute unit: two waves per SIMD)
 template <typename T, int KS>
