@@ -70,24 +70,35 @@ def algorithmic_bytes(wl, ell, n_acc):
 
 
 def draft_kernel_bytes(wl, kernel):
-    """Algorithmic bytes of one launch of the draft kernel `kernel`.
+    """Algorithmic bytes of one launch of the draft kernel `kernel`: the
+    draft's share of the step's bytes, each input read once.
 
     pdraft_kernel (one launch per block of gamma positions): every U row, the
-    W2 factor once, the gathered W1 rows, the per-(request, position, tile)
-    statistics written (packed max and sum, plus the argmax of greedy rows)
-    and the per-position outputs.  draft_stats_kernel (one launch per
-    position): that position's U rows, its W1 rows, W2 once per launch, its
-    tile statistics.
+    W2 factor once, the gathered W1 rows (one per position and request), the
+    anchors, temperatures and draw uniforms, and the four [B, gamma] outputs.
+    draft_stats_kernel (one launch per position): that position's U rows and
+    W1 rows, and 1/gamma of W2 (the per-position launches read W2 again each
+    time; the step needs it once).  The kernels' own tile statistics are
+    intermediates, reported by draft_intermediate_bytes, not counted here.
     """
-    import numpy as np
     e = 2 if wl.dtype == "bf16" else 4
-    nT = (wl.V + 63) // 64
     B, g, V, r = wl.B, wl.gamma, wl.V, wl.rank
-    greedy = int(np.sum(~(np.asarray(wl.temperature) > 0)))
-    stats = 8 * B * nT + 4 * greedy * nT          # per position
     if kernel == "pdraft_kernel":
-        return e * B * g * V + e * r * V + e * B * g * r + g * stats + 4 * B * g * 4
-    return e * B * V + e * B * r + e * r * V + stats
+        return (e * B * g * V + e * r * V + e * B * g * r
+                + 4 * B + 4 * B + 4 * B * g + 4 * B * g * 4)
+    return e * B * V + e * B * r + e * r * V / g
+
+
+def draft_intermediate_bytes(wl, kernel):
+    """Bytes of the draft kernel's own intermediates per launch: the packed
+    per-(request, tile) statistics words (and greedy rows' argmax words)
+    written each position and read back by the request's owner."""
+    import numpy as np
+    nT = (wl.V + 63) // 64
+    B, g = wl.B, wl.gamma
+    greedy = int(np.sum(~(np.asarray(wl.temperature) > 0)))
+    per_pos = 2 * (8 * B * nT + 4 * greedy * nT)
+    return g * per_pos if kernel == "pdraft_kernel" else per_pos
 
 
 KERNEL_SOURCES = ["draft_verify_sampling_block_amd/csrc/draft.hip",
@@ -126,20 +137,36 @@ def counter_traffic(kernel, cfg):
 
 def kernel_bytes(wl, ell, n_acc):
     """Algorithmic bytes per launch of the step's streaming kernels, from the
-    realised verify lengths: verify_rows_kernel reads the target rows of every
-    slot up to each request's verify length (bonus slot included); the verify
-    statistics read each sampled request's final slot row, the base-logit row
-    of each rejecting request and W2 once; the confidence head reads the
-    hidden states and the gathered W1 rows."""
+    realised outcomes (each kernel's share of the step's bytes, nothing
+    counted twice): verify_rows_kernel the target rows of slots 0..j_b - 1,
+    j_b = n_accepted + 1 (up to the first reject, or the bonus slot); the
+    verify statistics the base-logit row of each sampled request that
+    rejected (the q recompute); the confidence head the hidden states and the
+    gathered W1 rows."""
     import numpy as np
     e = 2 if wl.dtype == "bf16" else 4
     B, g, V, r, H = wl.B, wl.gamma, wl.V, wl.rank, wl.H
     sampled = np.asarray(wl.temperature) > 0
     rejected = (n_acc < ell) & sampled
-    stats = e * V * (int(sampled.sum()) + int(rejected.sum())) + e * r * V
-    return {"verify_rows_kernel": e * V * int((np.asarray(ell) + 1).sum()),
+    stats = e * V * int(rejected.sum())
+    return {"verify_rows_kernel": e * V * int((np.asarray(n_acc) + 1).sum()),
             "verify_tile_stats_kernel": stats, "verify_final_stats_kernel": stats,
             "confidence_kernel": e * B * g * (H + r) + 4 * B * g}
+
+
+def kernel_bytes_read(wl, ell, n_acc):
+    """Bytes the same kernels read as built (re-reads included):
+    verify_rows_kernel reads every slot up to the verify length ell_b (the
+    bonus slot included); the verify statistics read each sampled request's
+    final slot row again, the base-logit rows at rejects and W2 again."""
+    import numpy as np
+    e = 2 if wl.dtype == "bf16" else 4
+    V, r = wl.V, wl.rank
+    sampled = np.asarray(wl.temperature) > 0
+    rejected = (n_acc < ell) & sampled
+    stats = e * V * (int(sampled.sum()) + int(rejected.sum())) + e * r * V
+    return {"verify_rows_kernel": e * V * int((np.asarray(ell) + 1).sum()),
+            "verify_tile_stats_kernel": stats, "verify_final_stats_kernel": stats}
 
 
 def tv_label_bytes(wl):
@@ -175,7 +202,7 @@ def next_rows(st, wl, reps):
                                                                  order=order, stats=stats),
         "schedule_threshold": lambda: dv.dspark_schedule_threshold(st.conf, 0.5, ell=ell,
                                                                    order=order, stats=stats),
-        "tv_label": lambda: dv.dspark_tv_label(d.target, d.U, d.W1, d.W2t, d.anchor, st.tokens,
+        "tv_label": lambda: dv.dspark_tv_label(d.target, d.U, d.W1, d.W2, d.anchor, st.tokens,
                                                st.row_max, st.row_logZ, d.temperature, tv=tv,
                                                label=label, workspace=ws),
     }
@@ -230,20 +257,26 @@ def cpu_baseline(cfg, n_req):
     from gen import make_config
 
     wl = make_config(cfg, requests=range(n_req))
+    # the oracle's loops are single-threaded Python; its vector products run
+    # in the BLAS library, so the threads it uses are the BLAS threads
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
     def one_pass():
-        W1, W2t = O.f64(wl.W1), O.f64(wl.W2t)
-        d = O.draft_block(wl.U, W1, W2t, wl.anchor, wl.temperature, wl.uniforms)
+        W1, W2 = O.f64(wl.W1), O.f64(wl.W2)
+        d = O.draft_block(wl.U, W1, W2, wl.anchor, wl.temperature, wl.uniforms)
         c = O.confidence(wl.hidden, W1, wl.anchor, d["tokens"], wl.w, wl.b0)
         if wl.spec.scheduler and wl.sps is not None:
             ell = O.schedule(c, wl.sps)["ell"]
         else:
             ell = np.full(wl.B, wl.gamma)
-        O.verify(wl.target, wl.U, W1, W2t, wl.anchor, d["tokens"], d["q_tok"], wl.temperature,
+        O.verify(wl.target, wl.U, W1, W2, wl.anchor, d["tokens"], d["q_tok"], wl.temperature,
                  wl.uniforms, ell)
 
     # whole passes over the sample until about 10 s of CPU work (at most 5)
@@ -254,6 +287,7 @@ def cpu_baseline(cfg, n_req):
         reps += 1
     dt = (time.perf_counter() - t0) / reps
     return {"value": n_req * wl.gamma / dt, "unit": "positions/s", "cores": int(cores),
+            "cpu_count": os.cpu_count(), "affinity_cpus": affinity, "blas_threads": int(cores),
             "kind": "oracle",
             "sample": f"first {n_req} of {wl.spec.B} requests of {wl.spec.name} "
                       f"({n_req * wl.gamma} positions; scheduler over the sample), "
@@ -297,17 +331,24 @@ def main():
     for _ in range(args.warmup):
         st.run()
     torch.cuda.synchronize()
+    # one device status word per timed step (zeroed beforehand), so a flag
+    # raised by any step is seen and traced to that step
+    # (16 bytes apart: the library takes 16-byte-aligned pointers)
+    step_status = torch.zeros((args.steps, 4), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(args.steps):
-        st.run()
+    for i in range(args.steps):
+        st.run(status=step_status[i, :1])
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     print(f"[bench] {args.steps} steps, {ms:.4f} ms/step", file=sys.stderr, flush=True)
-    status = int(st.status.item())
+    per_step_status = [int(x) for x in step_status[:, 0].cpu().tolist()]
+    status = 0
+    for x in per_step_status:
+        status |= x
     ell = st.ell_used().cpu().numpy()
     n_acc = st.n_accepted.cpu().numpy()
 
@@ -325,6 +366,8 @@ def main():
     stats_bytes = draft_kernel_bytes(wl, draft_kernel)
     avg_s = kern_ms[draft_kernel] / 1e3
     achieved = stats_bytes / avg_s / 1e9
+    traffic = counter_traffic(draft_kernel, cfg)
+    kb_read = kernel_bytes_read(wl, ell, n_acc)
     bytes_step = algorithmic_bytes(wl, ell, n_acc)
 
     out = {
@@ -346,19 +389,23 @@ def main():
                    "scheduler": bool(spec.scheduler), "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": draft_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counter_traffic(draft_kernel, cfg),
+                     "traffic": traffic,
+                     "traffic_over_alg": None if traffic is None else traffic / stats_bytes,
                      "bytes_per_launch": stats_bytes,
+                     "intermediate_bytes": draft_intermediate_bytes(wl, draft_kernel),
                      "mean_launch_us": avg_s * 1e6},
         "step": {"bytes_alg": bytes_step, "hbm_gbs": bytes_step / (ms / 1e3) / 1e9,
                  "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                  "mean_ell": float(ell.mean()), "mean_accepted": float(n_acc.mean()),
                  "dominant_kernel": dom,
                  "kernel_gbs": {k: {"bytes_alg": nb, "gbs": nb / (kern_ms[k] / 1e3) / 1e9,
-                                    "frac": nb / (kern_ms[k] / 1e3) / 1e9 / HBM_PEAK_GBS}
+                                    "frac": nb / (kern_ms[k] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                    "bytes_read": kb_read.get(k)}
                                 for k, nb in kernel_bytes(wl, ell, n_acc).items()
                                 if k in kern_ms},
                  "kernel_ms_per_step": {k: round(v, 5) for k, v in per_step_ms.items()},
-                 "device_status": status},
+                 "device_status": status,
+                 "steps_with_status": sum(1 for x in per_step_status if x)},
     }
     out["next_rows"] = next_rows(st, wl, max(3, args.steps // 2))
     ceil = read_ceiling_gbs()

@@ -121,17 +121,36 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise DsparkError(-1, f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise DsparkError(-1, f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise DsparkError(-1, f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise DsparkError(-1, f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise DsparkError(-2, f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise DsparkError(-1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _out(t, name: str, dtype, shape, device):
+    """A caller-supplied output checked like an input, or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _need(t, name, dtype, shape, device)
+
+
+def _status(t, device):
+    """The optional device status word: None or one int32 on `device`."""
+    if t is None:
+        return None
+    _need(t, "status", torch.int32, None, device)
+    if t.numel() != 1:
+        raise DsparkError(-1, f"status must hold one int32, got {t.numel()}")
     return t
 
 
@@ -180,29 +199,35 @@ def dspark_schedule_workspace(R, gamma) -> int:
 
 def _workspace(nbytes: int, device, given=None):
     if given is not None:
+        _need(given, "workspace", torch.uint8, None, device)
+        if given.dim() != 1 or given.numel() < nbytes:
+            raise DsparkError(-4, f"workspace must be a 1-D uint8 tensor of at least {nbytes} "
+                                  f"bytes, got shape {tuple(given.shape)}")
         return given
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def dspark_draft_block(U, W1, W2t, anchor, temperature, uniforms, *, tokens=None, q_tok=None,
+def dspark_draft_block(U, W1, W2, anchor, temperature, uniforms, *, tokens=None, q_tok=None,
                        row_max=None, row_logZ=None, status=None, workspace=None):
-    """Markov-head block drafting.  U [B,gamma,V]; W1, W2t [V,rank]; returns
+    """Markov-head block drafting.  U [B,gamma,V]; W1 [V,rank], W2 [rank,V]; returns
     dict(tokens, q_tok, row_max, row_logZ)."""
     lib = load()
     B, gamma, V = U.shape
     rank = W1.shape[1]
     dt = _dtype_code(U)
     dev = U.device
-    _need(U, "U"); _need(W1, "W1", U.dtype, (V, rank)); _need(W2t, "W2t", U.dtype, (V, rank))
-    _need(anchor, "anchor", torch.int32, (B,)); _need(temperature, "temperature", torch.float32, (B,))
-    _need(uniforms, "uniforms", torch.float32, (B, gamma + 1, 2))
-    tokens = tokens if tokens is not None else torch.empty((B, gamma), dtype=torch.int32, device=dev)
-    q_tok = q_tok if q_tok is not None else torch.empty((B, gamma), dtype=torch.float32, device=dev)
-    row_max = row_max if row_max is not None else torch.empty((B, gamma), dtype=torch.float32, device=dev)
-    row_logZ = row_logZ if row_logZ is not None else torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    _need(U, "U"); _need(W1, "W1", U.dtype, (V, rank), dev); _need(W2, "W2", U.dtype, (rank, V), dev)
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, gamma + 1, 2), dev)
+    tokens = _out(tokens, "tokens", torch.int32, (B, gamma), dev)
+    q_tok = _out(q_tok, "q_tok", torch.float32, (B, gamma), dev)
+    row_max = _out(row_max, "row_max", torch.float32, (B, gamma), dev)
+    row_logZ = _out(row_logZ, "row_logZ", torch.float32, (B, gamma), dev)
+    status = _status(status, dev)
     need = dspark_draft_block_workspace(B, gamma, V, rank, dt)
     ws = _workspace(need, dev, workspace)
-    _check(lib.dspark_draft_block(B, gamma, V, rank, dt, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(anchor),
+    _check(lib.dspark_draft_block(B, gamma, V, rank, dt, _ptr(U), _ptr(W1), _ptr(W2), _ptr(anchor),
                                   _ptr(temperature), _ptr(uniforms), _ptr(tokens), _ptr(q_tok),
                                   _ptr(row_max), _ptr(row_logZ), _ptr(status), _ptr(ws),
                                   ws.numel(), _stream()))
@@ -215,10 +240,13 @@ def dspark_confidence(hidden, W1, anchor, tokens, w, bias=0.0, *, conf=None, sta
     B, gamma, H = hidden.shape
     V, rank = W1.shape
     dt = _dtype_code(hidden)
-    _need(hidden, "hidden"); _need(W1, "W1", hidden.dtype)
-    _need(anchor, "anchor", torch.int32, (B,)); _need(tokens, "tokens", torch.int32, (B, gamma))
-    _need(w, "w", torch.float32, (H + rank,))
-    conf = conf if conf is not None else torch.empty((B, gamma), dtype=torch.float32, device=hidden.device)
+    dev = hidden.device
+    _need(hidden, "hidden"); _need(W1, "W1", hidden.dtype, None, dev)
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(tokens, "tokens", torch.int32, (B, gamma), dev)
+    _need(w, "w", torch.float32, (H + rank,), dev)
+    conf = _out(conf, "conf", torch.float32, (B, gamma), dev)
+    status = _status(status, dev)
     _check(lib.dspark_confidence(B, gamma, H, V, rank, dt, _ptr(hidden), _ptr(W1), _ptr(anchor),
                                  _ptr(tokens), _ptr(w), ctypes.c_float(bias), _ptr(conf),
                                  _ptr(status), _stream()))
@@ -231,13 +259,10 @@ def dspark_schedule(conf, sps, *, ell=None, order=None, stats=None, status=None,
     lib = load()
     R, gamma = conf.shape
     dev = conf.device
-    _need(conf, "conf", torch.float32); _need(sps, "sps", torch.float64)
-    ell = ell if ell is not None else torch.empty((R,), dtype=torch.int32, device=dev)
-    if order is None and want_order:
-        order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
-    stats = stats if stats is not None else torch.empty((3,), dtype=torch.float64, device=dev)
-    need = dspark_schedule_workspace(R, gamma)
-    ws = _workspace(need, dev, workspace) if need else None
+    _need(sps, "sps", torch.float64, None, conf.device)
+    R, gamma, ell, order, stats, ws = _schedule_outputs(conf, ell, order, stats, want_order,
+                                                        workspace)
+    status = _status(status, dev)
     _check(lib.dspark_schedule(R, gamma, _ptr(conf), _ptr(sps), int(sps.numel()), _ptr(ell),
                                _ptr(order), _ptr(stats), _ptr(status), _ptr(ws),
                                0 if ws is None else ws.numel(), _stream()))
@@ -248,10 +273,10 @@ def _schedule_outputs(conf, ell, order, stats, want_order, workspace=None):
     R, gamma = conf.shape
     dev = conf.device
     _need(conf, "conf", torch.float32)
-    ell = ell if ell is not None else torch.empty((R,), dtype=torch.int32, device=dev)
-    if order is None and want_order:
-        order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
-    stats = stats if stats is not None else torch.empty((3,), dtype=torch.float64, device=dev)
+    ell = _out(ell, "ell", torch.int32, (R,), dev)
+    if order is not None or want_order:
+        order = _out(order, "order", torch.int32, (R * gamma,), dev)
+    stats = _out(stats, "stats", torch.float64, (3,), dev)
     need = dspark_schedule_workspace(R, gamma)
     ws = _workspace(need, dev, workspace) if need else None
     return R, gamma, ell, order, stats, ws
@@ -264,6 +289,7 @@ def dspark_schedule_capacity(conf, capacity, *, ell=None, order=None, stats=None
     lib = load()
     R, gamma, ell, order, stats, ws = _schedule_outputs(conf, ell, order, stats, want_order,
                                                         workspace)
+    status = _status(status, conf.device)
     if not (isinstance(capacity, torch.Tensor) and capacity.dtype == torch.float64
             and capacity.device == conf.device and capacity.numel() >= 1):
         raise DsparkError(-1, "capacity must be a float64 tensor on the device of conf")
@@ -279,13 +305,14 @@ def dspark_schedule_threshold(conf, threshold, *, ell=None, order=None, stats=No
     lib = load()
     R, gamma, ell, order, stats, ws = _schedule_outputs(conf, ell, order, stats, want_order,
                                                         workspace)
+    status = _status(status, conf.device)
     _check(lib.dspark_schedule_threshold(R, gamma, _ptr(conf), ctypes.c_double(threshold),
                                          _ptr(ell), _ptr(order), _ptr(stats), _ptr(status),
                                          _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
     return ell, order, stats
 
 
-def dspark_verify(target, U, W1, W2t, anchor, tokens, q_tok, row_max, row_logZ, temperature,
+def dspark_verify(target, U, W1, W2, anchor, tokens, q_tok, row_max, row_logZ, temperature,
                   uniforms, ell, *, out_tokens=None, n_accepted=None, ratio=None, status=None,
                   workspace=None, want_ratio=True):
     """Lossless verification; returns (out_tokens [B,gamma+1], n_accepted [B], ratio [B,gamma])."""
@@ -294,20 +321,25 @@ def dspark_verify(target, U, W1, W2t, anchor, tokens, q_tok, row_max, row_logZ, 
     rank = W1.shape[1]
     dt = _dtype_code(U)
     dev = U.device
-    _need(target, "target", U.dtype, (B, gamma + 1, V)); _need(U, "U")
-    _need(W1, "W1", U.dtype, (V, rank)); _need(W2t, "W2t", U.dtype, (V, rank))
-    for name, t, dtp in (("anchor", anchor, torch.int32), ("tokens", tokens, torch.int32),
-                         ("q_tok", q_tok, torch.float32), ("row_max", row_max, torch.float32),
-                         ("row_logZ", row_logZ, torch.float32), ("temperature", temperature, torch.float32),
-                         ("uniforms", uniforms, torch.float32), ("ell", ell, torch.int32)):
-        _need(t, name, dtp)
-    out_tokens = out_tokens if out_tokens is not None else torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
-    n_accepted = n_accepted if n_accepted is not None else torch.empty((B,), dtype=torch.int32, device=dev)
-    if ratio is None and want_ratio:
-        ratio = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    _need(U, "U"); _need(target, "target", U.dtype, (B, gamma + 1, V), dev)
+    _need(W1, "W1", U.dtype, (V, rank), dev); _need(W2, "W2", U.dtype, (rank, V), dev)
+    for name, t, dtp, shp in (
+            ("anchor", anchor, torch.int32, (B,)), ("tokens", tokens, torch.int32, (B, gamma)),
+            ("q_tok", q_tok, torch.float32, (B, gamma)),
+            ("row_max", row_max, torch.float32, (B, gamma)),
+            ("row_logZ", row_logZ, torch.float32, (B, gamma)),
+            ("temperature", temperature, torch.float32, (B,)),
+            ("uniforms", uniforms, torch.float32, (B, gamma + 1, 2)),
+            ("ell", ell, torch.int32, (B,))):
+        _need(t, name, dtp, shp, dev)
+    out_tokens = _out(out_tokens, "out_tokens", torch.int32, (B, gamma + 1), dev)
+    n_accepted = _out(n_accepted, "n_accepted", torch.int32, (B,), dev)
+    if ratio is not None or want_ratio:
+        ratio = _out(ratio, "ratio", torch.float32, (B, gamma), dev)
+    status = _status(status, dev)
     need = dspark_verify_workspace(B, gamma, V, rank, dt)
     ws = _workspace(need, dev, workspace)
-    _check(lib.dspark_verify(B, gamma, V, rank, dt, _ptr(target), _ptr(U), _ptr(W1), _ptr(W2t),
+    _check(lib.dspark_verify(B, gamma, V, rank, dt, _ptr(target), _ptr(U), _ptr(W1), _ptr(W2),
                              _ptr(anchor), _ptr(tokens), _ptr(q_tok), _ptr(row_max), _ptr(row_logZ),
                              _ptr(temperature), _ptr(uniforms), _ptr(ell), _ptr(out_tokens),
                              _ptr(n_accepted), _ptr(ratio), _ptr(status), _ptr(ws), ws.numel(),
@@ -319,7 +351,7 @@ def dspark_tv_label_workspace(B, gamma, V, rank, dtype) -> int:
     return int(load().dspark_tv_label_workspace(B, gamma, V, rank, dtype))
 
 
-def dspark_tv_label(target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature, *,
+def dspark_tv_label(target, U, W1, W2, anchor, tokens, row_max, row_logZ, temperature, *,
                     tv=None, label=None, status=None, workspace=None, want_label=True):
     """Acceptance label 1 - TV(draft, target) per drafted position; returns (tv, label)."""
     lib = load()
@@ -327,18 +359,21 @@ def dspark_tv_label(target, U, W1, W2t, anchor, tokens, row_max, row_logZ, tempe
     rank = W1.shape[1]
     dt = _dtype_code(U)
     dev = U.device
-    _need(target, "target", U.dtype, (B, gamma + 1, V)); _need(U, "U")
-    _need(W1, "W1", U.dtype, (V, rank)); _need(W2t, "W2t", U.dtype, (V, rank))
-    for name, t, dtp in (("anchor", anchor, torch.int32), ("tokens", tokens, torch.int32),
-                         ("row_max", row_max, torch.float32), ("row_logZ", row_logZ, torch.float32),
-                         ("temperature", temperature, torch.float32)):
-        _need(t, name, dtp)
-    tv = tv if tv is not None else torch.empty((B, gamma), dtype=torch.float32, device=dev)
-    if label is None and want_label:
-        label = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    _need(U, "U"); _need(target, "target", U.dtype, (B, gamma + 1, V), dev)
+    _need(W1, "W1", U.dtype, (V, rank), dev); _need(W2, "W2", U.dtype, (rank, V), dev)
+    for name, t, dtp, shp in (
+            ("anchor", anchor, torch.int32, (B,)), ("tokens", tokens, torch.int32, (B, gamma)),
+            ("row_max", row_max, torch.float32, (B, gamma)),
+            ("row_logZ", row_logZ, torch.float32, (B, gamma)),
+            ("temperature", temperature, torch.float32, (B,))):
+        _need(t, name, dtp, shp, dev)
+    tv = _out(tv, "tv", torch.float32, (B, gamma), dev)
+    if label is not None or want_label:
+        label = _out(label, "label", torch.float32, (B, gamma), dev)
+    status = _status(status, dev)
     need = dspark_tv_label_workspace(B, gamma, V, rank, dt)
     ws = _workspace(need, dev, workspace)
-    _check(lib.dspark_tv_label(B, gamma, V, rank, dt, _ptr(target), _ptr(U), _ptr(W1), _ptr(W2t),
+    _check(lib.dspark_tv_label(B, gamma, V, rank, dt, _ptr(target), _ptr(U), _ptr(W1), _ptr(W2),
                                _ptr(anchor), _ptr(tokens), _ptr(row_max), _ptr(row_logZ),
                                _ptr(temperature), _ptr(tv), _ptr(label), _ptr(status), _ptr(ws),
                                ws.numel(), _stream()))

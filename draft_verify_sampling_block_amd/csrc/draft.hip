@@ -8,7 +8,7 @@
 //
 //  * persistent (bf16, rank <= 256, one work-group per compute unit, launched
 //    cooperatively so all work-groups are resident): each work-group owns a
-//    fixed set of 64-entry vocabulary tiles for the whole block; the W2t
+//    fixed set of 64-entry vocabulary tiles for the whole block; the W2
 //    rows of those tiles stay resident (8 tiles in registers, one per wave,
 //    the rest in LDS) across all gamma positions, so W2 is read from memory
 //    once per call.  Per position: gather the W1 rows of the previous
@@ -120,7 +120,7 @@ struct SampShared {
   __attribute__((aligned(16))) char arow[kMaxKSteps * 32];  // W1 row of the request (bf16)
   __attribute__((aligned(16))) char useg[kTileV * 4];        // base logits of the crossing tile
 };
-// LDS the sampler needs besides SampShared: the crossing tile's W2t rows,
+// LDS the sampler needs besides SampShared: the crossing tile's W2 rows,
 // then a copy of the request's tile statistics
 constexpr int kSampScratchBytes = kLdsTileBytes + 2 * kMaxTiles * 4;
 
@@ -130,7 +130,7 @@ constexpr int kSampScratchBytes = kLdsTileBytes + 2 * kMaxTiles * 4;
 template <typename T, int KS, int NTHR>
 __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, int prev,
                                const T* __restrict__ U, const T* __restrict__ W1,
-                               const T* __restrict__ W2t, const float* __restrict__ temperature,
+                               const T* __restrict__ W2, const float* __restrict__ temperature,
                                const float* __restrict__ uniforms, const TileStats& ts,
                                int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
                                int32_t* status, char* scratch, SampShared& sh,
@@ -242,36 +242,32 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
   const bool mine = tid < kWave && c == mrow;
   const int rem = V - (v0 + 16 * h);   // usable entries: j < rem - 32t
   if constexpr (kIsBf16<T>) {
-    // tile rows, the request's W1 row and base logits of the tile: all by DMA
-    stage_tile(W2t, v0, V, rank, scratch);
+    // the request's W1 row and base logits of the tile by DMA, the tile's
+    // transposed W2 image by every thread; waves 0 and 1 then recompute
+    // sub-tiles 0 and 1
     dma_copy<false>(W1 + (size_t)prev * rank, sh.arow, rank / 8);
     dma_copy<false>(U + out * V + v0, sh.useg, min(kTileV, V - v0) / 8);
+    stage_tile(W2, v0, V, rank, scratch);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const uint16_t* useg = reinterpret_cast<const uint16_t*>(sh.useg) + 16 * h;
-    if (tid < kWave) {
+    if (tid < kSub * kWave) {
+      const int t = tid >> 6;
+      const bool own = c == mrow;
+      const uint16_t* useg = reinterpret_cast<const uint16_t*>(sh.useg) + 32 * t + 16 * h;
       const bf16x8_t zero = bf16x8_t{};
       auto bfrag = [&](int ks) {
         const bf16x8_t f = *reinterpret_cast<const bf16x8_t*>(sh.arow + 16 * (2 * ks + h));
-        return mine ? f : zero;
+        return own ? f : zero;
       };
-      // both sub-tiles' chains interleaved, operands double-buffered: the
-      // same instruction sequence per accumulator as the statistics pass
-      f32x16_t acc[kSub];
+      f32x16_t acc;
 #pragma unroll
-      for (int t = 0; t < kSub; ++t) {
+      for (int j = 0; j < 16; ++j)
+        acc[j] = (32 * t + j < rem) ? bf16_to_f32(useg[j]) : -INFINITY;
+      bias_subtile_ldsA<KS>(bfrag, scratch, t, acc);
+      if (own) {
+        float* se = sh.se + 32 * t + 16 * h;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          acc[t][j] = (32 * t + j < rem) ? bf16_to_f32(useg[32 * t + j]) : -INFINITY;
-      }
-      bias_tile_ldsA<KS>(bfrag, scratch, acc);
-      if (mine) {
-#pragma unroll
-        for (int t = 0; t < kSub; ++t) {
-          float* se = sh.se + 32 * t + 16 * h;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) se[j] = tile_term(acc[t][j], ce, mc);
-        }
+        for (int j = 0; j < 16; ++j) se[j] = tile_term(acc[j], ce, mc);
       }
     }
   } else {
@@ -281,7 +277,7 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
       f32x16_t acc[kSub];
       init_acc<T>(ur, rem, acc);
       bias_tile_f32(reinterpret_cast<const float*>(W1), mine ? prev : -1,
-                    reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
+                    reinterpret_cast<const float*>(W2), v0, V, rank, acc);
       if (mine) {
 #pragma unroll
         for (int t = 0; t < kSub; ++t) {
@@ -321,7 +317,7 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void draft_stats_kernel(
     int B, int gamma, int V, int rank, int k, const T* __restrict__ U, const T* __restrict__ W1,
-    const T* __restrict__ W2t, const int32_t* __restrict__ prev_src, int prev_stride,
+    const T* __restrict__ W2, const int32_t* __restrict__ prev_src, int prev_stride,
     const float* __restrict__ temperature, TileStats ts, int32_t* status) {
   __shared__ __attribute__((aligned(16))) char w2s[kIsBf16<T> ? kLdsTileBytes : 16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -330,7 +326,7 @@ __global__ __launch_bounds__(256) void draft_stats_kernel(
   const int nT = n_tiles(V);
   const int vt = blockIdx.x, v0 = vt * kTileV;
 
-  if constexpr (kIsBf16<T>) stage_tile(W2t, v0, V, rank, w2s);
+  if constexpr (kIsBf16<T>) stage_tile(W2, v0, V, rank, w2s);
   int rb = wave;
   bf16x8_t bfrag[KS];
   URow<T> ur;
@@ -357,7 +353,7 @@ __global__ __launch_bounds__(256) void draft_stats_kernel(
     if constexpr (kIsBf16<T>)
       bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
     else
-      bias_tile_f32(reinterpret_cast<const float*>(W1), tok, reinterpret_cast<const float*>(W2t),
+      bias_tile_f32(reinterpret_cast<const float*>(W1), tok, reinterpret_cast<const float*>(W2),
                     v0, V, rank, acc);
     const int b = rb * kTileM + c;
     const bool any_greedy = __ballot((b < B) && !(it > 0.f)) != 0;
@@ -371,7 +367,7 @@ __global__ __launch_bounds__(256) void draft_stats_kernel(
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void draft_sample_kernel(
     int B, int gamma, int V, int rank, int k, const T* __restrict__ U, const T* __restrict__ W1,
-    const T* __restrict__ W2t, const int32_t* __restrict__ prev_src, int prev_stride,
+    const T* __restrict__ W2, const int32_t* __restrict__ prev_src, int prev_stride,
     const float* __restrict__ temperature, const float* __restrict__ uniforms, TileStats ts,
     int32_t* __restrict__ tokens, float* __restrict__ q_tok, float* __restrict__ row_max,
     float* __restrict__ row_logZ, int32_t* status) {
@@ -379,7 +375,7 @@ __global__ __launch_bounds__(256) void draft_sample_kernel(
   __shared__ SampShared sh;
   const int b = blockIdx.x;
   const int prev = clamp_token(prev_src[(size_t)b * prev_stride], V, nullptr);
-  sample_request<T, KS, 256>(b, k, B, gamma, V, rank, prev, U, W1, W2t, temperature, uniforms,
+  sample_request<T, KS, 256>(b, k, B, gamma, V, rank, prev, U, W1, W2, temperature, uniforms,
                              ts, tokens, q_tok, row_max, row_logZ, status, scratch, sh, nullptr);
 }
 
@@ -399,7 +395,7 @@ struct PdArgs {
   int B, gamma, V, rank, P;
   const uint16_t* U;
   const uint16_t* W1;
-  const uint16_t* W2t;
+  const uint16_t* W2;
   const int32_t* anchor;
   const float* temperature;
   const float* uniforms;
@@ -458,7 +454,7 @@ __device__ inline void stores_done_group() {
   __syncthreads();
 }
 
-// NW waves per group; each wave holds R = kPdRegTiles / NW W2t tiles in
+// NW waves per group; each wave holds R = kPdRegTiles / NW W2 tiles in
 // registers (NW = 8: two waves per SIMD, 128 registers of tile each at rank
 // 256; NW = 4: one wave per SIMD with two tiles, the tiles and the
 // accumulators split over the architectural and accumulation registers).
@@ -489,7 +485,7 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
   const int B = a.B, V = a.V, gamma = a.gamma;
   const int nT = n_tiles(V);
 
-  // Resident W2t tiles: group p owns the contiguous tiles [tbase, tbase +
+  // Resident W2 tiles: group p owns the contiguous tiles [tbase, tbase +
   // tcount) (the first nT % P groups one more), so that its statistics of a
   // request form one contiguous run.  Tile slot s is tile tbase + s:
   // register tile i of wave w is slot w + NW i, LDS tile i slot
@@ -497,18 +493,67 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
   const int tcount = nT / P + (p < nT % P ? 1 : 0);
   const int tbase = p * (nT / P) + min(p, nT % P);
   auto slot_tile = [&](int slot) { return slot < tcount ? tbase + slot : nT; };  // nT: none
-  bf16x8_t wreg[R][KS][kSub];
+  // W2 is [rank, V]: every resident tile passes through its transposed LDS
+  // image.  The blocks of the eight register tiles are loaded in one shot;
+  // they pass four at a time through the four image areas (the two LDS tile
+  // areas and the W1 row area), the LDS tiles' blocks loading while the
+  // first four images are read; then the LDS tiles are staged in place.
+  // Blocks of slots without a tile load (clamped, in-bounds) addresses and
+  // are never stored.
+  static_assert(kPdRowBytes >= 2 * kLdsTileBytes && kPdRegTiles == 8 && kPdLdsTiles == 2,
+                "four tile images at a time");
+  auto img = [&](int j) {   // image area j of 4
+    return j < 2 ? ldsL + j * kLdsTileBytes : ldsA + (j - 2) * kLdsTileBytes;
+  };
+  const int nbk = w2_blocks(a.rank);
+  const int nthr = NW * 64;
+  // block threadIdx.x + nthr q of slot s, for every q with a block there
+  constexpr int kQ = (32 * KS + NW * 64 - 1) / (NW * 64);   // blocks per slot (rank 16 KS)
+  auto load_slot = [&](int sl, W2Block (&bk)[kQ]) {
+    const int tl = min(slot_tile(sl), nT - 1);
 #pragma unroll
-  for (int i = 0; i < R; ++i) load_wreg<KS>(a.W2t, slot_tile(wave + NW * i), V, wreg[i]);
-  int nL = 0;
-  for (int i = 0; i < kPdLdsTiles; ++i) {
-    const int tl = slot_tile(kPdRegTiles + i);
-    if (tl < nT) {
-      stage_tile(a.W2t, tl * kTileV, V, a.rank, ldsL + i * kLdsTileBytes);
-      ++nL;
+    for (int q = 0; q < kQ; ++q)
+      w2_block_load(a.W2, V, tl * kTileV, min((int)threadIdx.x + nthr * q, nbk - 1), bk[q]);
+  };
+  auto store_slot = [&](int sl, const W2Block (&bk)[kQ], char* dst) {
+    if (slot_tile(sl) < nT) {
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int sb = (int)threadIdx.x + nthr * q;
+        if (sb < nbk) w2_block_store(bk[q], sb, dst, 2 * KS);
+      }
     }
+  };
+  auto read_round = [&](int s0, bf16x8_t (&wr)[R][KS][kSub]) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int sl = wave + NW * i;
+      if (sl >= s0 && sl < s0 + 4) wreg_from_lds<KS>(img(sl - s0), wr[i]);
+    }
+  };
+  bf16x8_t wreg[R][KS][kSub];
+  {
+    W2Block blk[kPdRegTiles][kQ];
+#pragma unroll
+    for (int j = 0; j < kPdRegTiles; ++j) load_slot(j, blk[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) store_slot(j, blk[j], img(j));
+    __syncthreads();
+    W2Block lblk[kPdLdsTiles][kQ];
+#pragma unroll
+    for (int j = 0; j < kPdLdsTiles; ++j) load_slot(kPdRegTiles + j, lblk[j]);
+    read_round(0, wreg);
+    __syncthreads();
+#pragma unroll
+    for (int j = 4; j < 8; ++j) store_slot(j, blk[j], img(j - 4));
+    __syncthreads();
+    read_round(4, wreg);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPdLdsTiles; ++j) store_slot(kPdRegTiles + j, lblk[j], img(j));
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  int nL = 0;
+  for (int i = 0; i < kPdLdsTiles; ++i) nL += slot_tile(kPdRegTiles + i) < nT ? 1 : 0;
   __syncthreads();
 
   // Block-tasks of this wave for one position, in order: per chunk of up to
@@ -532,7 +577,7 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
   };
   // A ring of D prefetched tasks: base logits (they do not depend on the
   // drafted tokens, so the first ones of a position are requested before
-  // its tokens are known) and the task's tile / block / W2t location
+  // its tokens are known) and the task's tile / block / W2 location
   // (which: -1 - i = register tile i, >= 0 = LDS tile).  One slot ahead is
   // enough at two waves per SIMD; one wave per SIMD keeps two.
   constexpr int D = NW >= 8 ? 1 : 2;
@@ -569,7 +614,7 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
 #pragma unroll
         for (int q = 0; q < URow<uint16_t>::kLoads; ++q)   // four distinct 16-byte words
           sl.u.w[t][q] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4_t*>(a.W2t) + t * URow<uint16_t>::kLoads + q);
+              reinterpret_cast<const u32x4_t*>(a.W2) + t * URow<uint16_t>::kLoads + q);
       }
       return;
     }
@@ -793,7 +838,7 @@ __global__ __launch_bounds__(NW * 64, 1) void pdraft_kernel(PdArgs a) {
       }
       const int prev = clamp_token(
           k == 0 ? a.anchor[b] : (int)(ld_dev(a.tok_flag + b) & 0xFFFFFFu), V, nullptr);
-      sample_request<uint16_t, KS, NW * 64>(b, k, B, gamma, V, a.rank, prev, a.U, a.W1, a.W2t,
+      sample_request<uint16_t, KS, NW * 64>(b, k, B, gamma, V, a.rank, prev, a.U, a.W1, a.W2,
                                             a.temperature, a.uniforms, a.ts, a.tokens, a.q_tok,
                                             a.row_max, a.row_logZ, a.status, ldsA, sh,
                                             a.tok_flag);
@@ -862,7 +907,7 @@ static TileStats carve_stats(void* ws, int B, int V) {
 
 template <typename T, int KS>
 static hipError_t draft_multi(int B, int gamma, int V, int rank, const T* U, const T* W1,
-                              const T* W2t, const int32_t* anchor, const float* temperature,
+                              const T* W2, const int32_t* anchor, const float* temperature,
                               const float* uniforms, int32_t* tokens, float* q_tok,
                               float* row_max, float* row_logZ, int32_t* status, void* ws,
                               hipStream_t stream) {
@@ -874,10 +919,10 @@ static hipError_t draft_multi(int B, int gamma, int V, int rank, const T* U, con
     {
       TraceScope t("draft_stats_kernel", stream);
       draft_stats_kernel<T, KS><<<dim3((unsigned)n_tiles(V)), blk, 0, stream>>>(
-          B, gamma, V, rank, k, U, W1, W2t, prev, stride, temperature, ts, status);
+          B, gamma, V, rank, k, U, W1, W2, prev, stride, temperature, ts, status);
     }
     TraceScope t("draft_sample_kernel", stream);
-    draft_sample_kernel<T, KS><<<dim3(B), blk, 0, stream>>>(B, gamma, V, rank, k, U, W1, W2t,
+    draft_sample_kernel<T, KS><<<dim3(B), blk, 0, stream>>>(B, gamma, V, rank, k, U, W1, W2,
                                                            prev, stride, temperature, uniforms,
                                                            ts, tokens, q_tok, row_max, row_logZ,
                                                            status);
@@ -888,7 +933,7 @@ static hipError_t draft_multi(int B, int gamma, int V, int rank, const T* U, con
 // Returns hipErrorNotSupported when the persistent kernel cannot run here.
 template <int KS>
 static hipError_t draft_persistent(int B, int gamma, int V, int rank, const uint16_t* U,
-                                   const uint16_t* W1, const uint16_t* W2t,
+                                   const uint16_t* W1, const uint16_t* W2,
                                    const int32_t* anchor, const float* temperature,
                                    const float* uniforms, int32_t* tokens, float* q_tok,
                                    float* row_max, float* row_logZ, int32_t* status, void* ws,
@@ -910,7 +955,7 @@ static hipError_t draft_persistent(int B, int gamma, int V, int rank, const uint
     return hipErrorNotSupported;
   PdArgs a;
   a.B = B; a.gamma = gamma; a.V = V; a.rank = rank; a.P = P;
-  a.U = U; a.W1 = W1; a.W2t = W2t; a.anchor = anchor; a.temperature = temperature;
+  a.U = U; a.W1 = W1; a.W2 = W2; a.anchor = anchor; a.temperature = temperature;
   a.uniforms = uniforms; a.tokens = tokens; a.q_tok = q_tok; a.row_max = row_max;
   a.row_logZ = row_logZ; a.status = status;
   a.ts = carve_stats(ws, B, V);
@@ -931,14 +976,14 @@ static hipError_t draft_persistent(int B, int gamma, int V, int rank, const uint
 }
 
 hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U,
-                              const void* W1, const void* W2t, const int32_t* anchor,
+                              const void* W1, const void* W2, const int32_t* anchor,
                               const float* temperature, const float* uniforms, int32_t* tokens,
                               float* q_tok, float* row_max, float* row_logZ, int32_t* status,
                               void* ws, hipStream_t stream) {
   if (dtype == DSPARK_BF16) {
     auto* u = static_cast<const uint16_t*>(U);
     auto* w1 = static_cast<const uint16_t*>(W1);
-    auto* w2 = static_cast<const uint16_t*>(W2t);
+    auto* w2 = static_cast<const uint16_t*>(W2);
 #define DSPARK_DRAFT_KS(KS)                                                                     \
   {                                                                                             \
     if (g_draft_path != 1) {                                                                    \
@@ -960,7 +1005,7 @@ hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, cons
 #undef DSPARK_DRAFT_KS
   }
   return draft_multi<float, 1>(B, gamma, V, rank, static_cast<const float*>(U),
-                               static_cast<const float*>(W1), static_cast<const float*>(W2t),
+                               static_cast<const float*>(W1), static_cast<const float*>(W2),
                                anchor, temperature, uniforms, tokens, q_tok, row_max, row_logZ,
                                status, ws, stream);
 }

@@ -93,14 +93,14 @@ size_t dspark_draft_block_workspace(int B, int gamma, int V, int rank, int dtype
 }
 
 int dspark_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U, const void* W1,
-                       const void* W2t, const int32_t* anchor, const float* temperature,
+                       const void* W2, const int32_t* anchor, const float* temperature,
                        const float* uniforms, int32_t* tokens, float* q_tok, float* row_max,
                        float* row_logZ, int32_t* status, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
   const char* fn = "dspark_draft_block";
   int rc = check_dims(fn, B, gamma, V, rank, dtype);
   if (rc) return rc;
-  REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2t); REQUIRE_PTR(anchor);
+  REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2); REQUIRE_PTR(anchor);
   REQUIRE_PTR(temperature); REQUIRE_PTR(uniforms); REQUIRE_PTR(tokens); REQUIRE_PTR(q_tok);
   REQUIRE_PTR(row_max); REQUIRE_PTR(row_logZ); OPT_PTR(status);
   const size_t need = dspark::draft_workspace_bytes(B, gamma, V, rank, dtype);
@@ -108,7 +108,7 @@ int dspark_draft_block(int B, int gamma, int V, int rank, int dtype, const void*
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
-  return hip_status(fn, dspark::launch_draft_block(B, gamma, V, rank, dtype, U, W1, W2t, anchor,
+  return hip_status(fn, dspark::launch_draft_block(B, gamma, V, rank, dtype, U, W1, W2, anchor,
                                                    temperature, uniforms, tokens, q_tok, row_max,
                                                    row_logZ, status, workspace, stream));
 }
@@ -199,7 +199,7 @@ size_t dspark_verify_workspace(int B, int gamma, int V, int rank, int dtype) {
 }
 
 int dspark_verify(int B, int gamma, int V, int rank, int dtype, const void* target, const void* U,
-                  const void* W1, const void* W2t, const int32_t* anchor, const int32_t* tokens,
+                  const void* W1, const void* W2, const int32_t* anchor, const int32_t* tokens,
                   const float* q_tok, const float* row_max, const float* row_logZ,
                   const float* temperature, const float* uniforms, const int32_t* ell,
                   int32_t* out_tokens, int32_t* n_accepted, float* ratio, int32_t* status,
@@ -207,7 +207,7 @@ int dspark_verify(int B, int gamma, int V, int rank, int dtype, const void* targ
   const char* fn = "dspark_verify";
   int rc = check_dims(fn, B, gamma, V, rank, dtype);
   if (rc) return rc;
-  REQUIRE_PTR(target); REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2t); REQUIRE_PTR(anchor);
+  REQUIRE_PTR(target); REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2); REQUIRE_PTR(anchor);
   REQUIRE_PTR(tokens); REQUIRE_PTR(q_tok); REQUIRE_PTR(row_max); REQUIRE_PTR(row_logZ);
   REQUIRE_PTR(temperature); REQUIRE_PTR(uniforms); REQUIRE_PTR(ell); REQUIRE_PTR(out_tokens);
   REQUIRE_PTR(n_accepted); OPT_PTR(ratio); OPT_PTR(status);
@@ -216,7 +216,7 @@ int dspark_verify(int B, int gamma, int V, int rank, int dtype, const void* targ
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
-  return hip_status(fn, dspark::launch_verify(B, gamma, V, rank, dtype, target, U, W1, W2t, anchor,
+  return hip_status(fn, dspark::launch_verify(B, gamma, V, rank, dtype, target, U, W1, W2, anchor,
                                               tokens, q_tok, row_max, row_logZ, temperature,
                                               uniforms, ell, out_tokens, n_accepted, ratio, status,
                                               workspace, stream));
@@ -230,14 +230,14 @@ size_t dspark_tv_label_workspace(int B, int gamma, int V, int rank, int dtype) {
 }
 
 int dspark_tv_label(int B, int gamma, int V, int rank, int dtype, const void* target,
-                    const void* U, const void* W1, const void* W2t, const int32_t* anchor,
+                    const void* U, const void* W1, const void* W2, const int32_t* anchor,
                     const int32_t* tokens, const float* row_max, const float* row_logZ,
                     const float* temperature, float* tv, float* label, int32_t* status,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "dspark_tv_label";
   int rc = check_dims(fn, B, gamma, V, rank, dtype);
   if (rc) return rc;
-  REQUIRE_PTR(target); REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2t); REQUIRE_PTR(anchor);
+  REQUIRE_PTR(target); REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2); REQUIRE_PTR(anchor);
   REQUIRE_PTR(tokens); REQUIRE_PTR(row_max); REQUIRE_PTR(row_logZ); REQUIRE_PTR(temperature);
   REQUIRE_PTR(tv); OPT_PTR(label); OPT_PTR(status);
   const size_t need = dspark::tv_workspace_bytes(B, gamma, V);
@@ -245,7 +245,7 @@ int dspark_tv_label(int B, int gamma, int V, int rank, int dtype, const void* ta
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
-  return hip_status(fn, dspark::launch_tv_label(B, gamma, V, rank, dtype, target, U, W1, W2t,
+  return hip_status(fn, dspark::launch_tv_label(B, gamma, V, rank, dtype, target, U, W1, W2,
                                                 anchor, tokens, row_max, row_logZ, temperature,
                                                 tv, label, status, workspace, stream));
 }

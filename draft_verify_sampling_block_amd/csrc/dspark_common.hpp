@@ -10,7 +10,7 @@
 //     A: row c,    k = 8h .. 8h+7 of the k-step      (8 bf16 per lane)
 //     B: column c, k = 8h .. 8h+7 of the k-step      (8 bf16 per lane)
 //     D: column c, rows 8*(j/4) + 4h + (j%4) for j = 0..15
-// Rows are vocabulary entries (A = W2t rows, k-contiguous) and columns are
+// Rows are vocabulary entries (A = W2 columns, 8 consecutive k) and columns are
 // requests (B = the W1 rows of the requests' previous tokens).  Matrix row
 // i of sub-tile t stands for vocabulary entry v0 + 32t + sub_row_vocab(i),
 // chosen so that accumulator element j of lane (c, h) is entry
@@ -20,7 +20,8 @@
 // lane's own, and the per-tile reductions run inside the lane with one
 // exchange between the two half-waves.
 //
-// W2t tile rows staged in LDS are stored in matrix-row order (LDS row
+// W2 tiles staged in LDS are stored transposed, k-contiguous per
+// vocabulary entry, in matrix-row order (LDS row
 // 32t + i holds entry v0 + 32t + sub_row_vocab(i)), each row padded by one
 // 16-byte chunk, so that the 16 lanes of each quarter-wave, which read 16
 // consecutive rows at one k-chunk, hit 16 distinct bank groups.  The per-tile statistics (max, lowest argmax, sum of exp(y - max))
@@ -196,7 +197,7 @@ __host__ __device__ inline int sub_row_vocab(int i) {
 __host__ __device__ inline int tile_row_vocab(int r) { return (r & 32) + sub_row_vocab(r & 31); }
 
 // ---------------------------------------------------------------------------
-// Rows of rank bf16 in LDS (W2t tile rows, or gathered W1 rows): nq = rank/8
+// Rows of rank bf16 in LDS (transposed W2 tiles, or gathered W1 rows): nq = rank/8
 // chunks of 16 bytes per row plus one pad chunk, so a row takes nq + 1
 // chunks.  nq + 1 is odd, so 16 consecutive rows read at one chunk land in
 // 16 distinct 16-byte bank groups, and chunk q of row r sits at the fixed
@@ -226,15 +227,106 @@ __device__ inline void stage_rows_lds(const uint16_t* __restrict__ src, int rank
   }
 }
 
-// The 64 rows of W2t tile v0 in matrix-row order: LDS row r <- W2t row
-// v0 + tile_row_vocab(r), clamped to V - 1 (rows past V are never used:
-// their logits start at -inf).
-__device__ inline void stage_tile(const uint16_t* __restrict__ W2t, int v0, int V, int rank,
+// Matrix row of the tile (the inverse of tile_row_vocab): vocabulary offset
+// o in [0, 64) sits in tile row (o & 32) + 8 ((o >> 2) & 3) + 4 ((o >> 4) & 1)
+// + (o & 3).
+__host__ __device__ inline int tile_vocab_row(int o) {
+  return (o & 32) | (((o >> 2) & 3) << 3) | (((o >> 4) & 1) << 2) | (o & 3);
+}
+
+// ---------------------------------------------------------------------------
+// W2 is stored [rank, V]: row k holds coordinate k's weights over the whole
+// vocabulary, so the 64 entries of one tile at one k are 128 contiguous
+// bytes.  The matrix-core operand wants 8 consecutive k of ONE entry per
+// lane, so a tile is transposed on its way into LDS: a thread loads a block
+// of 4 k-rows x 8 entries (four 16-byte loads) and writes it as eight 8-byte
+// k-runs, one per entry, into the padded k-contiguous image that the LDS
+// operand readers use (LDS row r = entry v0 + tile_row_vocab(r); chunk q =
+// k 8q .. 8q + 7).  A tile has (rank / 4) x 8 blocks.
+// ---------------------------------------------------------------------------
+struct W2Block {
+  u32x4_t r[4];   // r[i] = W2[4 kb + i][v0 + 8 vb .. + 8)
+};
+__host__ __device__ inline int w2_blocks(int rank) { return (rank >> 2) * 8; }
+// block s: kb = s / 8, vb = s % 8; a block past V reads entries V-8 .. V-1
+// instead (any valid address: rows past V start at -inf, so their bias is
+// never used).  V % 8 == 0 keeps a block wholly inside or outside the row.
+__device__ inline void w2_block_load(const uint16_t* __restrict__ W2, int V, int v0, int s,
+                                     W2Block& blk) {
+  const int kb = s >> 3, vb = s & 7;
+  const int v = min(v0 + 8 * vb, V - 8);
+  const uint16_t* p = W2 + (size_t)(4 * kb) * V + v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    blk.r[i] = *reinterpret_cast<const u32x4_t*>(p + (size_t)i * V);
+}
+__device__ inline void w2_block_store(const W2Block& blk, int s, char* lds, int nq) {
+  const int kb = s >> 3, vb = s & 7;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = j >> 1;
+    uint32_t lo, hi;   // (k0, k1) and (k2, k3) of entry 8 vb + j
+    if (j & 1) {
+      lo = (blk.r[0][m] >> 16) | (blk.r[1][m] & 0xFFFF0000u);
+      hi = (blk.r[2][m] >> 16) | (blk.r[3][m] & 0xFFFF0000u);
+    } else {
+      lo = (blk.r[0][m] & 0xFFFFu) | (blk.r[1][m] << 16);
+      hi = (blk.r[2][m] & 0xFFFFu) | (blk.r[3][m] << 16);
+    }
+    const int r = tile_vocab_row(8 * vb + j);
+    *reinterpret_cast<u32x2_t*>(lds + r * lds_row_bytes(nq) + kb * 8) = u32x2_t{lo, hi};
+  }
+}
+
+// The padded k-contiguous LDS image of W2 tile v0 (see above), written by
+// every thread of the work-group (loads, then LDS stores).  Completion:
+// barrier by the caller.
+__device__ inline void stage_tile(const uint16_t* __restrict__ W2, int v0, int V, int rank,
                                   char* lds) {
-  stage_rows_lds(W2t, rank, lds, kTileV, [&](int r) {
-    const int v = v0 + tile_row_vocab(r);
-    return v < V ? v : V - 1;
-  });
+  const int nq = rank >> 3, nb = w2_blocks(rank);
+  for (int s = threadIdx.x; s < nb; s += blockDim.x) {
+    W2Block blk;
+    w2_block_load(W2, V, v0, s, blk);
+    w2_block_store(blk, s, lds, nq);
+  }
+}
+
+// Raw W2 rows of ONE tile in LDS, for the single-tile recomputes of the
+// samplers: k-row k (the tile's 64 entries, 128 bytes) at byte
+// raw_off(k) = 128 k + 16 (k / 8).  The rows arrive by DMA, eight per
+// instruction (each 1 KB run followed by a 16-byte gap, so that rows k and
+// k + 8, read together by the two half-waves, fall on different banks); the
+// matrix operand is then gathered from them 16 bits at a time.
+constexpr int kRawTileBytes = kMaxKSteps * 16 * 128 + kMaxKSteps * 2 * 16;   // rank 256
+__host__ __device__ inline int raw_off(int k) { return 128 * k + 16 * (k >> 3); }
+// DMA of tile v0's rows (rank multiple of 8); every wave of the group takes
+// part.  Completion: s_waitcnt + barrier by the caller.
+__device__ inline void dma_tile_raw(const uint16_t* __restrict__ W2, int V, int v0, int rank,
+                                    char* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  for (int g = wave; g < rank / 8; g += nwaves) {   // rows 8g .. 8g + 7
+    const int s = g * 64 + lane;
+    const int k = s >> 3, pc = s & 7;
+    const int v = min(v0 + 8 * pc, V - 8);           // pieces past V: any valid address
+    __builtin_amdgcn_global_load_lds(W2 + (size_t)k * V + v, lds + g * (1024 + 16), 16, 0, 0);
+  }
+}
+// This lane's A operand of sub-tile t, k-step ks, from the raw rows: the
+// 8 consecutive k of entry 32 t + sub_row_vocab(c) (the values the tile
+// images hold, bit for bit).
+__device__ inline bf16x8_t raw_frag(const char* lds, int t, int ks) {
+  const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
+  const int k0 = 16 * ks + 8 * h;
+  const char* base = lds + raw_off(k0) + 2 * (32 * t + sub_row_vocab(c));
+  u32x4_t w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = *reinterpret_cast<const uint16_t*>(base + 256 * i);
+    const uint32_t hi = *reinterpret_cast<const uint16_t*>(base + 256 * i + 128);
+    w[i] = lo | (hi << 16);
+  }
+  return __builtin_bit_cast(bf16x8_t, w);
 }
 
 // Gathered rows: LDS row r <- src row ids[r] (ids in LDS or memory).
@@ -264,9 +356,9 @@ __device__ inline bf16x8_t lds_frag(const char* lds, int r, int q, int nq) {
   return *reinterpret_cast<const bf16x8_t*>(lds + lds_off(r, q, nq));
 }
 
-// Markov bias of one block-tile with the W2t tile (A) read from LDS and the
+// Markov bias of one block-tile with the W2 tile (A) read from its LDS image and the
 // request operand (B) given per k-step by `bfrag`, accumulated onto acc:
-//   acc[t][j] += sum_k W2t[v0 + 32t + 16h + j][k] * Wrow_c[k]
+//   acc[t][j] += sum_k W2[k][v0 + 32t + 16h + j] * Wrow_c[k]
 // (k-steps in ascending order) where Wrow_c is the W1 row fed by the lanes
 // of column c.  The callers start acc at the base logits (init_acc), so the
 // result is the biased logit itself.  Each output element depends only on
@@ -314,7 +406,23 @@ __device__ inline void bias_subtile_ldsA(BF&& bfrag, const char* ldsA, int t, f3
   }
 }
 
-// The same contraction with the W2t tile held in registers (see load_wreg).
+// Sub-tile t of the contraction with both operands given per k-step (the
+// instruction chain bias_subtile_ldsA runs; any source of the same operand
+// values gives the same result bit for bit).
+template <int KS, typename AF, typename BF>
+__device__ inline void bias_subtile(AF&& afrag, BF&& bfrag, f32x16_t& acc) {
+  bf16x8_t acur = afrag(0), anext;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) anext = afrag(ks + 1);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur, bfrag(ks), acc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    acur = anext;
+  }
+}
+
+// The same contraction with the W2 tile operands held in registers (see
+// wreg_from_lds).
 template <int KS, typename BF>
 __device__ inline void bias_tile_regA(BF&& bfrag, const bf16x8_t (&wreg)[KS][kSub],
                                       f32x16_t acc[kSub]) {
@@ -330,23 +438,15 @@ __device__ inline void bias_tile_regA(BF&& bfrag, const bf16x8_t (&wreg)[KS][kSu
   }
 }
 
-// This lane's A operand of W2t tile `vt` for every k-step (zeros past V, or
-// for a tile index >= nT).
+// This lane's A operand of a tile for every k-step, read from the tile's
+// LDS image (stage_tile): the operands bias_tile_ldsA reads, bit for bit.
 template <int KS>
-__device__ inline void load_wreg(const uint16_t* __restrict__ W2t, int vt, int V,
-                                 bf16x8_t (&wreg)[KS][kSub]) {
+__device__ inline void wreg_from_lds(const char* img, bf16x8_t (&wreg)[KS][kSub]) {
   const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
-  const bf16x8_t zero = bf16x8_t{};
 #pragma unroll
   for (int t = 0; t < kSub; ++t) {
-    int v = vt * kTileV + 32 * t + sub_row_vocab(c);
-    const bool vok = v < V;
-    v = vok ? v : 0;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8_t f = load_bf16x8(W2t + (size_t)v * (16 * KS) + 16 * ks + 8 * h);
-      wreg[ks][t] = vok ? f : zero;
-    }
+    for (int ks = 0; ks < KS; ++ks) wreg[ks][t] = lds_frag(img, 32 * t + c, 2 * ks + h, 2 * KS);
   }
 }
 
@@ -366,10 +466,11 @@ __device__ inline void load_bfrag(const uint16_t* __restrict__ W1, int tok, bf16
 
 // fp32 inputs: plain FMA dot products (k ascending) in the same layout,
 // accumulated onto acc.  `tok` is the W1 row of this lane's request column
-// (-1 = nothing added).  16-byte loads; the 16 entries' chains of one
-// sub-tile advance together (each still k ascending, one fma per k).
+// (-1 = nothing added).  W2 is [rank, V]: per k the lane's 16 consecutive
+// entries are four 16-byte loads of row k; the 16 entries' chains advance
+// together (each k ascending, one fma per k).
 __device__ inline void bias_tile_f32(const float* __restrict__ W1, int tok,
-                                     const float* __restrict__ W2t, int v0, int V, int rank,
+                                     const float* __restrict__ W2, int v0, int V, int rank,
                                      f32x16_t acc[kSub]) {
   if (tok < 0) return;
   const int h = (threadIdx.x & 63) >> 5;
@@ -377,19 +478,26 @@ __device__ inline void bias_tile_f32(const float* __restrict__ W1, int tok,
 #pragma unroll
   for (int t = 0; t < kSub; ++t) {
     const int vb = v0 + 32 * t + 16 * h;
+    // column of each group of 4 entries; groups past V read column 0 (V % 4
+    // == 0 keeps a group wholly inside or outside): computed, not kept
+    int col[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) col[q] = vb + 4 * q < V ? vb + 4 * q : 0;
     float s[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) s[j] = acc[t][j];
     for (int i = 0; i < rank; i += 4) {
       const f32x4_t a4 = *reinterpret_cast<const f32x4_t*>(arow + i);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int v = vb + j < V ? vb + j : 0;   // rows past V: computed, not kept
-        const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(W2t + (size_t)v * rank + i);
-        s[j] = fmaf(a4.x, b4.x, s[j]);
-        s[j] = fmaf(a4.y, b4.y, s[j]);
-        s[j] = fmaf(a4.z, b4.z, s[j]);
-        s[j] = fmaf(a4.w, b4.w, s[j]);
+      for (int kk = 0; kk < 4; ++kk) {
+        const float* row = W2 + (size_t)(i + kk) * V;
+        const float ak = a4[kk];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(row + col[q]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[4 * q + e] = fmaf(ak, b4[e], s[4 * q + e]);
+        }
       }
     }
 #pragma unroll

@@ -20,7 +20,7 @@ int get_draft_path();
 // compute units of the current device (cached per device)
 int device_cu_count();
 hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U,
-                              const void* W1, const void* W2t, const int32_t* anchor,
+                              const void* W1, const void* W2, const int32_t* anchor,
                               const float* temperature, const float* uniforms, int32_t* tokens,
                               float* q_tok, float* row_max, float* row_logZ, int32_t* status,
                               void* ws, hipStream_t stream);
@@ -36,7 +36,7 @@ size_t schedule_workspace_bytes(int R, int gamma);
 
 size_t verify_workspace_bytes(int B, int gamma, int V, int rank, int dtype);
 hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const void* target,
-                         const void* U, const void* W1, const void* W2t, const int32_t* anchor,
+                         const void* U, const void* W1, const void* W2, const int32_t* anchor,
                          const int32_t* tokens, const float* q_tok, const float* row_max,
                          const float* row_logZ, const float* temperature, const float* uniforms,
                          const int32_t* ell, int32_t* out_tokens, int32_t* n_accepted,

@@ -16,7 +16,7 @@
 //   tv_tile_kernel    one work-group per 64-entry vocabulary tile, waves over
 //                     (32-request block, position) tasks: the draft logits
 //                     are recomputed exactly as the draft computed them (base
-//                     logits + Markov bias on the matrix cores, W2t tile in
+//                     logits + Markov bias on the matrix cores, W2 tile in
 //                     LDS) and normalised with the draft's stored row max and
 //                     log-sum-exp; each request's |p - q| over the tile goes
 //                     to a per-(row, tile) partial.
@@ -92,7 +92,7 @@ constexpr int kTvStageBytes = kTileM * 128;
 template <typename T, int KS>
 __global__ __launch_bounds__(256, 2) void tv_tile_kernel(
     int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
-    const T* __restrict__ W1, const T* __restrict__ W2t, const int32_t* __restrict__ anchor,
+    const T* __restrict__ W1, const T* __restrict__ W2, const int32_t* __restrict__ anchor,
     const int32_t* __restrict__ tokens, const float* __restrict__ row_max,
     const float* __restrict__ row_logZ, const float* __restrict__ temperature, TvWs ws) {
   constexpr bool bf = sizeof(T) == 2;
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void tv_tile_kernel(
   const int vt = blockIdx.x, v0 = vt * kTileV;
   const int ntask = nRB * gamma;
 
-  if constexpr (bf) stage_tile(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s);
+  if constexpr (bf) stage_tile(reinterpret_cast<const uint16_t*>(W2), v0, V, rank, w2s);
 
   // the label partial of the lane's request over this tile (acc: its draft
   // logits, tp: its target entries)
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void tv_tile_kernel(
       init_acc<T>(up, V - (v0 + 16 * h), acc);
       if (__ballot(sampled) != 0)
         bias_tile_f32(reinterpret_cast<const float*>(W1), prev,
-                      reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
+                      reinterpret_cast<const float*>(W2), v0, V, rank, acc);
       finish_task(b, k, it, sampled, tp, acc);
     }
   }
@@ -291,7 +291,7 @@ size_t tv_workspace_bytes(int B, int gamma, int V) {
 
 template <typename T, int KS>
 static hipError_t tv_impl(int B, int gamma, int V, int rank, const T* target, const T* U,
-                          const T* W1, const T* W2t, const int32_t* anchor, const int32_t* tokens,
+                          const T* W1, const T* W2, const int32_t* anchor, const int32_t* tokens,
                           const float* row_max, const float* row_logZ, const float* temperature,
                           float* tv, float* label, int32_t* status, void* wsp,
                           hipStream_t stream) {
@@ -304,7 +304,7 @@ static hipError_t tv_impl(int B, int gamma, int V, int rank, const T* target, co
   {
     TraceScope t2("tv_tile_kernel", stream);
     tv_tile_kernel<T, KS><<<dim3(n_tiles(V)), dim3(256), 0, stream>>>(
-        B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
+        B, gamma, V, rank, target, U, W1, W2, anchor, tokens, row_max, row_logZ, temperature,
         ws);
   }
   TraceScope t3("tv_finish_kernel", stream);
@@ -315,7 +315,7 @@ static hipError_t tv_impl(int B, int gamma, int V, int rank, const T* target, co
 }
 
 hipError_t launch_tv_label(int B, int gamma, int V, int rank, int dtype, const void* target,
-                           const void* U, const void* W1, const void* W2t,
+                           const void* U, const void* W1, const void* W2,
                            const int32_t* anchor, const int32_t* tokens, const float* row_max,
                            const float* row_logZ, const float* temperature, float* tv,
                            float* label, int32_t* status, void* ws, hipStream_t stream) {
@@ -323,7 +323,7 @@ hipError_t launch_tv_label(int B, int gamma, int V, int rank, int dtype, const v
     auto* tg = static_cast<const uint16_t*>(target);
     auto* u = static_cast<const uint16_t*>(U);
     auto* w1 = static_cast<const uint16_t*>(W1);
-    auto* w2 = static_cast<const uint16_t*>(W2t);
+    auto* w2 = static_cast<const uint16_t*>(W2);
 #define DSPARK_TV_KS(KS)                                                                    \
   return tv_impl<uint16_t, KS>(B, gamma, V, rank, tg, u, w1, w2, anchor, tokens, row_max,    \
                                row_logZ, temperature, tv, label, status, ws, stream)
@@ -337,7 +337,7 @@ hipError_t launch_tv_label(int B, int gamma, int V, int rank, int dtype, const v
   }
   return tv_impl<float, 1>(B, gamma, V, rank, static_cast<const float*>(target),
                            static_cast<const float*>(U), static_cast<const float*>(W1),
-                           static_cast<const float*>(W2t), anchor, tokens, row_max, row_logZ,
+                           static_cast<const float*>(W2), anchor, tokens, row_max, row_logZ,
                            temperature, tv, label, status, ws, stream);
 }
 

@@ -11,7 +11,7 @@ namespace dspark {
 
 size_t tv_workspace_bytes(int B, int gamma, int V);
 hipError_t launch_tv_label(int B, int gamma, int V, int rank, int dtype, const void* target,
-                           const void* U, const void* W1, const void* W2t,
+                           const void* U, const void* W1, const void* W2,
                            const int32_t* anchor, const int32_t* tokens, const float* row_max,
                            const float* row_logZ, const float* temperature, float* tv,
                            float* label, int32_t* status, void* ws, hipStream_t stream);

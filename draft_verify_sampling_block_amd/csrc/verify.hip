@@ -242,7 +242,7 @@ __device__ inline void subtile_sums(const FinalParams& f, const float (&yt)[16],
 // One (64-entry tile, 32-request block) task of the final statistics for
 // the lane's request b (column c): the q logits of residual requests start
 // at the base logits and get the Markov bias on the matrix cores (A = the
-// W2t tile in LDS, B = the W1 rows of the previous tokens), then the
+// W2 tile in LDS, B = the W1 rows of the previous tokens), then the
 // residual and p masses of the tile are summed per request.  All 64 lanes
 // call it; tp holds the lane's target entries and acc starts at its base
 // logits (init_acc).
@@ -250,7 +250,7 @@ template <typename T, int KS>
 __device__ inline void final_task(const FinalRow& mine, int b, int vt, int V, int gamma, int nT,
                                   int rank, const URow<T>& tp, f32x16_t (&acc)[kSub],
                                   const bf16x8_t (&bfrag)[KS], const char* w2s,
-                                  const T* __restrict__ W1, const T* __restrict__ W2t,
+                                  const T* __restrict__ W1, const T* __restrict__ W2,
                                   const float* __restrict__ row_max,
                                   const float* __restrict__ row_logZ,
                                   const float* __restrict__ temperature, const VerifyWs& ws) {
@@ -263,7 +263,7 @@ __device__ inline void final_task(const FinalRow& mine, int b, int vt, int V, in
       bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
     else
       bias_tile_f32(reinterpret_cast<const float*>(W1), mine.mode == 1 ? mine.prev : -1,
-                    reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
+                    reinterpret_cast<const float*>(W2), v0, V, rank, acc);
   }
   float sr = 0.f, sp = 0.f;
   const FinalParams fp = final_params(mine, b, gamma, row_max, row_logZ, temperature, ws);
@@ -288,7 +288,7 @@ __device__ inline void final_task(const FinalRow& mine, int b, int vt, int V, in
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void verify_final_stats_kernel(
     int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
-    const T* __restrict__ W1, const T* __restrict__ W2t, const int32_t* __restrict__ anchor,
+    const T* __restrict__ W1, const T* __restrict__ W2, const int32_t* __restrict__ anchor,
     const int32_t* __restrict__ tokens, const float* __restrict__ row_max,
     const float* __restrict__ row_logZ, const float* __restrict__ temperature,
     const int32_t* __restrict__ ell, VerifyWs ws, int32_t* status) {
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
 
   // does any request of the batch need the q recompute (a residual draw)?
   const bool any_res = *ws.any_res != 0;
-  if (bf && any_res) stage_tile(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s);
+  if (bf && any_res) stage_tile(reinterpret_cast<const uint16_t*>(W2), v0, V, rank, w2s);
 
   auto plan_of = [&](int r) {   // the final-draw plan of request r (mode 0 past the batch)
     FinalRow f{0, 0, -1};
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
       if (!live) break;
       f32x16_t acc[kSub];
       init_acc<uint16_t>(up, V - (v0 + 16 * h), acc);   // q logits start at the base logits
-      final_task<T, KS>(mine, b, vt, V, gamma, nT, rank, tp, acc, bfrag, w2s, W1, W2t, row_max,
+      final_task<T, KS>(mine, b, vt, V, gamma, nT, rank, tp, acc, bfrag, w2s, W1, W2, row_max,
                         row_logZ, temperature, ws);
     }
   } else {
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
       load_urow<T>(up, U + ((size_t)b * gamma + mine.slot) * V, v0, V, mine.mode == 1, U);
       f32x16_t acc[kSub];
       init_acc<T>(up, V - (v0 + 16 * h), acc);   // q logits start at the base logits
-      final_task<T, KS>(mine, b, vt, V, gamma, nT, rank, tp, acc, bfrag, w2s, W1, W2t, row_max,
+      final_task<T, KS>(mine, b, vt, V, gamma, nT, rank, tp, acc, bfrag, w2s, W1, W2, row_max,
                         row_logZ, temperature, ws);
     }
   }
@@ -424,11 +424,11 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
 // The same statistics in tile-loop form (bf16, at most kVtMaxRows
 // requests): one work-group of 8 waves per compute unit.  Work-group p owns
 // the contiguous tiles [tbase, tbase + tcount) and walks them one by one;
-// wave w computes sub-tile w % 2 of 32-request block w / 2 (A = the W2t tile
+// wave w computes sub-tile w % 2 of 32-request block w / 2 (A = the W2 tile
 // in LDS, B = the W1 row of the lane's previous token, held in registers),
 // so each element is computed exactly as verify_final_stats_kernel computes
 // it and the sub-tile sums are combined in the same order.  The next tile's
-// W2t rows are loaded into registers while the current one is processed and
+// W2 rows are loaded into registers while the current one is processed and
 // written to the other LDS buffer; the chunk sums collect in LDS and are
 // written out every kVtOutTiles tiles.
 //
@@ -446,15 +446,15 @@ template <int KS>
 __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
     int B, int gamma, int V, int rank, const uint16_t* __restrict__ target,
     const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1,
-    const uint16_t* __restrict__ W2t, const int32_t* __restrict__ anchor,
+    const uint16_t* __restrict__ W2, const int32_t* __restrict__ anchor,
     const int32_t* __restrict__ tokens, const float* __restrict__ row_max,
     const float* __restrict__ row_logZ, const float* __restrict__ temperature,
     const int32_t* __restrict__ ell, VerifyWs ws) {
   constexpr int nq = 2 * KS, nc = nq + 1;
   constexpr int kRowB = nc * 16;                 // bytes of one padded LDS row
   constexpr int kThr = kVtWaves * 64;
-  constexpr int kChunks = kTileV * nq;           // 16-byte chunks of one tile
-  constexpr int kPer = (kChunks + kThr - 1) / kThr;
+  constexpr int kBlocks = 32 * KS;               // 4 x 8 blocks of one tile (rank 16 KS)
+  constexpr int kPer = (kBlocks + kThr - 1) / kThr;
   __shared__ __attribute__((aligned(16))) char w2s[2][kTileV * kRowB];
   // per wave: [target | base logits][32 rows][kVtStageRow]
   __shared__ __attribute__((aligned(16))) char s_stage[kVtWaves][2][kTileM][kVtStageRow];
@@ -484,29 +484,20 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
   __syncthreads();
   const bool any_res = s_any != 0;   // some request of the batch draws from a residual
 
-  // tile vt's rows in the stage_tile image: row r <- W2t row v0 +
-  // tile_row_vocab(r) (clamped); thread chunks (r, q < nq), the pad chunk
-  // written from chunk 0.  Two register stages: tile i + 1 waits in one
-  // while tile i + 2 loads into the other.
-  u32x4_t stA[kPer], stB[kPer];
-  auto load_tile = [&](u32x4_t (&st)[kPer], int vt) {
+  // tile vt's transposed image (as stage_tile writes it): thread blocks
+  // tid + kThr j of 4 k-rows x 8 entries of W2 [rank, V].  Two register
+  // stages: tile i + 1 waits in one while tile i + 2 loads into the other.
+  W2Block stA[kPer], stB[kPer];
+  auto load_tile = [&](W2Block (&st)[kPer], int vt) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int s = min(tid + kThr * j, kChunks - 1);
-      const int r = s / nq, q = s - r * nq;
-      const int v = min(vt * kTileV + tile_row_vocab(r), V - 1);
-      st[j] = *reinterpret_cast<const u32x4_t*>(W2t + (size_t)v * rank + q * 8);
-    }
+    for (int j = 0; j < kPer; ++j)
+      w2_block_load(W2, V, vt * kTileV, min(tid + kThr * j, kBlocks - 1), st[j]);
   };
-  auto write_tile = [&](const u32x4_t (&st)[kPer], int buf) {
+  auto write_tile = [&](const W2Block (&st)[kPer], int buf) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int s = tid + kThr * j;
-      const int r = s / nq, q = s - r * nq;
-      if (kChunks % kThr == 0 || s < kChunks) {
-        *reinterpret_cast<u32x4_t*>(w2s[buf] + r * kRowB + q * 16) = st[j];
-        if (q == 0) *reinterpret_cast<u32x4_t*>(w2s[buf] + r * kRowB + nq * 16) = st[j];
-      }
+      const int sb = tid + kThr * j;
+      if (kBlocks % kThr == 0 || sb < kBlocks) w2_block_store(st[j], sb, w2s[buf], nq);
     }
   };
   // every load below is issued unconditionally (safe or clamped addresses
@@ -549,7 +540,7 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
           reinterpret_cast<const u32x4_t*>(in && lu_on[g] ? lu[g] + e : U));
     }
   };
-  // the first tile's entries, W2t rows and W1 fragments requested together
+  // the first tile's entries, W2 rows and W1 fragments requested together
   fetch(ldA, tbase);
   if (any_res) {
     load_tile(stA, tbase);
@@ -600,7 +591,7 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
     // tile i from LDS buffer i & 1; `next` holds tile i + 1, `after`
     // receives tile i + 2; `ld` holds tile i's entries, `ld1` receives
     // tile i + 1's
-    auto step = [&](int i, const u32x4_t (&next)[kPer], u32x4_t (&after)[kPer],
+    auto step = [&](int i, const W2Block (&next)[kPer], W2Block (&after)[kPer],
                     const u32x4_t (&ld)[4], u32x4_t (&ld1)[4]) {
       const int vt = tbase + i;
       u32x4_t tq[2], uq[2];
@@ -655,14 +646,14 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void verify_finish_kernel(
     int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
-    const T* __restrict__ W1, const T* __restrict__ W2t, const int32_t* __restrict__ anchor,
+    const T* __restrict__ W1, const T* __restrict__ W2, const int32_t* __restrict__ anchor,
     const int32_t* __restrict__ tokens, const float* __restrict__ row_max,
     const float* __restrict__ row_logZ, const float* __restrict__ temperature,
     const float* __restrict__ uniforms, const int32_t* __restrict__ ell, VerifyWs ws,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ n_accepted,
     float* __restrict__ ratio, int32_t* status) {
   constexpr bool bf = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) char w2s[bf ? kLdsTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) char w2s[bf ? kRawTileBytes : 16];
   __shared__ double red[8];
   __shared__ int s_tile, s_pick;
   __shared__ double s_before;
@@ -728,11 +719,14 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
       y = 0;
     } else {
       // recompute the crossing tile exactly as verify_final_stats did:
-      // same operands, request b in its own column b % 32
+      // same operands, request b in its own column b % 32; bf16: waves 0
+      // and 1 take sub-tiles 0 and 1 (A gathered from the tile's raw W2
+      // rows), fp32: wave 0 takes both
       const int v0 = vt * kTileV;
       const int mrow = b % kTileM;
       const int lane = tid & 63, c = lane & 31, h = lane >> 5;
-      const bool mine = tid < kWave && c == mrow;
+      const int tw = tid >> 6;   // bf16: the sub-tile of waves 0 and 1
+      const bool mine = tid < (bf ? kSub : 1) * kWave && c == mrow;
       const int prev = residual
           ? clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1], V, nullptr)
           : -1;
@@ -743,17 +737,21 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
       init_acc<T>(ur, V - (v0 + 16 * h), acc);
       if (residual) {
         if constexpr (bf) {
-          stage_tile(reinterpret_cast<const uint16_t*>(W2t), v0, V, rank, w2s);
+          dma_tile_raw(reinterpret_cast<const uint16_t*>(W2), V, v0, rank, w2s);
           bf16x8_t bfrag[KS];
-          if (tid < kWave)
+          if (tid < kSub * kWave)
             load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), mine ? prev : -1, bfrag);
           __builtin_amdgcn_s_waitcnt(0);
           __syncthreads();
-          if (tid < kWave) bias_tile_ldsA<KS>([&](int ks) { return bfrag[ks]; }, w2s, acc);
+          auto bf_ = [&](int ks) { return bfrag[ks]; };
+          if (tw == 0)
+            bias_subtile<KS>([&](int ks) { return raw_frag(w2s, 0, ks); }, bf_, acc[0]);
+          else if (tw == 1)
+            bias_subtile<KS>([&](int ks) { return raw_frag(w2s, 1, ks); }, bf_, acc[1]);
         } else {
           if (tid < kWave)
             bias_tile_f32(reinterpret_cast<const float*>(W1), mine ? prev : -1,
-                          reinterpret_cast<const float*>(W2t), v0, V, rank, acc);
+                          reinterpret_cast<const float*>(W2), v0, V, rank, acc);
         }
       }
       if (mine) {
@@ -764,6 +762,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
         const int rem = V - (v0 + 16 * h);
 #pragma unroll
         for (int t = 0; t < kSub; ++t) {
+          if (bf && t != tw) continue;
           float* so = se + 32 * t + 16 * h;
 #pragma unroll
           for (int jj = 0; jj < 16; ++jj) {
@@ -820,7 +819,7 @@ size_t verify_workspace_bytes(int B, int gamma, int V, int rank, int dtype) {
 
 template <typename T, int KS>
 static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target, const T* U,
-                              const T* W1, const T* W2t, const int32_t* anchor,
+                              const T* W1, const T* W2, const int32_t* anchor,
                               const int32_t* tokens, const float* q_tok, const float* row_max,
                               const float* row_logZ, const float* temperature,
                               const float* uniforms, const int32_t* ell, int32_t* out_tokens,
@@ -841,7 +840,7 @@ static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target
       const int P = std::min(cus, n_tiles(V));
       TraceScope t2("verify_tile_stats_kernel", stream);
       verify_tile_stats_kernel<KS><<<dim3(P), dim3(kVtWaves * 64), 0, stream>>>(
-          B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
+          B, gamma, V, rank, target, U, W1, W2, anchor, tokens, row_max, row_logZ, temperature,
           ell, ws);
       tiles = true;
     }
@@ -859,18 +858,18 @@ static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target
     }
     TraceScope t2("verify_final_stats_kernel", stream);
     verify_final_stats_kernel<T, KS><<<dim3(n_tiles(V)), dim3(256), 0, stream>>>(
-        B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
+        B, gamma, V, rank, target, U, W1, W2, anchor, tokens, row_max, row_logZ, temperature,
         ell, ws, status);
   }
   TraceScope t3("verify_finish_kernel", stream);
   verify_finish_kernel<T, KS><<<dim3(B), dim3(256), 0, stream>>>(
-      B, gamma, V, rank, target, U, W1, W2t, anchor, tokens, row_max, row_logZ, temperature,
+      B, gamma, V, rank, target, U, W1, W2, anchor, tokens, row_max, row_logZ, temperature,
       uniforms, ell, ws, out_tokens, n_accepted, ratio, status);
   return hipGetLastError();
 }
 
 hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const void* target,
-                         const void* U, const void* W1, const void* W2t, const int32_t* anchor,
+                         const void* U, const void* W1, const void* W2, const int32_t* anchor,
                          const int32_t* tokens, const float* q_tok, const float* row_max,
                          const float* row_logZ, const float* temperature, const float* uniforms,
                          const int32_t* ell, int32_t* out_tokens, int32_t* n_accepted,
@@ -879,7 +878,7 @@ hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const voi
     auto* tg = static_cast<const uint16_t*>(target);
     auto* u = static_cast<const uint16_t*>(U);
     auto* w1 = static_cast<const uint16_t*>(W1);
-    auto* w2 = static_cast<const uint16_t*>(W2t);
+    auto* w2 = static_cast<const uint16_t*>(W2);
 #define DSPARK_VERIFY_KS(KS)                                                                  \
   return verify_impl<uint16_t, KS>(B, gamma, V, rank, tg, u, w1, w2, anchor, tokens, q_tok,    \
                                    row_max, row_logZ, temperature, uniforms, ell, out_tokens,  \
@@ -894,7 +893,7 @@ hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const voi
   }
   return verify_impl<float, 1>(B, gamma, V, rank, static_cast<const float*>(target),
                                static_cast<const float*>(U), static_cast<const float*>(W1),
-                               static_cast<const float*>(W2t), anchor, tokens, q_tok, row_max,
+                               static_cast<const float*>(W2), anchor, tokens, q_tok, row_max,
                                row_logZ, temperature, uniforms, ell, out_tokens, n_accepted, ratio,
                                status, ws, stream);
 }

@@ -24,7 +24,7 @@ class DeviceInputs:
     U: torch.Tensor
     target: torch.Tensor
     W1: torch.Tensor
-    W2t: torch.Tensor
+    W2: torch.Tensor
     w: torch.Tensor
     b0: float
     hidden: torch.Tensor
@@ -49,7 +49,7 @@ def upload(wl, device="cuda", scheduler: bool | None = None) -> DeviceInputs:
     return DeviceInputs(
         B=B, gamma=g, V=wl.V, rank=wl.rank, H=wl.H,
         U=_dev(wl.U, device), target=_dev(wl.target, device), W1=_dev(wl.W1, device),
-        W2t=_dev(wl.W2t, device), w=_dev(wl.w.astype(np.float32), device), b0=float(wl.b0),
+        W2=_dev(wl.W2, device), w=_dev(wl.w.astype(np.float32), device), b0=float(wl.b0),
         hidden=_dev(wl.hidden, device), anchor=_dev(wl.anchor.astype(np.int32), device),
         temperature=_dev(wl.temperature.astype(np.float32), device),
         uniforms=_dev(wl.uniforms.astype(np.float32), device),
@@ -88,22 +88,29 @@ class Step:
         self.ws_sched = torch.empty(max(256, dspark_schedule_workspace(B, g)), dtype=torch.uint8,
                                     device=dev)
 
-    def run(self):
+    def run(self, status: torch.Tensor | None = None):
+        """Enqueue one step.  Device flags go to `status` (a (1,) int32
+        device tensor the caller cleared) or, when None, to self.status,
+        which is cleared first by a fill kernel (no memset node, so the step
+        stays capturable in a graph)."""
         d = self.d
-        dspark_draft_block(d.U, d.W1, d.W2t, d.anchor, d.temperature, d.uniforms,
+        if status is None:
+            self.status.zero_()
+            status = self.status
+        dspark_draft_block(d.U, d.W1, d.W2, d.anchor, d.temperature, d.uniforms,
                            tokens=self.tokens, q_tok=self.q_tok, row_max=self.row_max,
-                           row_logZ=self.row_logZ, status=self.status, workspace=self.ws_draft)
+                           row_logZ=self.row_logZ, status=status, workspace=self.ws_draft)
         dspark_confidence(d.hidden, d.W1, d.anchor, self.tokens, d.w, d.b0, conf=self.conf,
-                          status=self.status)
+                          status=status)
         if d.sps is not None:
             dspark_schedule(self.conf, d.sps, ell=self.ell, order=self.order, stats=self.stats,
-                            status=self.status, workspace=self.ws_sched)
+                            status=status, workspace=self.ws_sched)
             ell = self.ell
         else:
             ell = d.fixed_ell
-        dspark_verify(d.target, d.U, d.W1, d.W2t, d.anchor, self.tokens, self.q_tok, self.row_max,
+        dspark_verify(d.target, d.U, d.W1, d.W2, d.anchor, self.tokens, self.q_tok, self.row_max,
                       self.row_logZ, d.temperature, d.uniforms, ell, out_tokens=self.out_tokens,
-                      n_accepted=self.n_accepted, ratio=self.ratio, status=self.status,
+                      n_accepted=self.n_accepted, ratio=self.ratio, status=status,
                       workspace=self.ws_verify)
         return self
 

@@ -87,7 +87,7 @@ class Workload:
     U: np.ndarray          # [B, gamma, V]     uint16 (bf16 bits) or float32
     target: np.ndarray     # [B, gamma+1, V]   slot gamma = bonus slot
     W1: np.ndarray         # [V, rank]
-    W2t: np.ndarray        # [V, rank]         projection rank -> V, stored V-major
+    W2: np.ndarray         # [rank, V]         projection rank -> V
     w: np.ndarray          # [H + rank] float32 confidence weight ([w_h ; w_e])
     b0: float              # confidence bias
     hidden: np.ndarray     # [B, gamma, H]
@@ -214,7 +214,9 @@ def make_config(index: int, seed: int | None = None, requests=None, threads: int
     anchor, uniforms, low_class, temperature = _global_draws(spec, seed)
 
     W1 = _rng(seed, _C_W1).standard_normal((spec.V, spec.rank), dtype=np.float32) * np.float32(spec.w_std)
-    W2t = _rng(seed, _C_W2).standard_normal((spec.V, spec.rank), dtype=np.float32) * np.float32(spec.w_std)
+    # drawn [V, rank] and stored transposed, [rank, V]
+    W2 = np.ascontiguousarray((_rng(seed, _C_W2).standard_normal((spec.V, spec.rank), dtype=np.float32)
+                               * np.float32(spec.w_std)).T)
     w = (_rng(seed, _C_W).standard_normal(spec.H + spec.rank) * 0.1).astype(np.float32)
     w_h = w[: spec.H].astype(np.float64)
 
@@ -250,12 +252,12 @@ def make_config(index: int, seed: int | None = None, requests=None, threads: int
             one(i)
 
     if bf:
-        W1s, W2s = to_bf16_bits(W1), to_bf16_bits(W2t)
+        W1s, W2s = to_bf16_bits(W1), to_bf16_bits(W2)
     else:
-        W1s, W2s = W1, W2t
+        W1s, W2s = W1, W2
     return Workload(
         spec=spec, B=nb, gamma=g, V=V, rank=spec.rank, H=spec.H, dtype=spec.dtype,
-        U=U, target=target, W1=W1s, W2t=W2s, w=w, b0=0.0, hidden=hidden,
+        U=U, target=target, W1=W1s, W2=W2s, w=w, b0=0.0, hidden=hidden,
         anchor=anchor[req].copy(), temperature=temperature[req].copy(),
         uniforms=uniforms[req].copy(), sps=sps_table(spec.sps_kind), requests=req,
     )
@@ -275,7 +277,8 @@ def make_custom(B: int, gamma: int, V: int, rank: int, H: int, dtype: str = "bf1
                 sps_kind != "none", temperature, greedy_frac=greedy_frac, sps_kind=sps_kind)
     anchor, uniforms, low_class, temp = _global_draws(spec, seed)
     W1 = _rng(seed, _C_W1).standard_normal((V, rank), dtype=np.float32) * np.float32(w_std)
-    W2t = _rng(seed, _C_W2).standard_normal((V, rank), dtype=np.float32) * np.float32(w_std)
+    W2 = np.ascontiguousarray((_rng(seed, _C_W2).standard_normal((V, rank), dtype=np.float32)
+                               * np.float32(w_std)).T)
     w = (_rng(seed, _C_W).standard_normal(H + rank) * 0.1).astype(np.float32)
     w_h = w[:H].astype(np.float64)
     bf = dtype == "bf16"
@@ -299,6 +302,6 @@ def make_custom(B: int, gamma: int, V: int, rank: int, H: int, dtype: str = "bf1
         sps = sps_table(sps_kind)
     return Workload(spec=spec, B=B, gamma=gamma, V=V, rank=rank, H=H, dtype=dtype,
                     U=U, target=target, W1=to_bf16_bits(W1) if bf else W1,
-                    W2t=to_bf16_bits(W2t) if bf else W2t, w=w, b0=0.0, hidden=hidden,
+                    W2=to_bf16_bits(W2) if bf else W2, w=w, b0=0.0, hidden=hidden,
                     anchor=anchor, temperature=temp, uniforms=uniforms, sps=sps,
                     requests=np.arange(B))

@@ -26,12 +26,12 @@
  *    which the caller clears before the step, and the affected outputs stay
  *    in range (token ids within [0, V)).
  *  - dtype selects the element type of the large tensors (U, target, W1,
- *    W2t, hidden): DSPARK_BF16 (bit patterns, round-to-nearest-even) or
+ *    W2, hidden): DSPARK_BF16 (bit patterns, round-to-nearest-even) or
  *    DSPARK_F32.  Accumulation is fp32 (bf16 inputs use MFMA), cross-tile
  *    sums and cumulative sums are fp64.
  *  - Shapes: V % 8 == 0 and V <= 262144 (larger: DSPARK_EUNSUPPORTED);
  *    rank in {32, 64, 128, 256} for bf16 (the matrix-core path keeps
- *    64 x rank tiles of W2t in LDS and registers), any multiple of 32 in
+ *    64 x rank tiles of W2 in LDS and registers), any multiple of 32 in
  *    [32, 512] for fp32; H % 8 == 0; 1 <= gamma <= 64; B >= 1.
  *  - Positions are 0-based: draft position k (0..gamma-1) is the pages'
  *    x_{k+1}.
@@ -89,10 +89,11 @@ const char* dspark_version(void);
  *     z      = U[b,k,:] + W1[prev,:] @ W2          (rank-r transition bias)
  *     x      = inverse-CDF draw from softmax(z / T_b) with uniforms[b,k,0]
  *     prev   = x
- * W2 (the rank -> V projection) is stored as W2t [V, rank], i.e. the weight
- * layout of a linear map from rank to V: bias[v] = sum_i W1[prev,i]*W2t[v,i].
+ * W2 is the rank -> V projection, [rank, V] row-major: bias[v] =
+ * sum_i W1[prev,i] * W2[i,v].  The kernels transpose each 64-entry tile of
+ * W2 on chip; no transposed copy is made in memory.
  *
- * in : U [B,gamma,V], W1 [V,rank], W2t [V,rank] (dtype); anchor [B] int32;
+ * in : U [B,gamma,V], W1 [V,rank], W2 [rank,V] (dtype); anchor [B] int32;
  *      temperature [B], uniforms [B,gamma+1,2] fp32
  * out: tokens [B,gamma] int32; q_tok [B,gamma] fp32 = q_k(x_k);
  *      row_max [B,gamma] = max_v z/T (max z when greedy);
@@ -102,7 +103,7 @@ const char* dspark_version(void);
  * ---------------------------------------------------------------------- */
 size_t dspark_draft_block_workspace(int B, int gamma, int V, int rank, int dtype);
 int dspark_draft_block(int B, int gamma, int V, int rank, int dtype,
-                       const void* U, const void* W1, const void* W2t,
+                       const void* U, const void* W1, const void* W2,
                        const int32_t* anchor, const float* temperature,
                        const float* uniforms,
                        int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
@@ -197,13 +198,13 @@ int dspark_schedule_threshold(int R, int gamma, const float* conf,
  * For request b with verify length L = ell[b] (0..gamma):
  *   for k = 0..L-1: p = softmax(target[b,k,:]/T); accept draft token x_k iff
  *     uniforms[b,k,1] < p(x_k)/q_tok[b,k]; stop at the first reject j.
- *   reject at j: q_j is recomputed from U[b,j], W1, W2t and prev_j (bit-
+ *   reject at j: q_j is recomputed from U[b,j], W1, W2 and prev_j (bit-
  *     identical to the draft's logits; row_max/row_logZ normalise it), and
  *     one token is drawn from norm(max(0, p_j - q_j)) with uniforms[b,gamma,0].
  *   no reject : one bonus token is drawn from softmax(target[b,L,:]/T) with
  *     uniforms[b,gamma,0].
  * in : target [B,gamma+1,V] (slot gamma is the bonus slot when ell = gamma),
- *      U, W1, W2t (dtype); anchor, tokens int32; q_tok, row_max, row_logZ
+ *      U [B,gamma,V], W1 [V,rank], W2 [rank,V] (dtype); anchor, tokens int32; q_tok, row_max, row_logZ
  *      (outputs of dspark_draft_block); temperature, uniforms; ell [B]
  * out: out_tokens [B,gamma+1] int32: accepted prefix then the one drawn
  *      token, -1 padded; n_accepted [B] int32 (emitted = n_accepted + 1;
@@ -213,7 +214,7 @@ int dspark_schedule_threshold(int R, int gamma, const float* conf,
  * ---------------------------------------------------------------------- */
 size_t dspark_verify_workspace(int B, int gamma, int V, int rank, int dtype);
 int dspark_verify(int B, int gamma, int V, int rank, int dtype,
-                  const void* target, const void* U, const void* W1, const void* W2t,
+                  const void* target, const void* U, const void* W1, const void* W2,
                   const int32_t* anchor, const int32_t* tokens, const float* q_tok,
                   const float* row_max, const float* row_logZ,
                   const float* temperature, const float* uniforms, const int32_t* ell,
@@ -227,7 +228,7 @@ int dspark_verify(int B, int gamma, int V, int rank, int dtype,
  *     tv[b,k]    = 0.5 * sum_v |p_k(v) - q_k(v)|
  *     label[b,k] = 1 - tv[b,k]  (= the probability that the acceptance test
  *                                 of dspark_verify keeps drafted token k)
- *   q_k = softmax((U[b,k] + W1[prev] W2t^T) / T), prev = anchor[b] (k = 0)
+ *   q_k = softmax((U[b,k] + W1[prev] W2) / T), prev = anchor[b] (k = 0)
  *         or tokens[b,k-1]: the distribution dspark_draft_block drew token k
  *         from, recomputed bit-identically and normalised with its row_max /
  *         row_logZ outputs;
@@ -236,7 +237,7 @@ int dspark_verify(int B, int gamma, int V, int rank, int dtype,
  *   greedy requests (T <= 0): tv = 0 if tokens[b,k] is the target row's
  *         lowest-index argmax, else 1.
  * Sums: per element fp32, per 64-entry tile fp32, across tiles fp64.
- * in : target [B,gamma+1,V], U [B,gamma,V], W1, W2t [V,rank] (dtype);
+ * in : target [B,gamma+1,V], U [B,gamma,V], W1 [V,rank], W2 [rank,V] (dtype);
  *      anchor [B], tokens [B,gamma] int32; row_max, row_logZ [B,gamma] fp32
  *      (dspark_draft_block outputs); temperature [B]
  * out: tv [B,gamma] fp32; label [B,gamma] fp32 (or NULL)
@@ -245,7 +246,7 @@ int dspark_verify(int B, int gamma, int V, int rank, int dtype,
  * ---------------------------------------------------------------------- */
 size_t dspark_tv_label_workspace(int B, int gamma, int V, int rank, int dtype);
 int dspark_tv_label(int B, int gamma, int V, int rank, int dtype,
-                    const void* target, const void* U, const void* W1, const void* W2t,
+                    const void* target, const void* U, const void* W1, const void* W2,
                     const int32_t* anchor, const int32_t* tokens,
                     const float* row_max, const float* row_logZ,
                     const float* temperature, float* tv, float* label,
@@ -272,7 +273,7 @@ int dspark_trace_summary(char* buf, size_t len);
  * 1 = always one launch pair per position;
  * 2 = persistent only: dspark_draft_block returns DSPARK_EHIP where it
  *     cannot run;
- * 3, 4 = persistent only, with 8 (one register-resident W2t tile each) or
+ * 3, 4 = persistent only, with 8 (one register-resident W2 tile each) or
  *     4 (two each) waves per work-group; 2 picks 8.
  * All settings return identical results.
  * Returns the previous setting, or DSPARK_EINVAL for another value.

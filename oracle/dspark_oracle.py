@@ -77,18 +77,17 @@ def f64(a) -> np.ndarray:
 # (1) semi-autoregressive block drafting with the vanilla Markov head
 # ----------------------------------------------------------------------------
 
-def markov_bias(W1, W2t, prev: int) -> np.ndarray:
+def markov_bias(W1, W2, prev: int) -> np.ndarray:
     """Transition bias B(prev, .) = W1[prev] @ W2 over the whole vocabulary.
 
     [weigao] part 2 and [billytse] 3.3: the V x V first-order transition
     matrix is replaced by a rank-r product; the row for the previous token is
-    the previous token's r-vector times the r x V projection.  ``W2t`` holds
-    that projection stored as [V, r] (the weight layout of a linear map from
-    r to V), so bias[v] = sum_i W1[prev, i] * W2t[v, i].
+    the previous token's r-vector times the r x V projection ``W2`` [r, V],
+    so bias[v] = sum_i W1[prev, i] * W2[i, v].
     """
     W1 = f64(W1) if not (isinstance(W1, np.ndarray) and W1.dtype == np.float64) else W1
-    W2t = f64(W2t) if not (isinstance(W2t, np.ndarray) and W2t.dtype == np.float64) else W2t
-    return W2t @ W1[int(prev)]
+    W2 = f64(W2) if not (isinstance(W2, np.ndarray) and W2.dtype == np.float64) else W2
+    return W1[int(prev)] @ W2
 
 
 def inverse_cdf(weights: np.ndarray, u: float):
@@ -129,7 +128,7 @@ def draft_row(z: np.ndarray, temperature: float, u: float):
     return dict(x=x, q=1.0, m=m, logZ=0.0, lo=0.0, hi=1.0)
 
 
-def draft_block(U, W1, W2t, anchor, temperature, uniforms):
+def draft_block(U, W1, W2, anchor, temperature, uniforms):
     """Sequential Markov sampling over a block, per request.
 
     [billytse] 3.3 sampling loop: start from the anchor token; at each block
@@ -137,14 +136,14 @@ def draft_block(U, W1, W2t, anchor, temperature, uniforms):
     base logits, take the softmax, sample, and make the sample the next
     previous token.
 
-    U: [B, gamma, V]; W1: [V, r]; W2t: [V, r]; anchor: [B]; temperature: [B];
+    U: [B, gamma, V]; W1: [V, r]; W2: [r, V]; anchor: [B]; temperature: [B];
     uniforms: [B, gamma+1, 2].  Returns arrays tokens [B,gamma] int64,
     q_tok, row_max, row_logZ, lo, hi, margin [B,gamma] float64.  ``margin``
     is the distance of u from the nearest edge of x's interval.
     """
     U = f64(U)
     W1 = f64(W1)
-    W2t = f64(W2t)
+    W2 = f64(W2)
     uni = np.asarray(uniforms, dtype=np.float64)
     B, gamma, V = U.shape
     out = {k: np.zeros((B, gamma)) for k in ("q_tok", "row_max", "row_logZ", "lo", "hi", "margin")}
@@ -153,7 +152,7 @@ def draft_block(U, W1, W2t, anchor, temperature, uniforms):
         prev = int(anchor[b])
         T = float(temperature[b])
         for k in range(gamma):
-            z = U[b, k] + markov_bias(W1, W2t, prev)
+            z = U[b, k] + markov_bias(W1, W2, prev)
             u = float(uni[b, k, 0])
             r = draft_row(z, T, u)
             tokens[b, k] = r["x"]
@@ -169,7 +168,7 @@ def draft_block(U, W1, W2t, anchor, temperature, uniforms):
     return out
 
 
-def draft_forced(U, W1, W2t, anchor, temperature, tokens, uniforms=None, rows=None):
+def draft_forced(U, W1, W2, anchor, temperature, tokens, uniforms=None, rows=None):
     """Draft statistics with the sampled tokens given (teacher forcing).
 
     Computes, for the listed (b, k) rows (all rows if ``rows`` is None), the
@@ -180,7 +179,7 @@ def draft_forced(U, W1, W2t, anchor, temperature, tokens, uniforms=None, rows=No
     """
     U_is64 = isinstance(U, np.ndarray) and U.dtype == np.float64
     W1 = W1 if (isinstance(W1, np.ndarray) and W1.dtype == np.float64) else f64(W1)
-    W2t = W2t if (isinstance(W2t, np.ndarray) and W2t.dtype == np.float64) else f64(W2t)
+    W2 = W2 if (isinstance(W2, np.ndarray) and W2.dtype == np.float64) else f64(W2)
     B, gamma = np.asarray(tokens).shape
     if rows is None:
         rows = [(b, k) for b in range(B) for k in range(gamma)]
@@ -188,7 +187,7 @@ def draft_forced(U, W1, W2t, anchor, temperature, tokens, uniforms=None, rows=No
     for b, k in rows:
         prev = int(anchor[b]) if k == 0 else int(tokens[b, k - 1])
         Urow = U[b, k] if U_is64 else f64(U[b, k])
-        z = Urow + markov_bias(W1, W2t, prev)
+        z = Urow + markov_bias(W1, W2, prev)
         T = float(temperature[b])
         x = int(tokens[b, k])
         if T > 0:
@@ -407,7 +406,7 @@ def _draft_probs(z: np.ndarray, temperature: float) -> np.ndarray:
     return q
 
 
-def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell,
+def verify(target, U, W1, W2, anchor, tokens, q_tok, temperature, uniforms, ell,
            requests=None, keep_final=False):
     """Speculative rejection sampling over each request's verified prefix.
 
@@ -419,7 +418,7 @@ def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell
     are the accepted prefix plus that one token.
 
     ``q_tok[b, k]`` is the draft probability of tokens[b, k].  At a reject
-    the full draft row q is recomputed from U, W1, W2t and the previous
+    the full draft row q is recomputed from U, W1, W2 and the previous
     token.  Accept iff u < p/q (written u*q < p; a ratio >= 1 always passes
     since u < 1).  A residual with no mass (reachable only by rounding) falls
     back to p and is flagged in ``degenerate``.
@@ -433,7 +432,7 @@ def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell
     the normalised cumulative distribution of the final draw (``final_cdf``).
     """
     W1 = W1 if (isinstance(W1, np.ndarray) and W1.dtype == np.float64) else f64(W1)
-    W2t = W2t if (isinstance(W2t, np.ndarray) and W2t.dtype == np.float64) else f64(W2t)
+    W2 = W2 if (isinstance(W2, np.ndarray) and W2.dtype == np.float64) else f64(W2)
     tokens = np.asarray(tokens)
     B, gamma = tokens.shape
     q_tok = np.asarray(q_tok, dtype=np.float64)
@@ -462,7 +461,7 @@ def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell
         if rejected_at >= 0:
             j = rejected_at
             prev = int(anchor[b]) if j == 0 else int(tokens[b, j - 1])
-            z = f64(U[b, j]) + markov_bias(W1, W2t, prev)
+            z = f64(U[b, j]) + markov_bias(W1, W2, prev)
             q = _draft_probs(z, T)
             res = np.maximum(0.0, p - q)
             if not (np.sum(res) > 0.0):
@@ -493,7 +492,7 @@ def verify(target, U, W1, W2t, anchor, tokens, q_tok, temperature, uniforms, ell
 # (5) acceptance label: total variation between draft and target
 # ----------------------------------------------------------------------------
 
-def tv_label(target, U, W1, W2t, anchor, tokens, temperature, rows=None):
+def tv_label(target, U, W1, W2, anchor, tokens, temperature, rows=None):
     """Per-position acceptance label from the total variation distance.
 
     [weigao] part 3 (the confidence head's training target) and [billytse]
@@ -524,7 +523,7 @@ def tv_label(target, U, W1, W2t, anchor, tokens, temperature, rows=None):
             tv[b, k] = 0.0 if int(np.argmax(target[b, k])) == x else 1.0
             continue
         prev = int(anchor[b]) if k == 0 else int(tokens[b, k - 1])
-        q = _draft_probs(U[b, k] + markov_bias(W1, W2t, prev), T)
+        q = _draft_probs(U[b, k] + markov_bias(W1, W2, prev), T)
         p = target_probs(target[b, k], T)
         tv[b, k] = 0.5 * math.fsum(np.abs(p - q))
     return dict(tv=tv, label=1.0 - tv)

@@ -42,9 +42,9 @@ def _req(cond, msg):
         raise Mismatch(msg)
 
 
-def check_draft(wl, W1_64, W2t_64, tokens, q_tok, row_max, row_logZ, rows=None):
+def check_draft(wl, W1_64, W2_64, tokens, q_tok, row_max, row_logZ, rows=None):
     """tokens etc. are host numpy arrays of the device outputs."""
-    forced = O.draft_forced(wl.U, W1_64, W2t_64, wl.anchor, wl.temperature, tokens,
+    forced = O.draft_forced(wl.U, W1_64, W2_64, wl.anchor, wl.temperature, tokens,
                             uniforms=wl.uniforms, rows=rows)
     rep = dict(rows=len(forced), identical=0, band=0)
     for d in forced:
@@ -98,14 +98,14 @@ def check_schedule_mode(conf, mode, arg, ell, order, stats):
     return dict(n_admitted=s["n_admitted"], mean_ell=float(np.mean(s["ell"])))
 
 
-def check_verify(wl, W1_64, W2t_64, tokens, ell, out_tokens, n_accepted, ratio, requests=None):
+def check_verify(wl, W1_64, W2_64, tokens, ell, out_tokens, n_accepted, ratio, requests=None):
     B, gamma = tokens.shape
     reqs = list(range(B)) if requests is None else list(requests)
     rows = [(b, k) for b in reqs for k in range(int(ell[b]))]
     q = np.full((B, gamma), np.nan)
-    for d in O.draft_forced(wl.U, W1_64, W2t_64, wl.anchor, wl.temperature, tokens, rows=rows):
+    for d in O.draft_forced(wl.U, W1_64, W2_64, wl.anchor, wl.temperature, tokens, rows=rows):
         q[d["b"], d["k"]] = d["q"]
-    v = O.verify(wl.target, wl.U, W1_64, W2t_64, wl.anchor, tokens, q, wl.temperature,
+    v = O.verify(wl.target, wl.U, W1_64, W2_64, wl.anchor, tokens, q, wl.temperature,
                  wl.uniforms, ell, requests=reqs, keep_final=True)
     rep = dict(requests=len(reqs), accept_flips=0, final_identical=0, final_band=0)
     for b in reqs:
@@ -139,12 +139,12 @@ def check_verify(wl, W1_64, W2t_64, tokens, ell, out_tokens, n_accepted, ratio, 
     return rep
 
 
-def check_tv(wl, W1_64, W2t_64, tokens, tv, label, rows=None):
+def check_tv(wl, W1_64, W2_64, tokens, tv, label, rows=None):
     """Acceptance labels: tv and 1 - tv against the oracle on the GPU's own
     drafted tokens; continuous tolerance, greedy rows exact."""
     B, gamma = tokens.shape
     todo = [(b, k) for b in range(B) for k in range(gamma)] if rows is None else list(rows)
-    ref = O.tv_label(wl.target, wl.U, W1_64, W2t_64, wl.anchor, tokens, wl.temperature, rows=todo)
+    ref = O.tv_label(wl.target, wl.U, W1_64, W2_64, wl.anchor, tokens, wl.temperature, rows=todo)
     worst = 0.0
     for b, k in todo:
         r = ref["tv"][b, k]

@@ -39,12 +39,12 @@ class TinyStep:
     """
 
     def __init__(self, R, gamma, V, rank, seed, T=1.0, ell=None, conf=None, sps=None,
-                 w_scale=0.8, U=None, W1=None, W2t=None, ptab=None, anchor=None, sched=None):
+                 w_scale=0.8, U=None, W1=None, W2=None, ptab=None, anchor=None, sched=None):
         rng = np.random.default_rng(seed)
         self.R, self.gamma, self.V = R, gamma, V
         self.U = rng.normal(0.0, 1.0, (R, gamma, V)) if U is None else np.asarray(U, dtype=np.float64)
         self.W1 = rng.normal(0.0, w_scale, (V, rank)) if W1 is None else np.asarray(W1, dtype=np.float64)
-        self.W2t = rng.normal(0.0, w_scale, (V, rank)) if W2t is None else np.asarray(W2t, dtype=np.float64)
+        self.W2 = rng.normal(0.0, w_scale, (V, rank)).T if W2 is None else np.asarray(W2, dtype=np.float64)
         self.anchor = rng.integers(0, V, R) if anchor is None else np.asarray(anchor)
         self.T = np.full(R, float(T))
         if ptab is None:
@@ -74,7 +74,7 @@ class TinyStep:
     def run(self, uni):
         key = np.ascontiguousarray(uni[:, : self.gamma, 0]).tobytes()
         if key not in self._draft_cache:
-            d = O.draft_block(self.U, self.W1, self.W2t, self.anchor, self.T, uni)
+            d = O.draft_block(self.U, self.W1, self.W2, self.anchor, self.T, uni)
             if self.ell is not None:
                 ell = self.ell
             else:
@@ -83,7 +83,7 @@ class TinyStep:
                        else O.schedule(c, self.sps)["ell"])
             self._draft_cache[key] = (d, ell)
         d, ell = self._draft_cache[key]
-        v = O.verify(self.target_logits(d["tokens"]), self.U, self.W1, self.W2t, self.anchor,
+        v = O.verify(self.target_logits(d["tokens"]), self.U, self.W1, self.W2, self.anchor,
                      d["tokens"], d["q_tok"], self.T, uni, ell)
         return d, ell, v
 

@@ -26,12 +26,22 @@ def test_step_bytes_count_each_input_once():
 
 
 def test_draft_kernel_bytes():
-    wl = make_custom(3, 4, 200, 32, 16, "bf16", "gaussian", seed=0)
+    # every U row, W2 once, one W1 row per (request, position), anchors,
+    # temperatures, draw uniforms and four [B, gamma] outputs; the tile
+    # statistics are the kernel's intermediates and are not counted
+    wl = make_custom(3, 4, 200, 32, 16, "bf16", "gaussian", seed=0, greedy_frac=0.34)
+    want = (2 * 3 * 4 * 200 + 2 * 32 * 200 + 2 * 3 * 4 * 32
+            + 4 * 3 + 4 * 3 + 4 * 3 * 4 + 4 * 3 * 4 * 4)
+    assert bench.draft_kernel_bytes(wl, "pdraft_kernel") == want
     nT = (200 + 63) // 64
     greedy = int(np.sum(~(np.asarray(wl.temperature) > 0)))
-    per_pos = 8 * 3 * nT + 4 * greedy * nT
-    want = 2 * 3 * 4 * 200 + 2 * 32 * 200 + 2 * 3 * 4 * 32 + 4 * per_pos + 4 * 3 * 4 * 4
-    assert bench.draft_kernel_bytes(wl, "pdraft_kernel") == want
+    assert greedy == 1
+    # written once and read once per position: packed (max, sum) words for
+    # every request, argmax words for the greedy one
+    assert bench.draft_intermediate_bytes(wl, "pdraft_kernel") == 4 * 2 * (8 * 3 * nT + 4 * nT)
+    # per-position launches: that position's rows and a 1/gamma share of W2
+    assert bench.draft_kernel_bytes(wl, "draft_stats_kernel") == (
+        2 * 3 * 200 + 2 * 3 * 32 + 2 * 32 * 200 / 4)
 
 
 def test_tv_label_bytes():
@@ -67,7 +77,12 @@ def test_kernel_bytes_per_launch():
     ell = np.array([4, 2, 0])
     n_acc = np.array([4, 1, 0])
     kb = bench.kernel_bytes(wl, ell, n_acc)
-    assert kb["verify_rows_kernel"] == 2 * 64 * (5 + 3 + 1)
-    # three sampled final rows, one rejecting request's base-logit row, W2 once
-    assert kb["verify_tile_stats_kernel"] == 2 * 64 * (3 + 1) + 2 * 32 * 64
+    # target rows up to the first reject or the bonus slot: 5 + 2 + 1
+    assert kb["verify_rows_kernel"] == 2 * 64 * (5 + 2 + 1)
+    # the one rejecting request's base-logit row (the q recompute)
+    assert kb["verify_tile_stats_kernel"] == 2 * 64 * 1
     assert kb["confidence_kernel"] == 2 * 3 * 4 * (16 + 32) + 4 * 3 * 4
+    rd = bench.kernel_bytes_read(wl, ell, n_acc)
+    # as built: every slot up to ell (bonus included), the final rows and W2 again
+    assert rd["verify_rows_kernel"] == 2 * 64 * (5 + 3 + 1)
+    assert rd["verify_tile_stats_kernel"] == 2 * 64 * (3 + 1) + 2 * 32 * 64

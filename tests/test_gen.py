@@ -18,9 +18,9 @@ def test_tiny_config_shapes_and_determinism():
     a = make_config(0)
     b = make_config(0)
     assert a.U.shape == (4, 5, 1024) and a.target.shape == (4, 6, 1024)
-    assert a.W1.shape == (1024, 32) and a.W2t.shape == (1024, 32) and a.w.shape == (96,)
+    assert a.W1.shape == (1024, 32) and a.W2.shape == (32, 1024) and a.w.shape == (96,)
     assert a.uniforms.shape == (4, 6, 2) and np.all(a.uniforms < 1) and np.all(a.uniforms >= 0)
-    for f in ("U", "target", "W1", "W2t", "w", "hidden", "anchor", "uniforms"):
+    for f in ("U", "target", "W1", "W2", "w", "hidden", "anchor", "uniforms"):
         np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
     assert a.sps[0] == 0 and abs(a.sps[64] - 500.0) < 1e-12
 

@@ -54,14 +54,14 @@ def run_step(wl, scheduler=None):
 
 
 def check_all(wl, out, draft_rows=None, verify_requests=None):
-    W1_64, W2t_64 = f64(wl.W1), f64(wl.W2t)
+    W1_64, W2_64 = f64(wl.W1), f64(wl.W2)
     rep = {}
-    rep["draft"] = check_draft(wl, W1_64, W2t_64, out["tokens"], out["q_tok"], out["row_max"],
+    rep["draft"] = check_draft(wl, W1_64, W2_64, out["tokens"], out["q_tok"], out["row_max"],
                                out["row_logZ"], rows=draft_rows)
     rep["conf"] = check_confidence(wl, out["tokens"], out["conf"])
     if out["sched"]:
         rep["sched"] = check_schedule(out["conf"], wl.sps, out["ell"], out["order"], out["stats"])
-    rep["verify"] = check_verify(wl, W1_64, W2t_64, out["tokens"], out["ell"], out["out_tokens"],
+    rep["verify"] = check_verify(wl, W1_64, W2_64, out["tokens"], out["ell"], out["out_tokens"],
                                  out["n_accepted"], out["ratio"], requests=verify_requests)
     assert out["status"] == 0, f"device status flags {out['status']}"
     print(rep, flush=True)
@@ -123,9 +123,9 @@ def test_strong_bias_changes_the_draft():
     wl = SMALL["bf16-strong-bias"]()
     out = run_step(wl)
     wl0 = SMALL["bf16-strong-bias"]()
-    wl0.W2t = np.zeros_like(wl0.W2t)
+    wl0.W2 = np.zeros_like(wl0.W2)
     out0 = run_step(wl0)
-    check_draft(wl0, f64(wl0.W1), f64(wl0.W2t), out0["tokens"], out0["q_tok"], out0["row_max"],
+    check_draft(wl0, f64(wl0.W1), f64(wl0.W2), out0["tokens"], out0["q_tok"], out0["row_max"],
                 out0["row_logZ"])
     assert (out["tokens"] != out0["tokens"]).mean() > 0.3
 
@@ -142,7 +142,7 @@ def test_verify_extreme_lengths(ell_value):
     st = Step(d).run()
     torch.cuda.synchronize()
     h = lambda t: t.cpu().numpy()
-    rep = check_verify(wl, f64(wl.W1), f64(wl.W2t), h(st.tokens), h(d.fixed_ell), h(st.out_tokens),
+    rep = check_verify(wl, f64(wl.W1), f64(wl.W2), h(st.tokens), h(d.fixed_ell), h(st.out_tokens),
                        h(st.n_accepted), h(st.ratio))
     if L == 0:
         assert np.all(h(st.n_accepted) == 0)
@@ -163,7 +163,7 @@ def test_verify_rejections_past_eight_slots():
     st = Step(d).run()
     torch.cuda.synchronize()
     h = lambda t: t.cpu().numpy()
-    rep = check_verify(wl, f64(wl.W1), f64(wl.W2t), h(st.tokens), h(d.fixed_ell), h(st.out_tokens),
+    rep = check_verify(wl, f64(wl.W1), f64(wl.W2), h(st.tokens), h(d.fixed_ell), h(st.out_tokens),
                        h(st.n_accepted), h(st.ratio))
     n = h(st.n_accepted)
     assert np.any(n < 8) and np.any((n > 8) & (n < wl.gamma)) and np.any(n == wl.gamma), n
@@ -251,7 +251,7 @@ def test_draft_paths_agree(name):
         old = dv.dspark_set_draft_path(path)
         try:
             st = torch.zeros((1,), dtype=torch.int32, device="cuda")
-            out = dv.dspark_draft_block(d.U, d.W1, d.W2t, d.anchor, d.temperature, d.uniforms,
+            out = dv.dspark_draft_block(d.U, d.W1, d.W2, d.anchor, d.temperature, d.uniforms,
                                         status=st)
             torch.cuda.synchronize()
         finally:
@@ -267,7 +267,7 @@ def test_draft_paths_agree(name):
     if B * g > 200:
         rng = np.random.default_rng(7)
         rows = [(int(i) // g, int(i) % g) for i in rng.choice(B * g, 40, replace=False)]
-    print(check_draft(wl, f64(wl.W1), f64(wl.W2t), *res[1][:4], rows=rows), flush=True)
+    print(check_draft(wl, f64(wl.W1), f64(wl.W2), *res[1][:4], rows=rows), flush=True)
 
 
 def test_repeat_is_deterministic():

@@ -44,18 +44,18 @@ def test_mean_accepted_length_matches_closed_form(T):
         hidden=np.repeat(one.hidden, nb, axis=0), anchor=np.repeat(one.anchor, nb),
         temperature=np.repeat(one.temperature, nb),
         uniforms=rng.random((nb, gamma + 1, 2), dtype=np.float32),
-        W2t=to_bf16_bits(np.zeros((V, 256), dtype=np.float32)), requests=np.arange(nb))
+        W2=to_bf16_bits(np.zeros((256, V), dtype=np.float32)), requests=np.arange(nb))
     d = upload(wl, "cuda", scheduler=False)
     st = torch.zeros((1,), dtype=torch.int32, device="cuda")
-    dr = dv.dspark_draft_block(d.U, d.W1, d.W2t, d.anchor, d.temperature, d.uniforms, status=st)
-    _, n_acc, _ = dv.dspark_verify(d.target, d.U, d.W1, d.W2t, d.anchor, dr["tokens"],
+    dr = dv.dspark_draft_block(d.U, d.W1, d.W2, d.anchor, d.temperature, d.uniforms, status=st)
+    _, n_acc, _ = dv.dspark_verify(d.target, d.U, d.W1, d.W2, d.anchor, dr["tokens"],
                                    dr["q_tok"], dr["row_max"], dr["row_logZ"], d.temperature,
                                    d.uniforms, d.fixed_ell, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     n = n_acc.cpu().numpy().astype(np.float64)
     # per-position acceptance probabilities of the (prefix-independent) rows
-    alpha = O.tv_label(one.target, one.U, O.f64(one.W1), np.zeros((V, 256)), one.anchor,
+    alpha = O.tv_label(one.target, one.U, O.f64(one.W1), np.zeros((256, V)), one.anchor,
                        np.zeros((1, gamma), dtype=np.int64), one.temperature)["label"][0]
     surv = np.cumprod(alpha)                      # P(n >= j), j = 1..gamma
     mean = surv.sum()

@@ -68,8 +68,8 @@ def _run(wl):
     from draft_verify_sampling_block_amd.step import upload
     d = upload(wl, "cuda", scheduler=False)
     st = torch.zeros((1,), dtype=torch.int32, device="cuda")
-    dr = dv.dspark_draft_block(d.U, d.W1, d.W2t, d.anchor, d.temperature, d.uniforms, status=st)
-    tv, label = dv.dspark_tv_label(d.target, d.U, d.W1, d.W2t, d.anchor, dr["tokens"],
+    dr = dv.dspark_draft_block(d.U, d.W1, d.W2, d.anchor, d.temperature, d.uniforms, status=st)
+    tv, label = dv.dspark_tv_label(d.target, d.U, d.W1, d.W2, d.anchor, dr["tokens"],
                                    dr["row_max"], dr["row_logZ"], d.temperature, status=st)
     torch.cuda.synchronize()
     h = lambda t: t.cpu().numpy()
@@ -82,7 +82,7 @@ def test_tv_label_small(name):
     wl = CASES[name]()
     tokens, tv, label, status = _run(wl)
     assert status == 0, status
-    rep = check_tv(wl, f64(wl.W1), f64(wl.W2t), tokens, tv, label)
+    rep = check_tv(wl, f64(wl.W1), f64(wl.W2), tokens, tv, label)
     print(rep, flush=True)
     assert np.all((tv >= -1e-6) & (tv <= 1 + 1e-6))
 
@@ -96,7 +96,7 @@ def test_tv_label_full_size(cfg):
     rng = np.random.default_rng(cfg)
     B, g = tokens.shape
     rows = [(int(i) // g, int(i) % g) for i in rng.choice(B * g, 24, replace=False)]
-    rep = check_tv(wl, f64(wl.W1), f64(wl.W2t), tokens, tv, label, rows=rows)
+    rep = check_tv(wl, f64(wl.W1), f64(wl.W2), tokens, tv, label, rows=rows)
     print(rep, flush=True)
     assert np.all(np.isfinite(tv))
 

@@ -23,9 +23,9 @@ def test_bias_is_row_of_explicit_transition_matrix():
     for a in range(V):                     # explicit transition matrix, entry by entry
         for b in range(V):
             M[a, b] = sum(A[a, i] * Bm[i, b] for i in range(r))
-    W2t = Bm.T.copy()                      # stored [V, r]
+    W2 = Bm                               # stored [r, V]
     for prev in range(V):
-        np.testing.assert_allclose(O.markov_bias(A, W2t, prev), M[prev], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(O.markov_bias(A, W2, prev), M[prev], rtol=0, atol=1e-12)
 
 
 def test_bias_full_rank_identity_embedding_recovers_matrix():
@@ -35,7 +35,7 @@ def test_bias_full_rank_identity_embedding_recovers_matrix():
     V = 9
     M = rng.normal(size=(V, V))
     for prev in range(V):
-        np.testing.assert_array_equal(O.markov_bias(np.eye(V), M.T.copy(), prev), M[prev])
+        np.testing.assert_array_equal(O.markov_bias(np.eye(V), M, prev), M[prev])
 
 
 def _cells(fn, n):
@@ -103,7 +103,7 @@ def test_block_follows_a_dominant_transition_chain():
     anchor = np.array([0, 4, 10])
     rng = np.random.default_rng(3)
     uni = rng.random((B, gamma + 1, 2))
-    out = O.draft_block(U, np.eye(V), M.T.copy(), anchor, np.ones(B), uni)
+    out = O.draft_block(U, np.eye(V), M, anchor, np.ones(B), uni)
     for b in range(B):
         expect = [(anchor[b] + 3 * (k + 1)) % V for k in range(gamma)]
         assert list(out["tokens"][b]) == expect
@@ -119,8 +119,8 @@ def test_w2_zero_is_a_parallel_drafter():
     U = np.log(wts)
     W1 = rng.normal(size=(V, r))
     uni = rng.random((B, gamma + 1, 2))
-    a = O.draft_block(U, W1, np.zeros((V, r)), np.array([0, 1]), np.ones(B), uni)
-    b = O.draft_block(U, W1, np.zeros((V, r)), np.array([5, 2]), np.ones(B), uni)
+    a = O.draft_block(U, W1, np.zeros((r, V)), np.array([0, 1]), np.ones(B), uni)
+    b = O.draft_block(U, W1, np.zeros((r, V)), np.array([5, 2]), np.ones(B), uni)
     np.testing.assert_array_equal(a["tokens"], b["tokens"])
     for bb in range(B):
         for k in range(gamma):
@@ -135,12 +135,12 @@ def test_forced_draft_matches_free_draft_on_its_own_tokens():
     rng = np.random.default_rng(5)
     B, gamma, V, r = 3, 4, 17, 4
     U = rng.normal(size=(B, gamma, V))
-    W1, W2t = rng.normal(size=(V, r)), rng.normal(size=(V, r))
+    W1, W2 = rng.normal(size=(V, r)), rng.normal(size=(V, r)).T
     anchor = rng.integers(0, V, B)
     T = np.array([1.0, 0.6, 0.0])
     uni = rng.random((B, gamma + 1, 2))
-    free = O.draft_block(U, W1, W2t, anchor, T, uni)
-    forced = O.draft_forced(U, W1, W2t, anchor, T, free["tokens"], uniforms=uni)
+    free = O.draft_block(U, W1, W2, anchor, T, uni)
+    forced = O.draft_forced(U, W1, W2, anchor, T, free["tokens"], uniforms=uni)
     for d in forced:
         b, k = d["b"], d["k"]
         assert d["x_oracle"] == free["tokens"][b, k]

@@ -30,24 +30,24 @@ def _case(seed, B=3, gamma=3, V=7, rank=3, T=1.0, w=0.7, noise=0.8):
     rng = np.random.default_rng(seed)
     U = rng.normal(0, 1.0, (B, gamma, V))
     W1 = rng.normal(0, w, (V, rank))
-    W2t = rng.normal(0, w, (V, rank))
+    W2 = rng.normal(0, w, (V, rank)).T
     target = np.concatenate([U, rng.normal(0, 1.0, (B, 1, V))], axis=1)
     target = target + rng.normal(0, noise, target.shape)
     anchor = rng.integers(0, V, B)
     tokens = rng.integers(0, V, (B, gamma))
     temp = np.full(B, T)
-    return U, W1, W2t, target, anchor, tokens, temp
+    return U, W1, W2, target, anchor, tokens, temp
 
 
 @pytest.mark.parametrize("seed", range(10))
 def test_label_is_the_accept_mass(seed):
-    U, W1, W2t, target, anchor, tokens, temp = _case(seed, T=[0.6, 1.0, 1.7][seed % 3])
-    out = O.tv_label(target, U, W1, W2t, anchor, tokens, temp)
+    U, W1, W2, target, anchor, tokens, temp = _case(seed, T=[0.6, 1.0, 1.7][seed % 3])
+    out = O.tv_label(target, U, W1, W2, anchor, tokens, temp)
     B, gamma, V = U.shape
     for b in range(B):
         for k in range(gamma):
             prev = anchor[b] if k == 0 else tokens[b, k - 1]
-            z = U[b, k] + W2t @ W1[prev]
+            z = U[b, k] + W1[prev] @ W2
             q = _softmax(z / temp[b])
             p = _softmax(target[b, k] / temp[b])
             mass = math.fsum(q[x] * min(1.0, p[x] / q[x]) for x in range(V))
@@ -63,7 +63,7 @@ def test_label_matches_empirical_acceptance_of_verification():
     V, rank = 6, 2
     U = rng.normal(0, 1.0, (1, 1, V))
     W1 = rng.normal(0, 0.9, (V, rank))
-    W2t = rng.normal(0, 0.9, (V, rank))
+    W2 = rng.normal(0, 0.9, (V, rank)).T
     target = rng.normal(0, 1.2, (1, 2, V))
     anchor = np.array([2])
     temp = np.array([0.9])
@@ -72,12 +72,12 @@ def test_label_matches_empirical_acceptance_of_verification():
     lab = 0.0
     for _ in range(n):
         uni = rng.random((1, 2, 2))
-        d = O.draft_block(U, W1, W2t, anchor, temp, uni)
-        v = O.verify(target, U, W1, W2t, anchor, d["tokens"], d["q_tok"], temp, uni,
+        d = O.draft_block(U, W1, W2, anchor, temp, uni)
+        v = O.verify(target, U, W1, W2, anchor, d["tokens"], d["q_tok"], temp, uni,
                      np.array([1]))
         acc += int(v["n_accepted"][0])
     # the label does not depend on which token was drafted at k = 0
-    lab = O.tv_label(target, U, W1, W2t, anchor, np.zeros((1, 1), dtype=int), temp)["label"][0, 0]
+    lab = O.tv_label(target, U, W1, W2, anchor, np.zeros((1, 1), dtype=int), temp)["label"][0, 0]
     rate = acc / n
     sigma = math.sqrt(lab * (1 - lab) / n)
     assert abs(rate - lab) < 5 * sigma, (rate, lab, sigma)
@@ -89,11 +89,11 @@ def test_equal_distributions_give_one_and_disjoint_give_zero():
     U[0, 0] = [0.1, 0.5, -0.3, 0.2, 0.0]
     U[0, 1] = [-40.0, 40.0, -40.0, -40.0, -40.0]
     W1 = np.zeros((V, 2))
-    W2t = np.zeros((V, 2))
+    W2 = np.zeros((2, V))
     target = np.zeros((1, 3, V))
     target[0, 0] = U[0, 0]                               # p == q
     target[0, 1] = [40.0, -40.0, -40.0, -40.0, -40.0]    # mass on another token
-    out = O.tv_label(target, U, W1, W2t, np.array([0]), np.array([[1, 1]]), np.array([1.0]))
+    out = O.tv_label(target, U, W1, W2, np.array([0]), np.array([[1, 1]]), np.array([1.0]))
     assert abs(out["label"][0, 0] - 1.0) < 1e-15
     assert out["label"][0, 1] < 1e-30
 
@@ -104,27 +104,27 @@ def test_greedy_rows_compare_argmaxes():
     target = np.zeros((2, 3, V))
     target[:, :, 2] = 1.0
     target[1, 1, 3] = 5.0
-    out = O.tv_label(target, U, np.zeros((V, 1)), np.zeros((V, 1)), np.array([0, 0]),
+    out = O.tv_label(target, U, np.zeros((V, 1)), np.zeros((1, V)), np.array([0, 0]),
                      np.array([[2, 2], [2, 2]]), np.array([0.0, 0.0]))
     assert out["label"].tolist() == [[1.0, 1.0], [1.0, 0.0]]
 
 
 def test_total_variation_is_symmetric():
     # with no Markov bias, swapping draft and target logits keeps the label
-    U, W1, W2t, target, anchor, tokens, temp = _case(5)
-    Z = np.zeros_like(W1)
-    a = O.tv_label(target, U, Z, Z, anchor, tokens, temp)["tv"]
+    U, W1, W2, target, anchor, tokens, temp = _case(5)
+    Z1, Z2 = np.zeros_like(W1), np.zeros_like(W2)
+    a = O.tv_label(target, U, Z1, Z2, anchor, tokens, temp)["tv"]
     swapped_target = np.concatenate([U, target[:, -1:]], axis=1)
-    b = O.tv_label(swapped_target, target[:, :-1], Z, Z, anchor, tokens, temp)["tv"]
+    b = O.tv_label(swapped_target, target[:, :-1], Z1, Z2, anchor, tokens, temp)["tv"]
     np.testing.assert_allclose(a, b, atol=1e-14)
 
 
 def test_label_reads_the_previous_drafted_token():
-    U, W1, W2t, target, anchor, tokens, temp = _case(8, w=1.5)
-    base = O.tv_label(target, U, W1, W2t, anchor, tokens, temp)["label"]
+    U, W1, W2, target, anchor, tokens, temp = _case(8, w=1.5)
+    base = O.tv_label(target, U, W1, W2, anchor, tokens, temp)["label"]
     t2 = tokens.copy()
     t2[:, 1] = (t2[:, 1] + 1) % U.shape[2]
-    moved = O.tv_label(target, U, W1, W2t, anchor, t2, temp)["label"]
+    moved = O.tv_label(target, U, W1, W2, anchor, t2, temp)["label"]
     # position 1's own token does not enter its label; position 2 reads it
     np.testing.assert_array_equal(base[:, :2], moved[:, :2])
     assert np.all(np.abs(base[:, 2] - moved[:, 2]) > 1e-9)

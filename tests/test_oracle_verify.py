@@ -71,7 +71,7 @@ def _tv(p, q):
 def test_acceptance_identity_exact(seed):
     step = TinyStep(R=1, gamma=1, V=5, rank=2, seed=20 + seed, T=1.0, ell=[1])
     # draft distribution of position 1 and target of slot 1, by construction
-    z = step.U[0, 0] + step.W2t @ step.W1[step.anchor[0]]
+    z = step.U[0, 0] + step.W1[step.anchor[0]] @ step.W2
     q = np.exp(z - z.max())
     q /= q.sum()
     p = step.ptab[0][()]
@@ -81,9 +81,9 @@ def test_acceptance_identity_exact(seed):
     t = 0.0
     while t < 1.0:
         u = np.array([[[t, 0.5], [0.5, 0.5]]])
-        d = O.draft_block(step.U, step.W1, step.W2t, step.anchor, step.T, u)
+        d = O.draft_block(step.U, step.W1, step.W2, step.anchor, step.T, u)
         lo, hi = d["lo"][0, 0], d["hi"][0, 0]
-        v = O.verify(step.target_logits(d["tokens"]), step.U, step.W1, step.W2t, step.anchor,
+        v = O.verify(step.target_logits(d["tokens"]), step.U, step.W1, step.W2, step.anchor,
                      d["tokens"], d["q_tok"], step.T, u, [1])
         total += (hi - lo) * min(1.0, v["ratio"][0, 0])
         t = hi if hi > t else np.nextafter(t, 2)
@@ -102,12 +102,12 @@ def test_acceptance_rate_statistical_matches_closed_form():
     U = np.broadcast_to(Ub, (N, gamma, V))
     target = np.broadcast_to(np.concatenate([tgt[0]]), (N, gamma + 1, V))
     W1 = rng.normal(size=(V, r))
-    W2t = np.zeros((V, r))
+    W2 = np.zeros((r, V))
     anchor = rng.integers(0, V, N)
     T = np.ones(N)
     uni = rng.random((N, gamma + 1, 2))
-    d = O.draft_block(U, W1, W2t, anchor, T, uni)
-    v = O.verify(target, U, W1, W2t, anchor, d["tokens"], d["q_tok"], T, uni, np.full(N, gamma))
+    d = O.draft_block(U, W1, W2, anchor, T, uni)
+    v = O.verify(target, U, W1, W2, anchor, d["tokens"], d["q_tok"], T, uni, np.full(N, gamma))
     alpha = []
     for k in range(gamma):
         q = np.exp(Ub[k] - Ub[k].max()); q /= q.sum()
@@ -159,7 +159,7 @@ def test_non_anticipation_counterexample_printed_numbers():
         return ell
 
     kw = dict(R=1, gamma=gamma, V=V, rank=1, seed=41, T=1.0, U=U, W1=np.zeros((V, 1)),
-              W2t=np.zeros((V, 1)), ptab=ptab, anchor=[0], sps=sps)
+              W2=np.zeros((1, V)), ptab=ptab, anchor=[0], sps=sps)
     early = enumerate_law(TinyStep(conf=conf, **kw))
     ahead = enumerate_law(TinyStep(conf=conf, sched=look_ahead, **kw))
 
@@ -177,14 +177,14 @@ def test_greedy_rows_reduce_to_argmax_comparison():
     rng = np.random.default_rng(50)
     B, gamma, V, r = 6, 4, 9, 3
     U = rng.normal(size=(B, gamma, V))
-    W1, W2t = rng.normal(size=(V, r)), rng.normal(size=(V, r))
+    W1, W2 = rng.normal(size=(V, r)), rng.normal(size=(V, r)).T
     anchor = rng.integers(0, V, B)
     target = U[:, [0, 1, 2, 3, 3]] + rng.normal(0, 0.7, (B, gamma + 1, V))
     T = np.zeros(B)
     uni = rng.random((B, gamma + 1, 2))
-    d = O.draft_block(U, W1, W2t, anchor, T, uni)
+    d = O.draft_block(U, W1, W2, anchor, T, uni)
     ell = rng.integers(0, gamma + 1, B)
-    v = O.verify(target, U, W1, W2t, anchor, d["tokens"], d["q_tok"], T, uni, ell)
+    v = O.verify(target, U, W1, W2, anchor, d["tokens"], d["q_tok"], T, uni, ell)
     for b in range(B):
         n = 0
         while n < ell[b] and d["tokens"][b, n] == np.argmax(target[b, n]):
@@ -203,9 +203,9 @@ def test_identical_draft_and_target_accept_everything():
     T = np.array([1.0, 0.5, 2.0, 1.0, 0.0])
     uni = rng.random((B, gamma + 1, 2))
     anchor = rng.integers(0, V, B)
-    d = O.draft_block(U, W1, np.zeros((V, r)), anchor, T, uni)
+    d = O.draft_block(U, W1, np.zeros((r, V)), anchor, T, uni)
     ell = np.array([4, 3, 0, 2, 4])
-    v = O.verify(target, U, W1, np.zeros((V, r)), anchor, d["tokens"], d["q_tok"], T, uni, ell)
+    v = O.verify(target, U, W1, np.zeros((r, V)), anchor, d["tokens"], d["q_tok"], T, uni, ell)
     np.testing.assert_array_equal(v["n_accepted"], ell)
 
 
@@ -217,8 +217,8 @@ def test_degenerate_residual_falls_back_to_target():
     U = np.log(w)[None, None]
     target = np.log(np.stack([w, w]))[None]
     uni = np.array([[[0.3, 0.9], [0.55, 0.0]]])
-    d = O.draft_block(U, np.zeros((V, 1)), np.zeros((V, 1)), [0], [1.0], uni)
-    v = O.verify(target, U, np.zeros((V, 1)), np.zeros((V, 1)), [0], d["tokens"],
+    d = O.draft_block(U, np.zeros((V, 1)), np.zeros((1, V)), [0], [1.0], uni)
+    v = O.verify(target, U, np.zeros((V, 1)), np.zeros((1, V)), [0], d["tokens"],
                  2 * d["q_tok"], [1.0], uni, [1])
     assert v["n_accepted"][0] == 0 and v["degenerate"][0]
     # u = 0.55 falls in token 3's cell of p = w / 10 ([0.6, ...) is token 3's end)
