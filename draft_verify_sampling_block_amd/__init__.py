@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "DsparkError", "lib_path", "load", "dspark_draft_block", "dspark_confidence",
-    "dspark_schedule", "dspark_schedule_capacity", "dspark_schedule_threshold", "dspark_verify",
+    "dspark_schedule", "dspark_schedule_noalloc", "dspark_schedule_capacity", "dspark_schedule_threshold", "dspark_verify",
     "dspark_tv_label", "dspark_tv_label_workspace", "dspark_draft_block_workspace",
     "dspark_verify_workspace", "dspark_schedule_workspace", "exported_names", "header_names",
     "dspark_trace_enable", "dspark_trace_summary", "dspark_set_draft_path",
@@ -60,6 +60,7 @@ _SIGS = {
     "dspark_confidence": (_I, [_I] * 6 + [_P] * 5 + [ctypes.c_float, _P, _P, _P]),
     "dspark_schedule_workspace": (_SZ, [_I, _I]),
     "dspark_schedule": (_I, [_I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dspark_schedule_noalloc": (_I, [_I, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
     "dspark_schedule_capacity": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dspark_schedule_threshold": (_I, [_I, _I, _P, ctypes.c_double, _P, _P, _P, _P, _P, _SZ,
                                        _P]),
@@ -266,6 +267,27 @@ def dspark_schedule(conf, sps, *, ell=None, order=None, stats=None, status=None,
     _check(lib.dspark_schedule(R, gamma, _ptr(conf), _ptr(sps), int(sps.numel()), _ptr(ell),
                                _ptr(order), _ptr(stats), _ptr(status), _ptr(ws),
                                0 if ws is None else ws.numel(), _stream()))
+    return ell, order, stats
+
+
+def dspark_schedule_noalloc(conf, sps, *, ell=None, order=None, stats=None, status=None,
+                            want_order=True):
+    """dspark_schedule without a workspace (the library's own per-device
+    scratch holds the ranks); calls overlapping on one device race.
+    Returns (ell, order, stats)."""
+    lib = load()
+    R, gamma = conf.shape
+    dev = conf.device
+    _need(sps, "sps", torch.float64, None, dev)
+    _need(conf, "conf", torch.float32)
+    ell = _out(ell, "ell", torch.int32, (R,), dev)
+    if order is not None or want_order:
+        order = _out(order, "order", torch.int32, (R * gamma,), dev)
+    stats = _out(stats, "stats", torch.float64, (3,), dev)
+    status = _status(status, dev)
+    _check(lib.dspark_schedule_noalloc(R, gamma, _ptr(conf), _ptr(sps), int(sps.numel()),
+                                       _ptr(ell), _ptr(order), _ptr(stats), _ptr(status),
+                                       _stream()))
     return ell, order, stats
 
 

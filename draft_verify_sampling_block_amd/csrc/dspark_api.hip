@@ -133,16 +133,22 @@ size_t dspark_schedule_workspace(int R, int gamma) {
 }
 
 namespace {
-// checks shared by the three scheduler entry points
-int check_schedule(const char* fn, int R, int gamma, const float* conf, int32_t* ell,
-                   int32_t* order, double* stats, int32_t* status, void* workspace,
-                   size_t workspace_bytes) {
+// checks shared by the scheduler entry points (all but the workspace)
+int check_schedule_args(const char* fn, int R, int gamma, const float* conf, int32_t* ell,
+                        int32_t* order, double* stats, int32_t* status) {
   if (R < 1) return fail(DSPARK_EINVAL, "%s: R=%d must be >= 1", fn, R);
   if (gamma < 1 || gamma > 64) return fail(DSPARK_EINVAL, "%s: gamma=%d outside [1,64]", fn, gamma);
   if ((long long)R * gamma > dspark::kScheduleMaxKeys)
     return fail(DSPARK_EUNSUPPORTED, "%s: R*gamma=%lld exceeds %d candidates", fn,
                 (long long)R * gamma, dspark::kScheduleMaxKeys);
   REQUIRE_PTR(conf); REQUIRE_PTR(ell); OPT_PTR(order); OPT_PTR(stats); OPT_PTR(status);
+  return DSPARK_OK;
+}
+int check_schedule(const char* fn, int R, int gamma, const float* conf, int32_t* ell,
+                   int32_t* order, double* stats, int32_t* status, void* workspace,
+                   size_t workspace_bytes) {
+  const int rc = check_schedule_args(fn, R, gamma, conf, ell, order, stats, status);
+  if (rc) return rc;
   const size_t need = dspark::schedule_workspace_bytes(R, gamma);
   if (need && (!workspace || workspace_bytes < need))
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
@@ -164,6 +170,31 @@ int dspark_schedule(int R, int gamma, const float* conf, const double* sps, int 
   return hip_status(fn, dspark::launch_schedule(R, gamma, conf, sps, sps_len, dspark::kSchedTheta,
                                                 0.0, nullptr, ell, order, stats, status,
                                                 workspace, stream));
+}
+
+int dspark_schedule_noalloc(int R, int gamma, const float* conf, const double* sps, int sps_len,
+                            int32_t* ell, int32_t* order, double* stats, int32_t* status,
+                            hipStream_t stream) {
+  const char* fn = "dspark_schedule_noalloc";
+  if (sps_len < 1) return fail(DSPARK_EINVAL, "%s: sps_len=%d must be >= 1", fn, sps_len);
+  REQUIRE_PTR(sps);
+  int rc = check_schedule_args(fn, R, gamma, conf, ell, order, stats, status);
+  if (rc) return rc;
+  const size_t need = dspark::schedule_workspace_bytes(R, gamma);
+  if (need > dspark::schedule_scratch_bytes())
+    return fail(DSPARK_EUNSUPPORTED,
+                "%s: R*gamma=%lld needs %zu bytes of scratch, more than the %zu bytes the "
+                "allocation-free variant holds", fn, (long long)R * gamma, need,
+                dspark::schedule_scratch_bytes());
+  int32_t* scr = nullptr;
+  if (need) {
+    hipError_t e = hipSuccess;
+    scr = dspark::schedule_scratch(&e);
+    if (!scr) return hip_status(fn, e != hipSuccess ? e : hipErrorInvalidSymbol);
+  }
+  return hip_status(fn, dspark::launch_schedule(R, gamma, conf, sps, sps_len, dspark::kSchedTheta,
+                                                0.0, nullptr, ell, order, stats, status, scr,
+                                                stream, /*traced=*/false));
 }
 
 int dspark_schedule_capacity(int R, int gamma, const float* conf, const double* capacity,

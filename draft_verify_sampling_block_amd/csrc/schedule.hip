@@ -30,6 +30,8 @@
 // are still ranked by their latest survival; the first K are taken) and
 // threshold ([billytse] 8 threshold sweep: every candidate whose survival is
 // at least the threshold).
+#include <mutex>
+
 #include "dspark_common.hpp"
 #include "dspark_launch.hpp"
 #include "schedule_launch.hpp"
@@ -420,21 +422,67 @@ size_t schedule_workspace_bytes(int R, int gamma) {
 hipError_t launch_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
                            int mode, double threshold, const double* capacity, int32_t* ell,
                            int32_t* order, double* stats, int32_t* status, void* ws,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool traced) {
   const int N = R * gamma;
   int32_t* ranks = nullptr;
   if (N <= kScheduleMergeKeys) {
     ranks = static_cast<int32_t*>(ws);
-    TraceScope tr("schedule_rank_kernel", stream);
+    TraceScope tr(traced ? "schedule_rank_kernel" : nullptr, stream);
     constexpr int kPerGroup = kRankThreads / kRankSplit;
     schedule_rank_kernel<<<dim3((N + kPerGroup - 1) / kPerGroup), dim3(kRankThreads), 0,
                            stream>>>(R, gamma, conf, ranks);
   }
-  TraceScope ts("schedule_kernel", stream);
+  TraceScope ts(traced ? "schedule_kernel" : nullptr, stream);
   schedule_kernel<<<dim3(1), dim3(1024), 0, stream>>>(R, gamma, conf, sps, sps_len, mode,
                                                       threshold, capacity, ell, order, stats,
                                                       ranks, status);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point (dspark_schedule_noalloc): the
+// candidates' ranks, int32, for up to kScheduleMergeKeys candidates (16 KB;
+// larger batches rank inside the one work-group and need none).  Every
+// device the library runs on holds one copy until the process ends; all
+// calls on a device share it, so calls that overlap on one device race.
+// Nothing in it needs clearing: the ranking kernel writes every rank the
+// scheduler kernel then reads.  In host code the array's name stands for a
+// host-side shadow, not a device address: host code only ever uses the
+// address schedule_scratch() looked up for the current device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) int32_t scratch[kScheduleMergeKeys];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+size_t schedule_scratch_bytes() { return (size_t)kScheduleMergeKeys * sizeof(int32_t); }
+
+int32_t* schedule_scratch(hipError_t* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kScratchDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {   // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *err = hipSuccess;
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace dspark

@@ -16,7 +16,9 @@ void trace_end(int slot, hipStream_t stream);
 struct TraceScope {
   int slot;
   hipStream_t stream;
-  TraceScope(const char* name, hipStream_t s) : slot(trace_begin(name, s)), stream(s) {}
+  // name NULL: this launch is never traced
+  TraceScope(const char* name, hipStream_t s)
+      : slot(name ? trace_begin(name, s) : -1), stream(s) {}
   ~TraceScope() { trace_end(slot, stream); }
 };
 

@@ -156,6 +156,24 @@ int dspark_schedule(int R, int gamma, const float* conf,
                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * dspark_schedule_noalloc: dspark_schedule for callers that cannot allocate
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * device allocation): the same arguments and results without a workspace.
+ * The candidates' ranks go to a scratch array of the library's own, 16 KB
+ * (4096 int32) per device, held from the first call on a device until the
+ * process ends; batches with R*gamma > 4096 need none.  The call allocates
+ * nothing (it never calls the tracer either).  Every call on one device
+ * shares that device's scratch: calls that overlap on one device (other
+ * streams, other host threads) race and give undefined results; serialise
+ * them.  R*gamma above what the scratch holds returns DSPARK_EUNSUPPORTED
+ * (with the size limits of dspark_schedule no such batch exists).
+ * ---------------------------------------------------------------------- */
+int dspark_schedule_noalloc(int R, int gamma, const float* conf,
+                            const double* sps, int sps_len,
+                            int32_t* ell, int32_t* order, double* stats,
+                            int32_t* status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * dspark_schedule_capacity: the two-step causal barrier ([billytse] 7;
  * [weigao] part 4, asynchronous scheduling).  The size of the next target
  * batch is fixed beforehand from older predictions; the current candidates

@@ -66,6 +66,9 @@ def test_host_validation_rejects_before_launch(lib):
                                   None) == -3
     assert lib.dspark_schedule(9000, 1, fake, fake, 10, fake, None, None, None, None, 0, None) == -5
     assert lib.dspark_schedule(4, 2, fake, fake, 0, fake, None, None, None, None, 0, None) == -1
+    assert lib.dspark_schedule_noalloc(9000, 1, fake, fake, 10, fake, None, None, None, None) == -5
+    assert lib.dspark_schedule_noalloc(4, 2, fake, fake, 0, fake, None, None, None, None) == -1
+    assert lib.dspark_schedule_noalloc(4, 2, fake + 4, fake, 5, fake, None, None, None, None) == -3
     assert lib.dspark_confidence(4, 5, 60, 1024, 32, 1, *([fake] * 5), ctypes.c_float(0.0), fake,
                                  None, None) == -1  # H % 8
     assert lib.dspark_verify(4, 5, 1024, 32, 1, *([fake] * 15), None, fake, 8, None) == -4
