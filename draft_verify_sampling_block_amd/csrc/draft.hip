@@ -21,6 +21,7 @@
 //  * multi-launch (any dtype / fallback): per position one
 //    vocabulary-parallel launch (draft_stats_kernel) and one request-parallel
 //    launch (draft_sample_kernel) doing the same two steps.
+#include <atomic>
 #include <type_traits>
 
 #include "dspark_common.hpp"
@@ -410,8 +411,20 @@ struct PdArgs {
   long long spin_cap;    // wall-clock ticks a wait may last
 };
 
+// Flag protocol between the work-groups of the running kernel.  Data and
+// flags are device-scope (agent) relaxed atomics: each access is coherent
+// across the chip's L2 slices.  A producer waits for its data stores to
+// complete (s_waitcnt, every wave, then a work-group barrier) before thread 0
+// stores the flag; a consumer issues its data loads only after it has seen
+// the flag.  The hardware waits give the ordering; compiler-only fences on
+// both sides keep the compiler from moving the data accesses across the flag
+// access.  (Agent-scope release/acquire would add a whole-L2 write-back or
+// invalidate per hop, which measured tens of microseconds per position.)
 __device__ inline uint32_t ld_flag(const uint32_t* p) { return ld_dev(p); }
-__device__ inline void st_flag(uint32_t* p, uint32_t v) { st_dev(p, v); }
+__device__ inline void st_flag(uint32_t* p, uint32_t v) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  st_dev(p, v);
+}
 
 // Wave 0 waits until flags[i*stride] >= want for all i < n; then the group
 // synchronises.  With `low` given (n <= kPdMaxRows), the low 24 bits of each
@@ -445,11 +458,13 @@ __device__ inline void wait_flags(const uint32_t* flags, int n, int stride, uint
     }
   }
   __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);   // data loads stay after the flags
 }
 
 // Every wave waits for its own stores to complete, then the group
 // synchronises; thread 0 may then raise a flag.
 __device__ inline void stores_done_group() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 }
@@ -858,7 +873,9 @@ __global__ void pdraft_reset_kernel(uint32_t* f0, int n0, uint32_t* f1, int n1) 
 // ---------------------------------------------------------------------------
 
 namespace {
-int g_draft_path = 0;  // 0 auto, 1 multi-launch, 2-4 persistent only (3: 8 waves, 4: 4 waves)
+// 0 auto, 1 multi-launch, 2-4 persistent only (3: 8 waves, 4: 4 waves);
+// process-wide, read by every call
+std::atomic<int> g_draft_path{0};
 
 struct DevInfo {
   int cus = 0;
@@ -885,9 +902,9 @@ DevInfo dev_info() {
 }
 }  // namespace
 
-void set_draft_path(int path) { g_draft_path = path; }
+int set_draft_path(int path) { return g_draft_path.exchange(path); }
 int device_cu_count() { return dev_info().cus; }
-int get_draft_path() { return g_draft_path; }
+int get_draft_path() { return g_draft_path.load(); }
 
 static size_t stats_bytes(int B, int V) { return align256((size_t)B * n_tiles(V) * 4); }
 
@@ -946,7 +963,7 @@ static hipError_t draft_persistent(int B, int gamma, int V, int rank, const uint
   // waves per group: 8 (one register tile each, two waves per SIMD, which
   // overlap one wave's reductions with the other's matrix instructions)
   // unless 4 (two tiles each) are asked for
-  const int nw = g_draft_path == 4 ? 4 : 8;
+  const int nw = get_draft_path() == 4 ? 4 : 8;
   const void* kern = nw == 8 ? reinterpret_cast<const void*>(pdraft_kernel<KS, 8, true>)
                              : reinterpret_cast<const void*>(pdraft_kernel<KS, 4, false>);
   int occ = 0;
@@ -980,17 +997,21 @@ hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, cons
                               const float* temperature, const float* uniforms, int32_t* tokens,
                               float* q_tok, float* row_max, float* row_logZ, int32_t* status,
                               void* ws, hipStream_t stream) {
+  // the persistent kernel reports a timed-out wait through the status word
+  // only, so without one the per-position launches (which never wait) run
+  const int path = get_draft_path();
+  const bool persist = path != 1 && status != nullptr;
   if (dtype == DSPARK_BF16) {
     auto* u = static_cast<const uint16_t*>(U);
     auto* w1 = static_cast<const uint16_t*>(W1);
     auto* w2 = static_cast<const uint16_t*>(W2);
 #define DSPARK_DRAFT_KS(KS)                                                                     \
   {                                                                                             \
-    if (g_draft_path != 1) {                                                                    \
+    if (persist) {                                                                              \
       hipError_t e = draft_persistent<KS>(B, gamma, V, rank, u, w1, w2, anchor, temperature,    \
                                           uniforms, tokens, q_tok, row_max, row_logZ, status,   \
                                           ws, stream);                                          \
-      if (e != hipErrorNotSupported || g_draft_path >= 2) return e;                             \
+      if (e != hipErrorNotSupported || path >= 2) return e;                                     \
     }                                                                                           \
     return draft_multi<uint16_t, KS>(B, gamma, V, rank, u, w1, w2, anchor, temperature,         \
                                      uniforms, tokens, q_tok, row_max, row_logZ, status, ws,    \

@@ -82,8 +82,7 @@ const char* dspark_version(void) { return "libdspark 0.1 gfx950"; }
 int dspark_set_draft_path(int path) {
   if (path < 0 || path > 4)
     return fail(DSPARK_EINVAL, "dspark_set_draft_path: path %d is not in 0..4", path);
-  const int old = dspark::get_draft_path();
-  dspark::set_draft_path(path);
+  const int old = dspark::set_draft_path(path);
   return old;
 }
 
@@ -103,6 +102,9 @@ int dspark_draft_block(int B, int gamma, int V, int rank, int dtype, const void*
   REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2); REQUIRE_PTR(anchor);
   REQUIRE_PTR(temperature); REQUIRE_PTR(uniforms); REQUIRE_PTR(tokens); REQUIRE_PTR(q_tok);
   REQUIRE_PTR(row_max); REQUIRE_PTR(row_logZ); OPT_PTR(status);
+  if (!status && dspark::get_draft_path() >= 2)
+    return fail(DSPARK_EINVAL, "%s: the persistent-only draft paths need a status word (a "
+                "timed-out wait is reported there only)", fn);
   const size_t need = dspark::draft_workspace_bytes(B, gamma, V, rank, dtype);
   if (!workspace || workspace_bytes < need)
     return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,

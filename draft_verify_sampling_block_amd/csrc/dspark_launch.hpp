@@ -15,7 +15,7 @@ size_t draft_workspace_bytes(int B, int gamma, int V, int rank, int dtype);
 // 0 = automatic (persistent kernel when possible), 1 = multi-launch only,
 // 2 = persistent only (fails with hipErrorNotSupported where it cannot run),
 // 3 / 4 = persistent only with 8 / 4 waves per work-group
-void set_draft_path(int path);
+int set_draft_path(int path);   // returns the previous setting
 int get_draft_path();
 // compute units of the current device (cached per device)
 int device_cu_count();

@@ -67,6 +67,10 @@ int dspark_trace_enable(int on) {
   std::lock_guard<std::mutex> lk(dspark::g_mu);
   dspark::recycle_all();
   dspark::g_on.store(on != 0);
+  if (!on) {   // tracing stops: every event is destroyed (none outlives it)
+    for (hipEvent_t e : dspark::g_pool) (void)hipEventDestroy(e);
+    dspark::g_pool.clear();
+  }
   return DSPARK_OK;
 }
 

@@ -17,7 +17,9 @@
  *    library never frees or retains it.  Arrays are dense, row-major, and
  *    16-byte aligned.  Nothing is allocated by the library.
  *  - Calls are asynchronous on `stream` (NULL = the default stream), keep no
- *    state between calls, and may be issued from several host threads.
+ *    state between calls (except the process-wide setting of
+ *    dspark_set_draft_path and the scratch of dspark_schedule_noalloc), and
+ *    may be issued from several host threads.
  *  - Arguments are validated on the host BEFORE anything is enqueued; on a
  *    validation error the call returns a negative status, enqueues nothing,
  *    and dspark_last_error() (thread-local) describes the problem.
@@ -100,6 +102,11 @@ const char* dspark_version(void);
  *      row_logZ [B,gamma] = log sum_v exp(z/T - row_max) (0 when greedy).
  * workspace: dspark_draft_block_workspace(...) bytes of device memory.
  * No full probability row is ever written.
+ * The single-launch (persistent) implementation synchronises its work-groups
+ * with bounded waits and reports a wait that gave up (DSPARK_DEV_TIMEOUT)
+ * through `status` only; with status NULL the per-position launches run
+ * instead (same results, no waits), and the persistent-only settings of
+ * dspark_set_draft_path make the call return DSPARK_EINVAL.
  * ---------------------------------------------------------------------- */
 size_t dspark_draft_block_workspace(int B, int gamma, int V, int rank, int dtype);
 int dspark_draft_block(int B, int gamma, int V, int rank, int dtype,
@@ -285,6 +292,8 @@ int dspark_trace_summary(char* buf, size_t len);
 
 /* ------------------------------------------------------------------------
  * Drafting implementation choice (process-wide; for tests and benchmarks).
+ * The setting is one atomic word read by every later dspark_draft_block
+ * call, from any host thread: the one exception to "keep no state".
  * 0 = automatic (default): the persistent single-launch kernel for bf16
  *     inputs when the device supports cooperative launch and the vocabulary
  *     fits its resident tiles, else one launch pair per position;
