@@ -54,6 +54,10 @@ __all__ = [
     "target_probs",
     "verify",
     "tv_label",
+    "bf16_round",
+    "rnn_step",
+    "rnn_draft_block",
+    "rnn_forced",
 ]
 
 
@@ -168,7 +172,7 @@ def draft_block(U, W1, W2, anchor, temperature, uniforms):
     return out
 
 
-def draft_forced(U, W1, W2, anchor, temperature, tokens, uniforms=None, rows=None):
+def draft_forced(U, W1, W2, anchor, temperature, tokens, uniforms=None, rows=None, emb=None):
     """Draft statistics with the sampled tokens given (teacher forcing).
 
     Computes, for the listed (b, k) rows (all rows if ``rows`` is None), the
@@ -176,6 +180,10 @@ def draft_forced(U, W1, W2, anchor, temperature, tokens, uniforms=None, rows=Non
     k == 0), and reports q at tokens[b, k], the row stats, the interval of u
     that selects tokens[b, k] and, when uniforms are given, the token the
     oracle itself would draw with uniforms[b, k, 0] and its margin.
+
+    ``emb`` [B, gamma, r] (optional): the vector each position projects
+    through W2 (the RNN head's output); the bias of (b, k) is then
+    emb[b, k] @ W2 instead of the Markov head's W1[prev] @ W2.
     """
     U_is64 = isinstance(U, np.ndarray) and U.dtype == np.float64
     W1 = W1 if (isinstance(W1, np.ndarray) and W1.dtype == np.float64) else f64(W1)
@@ -187,7 +195,7 @@ def draft_forced(U, W1, W2, anchor, temperature, tokens, uniforms=None, rows=Non
     for b, k in rows:
         prev = int(anchor[b]) if k == 0 else int(tokens[b, k - 1])
         Urow = U[b, k] if U_is64 else f64(U[b, k])
-        z = Urow + markov_bias(W1, W2, prev)
+        z = Urow + (markov_bias(W1, W2, prev) if emb is None else f64(emb[b, k]) @ W2)
         T = float(temperature[b])
         x = int(tokens[b, k])
         if T > 0:
@@ -407,7 +415,7 @@ def _draft_probs(z: np.ndarray, temperature: float) -> np.ndarray:
 
 
 def verify(target, U, W1, W2, anchor, tokens, q_tok, temperature, uniforms, ell,
-           requests=None, keep_final=False):
+           requests=None, keep_final=False, emb=None):
     """Speculative rejection sampling over each request's verified prefix.
 
     [billytse] 1 and [xhh] acceptance-rule Q&A: draft token x_k (drawn from
@@ -430,6 +438,8 @@ def verify(target, U, W1, W2, anchor, tokens, q_tok, temperature, uniforms, ell,
     ``requests`` restricts the work to those request indices (others stay at
     their fill values); ``keep_final`` also returns, per processed request,
     the normalised cumulative distribution of the final draw (``final_cdf``).
+    ``emb`` [B, gamma, r]: the drafter's projected vectors (RNN head); the
+    q recompute at a reject j then uses emb[b, j] @ W2 as its bias.
     """
     W1 = W1 if (isinstance(W1, np.ndarray) and W1.dtype == np.float64) else f64(W1)
     W2 = W2 if (isinstance(W2, np.ndarray) and W2.dtype == np.float64) else f64(W2)
@@ -461,7 +471,8 @@ def verify(target, U, W1, W2, anchor, tokens, q_tok, temperature, uniforms, ell,
         if rejected_at >= 0:
             j = rejected_at
             prev = int(anchor[b]) if j == 0 else int(tokens[b, j - 1])
-            z = f64(U[b, j]) + markov_bias(W1, W2, prev)
+            z = f64(U[b, j]) + (markov_bias(W1, W2, prev) if emb is None
+                                else f64(emb[b, j]) @ W2)
             q = _draft_probs(z, T)
             res = np.maximum(0.0, p - q)
             if not (np.sum(res) > 0.0):
@@ -492,7 +503,7 @@ def verify(target, U, W1, W2, anchor, tokens, q_tok, temperature, uniforms, ell,
 # (5) acceptance label: total variation between draft and target
 # ----------------------------------------------------------------------------
 
-def tv_label(target, U, W1, W2, anchor, tokens, temperature, rows=None):
+def tv_label(target, U, W1, W2, anchor, tokens, temperature, rows=None, emb=None):
     """Per-position acceptance label from the total variation distance.
 
     [weigao] part 3 (the confidence head's training target) and [billytse]
@@ -508,7 +519,8 @@ def tv_label(target, U, W1, W2, anchor, tokens, temperature, rows=None):
     it drew) and one-hot p at the target's lowest-index argmax, so its label
     is 1 when they agree, else 0.
 
-    rows: optional list of (b, k) to compute (others are NaN).
+    rows: optional list of (b, k) to compute (others are NaN).  ``emb``
+    [B, gamma, r]: the RNN head's projected vectors (bias emb[b, k] @ W2).
     Returns dict(tv [B, gamma], label [B, gamma]).
     """
     B, gamma, V = np.asarray(U).shape
@@ -523,7 +535,147 @@ def tv_label(target, U, W1, W2, anchor, tokens, temperature, rows=None):
             tv[b, k] = 0.0 if int(np.argmax(target[b, k])) == x else 1.0
             continue
         prev = int(anchor[b]) if k == 0 else int(tokens[b, k - 1])
-        q = _draft_probs(U[b, k] + markov_bias(W1, W2, prev), T)
+        bias = markov_bias(W1, W2, prev) if emb is None else f64(emb[b, k]) @ f64(W2)
+        q = _draft_probs(U[b, k] + bias, T)
         p = target_probs(target[b, k], T)
         tv[b, k] = 0.5 * math.fsum(np.abs(p - q))
     return dict(tv=tv, label=1.0 - tv)
+
+
+# ----------------------------------------------------------------------------
+# (6) RNN head: a recurrent sequential bias
+# ----------------------------------------------------------------------------
+
+def bf16_round(x) -> np.ndarray:
+    """Nearest bf16 value of each entry (ties to even), as float64.
+
+    bf16 keeps 8 significant bits and float32's exponent range; the rounding
+    is done directly from the float64 value (no float32 step).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m 2^e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                 # below 2^-126 the quantum stays 2^-133
+    return np.ldexp(np.round(np.ldexp(x, 8 - e)), e - 8)
+
+
+def _sigmoid(x):
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def rnn_step(state, emb, h, Wr, br):
+    """One step of the RNN head.
+
+    [weigao] part 2 (the ``_rnn_step`` description): the previous state, the
+    previous token's embedding and the position's hidden state are
+    concatenated and passed through one linear layer, whose output is split
+    into gate, candidate and output; state_k = gate * state_{k-1} + (1 -
+    gate) * candidate, and the position's bias is W2 applied to tanh(output).
+    [billytse] 3.3: the recurrence lets each position see the whole block
+    prefix.
+
+    Readings (the pages give the split, not the activations or sizes): the
+    three parts each have the state size r (tanh(output) enters the same
+    r -> V projection W2 as the Markov head's W1 row); gate = sigmoid,
+    candidate = tanh; the linear layer is Wr [3r, 2r + H] (rows: gate,
+    candidate, output; columns: state, embedding, hidden) plus br [3r].
+
+    Returns (state_k, tanh(output)).
+    """
+    state = np.asarray(state, dtype=np.float64)
+    r = state.shape[0]
+    x = np.concatenate([state, np.asarray(emb, dtype=np.float64), np.asarray(h, dtype=np.float64)])
+    pre = np.asarray(Wr, dtype=np.float64) @ x + np.asarray(br, dtype=np.float64)
+    gate = _sigmoid(pre[:r])
+    cand = np.tanh(pre[r:2 * r])
+    out = np.tanh(pre[2 * r:3 * r])
+    return gate * state + (1.0 - gate) * cand, out
+
+
+def rnn_forced(W1, hidden, Wr, br, anchor, tokens):
+    """The RNN head's recurrence with the drafted tokens given.
+
+    Position k's embedding is the W1 row of the previous token (the anchor
+    for k = 0; the Markov embedding the pages' heads share), its state input
+    is the state after position k - 1 (zero before the first position: the
+    recurrence runs within one block).  Returns dict(emb [B, gamma, r]: the
+    vectors tanh(output) each position projects, state [B, gamma, r]: the
+    state after each position), float64, unrounded.
+    """
+    W1 = f64(W1)
+    h = f64(hidden)
+    Wr = f64(Wr)
+    br = np.asarray(br, dtype=np.float64)
+    tokens = np.asarray(tokens)
+    B, gamma = tokens.shape
+    r = W1.shape[1]
+    emb = np.zeros((B, gamma, r))
+    st = np.zeros((B, gamma, r))
+    for b in range(B):
+        s = np.zeros(r)
+        for k in range(gamma):
+            prev = int(anchor[b]) if k == 0 else int(tokens[b, k - 1])
+            s, o = rnn_step(s, W1[prev], h[b, k], Wr, br)
+            emb[b, k] = o
+            st[b, k] = s
+    return dict(emb=emb, state=st)
+
+
+def rnn_draft_block(U, W1, W2, hidden, Wr, br, anchor, temperature, uniforms, emb_round=None):
+    """Sequential sampling over a block with the RNN head.
+
+    The [billytse] 3.3 loop with the RNN head's bias: at each position the
+    head steps its recurrence on the previous sampled token (rnn_step), the
+    bias tanh(output) @ W2 is added to the position's base logits, and the
+    token is drawn from the softmax exactly as with the Markov head
+    (draft_row).  ``emb_round="bf16"`` rounds each projected vector to bf16
+    before the projection (the precision in which a bf16 step feeds it to
+    the matrix cores); None keeps float64.
+
+    Returns the fields of draft_block plus emb [B, gamma, r] (the projected
+    vectors, after rounding) and state [B, gamma, r].
+    """
+    U = f64(U)
+    W1 = f64(W1)
+    W2 = f64(W2)
+    h = f64(hidden)
+    Wr = f64(Wr)
+    br = np.asarray(br, dtype=np.float64)
+    uni = np.asarray(uniforms, dtype=np.float64)
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    out = {k: np.zeros((B, gamma)) for k in ("q_tok", "row_max", "row_logZ", "lo", "hi", "margin")}
+    tokens = np.zeros((B, gamma), dtype=np.int64)
+    emb = np.zeros((B, gamma, r))
+    st = np.zeros((B, gamma, r))
+    for b in range(B):
+        prev = int(anchor[b])
+        s = np.zeros(r)
+        T = float(temperature[b])
+        for k in range(gamma):
+            s, o = rnn_step(s, W1[prev], h[b, k], Wr, br)
+            if emb_round == "bf16":
+                o = bf16_round(o)
+            emb[b, k] = o
+            st[b, k] = s
+            z = U[b, k] + o @ W2
+            u = float(uni[b, k, 0])
+            d = draft_row(z, T, u)
+            tokens[b, k] = d["x"]
+            out["q_tok"][b, k] = d["q"]
+            out["row_max"][b, k] = d["m"]
+            out["row_logZ"][b, k] = d["logZ"]
+            out["lo"][b, k] = d["lo"]
+            out["hi"][b, k] = d["hi"]
+            whole = d["lo"] <= 0.0 and d["hi"] >= 1.0
+            out["margin"][b, k] = np.inf if whole else min(u - d["lo"], d["hi"] - u)
+            prev = d["x"]
+    out["tokens"] = tokens
+    out["emb"] = emb
+    out["state"] = st
+    return out

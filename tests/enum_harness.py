@@ -39,7 +39,8 @@ class TinyStep:
     """
 
     def __init__(self, R, gamma, V, rank, seed, T=1.0, ell=None, conf=None, sps=None,
-                 w_scale=0.8, U=None, W1=None, W2=None, ptab=None, anchor=None, sched=None):
+                 w_scale=0.8, U=None, W1=None, W2=None, ptab=None, anchor=None, sched=None,
+                 rnn=None):
         rng = np.random.default_rng(seed)
         self.R, self.gamma, self.V = R, gamma, V
         self.U = rng.normal(0.0, 1.0, (R, gamma, V)) if U is None else np.asarray(U, dtype=np.float64)
@@ -60,6 +61,7 @@ class TinyStep:
         self.conf = conf          # callable tokens [R, gamma] -> c [R, gamma]
         self.sps = sps
         self.sched = sched        # callable (c, sps) -> ell; default: the oracle's greedy
+        self.rnn = rnn            # dict(hidden, Wr, br): draft with the RNN head instead
         self._draft_cache = {}
 
     # -- the step under test -------------------------------------------------
@@ -74,7 +76,11 @@ class TinyStep:
     def run(self, uni):
         key = np.ascontiguousarray(uni[:, : self.gamma, 0]).tobytes()
         if key not in self._draft_cache:
-            d = O.draft_block(self.U, self.W1, self.W2, self.anchor, self.T, uni)
+            if self.rnn is None:
+                d = O.draft_block(self.U, self.W1, self.W2, self.anchor, self.T, uni)
+            else:
+                d = O.rnn_draft_block(self.U, self.W1, self.W2, self.rnn["hidden"],
+                                      self.rnn["Wr"], self.rnn["br"], self.anchor, self.T, uni)
             if self.ell is not None:
                 ell = self.ell
             else:
@@ -84,7 +90,8 @@ class TinyStep:
             self._draft_cache[key] = (d, ell)
         d, ell = self._draft_cache[key]
         v = O.verify(self.target_logits(d["tokens"]), self.U, self.W1, self.W2, self.anchor,
-                     d["tokens"], d["q_tok"], self.T, uni, ell)
+                     d["tokens"], d["q_tok"], self.T, uni, ell,
+                     emb=None if self.rnn is None else d["emb"])
         return d, ell, v
 
     # -- reference law --------------------------------------------------------
