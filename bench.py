@@ -178,12 +178,27 @@ def tv_label_bytes(wl):
     return e * V * 2 * B * g + e * r * V + e * B * g * r + 4 * B * g * 4 + 4 * B
 
 
+def rnn_draft_bytes(wl):
+    """Algorithmic bytes of one dspark_draft_block_rnn call: every U row, W2
+    once, the hidden states, the RNN layer Wr once, the W1 rows of the
+    previous tokens, the anchors, temperatures and draw uniforms, and the
+    outputs (four [B, gamma] arrays, the projected vectors and the state)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    B, g, V, r, H = wl.B, wl.gamma, wl.V, wl.rank, wl.H
+    return (e * B * g * V + e * r * V + e * B * g * H + e * 3 * r * (2 * r + H) + 4 * 3 * r
+            + e * B * g * r + 4 * B * 2 + 4 * B * g + 4 * B * g * 4 + e * B * g * r
+            + 4 * B * g * r)
+
+
 def next_rows(st, wl, reps):
-    """Time the scheduler stop-rule variants and the acceptance-label kernels
-    on this step's confidences and drafts (events on the launch stream)."""
+    """Time the scheduler stop-rule variants, the acceptance-label kernels and
+    the RNN-head draft on this step's confidences and drafts (events on the
+    launch stream)."""
     import torch
 
     import draft_verify_sampling_block_amd as dv
+    from draft_verify_sampling_block_amd.step import _dev
+    from gen.workloads import rnn_weights
 
     d = st.d
     B, g = wl.B, wl.gamma
@@ -197,7 +212,20 @@ def next_rows(st, wl, reps):
     dt = dv.DSPARK_BF16 if wl.dtype == "bf16" else dv.DSPARK_F32
     ws = torch.empty(max(256, dv.dspark_tv_label_workspace(B, g, wl.V, wl.rank, dt)),
                      dtype=torch.uint8, device=dev)
+    rw = rnn_weights(wl.rank, wl.H, wl.dtype, seed=wl.spec.index)
+    Wr, br = _dev(rw["Wr"], dev), _dev(rw["br"], dev)
+    r_out = dict(tokens=torch.empty((B, g), dtype=torch.int32, device=dev),
+                 q_tok=torch.empty((B, g), dtype=torch.float32, device=dev),
+                 row_max=torch.empty((B, g), dtype=torch.float32, device=dev),
+                 row_logZ=torch.empty((B, g), dtype=torch.float32, device=dev),
+                 emb=torch.empty((B, g, wl.rank), dtype=d.U.dtype, device=dev))
+    ws_rnn = torch.empty(max(256, dv.dspark_draft_block_rnn_workspace(B, g, wl.V, wl.rank, wl.H,
+                                                                      dt)),
+                         dtype=torch.uint8, device=dev)
     calls = {
+        "draft_block_rnn": lambda: dv.dspark_draft_block_rnn(
+            d.U, d.W1, d.W2, d.hidden, Wr, br, d.anchor, d.temperature, d.uniforms,
+            workspace=ws_rnn, **r_out),
         "schedule_capacity": lambda: dv.dspark_schedule_capacity(st.conf, cap, ell=ell,
                                                                  order=order, stats=stats),
         "schedule_threshold": lambda: dv.dspark_schedule_threshold(st.conf, 0.5, ell=ell,
@@ -219,6 +247,10 @@ def next_rows(st, wl, reps):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / reps * 1e3
         out[name] = {"us_per_call": us}
+    nb = rnn_draft_bytes(wl)
+    gbs = nb / (out["draft_block_rnn"]["us_per_call"] / 1e6) / 1e9
+    out["draft_block_rnn"].update({"bytes_alg": nb, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                                   "path": "per-position launches"})
     nb = tv_label_bytes(wl)
     gbs = nb / (out["tv_label"]["us_per_call"] / 1e6) / 1e9
     out["tv_label"].update({"bytes_alg": nb, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,

@@ -24,6 +24,7 @@ __all__ = [
     "DsparkError", "lib_path", "load", "dspark_draft_block", "dspark_confidence",
     "dspark_schedule", "dspark_schedule_noalloc", "dspark_schedule_capacity", "dspark_schedule_threshold", "dspark_verify",
     "dspark_tv_label", "dspark_tv_label_workspace", "dspark_draft_block_workspace",
+    "dspark_draft_block_rnn", "dspark_draft_block_rnn_workspace", "dspark_verify_rnn",
     "dspark_verify_workspace", "dspark_schedule_workspace", "exported_names", "header_names",
     "dspark_trace_enable", "dspark_trace_summary", "dspark_set_draft_path",
     "DSPARK_F32", "DSPARK_BF16", "DEV_FLAGS",
@@ -68,6 +69,9 @@ _SIGS = {
     "dspark_tv_label_workspace": (_SZ, [_I, _I, _I, _I, _I]),
     "dspark_tv_label": (_I, [_I] * 5 + [_P] * 12 + [_P, _SZ, _P]),
     "dspark_verify": (_I, [_I] * 5 + [_P] * 15 + [_P, _P, _SZ, _P]),
+    "dspark_draft_block_rnn_workspace": (_SZ, [_I] * 6),
+    "dspark_draft_block_rnn": (_I, [_I] * 6 + [_P] * 16 + [_P, _SZ, _P]),
+    "dspark_verify_rnn": (_I, [_I] * 5 + [_P] * 15 + [_P, _P, _SZ, _P]),
     "dspark_trace_enable": (_I, [_I]),
     "dspark_trace_summary": (_I, [ctypes.c_char_p, _SZ]),
     "dspark_set_draft_path": (_I, [_I]),
@@ -235,6 +239,49 @@ def dspark_draft_block(U, W1, W2, anchor, temperature, uniforms, *, tokens=None,
     return dict(tokens=tokens, q_tok=q_tok, row_max=row_max, row_logZ=row_logZ)
 
 
+def dspark_draft_block_rnn_workspace(B, gamma, V, rank, H, dtype) -> int:
+    return int(load().dspark_draft_block_rnn_workspace(B, gamma, V, rank, H, dtype))
+
+
+def dspark_draft_block_rnn(U, W1, W2, hidden, Wr, br, anchor, temperature, uniforms, *,
+                           tokens=None, q_tok=None, row_max=None, row_logZ=None, emb=None,
+                           state=None, want_state=False, status=None, workspace=None):
+    """Block drafting with the RNN head.  U [B,gamma,V]; W1 [V,rank]; W2 [rank,V];
+    hidden [B,gamma,H]; Wr [3 rank, 2 rank + H] (dtype of U); br [3 rank] fp32.
+    Returns dict(tokens, q_tok, row_max, row_logZ, emb [B,gamma,rank], state)."""
+    lib = load()
+    B, gamma, V = U.shape
+    rank = W1.shape[1]
+    H = hidden.shape[2]
+    dt = _dtype_code(U)
+    dev = U.device
+    _need(U, "U"); _need(W1, "W1", U.dtype, (V, rank), dev); _need(W2, "W2", U.dtype, (rank, V), dev)
+    _need(hidden, "hidden", U.dtype, (B, gamma, H), dev)
+    _need(Wr, "Wr", U.dtype, (3 * rank, 2 * rank + H), dev)
+    _need(br, "br", torch.float32, (3 * rank,), dev)
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, gamma + 1, 2), dev)
+    tokens = _out(tokens, "tokens", torch.int32, (B, gamma), dev)
+    q_tok = _out(q_tok, "q_tok", torch.float32, (B, gamma), dev)
+    row_max = _out(row_max, "row_max", torch.float32, (B, gamma), dev)
+    row_logZ = _out(row_logZ, "row_logZ", torch.float32, (B, gamma), dev)
+    emb = _out(emb, "emb", U.dtype, (B, gamma, rank), dev)
+    if state is not None or want_state:
+        state = _out(state, "state", torch.float32, (B, gamma, rank), dev)
+    status = _status(status, dev)
+    need = dspark_draft_block_rnn_workspace(B, gamma, V, rank, H, dt)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.dspark_draft_block_rnn(B, gamma, V, rank, H, dt, _ptr(U), _ptr(W1), _ptr(W2),
+                                      _ptr(hidden), _ptr(Wr), _ptr(br), _ptr(anchor),
+                                      _ptr(temperature), _ptr(uniforms), _ptr(tokens),
+                                      _ptr(q_tok), _ptr(row_max), _ptr(row_logZ), _ptr(emb),
+                                      _ptr(state), _ptr(status), _ptr(ws), ws.numel(),
+                                      _stream()))
+    return dict(tokens=tokens, q_tok=q_tok, row_max=row_max, row_logZ=row_logZ, emb=emb,
+                state=state)
+
+
 def dspark_confidence(hidden, W1, anchor, tokens, w, bias=0.0, *, conf=None, status=None):
     """Confidence head; hidden [B,gamma,H]; w [H+rank] fp32; returns conf [B,gamma]."""
     lib = load()
@@ -366,6 +413,42 @@ def dspark_verify(target, U, W1, W2, anchor, tokens, q_tok, row_max, row_logZ, t
                              _ptr(temperature), _ptr(uniforms), _ptr(ell), _ptr(out_tokens),
                              _ptr(n_accepted), _ptr(ratio), _ptr(status), _ptr(ws), ws.numel(),
                              _stream()))
+    return out_tokens, n_accepted, ratio
+
+
+def dspark_verify_rnn(target, U, emb, W2, anchor, tokens, q_tok, row_max, row_logZ, temperature,
+                      uniforms, ell, *, out_tokens=None, n_accepted=None, ratio=None,
+                      status=None, workspace=None, want_ratio=True):
+    """dspark_verify for RNN-head drafts: emb [B,gamma,rank] (the drafter's projected
+    vectors) replaces W1.  Returns (out_tokens, n_accepted, ratio)."""
+    lib = load()
+    B, gamma, V = U.shape
+    rank = emb.shape[2]
+    dt = _dtype_code(U)
+    dev = U.device
+    _need(U, "U"); _need(target, "target", U.dtype, (B, gamma + 1, V), dev)
+    _need(emb, "emb", U.dtype, (B, gamma, rank), dev); _need(W2, "W2", U.dtype, (rank, V), dev)
+    for name, t, dtp, shp in (
+            ("anchor", anchor, torch.int32, (B,)), ("tokens", tokens, torch.int32, (B, gamma)),
+            ("q_tok", q_tok, torch.float32, (B, gamma)),
+            ("row_max", row_max, torch.float32, (B, gamma)),
+            ("row_logZ", row_logZ, torch.float32, (B, gamma)),
+            ("temperature", temperature, torch.float32, (B,)),
+            ("uniforms", uniforms, torch.float32, (B, gamma + 1, 2)),
+            ("ell", ell, torch.int32, (B,))):
+        _need(t, name, dtp, shp, dev)
+    out_tokens = _out(out_tokens, "out_tokens", torch.int32, (B, gamma + 1), dev)
+    n_accepted = _out(n_accepted, "n_accepted", torch.int32, (B,), dev)
+    if ratio is not None or want_ratio:
+        ratio = _out(ratio, "ratio", torch.float32, (B, gamma), dev)
+    status = _status(status, dev)
+    need = dspark_verify_workspace(B, gamma, V, rank, dt)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.dspark_verify_rnn(B, gamma, V, rank, dt, _ptr(target), _ptr(U), _ptr(emb),
+                                 _ptr(W2), _ptr(anchor), _ptr(tokens), _ptr(q_tok), _ptr(row_max),
+                                 _ptr(row_logZ), _ptr(temperature), _ptr(uniforms), _ptr(ell),
+                                 _ptr(out_tokens), _ptr(n_accepted), _ptr(ratio), _ptr(status),
+                                 _ptr(ws), ws.numel(), _stream()))
     return out_tokens, n_accepted, ratio
 
 

@@ -315,10 +315,14 @@ __device__ void sample_request(int b, int k, int B, int gamma, int V, int rank, 
 // Multi-launch path
 // ---------------------------------------------------------------------------
 
+// The bias row of request b: row prev_src[b * prev_stride] of W1 (the Markov
+// head: the previous token's embedding), or with emb_k >= 0 row
+// b * gamma + emb_k of the table passed as W1 (the RNN head's projected
+// vectors emb [B, gamma, rank]).
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void draft_stats_kernel(
     int B, int gamma, int V, int rank, int k, const T* __restrict__ U, const T* __restrict__ W1,
-    const T* __restrict__ W2, const int32_t* __restrict__ prev_src, int prev_stride,
+    const T* __restrict__ W2, const int32_t* __restrict__ prev_src, int prev_stride, int emb_k,
     const float* __restrict__ temperature, TileStats ts, int32_t* status) {
   __shared__ __attribute__((aligned(16))) char w2s[kIsBf16<T> ? kLdsTileBytes : 16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -338,7 +342,8 @@ __global__ __launch_bounds__(256) void draft_stats_kernel(
     tok = -1;
     it = 0.f;
     if (b < B) {
-      tok = clamp_token(prev_src[(size_t)b * prev_stride], V, h == 0 ? status : nullptr);
+      tok = emb_k >= 0 ? b * gamma + emb_k
+                       : clamp_token(prev_src[(size_t)b * prev_stride], V, h == 0 ? status : nullptr);
       it = inv_temp(temperature[b]);
     }
     if constexpr (kIsBf16<T>) load_bfrag<KS>(W1, tok, bfrag);
@@ -368,14 +373,15 @@ __global__ __launch_bounds__(256) void draft_stats_kernel(
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void draft_sample_kernel(
     int B, int gamma, int V, int rank, int k, const T* __restrict__ U, const T* __restrict__ W1,
-    const T* __restrict__ W2, const int32_t* __restrict__ prev_src, int prev_stride,
+    const T* __restrict__ W2, const int32_t* __restrict__ prev_src, int prev_stride, int emb_k,
     const float* __restrict__ temperature, const float* __restrict__ uniforms, TileStats ts,
     int32_t* __restrict__ tokens, float* __restrict__ q_tok, float* __restrict__ row_max,
     float* __restrict__ row_logZ, int32_t* status) {
   __shared__ __attribute__((aligned(16))) char scratch[kSampScratchBytes];
   __shared__ SampShared sh;
   const int b = blockIdx.x;
-  const int prev = clamp_token(prev_src[(size_t)b * prev_stride], V, nullptr);
+  const int prev = emb_k >= 0 ? b * gamma + emb_k
+                              : clamp_token(prev_src[(size_t)b * prev_stride], V, nullptr);
   sample_request<T, KS, 256>(b, k, B, gamma, V, rank, prev, U, W1, W2, temperature, uniforms,
                              ts, tokens, q_tok, row_max, row_logZ, status, scratch, sh, nullptr);
 }
@@ -936,13 +942,13 @@ static hipError_t draft_multi(int B, int gamma, int V, int rank, const T* U, con
     {
       TraceScope t("draft_stats_kernel", stream);
       draft_stats_kernel<T, KS><<<dim3((unsigned)n_tiles(V)), blk, 0, stream>>>(
-          B, gamma, V, rank, k, U, W1, W2, prev, stride, temperature, ts, status);
+          B, gamma, V, rank, k, U, W1, W2, prev, stride, -1, temperature, ts, status);
     }
     TraceScope t("draft_sample_kernel", stream);
     draft_sample_kernel<T, KS><<<dim3(B), blk, 0, stream>>>(B, gamma, V, rank, k, U, W1, W2,
-                                                           prev, stride, temperature, uniforms,
-                                                           ts, tokens, q_tok, row_max, row_logZ,
-                                                           status);
+                                                           prev, stride, -1, temperature,
+                                                           uniforms, ts, tokens, q_tok, row_max,
+                                                           row_logZ, status);
   }
   return hipGetLastError();
 }
@@ -1029,6 +1035,77 @@ hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, cons
                                static_cast<const float*>(W1), static_cast<const float*>(W2),
                                anchor, temperature, uniforms, tokens, q_tok, row_max, row_logZ,
                                status, ws, stream);
+}
+
+// ---------------------------------------------------------------------------
+// RNN head: per position, the recurrence (rnn.hip) produces emb[:, k], then
+// the statistics and draw launches take their bias rows from it
+// ---------------------------------------------------------------------------
+
+size_t draft_rnn_workspace_bytes(int B, int gamma, int V, int rank, int H, int dtype) {
+  (void)H;
+  return draft_workspace_bytes(B, gamma, V, rank, dtype) + rnn_workspace_bytes(B, gamma, rank);
+}
+
+template <typename T, int KS>
+static hipError_t draft_rnn_impl(int B, int gamma, int V, int rank, int H, int dtype,
+                                 const T* U, const T* W1, const T* W2, const void* hidden,
+                                 const void* Wr, const float* br, const int32_t* anchor,
+                                 const float* temperature, const float* uniforms, int32_t* tokens,
+                                 float* q_tok, float* row_max, float* row_logZ, T* emb,
+                                 float* state, int32_t* status, void* ws, hipStream_t stream) {
+  const TileStats ts = carve_stats(ws, B, V);
+  void* rws = static_cast<char*>(ws) + draft_workspace_bytes(B, gamma, V, rank, dtype);
+  hipError_t e = launch_rnn_hidden(B, gamma, rank, H, dtype, hidden, Wr, br, rws, stream);
+  if (e != hipSuccess) return e;
+  const dim3 blk(256);
+  for (int k = 0; k < gamma; ++k) {
+    e = launch_rnn_state(k, B, gamma, V, rank, H, dtype, Wr, W1, anchor, tokens, emb, state,
+                         status, rws, stream);
+    if (e != hipSuccess) return e;
+    {
+      TraceScope t("draft_stats_kernel", stream);
+      draft_stats_kernel<T, KS><<<dim3((unsigned)n_tiles(V)), blk, 0, stream>>>(
+          B, gamma, V, rank, k, U, emb, W2, anchor, 1, k, temperature, ts, status);
+    }
+    TraceScope t("draft_sample_kernel", stream);
+    draft_sample_kernel<T, KS><<<dim3(B), blk, 0, stream>>>(B, gamma, V, rank, k, U, emb, W2,
+                                                           anchor, 1, k, temperature, uniforms,
+                                                           ts, tokens, q_tok, row_max, row_logZ,
+                                                           status);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_block_rnn(int B, int gamma, int V, int rank, int H, int dtype,
+                                  const void* U, const void* W1, const void* W2,
+                                  const void* hidden, const void* Wr, const float* br,
+                                  const int32_t* anchor, const float* temperature,
+                                  const float* uniforms, int32_t* tokens, float* q_tok,
+                                  float* row_max, float* row_logZ, void* emb, float* state,
+                                  int32_t* status, void* ws, hipStream_t stream) {
+  if (dtype == DSPARK_BF16) {
+    auto* u = static_cast<const uint16_t*>(U);
+    auto* w1 = static_cast<const uint16_t*>(W1);
+    auto* w2 = static_cast<const uint16_t*>(W2);
+    auto* em = static_cast<uint16_t*>(emb);
+#define DSPARK_RNN_KS(KS)                                                                       \
+  return draft_rnn_impl<uint16_t, KS>(B, gamma, V, rank, H, dtype, u, w1, w2, hidden, Wr, br,  \
+                                      anchor, temperature, uniforms, tokens, q_tok, row_max,    \
+                                      row_logZ, em, state, status, ws, stream)
+    switch (rank) {
+      case 32: DSPARK_RNN_KS(2);
+      case 64: DSPARK_RNN_KS(4);
+      case 128: DSPARK_RNN_KS(8);
+      default: DSPARK_RNN_KS(16);
+    }
+#undef DSPARK_RNN_KS
+  }
+  return draft_rnn_impl<float, 1>(B, gamma, V, rank, H, dtype, static_cast<const float*>(U),
+                                  static_cast<const float*>(W1), static_cast<const float*>(W2),
+                                  hidden, Wr, br, anchor, temperature, uniforms, tokens, q_tok,
+                                  row_max, row_logZ, static_cast<float*>(emb), state, status, ws,
+                                  stream);
 }
 
 }  // namespace dspark

@@ -115,6 +115,40 @@ int dspark_draft_block(int B, int gamma, int V, int rank, int dtype, const void*
                                                    row_logZ, status, workspace, stream));
 }
 
+size_t dspark_draft_block_rnn_workspace(int B, int gamma, int V, int rank, int H, int dtype) {
+  if (check_dims("dspark_draft_block_rnn_workspace", B, gamma, V, rank, dtype) != DSPARK_OK)
+    return 0;
+  if (H < 8 || H % 8) return 0;
+  return dspark::draft_rnn_workspace_bytes(B, gamma, V, rank, H, dtype);
+}
+
+int dspark_draft_block_rnn(int B, int gamma, int V, int rank, int H, int dtype, const void* U,
+                           const void* W1, const void* W2, const void* hidden, const void* Wr,
+                           const float* br, const int32_t* anchor, const float* temperature,
+                           const float* uniforms, int32_t* tokens, float* q_tok,
+                           float* row_max, float* row_logZ, void* emb, float* state,
+                           int32_t* status, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const char* fn = "dspark_draft_block_rnn";
+  int rc = check_dims(fn, B, gamma, V, rank, dtype);
+  if (rc) return rc;
+  if (H < 8 || H % 8) return fail(DSPARK_EINVAL, "%s: H=%d must be a positive multiple of 8", fn, H);
+  REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2); REQUIRE_PTR(hidden); REQUIRE_PTR(Wr);
+  REQUIRE_PTR(br); REQUIRE_PTR(anchor); REQUIRE_PTR(temperature); REQUIRE_PTR(uniforms);
+  REQUIRE_PTR(tokens); REQUIRE_PTR(q_tok); REQUIRE_PTR(row_max); REQUIRE_PTR(row_logZ);
+  REQUIRE_PTR(emb); OPT_PTR(state); OPT_PTR(status);
+  const size_t need = dspark::draft_rnn_workspace_bytes(B, gamma, V, rank, H, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
+  return hip_status(fn, dspark::launch_draft_block_rnn(B, gamma, V, rank, H, dtype, U, W1, W2,
+                                                       hidden, Wr, br, anchor, temperature,
+                                                       uniforms, tokens, q_tok, row_max,
+                                                       row_logZ, emb, state, status, workspace,
+                                                       stream));
+}
+
 int dspark_confidence(int B, int gamma, int H, int V, int rank, int dtype, const void* hidden,
                       const void* W1, const int32_t* anchor, const int32_t* tokens,
                       const float* w, float bias, float* conf, int32_t* status,
@@ -256,6 +290,32 @@ int dspark_verify(int B, int gamma, int V, int rank, int dtype, const void* targ
 }
 
 }  // extern "C"
+
+int dspark_verify_rnn(int B, int gamma, int V, int rank, int dtype, const void* target,
+                      const void* U, const void* emb, const void* W2, const int32_t* anchor,
+                      const int32_t* tokens, const float* q_tok, const float* row_max,
+                      const float* row_logZ, const float* temperature, const float* uniforms,
+                      const int32_t* ell, int32_t* out_tokens, int32_t* n_accepted, float* ratio,
+                      int32_t* status, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  const char* fn = "dspark_verify_rnn";
+  int rc = check_dims(fn, B, gamma, V, rank, dtype);
+  if (rc) return rc;
+  REQUIRE_PTR(target); REQUIRE_PTR(U); REQUIRE_PTR(emb); REQUIRE_PTR(W2); REQUIRE_PTR(anchor);
+  REQUIRE_PTR(tokens); REQUIRE_PTR(q_tok); REQUIRE_PTR(row_max); REQUIRE_PTR(row_logZ);
+  REQUIRE_PTR(temperature); REQUIRE_PTR(uniforms); REQUIRE_PTR(ell); REQUIRE_PTR(out_tokens);
+  REQUIRE_PTR(n_accepted); OPT_PTR(ratio); OPT_PTR(status);
+  const size_t need = dspark::verify_workspace_bytes(B, gamma, V, rank, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
+  return hip_status(fn, dspark::launch_verify(B, gamma, V, rank, dtype, target, U, emb, W2,
+                                              anchor, tokens, q_tok, row_max, row_logZ,
+                                              temperature, uniforms, ell, out_tokens, n_accepted,
+                                              ratio, status, workspace, stream,
+                                              /*emb_rows=*/true));
+}
 
 size_t dspark_tv_label_workspace(int B, int gamma, int V, int rank, int dtype) {
   if (check_dims("dspark_tv_label_workspace", B, gamma, V, rank, dtype) != DSPARK_OK) return 0;

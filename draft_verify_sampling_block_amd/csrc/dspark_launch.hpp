@@ -25,6 +25,25 @@ hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, cons
                               float* q_tok, float* row_max, float* row_logZ, int32_t* status,
                               void* ws, hipStream_t stream);
 
+// RNN head (rnn.hip, draft.hip): the recurrence's workspace (pre-activations
+// of the hidden part for every position, two state buffers), its launches,
+// and the whole block draft (the draft workspace plus the recurrence's)
+size_t rnn_workspace_bytes(int B, int gamma, int rank);
+hipError_t launch_rnn_hidden(int B, int gamma, int rank, int H, int dtype, const void* hidden,
+                             const void* Wr, const float* br, void* ws, hipStream_t stream);
+hipError_t launch_rnn_state(int k, int B, int gamma, int V, int rank, int H, int dtype,
+                            const void* Wr, const void* W1, const int32_t* anchor,
+                            const int32_t* tokens, void* emb, float* state_out, int32_t* status,
+                            void* ws, hipStream_t stream);
+size_t draft_rnn_workspace_bytes(int B, int gamma, int V, int rank, int H, int dtype);
+hipError_t launch_draft_block_rnn(int B, int gamma, int V, int rank, int H, int dtype,
+                                  const void* U, const void* W1, const void* W2,
+                                  const void* hidden, const void* Wr, const float* br,
+                                  const int32_t* anchor, const float* temperature,
+                                  const float* uniforms, int32_t* tokens, float* q_tok,
+                                  float* row_max, float* row_logZ, void* emb, float* state,
+                                  int32_t* status, void* ws, hipStream_t stream);
+
 hipError_t launch_confidence(int B, int gamma, int H, int V, int rank, int dtype,
                              const void* hidden, const void* W1, const int32_t* anchor,
                              const int32_t* tokens, const float* w, float bias, float* conf,
@@ -40,6 +59,10 @@ hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const voi
                          const int32_t* tokens, const float* q_tok, const float* row_max,
                          const float* row_logZ, const float* temperature, const float* uniforms,
                          const int32_t* ell, int32_t* out_tokens, int32_t* n_accepted,
-                         float* ratio, int32_t* status, void* ws, hipStream_t stream);
+                         float* ratio, int32_t* status, void* ws, hipStream_t stream,
+                         bool emb_rows = false);
+// emb_rows: W1 is the RNN head's emb [B, gamma, rank], and the q recompute of
+// request b at slot j takes its bias row b * gamma + j (not the W1 row of the
+// previous token)
 
 }  // namespace dspark

@@ -40,6 +40,7 @@ struct VerifyWs {
   float* pchunk;       // [B][nC] p chunk sums of the residual slot (fallback)
   int4* plan;          // [B] final draw of the request: (mode, slot, prev, -)
   int32_t* any_res;    // [1] nonzero when some request draws from a residual
+  int emb_rows;        // the bias row of (b, j) is row b * gamma + j (RNN head)
 };
 
 VerifyWs carve(void* ws, int B, int gamma, int V) {
@@ -55,6 +56,7 @@ VerifyWs carve(void* ws, int B, int gamma, int V) {
   w.pchunk = reinterpret_cast<float*>(p); p += align256((size_t)B * nC * 4);
   w.plan = reinterpret_cast<int4*>(p); p += align256((size_t)B * 16);
   w.any_res = reinterpret_cast<int32_t*>(p); p += 256;
+  w.emb_rows = 0;
   return w;
 }
 
@@ -170,7 +172,9 @@ __device__ inline FinalRow final_row(int b, int B, int gamma, int V, const int32
   if (j < L) {
     f.mode = 1;
     f.slot = j;
-    f.prev = clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1], V, nullptr);
+    f.prev = ws.emb_rows ? b * gamma + j
+                         : clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1],
+                                       V, nullptr);
   } else {
     f.mode = 2;
     f.slot = L;
@@ -727,9 +731,11 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
       const int lane = tid & 63, c = lane & 31, h = lane >> 5;
       const int tw = tid >> 6;   // bf16: the sub-tile of waves 0 and 1
       const bool mine = tid < (bf ? kSub : 1) * kWave && c == mrow;
-      const int prev = residual
-          ? clamp_token(j == 0 ? anchor[b] : tokens[(size_t)b * gamma + j - 1], V, nullptr)
-          : -1;
+      const int prev = !residual ? -1
+                       : ws.emb_rows ? b * gamma + j
+                                     : clamp_token(j == 0 ? anchor[b]
+                                                          : tokens[(size_t)b * gamma + j - 1],
+                                                   V, nullptr);
       URow<T> tr, ur;
       load_urow<T>(tr, target + sk * V, v0, V, mine, target);
       load_urow<T>(ur, U + ((size_t)b * gamma + slot) * V, v0, V, mine && residual, U);
@@ -824,8 +830,9 @@ static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target
                               const float* row_logZ, const float* temperature,
                               const float* uniforms, const int32_t* ell, int32_t* out_tokens,
                               int32_t* n_accepted, float* ratio, int32_t* status, void* wsp,
-                              hipStream_t stream) {
+                              hipStream_t stream, bool emb_rows) {
   VerifyWs ws = carve(wsp, B, gamma, V);
+  ws.emb_rows = emb_rows ? 1 : 0;
   {
     TraceScope t1("verify_rows_kernel", stream);
     verify_rows_kernel<T><<<dim3(B * (gamma + 1)), dim3(256), 0, stream>>>(
@@ -873,7 +880,8 @@ hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const voi
                          const int32_t* tokens, const float* q_tok, const float* row_max,
                          const float* row_logZ, const float* temperature, const float* uniforms,
                          const int32_t* ell, int32_t* out_tokens, int32_t* n_accepted,
-                         float* ratio, int32_t* status, void* ws, hipStream_t stream) {
+                         float* ratio, int32_t* status, void* ws, hipStream_t stream,
+                         bool emb_rows) {
   if (dtype == DSPARK_BF16) {
     auto* tg = static_cast<const uint16_t*>(target);
     auto* u = static_cast<const uint16_t*>(U);
@@ -882,7 +890,7 @@ hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const voi
 #define DSPARK_VERIFY_KS(KS)                                                                  \
   return verify_impl<uint16_t, KS>(B, gamma, V, rank, tg, u, w1, w2, anchor, tokens, q_tok,    \
                                    row_max, row_logZ, temperature, uniforms, ell, out_tokens,  \
-                                   n_accepted, ratio, status, ws, stream)
+                                   n_accepted, ratio, status, ws, stream, emb_rows)
     switch (rank) {
       case 32: DSPARK_VERIFY_KS(2);
       case 64: DSPARK_VERIFY_KS(4);
@@ -895,7 +903,7 @@ hipError_t launch_verify(int B, int gamma, int V, int rank, int dtype, const voi
                                static_cast<const float*>(U), static_cast<const float*>(W1),
                                static_cast<const float*>(W2), anchor, tokens, q_tok, row_max,
                                row_logZ, temperature, uniforms, ell, out_tokens, n_accepted, ratio,
-                               status, ws, stream);
+                               status, ws, stream, emb_rows);
 }
 
 }  // namespace dspark

@@ -42,7 +42,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # component ids for the seed tree
-_C_W1, _C_W2, _C_W, _C_LOGITS, _C_HIDDEN, _C_GLOBAL = range(6)
+_C_W1, _C_W2, _C_W, _C_LOGITS, _C_HIDDEN, _C_GLOBAL, _C_RNN = range(7)
 
 
 @dataclasses.dataclass
@@ -305,3 +305,22 @@ def make_custom(B: int, gamma: int, V: int, rank: int, H: int, dtype: str = "bf1
                     W2=to_bf16_bits(W2) if bf else W2, w=w, b0=0.0, hidden=hidden,
                     anchor=anchor, temperature=temp, uniforms=uniforms, sps=sps,
                     requests=np.arange(B))
+
+
+def rnn_weights(rank: int, H: int, dtype: str = "bf16", seed: int = 0, w_std: float = 0.02):
+    """Weights of the RNN head (its own seed stream; no other draw changes).
+
+    Wr [3 rank, 2 rank + H] (rows gate | candidate | output; columns state |
+    embedding | hidden) with each column block scaled so that it adds O(1) to
+    the pre-activations: state N(0, 1/rank), embedding N(0, 1/(rank w_std^2))
+    (the W1 rows it multiplies have std w_std), hidden N(0, 1/H); br [3 rank]
+    ~ N(0, 0.1^2), float32.  Returns dict(Wr (bf16 bits or float32), br).
+    """
+    r = _rng(seed, _C_RNN)
+    Wr = np.empty((3 * rank, 2 * rank + H), dtype=np.float32)
+    Wr[:, :rank] = r.standard_normal((3 * rank, rank), dtype=np.float32) / np.float32(np.sqrt(rank))
+    Wr[:, rank:2 * rank] = (r.standard_normal((3 * rank, rank), dtype=np.float32)
+                            / np.float32(np.sqrt(rank) * w_std))
+    Wr[:, 2 * rank:] = r.standard_normal((3 * rank, H), dtype=np.float32) / np.float32(np.sqrt(H))
+    br = (r.standard_normal(3 * rank) * 0.1).astype(np.float32)
+    return dict(Wr=to_bf16_bits(Wr) if dtype == "bf16" else Wr, br=br)

@@ -118,6 +118,47 @@ int dspark_draft_block(int B, int gamma, int V, int rank, int dtype,
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * dspark_draft_block_rnn: block drafting with the RNN head instead of the
+ * Markov head ([weigao] part 2, the _rnn_step description; [billytse] 3.3:
+ * a recurrent state lets each position see the whole block prefix).
+ * For each request b, with s = 0 and prev = anchor[b], for k = 0..gamma-1:
+ *     pre   = Wr . [s ; W1[prev,:] ; hidden[b,k,:]] + br     (3 rank outputs)
+ *     gate  = sigmoid(pre[0:r]), cand = tanh(pre[r:2r]), out = tanh(pre[2r:3r])
+ *     s     = gate * s + (1 - gate) * cand
+ *     emb[b,k,:] = out                    (rounded to dtype: the bias operand)
+ *     z     = U[b,k,:] + emb[b,k,:] @ W2
+ *     x     = inverse-CDF draw from softmax(z / T_b) with uniforms[b,k,0]
+ *     prev  = x
+ * (r = rank.  The activations of gate and candidate, the state size, the
+ * layer's column order and the zero initial state are this library's
+ * readings; the pages give the split and the two formulas.)
+ * in : U [B,gamma,V], W1 [V,rank], W2 [rank,V], hidden [B,gamma,H],
+ *      Wr [3 rank, 2 rank + H] (dtype; rows gate | candidate | output,
+ *      columns state | embedding | hidden); br [3 rank] fp32; anchor,
+ *      temperature, uniforms as dspark_draft_block
+ * out: tokens, q_tok, row_max, row_logZ as dspark_draft_block;
+ *      emb [B,gamma,rank] (dtype): the vector each position projected
+ *      (dspark_verify_rnn takes it); state [B,gamma,rank] fp32: s after each
+ *      position (or NULL)
+ * Arithmetic: the hidden part of the layer for all positions is one bf16
+ * matrix-core GEMM (fp32 out); the recurrence is fp32 (the state enters the
+ * matrix cores as two bf16 parts, ~2^-17 relative); sampling as
+ * dspark_draft_block.  Per-position launches (the single-launch kernel
+ * serves the Markov head only).
+ * workspace: dspark_draft_block_rnn_workspace(...) bytes; H % 8 == 0.
+ * ---------------------------------------------------------------------- */
+size_t dspark_draft_block_rnn_workspace(int B, int gamma, int V, int rank, int H, int dtype);
+int dspark_draft_block_rnn(int B, int gamma, int V, int rank, int H, int dtype,
+                           const void* U, const void* W1, const void* W2, const void* hidden,
+                           const void* Wr, const float* br,
+                           const int32_t* anchor, const float* temperature,
+                           const float* uniforms,
+                           int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
+                           void* emb, float* state,
+                           int32_t* status, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * dspark_confidence: the confidence head ([weigao] part 3; [billytse] 5):
  *     conf[b,k] = sigmoid( w[0:H] . hidden[b,k,:] + w[H:H+rank] . W1[prev_k,:]
  *                          + bias )
@@ -246,6 +287,24 @@ int dspark_verify(int B, int gamma, int V, int rank, int dtype,
                   int32_t* out_tokens, int32_t* n_accepted, float* ratio,
                   int32_t* status, void* workspace, size_t workspace_bytes,
                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dspark_verify_rnn: dspark_verify for drafts of dspark_draft_block_rnn.
+ * Identical except that the q recompute at a rejected slot j takes its bias
+ * from the drafter's own projected vector: z = U[b,j] + emb[b,j,:] @ W2
+ * (bit-identical to the draft's logits), so the residual norm(max(0, p - q))
+ * uses exactly the q the token was drawn from ([billytse] 1; [xhh]
+ * acceptance-rule Q&A).  emb [B,gamma,rank] (dtype) replaces W1; every other
+ * argument, output and the workspace are those of dspark_verify.
+ * ---------------------------------------------------------------------- */
+int dspark_verify_rnn(int B, int gamma, int V, int rank, int dtype,
+                      const void* target, const void* U, const void* emb, const void* W2,
+                      const int32_t* anchor, const int32_t* tokens, const float* q_tok,
+                      const float* row_max, const float* row_logZ,
+                      const float* temperature, const float* uniforms, const int32_t* ell,
+                      int32_t* out_tokens, int32_t* n_accepted, float* ratio,
+                      int32_t* status, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * dspark_tv_label: the confidence head's training label per drafted

@@ -42,10 +42,11 @@ def _req(cond, msg):
         raise Mismatch(msg)
 
 
-def check_draft(wl, W1_64, W2_64, tokens, q_tok, row_max, row_logZ, rows=None):
-    """tokens etc. are host numpy arrays of the device outputs."""
+def check_draft(wl, W1_64, W2_64, tokens, q_tok, row_max, row_logZ, rows=None, emb=None):
+    """tokens etc. are host numpy arrays of the device outputs; ``emb``: the
+    device's RNN-head vectors (the bias of (b, k) is then emb[b, k] @ W2)."""
     forced = O.draft_forced(wl.U, W1_64, W2_64, wl.anchor, wl.temperature, tokens,
-                            uniforms=wl.uniforms, rows=rows)
+                            uniforms=wl.uniforms, rows=rows, emb=emb)
     rep = dict(rows=len(forced), identical=0, band=0)
     for d in forced:
         b, k = d["b"], d["k"]
@@ -63,6 +64,27 @@ def check_draft(wl, W1_64, W2_64, tokens, q_tok, row_max, row_logZ, rows=None):
         _req(close(row_max[b, k], d["m"]), f"row_max ({b},{k}): {row_max[b, k]} vs {d['m']}")
         _req(close(row_logZ[b, k], d["logZ"]), f"row_logZ ({b},{k}): {row_logZ[b, k]} vs {d['logZ']}")
     return rep
+
+
+def check_rnn(wl, rw, tokens, emb, state, bf16):
+    """The RNN head's recurrence on the device's own tokens: the projected
+    vectors within the storage rounding (bf16: half a unit in the 8th
+    significant bit, plus 2e-5 for the fp32 arithmetic; fp32: the continuous
+    tolerance) and the state within 1e-4 absolute."""
+    ref = O.rnn_forced(wl.W1, wl.hidden, rw["Wr"], rw["br"], wl.anchor, tokens)
+    e_ref, s_ref = ref["emb"], ref["state"]
+    lim = (2.0 ** -8 * np.abs(e_ref) + 2e-5) if bf16 else (TOL_ABS + TOL_REL * np.abs(e_ref))
+    bad = np.argwhere(np.abs(emb - e_ref) > lim)
+    _req(len(bad) == 0, f"rnn emb mismatch at {bad[:4].tolist()}: device "
+                        f"{[float(emb[tuple(i)]) for i in bad[:3]]} oracle "
+                        f"{[float(e_ref[tuple(i)]) for i in bad[:3]]}")
+    out = dict(rows=int(e_ref.shape[0] * e_ref.shape[1]),
+               emb_max_abs=float(np.max(np.abs(emb - e_ref))))
+    if state is not None:
+        ds = np.abs(state - s_ref)
+        _req(float(np.max(ds)) <= 1e-4, f"rnn state max |diff| {float(np.max(ds)):.3g}")
+        out["state_max_abs"] = float(np.max(ds))
+    return out
 
 
 def check_confidence(wl, tokens, conf):
@@ -98,15 +120,17 @@ def check_schedule_mode(conf, mode, arg, ell, order, stats):
     return dict(n_admitted=s["n_admitted"], mean_ell=float(np.mean(s["ell"])))
 
 
-def check_verify(wl, W1_64, W2_64, tokens, ell, out_tokens, n_accepted, ratio, requests=None):
+def check_verify(wl, W1_64, W2_64, tokens, ell, out_tokens, n_accepted, ratio, requests=None,
+                 emb=None):
     B, gamma = tokens.shape
     reqs = list(range(B)) if requests is None else list(requests)
     rows = [(b, k) for b in reqs for k in range(int(ell[b]))]
     q = np.full((B, gamma), np.nan)
-    for d in O.draft_forced(wl.U, W1_64, W2_64, wl.anchor, wl.temperature, tokens, rows=rows):
+    for d in O.draft_forced(wl.U, W1_64, W2_64, wl.anchor, wl.temperature, tokens, rows=rows,
+                            emb=emb):
         q[d["b"], d["k"]] = d["q"]
     v = O.verify(wl.target, wl.U, W1_64, W2_64, wl.anchor, tokens, q, wl.temperature,
-                 wl.uniforms, ell, requests=reqs, keep_final=True)
+                 wl.uniforms, ell, requests=reqs, keep_final=True, emb=emb)
     rep = dict(requests=len(reqs), accept_flips=0, final_identical=0, final_band=0)
     for b in reqs:
         L = int(ell[b])

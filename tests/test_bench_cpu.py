@@ -86,3 +86,12 @@ def test_kernel_bytes_per_launch():
     # as built: every slot up to ell (bonus included), the final rows and W2 again
     assert rd["verify_rows_kernel"] == 2 * 64 * (5 + 3 + 1)
     assert rd["verify_tile_stats_kernel"] == 2 * 64 * (3 + 1) + 2 * 32 * 64
+
+
+def test_rnn_draft_bytes():
+    wl = make_custom(3, 4, 64, 32, 16, "bf16", "gaussian", seed=0)
+    e, B, g, V, r, H = 2, 3, 4, 64, 32, 16
+    want = (e * B * g * V + e * r * V + e * B * g * H + e * 3 * r * (2 * r + H) + 4 * 3 * r
+            + e * B * g * r + 4 * B * 2 + 4 * B * g + 4 * B * g * 4 + e * B * g * r
+            + 4 * B * g * r)
+    assert bench.rnn_draft_bytes(wl) == want

@@ -2,7 +2,7 @@
 
 import numpy as np
 
-from gen import SPECS, make_config, to_bf16_bits, bf16_bits_to_f32
+from gen import SPECS, make_config, make_custom, to_bf16_bits, bf16_bits_to_f32
 
 
 def test_bf16_round_to_nearest_even():
@@ -42,3 +42,20 @@ def test_large_config_subset_structure():
     u = bf16_bits_to_f32(w.U[0, 0])
     # three peaks of +8..+12 over a N(0, 1.5) background
     assert (u > 7.0).sum() >= 3 and abs(u.std() - 1.5) < 0.05
+
+
+def test_rnn_weights_shapes_and_streams():
+    from gen.workloads import rnn_weights
+    a = rnn_weights(32, 64, "f32", seed=0)
+    b = rnn_weights(32, 64, "f32", seed=0)
+    c = rnn_weights(32, 64, "bf16", seed=0)
+    assert a["Wr"].shape == (96, 128) and a["br"].shape == (96,)
+    np.testing.assert_array_equal(a["Wr"], b["Wr"])
+    assert c["Wr"].dtype == np.uint16
+    # each column block adds O(1) to the pre-activations
+    assert 0.1 < float(np.std(a["Wr"][:, :32])) * np.sqrt(32) < 10
+    assert 0.1 < float(np.std(a["Wr"][:, 64:])) * np.sqrt(64) < 10
+    # the RNN draw leaves the other components' draws unchanged
+    w0 = make_custom(2, 3, 64, 32, 16, "f32", "gaussian", seed=0)
+    w1 = make_custom(2, 3, 64, 32, 16, "f32", "gaussian", seed=0)
+    np.testing.assert_array_equal(w0.W2, w1.W2)
