@@ -58,6 +58,11 @@ __all__ = [
     "rnn_step",
     "rnn_draft_block",
     "rnn_forced",
+    "confidence_logits",
+    "sts_apply",
+    "confidence_sts",
+    "sts_fit",
+    "ece",
 ]
 
 
@@ -679,3 +684,104 @@ def rnn_draft_block(U, W1, W2, hidden, Wr, br, anchor, temperature, uniforms, em
     out["emb"] = emb
     out["state"] = st
     return out
+
+
+# ----------------------------------------------------------------------------
+# (7) sequential temperature scaling (STS) of the confidence head
+# ----------------------------------------------------------------------------
+
+def confidence_logits(hidden, W1, anchor, tokens, w, b0: float = 0.0) -> np.ndarray:
+    """z[b, k] = w . [h_k ; W1[prev_k]] + b0: the confidence head's logit
+    (confidence() is sigmoid(z))."""
+    h = f64(hidden)
+    W1 = f64(W1)
+    w = f64(w)
+    B, gamma, H = h.shape
+    tokens = np.asarray(tokens)
+    z = np.zeros((B, gamma))
+    for b in range(B):
+        for k in range(gamma):
+            prev = int(anchor[b]) if k == 0 else int(tokens[b, k - 1])
+            z[b, k] = float(np.dot(w, np.concatenate([h[b, k], W1[prev]]))) + b0
+    return z
+
+
+def sts_apply(z, temps) -> np.ndarray:
+    """Calibrated conditional confidence c^[b, j] = sigmoid(z[b, j] / T_j).
+
+    [billytse] 5.2: the raw head ranks well but is overconfident; sequential
+    temperature scaling calibrates the cumulative survival left to right.
+    [weigao] part 3: the scheduler needs absolute probabilities.  Reading
+    (the pages give no formula): one temperature per block position divides
+    that position's logit; the survival the scheduler ranks by is the running
+    product of the calibrated conditionals, so it stays non-increasing along
+    a request and admitted sets stay prefixes.  T_j = 1 leaves c unchanged.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    T = np.asarray(temps, dtype=np.float64)
+    return _sigmoid(z / T[None, :])
+
+
+def confidence_sts(hidden, W1, anchor, tokens, w, b0, temps) -> np.ndarray:
+    """The confidence head followed by STS: sigmoid(z[b, k] / T_k)."""
+    return sts_apply(confidence_logits(hidden, W1, anchor, tokens, w, b0), temps)
+
+
+def _nll(p, y):
+    p = np.clip(p, 1e-300, 1.0 - 1e-16)
+    return -float(np.sum(y * np.log(p) + (1.0 - y) * np.log1p(-p)))
+
+
+def sts_fit(z, n_accepted, t_lo: float = 0.05, t_hi: float = 50.0, iters: int = 100):
+    """Fit the per-position temperatures left to right on calibration data.
+
+    z [N, gamma]: the head's logits of N calibration drafts; n_accepted [N]:
+    how many leading positions the target accepted.  The survival label of
+    position j is [n_accepted > j].  Position by position, with the earlier
+    temperatures fixed, T_j minimises the binary negative log-likelihood of
+    the cumulative survival a^_j = a^_{j-1} sigmoid(z_j / T_j) against those
+    labels (the quantity the scheduler uses, [billytse] 5.2: calibrate the
+    cumulative probability from left to right).  One-dimensional golden-
+    section search over log T in [t_lo, t_hi].  Returns temps [gamma].
+    """
+    z = np.asarray(z, dtype=np.float64)
+    n = np.asarray(n_accepted)
+    N, gamma = z.shape
+    temps = np.ones(gamma)
+    prev = np.ones(N)
+    g = (math.sqrt(5.0) - 1.0) / 2.0
+    for j in range(gamma):
+        y = (n > j).astype(np.float64)
+
+        def f(lt):
+            return _nll(prev * _sigmoid(z[:, j] / math.exp(lt)), y)
+
+        a, b = math.log(t_lo), math.log(t_hi)
+        c, d = b - g * (b - a), a + g * (b - a)
+        fc, fd = f(c), f(d)
+        for _ in range(iters):
+            if fc < fd:
+                b, d, fd = d, c, fc
+                c = b - g * (b - a)
+                fc = f(c)
+            else:
+                a, c, fc = c, d, fd
+                d = a + g * (b - a)
+                fd = f(d)
+        temps[j] = math.exp(0.5 * (a + b))
+        prev = prev * _sigmoid(z[:, j] / temps[j])
+    return temps
+
+
+def ece(prob, label, bins: int = 15) -> float:
+    """Expected calibration error: equal-width bins of the predicted
+    probability; the share-weighted mean of |mean label - mean prediction|."""
+    p = np.asarray(prob, dtype=np.float64).reshape(-1)
+    y = np.asarray(label, dtype=np.float64).reshape(-1)
+    idx = np.minimum((p * bins).astype(np.int64), bins - 1)
+    err = 0.0
+    for i in range(bins):
+        m = idx == i
+        if np.any(m):
+            err += m.mean() * abs(float(y[m].mean()) - float(p[m].mean()))
+    return err
