@@ -25,6 +25,7 @@ __all__ = [
     "dspark_schedule", "dspark_schedule_noalloc", "dspark_schedule_capacity", "dspark_schedule_threshold", "dspark_verify",
     "dspark_tv_label", "dspark_tv_label_workspace", "dspark_draft_block_workspace",
     "dspark_draft_block_rnn", "dspark_draft_block_rnn_workspace", "dspark_verify_rnn",
+    "dspark_confidence_sts",
     "dspark_verify_workspace", "dspark_schedule_workspace", "exported_names", "header_names",
     "dspark_trace_enable", "dspark_trace_summary", "dspark_set_draft_path",
     "DSPARK_F32", "DSPARK_BF16", "DEV_FLAGS",
@@ -59,6 +60,7 @@ _SIGS = {
     "dspark_draft_block_workspace": (_SZ, [_I, _I, _I, _I, _I]),
     "dspark_draft_block": (_I, [_I, _I, _I, _I, _I] + [_P] * 11 + [_P, _SZ, _P]),
     "dspark_confidence": (_I, [_I] * 6 + [_P] * 5 + [ctypes.c_float, _P, _P, _P]),
+    "dspark_confidence_sts": (_I, [_I] * 6 + [_P] * 5 + [ctypes.c_float, _P, _P, _P, _P]),
     "dspark_schedule_workspace": (_SZ, [_I, _I]),
     "dspark_schedule": (_I, [_I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "dspark_schedule_noalloc": (_I, [_I, _I, _P, _P, _I, _P, _P, _P, _P, _P]),
@@ -298,6 +300,28 @@ def dspark_confidence(hidden, W1, anchor, tokens, w, bias=0.0, *, conf=None, sta
     _check(lib.dspark_confidence(B, gamma, H, V, rank, dt, _ptr(hidden), _ptr(W1), _ptr(anchor),
                                  _ptr(tokens), _ptr(w), ctypes.c_float(bias), _ptr(conf),
                                  _ptr(status), _stream()))
+    return conf
+
+
+def dspark_confidence_sts(hidden, W1, anchor, tokens, w, bias, temps, *, conf=None,
+                          status=None):
+    """Confidence head with sequential temperature scaling: sigmoid(logit_k / temps[k]);
+    temps [gamma] fp32 device tensor.  Returns conf [B,gamma]."""
+    lib = load()
+    B, gamma, H = hidden.shape
+    V, rank = W1.shape
+    dt = _dtype_code(hidden)
+    dev = hidden.device
+    _need(hidden, "hidden"); _need(W1, "W1", hidden.dtype, None, dev)
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(tokens, "tokens", torch.int32, (B, gamma), dev)
+    _need(w, "w", torch.float32, (H + rank,), dev)
+    _need(temps, "temps", torch.float32, (gamma,), dev)
+    conf = _out(conf, "conf", torch.float32, (B, gamma), dev)
+    status = _status(status, dev)
+    _check(lib.dspark_confidence_sts(B, gamma, H, V, rank, dt, _ptr(hidden), _ptr(W1),
+                                     _ptr(anchor), _ptr(tokens), _ptr(w), ctypes.c_float(bias),
+                                     _ptr(temps), _ptr(conf), _ptr(status), _stream()))
     return conf
 
 

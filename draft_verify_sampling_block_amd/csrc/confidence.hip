@@ -5,6 +5,11 @@
 // sigmoid.  [xhh] non-anticipation note: position k reads x_{k-1} (the
 // anchor for k = 0), never x_k.  One wave per (b, k): the H + rank dot
 // product is read with 16-byte loads and reduced across the wave in fp32.
+//
+// With per-position temperatures (dspark_confidence_sts: sequential
+// temperature scaling, [billytse] 5.2; [weigao] part 3) the logit of
+// position k is divided by temps[k] before the sigmoid; a temperature that
+// is not finite and positive leaves the logit unchanged and is flagged.
 #include "dspark_common.hpp"
 #include "dspark_launch.hpp"
 #include "trace.hpp"
@@ -16,7 +21,7 @@ __global__ __launch_bounds__(256) void confidence_kernel(
     int B, int gamma, int H, int V, int rank, const T* __restrict__ hidden,
     const T* __restrict__ W1, const int32_t* __restrict__ anchor,
     const int32_t* __restrict__ tokens, const float* __restrict__ w, float bias,
-    float* __restrict__ conf, int32_t* status) {
+    const float* __restrict__ temps, float* __restrict__ conf, int32_t* status) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= B * gamma) return;
@@ -43,24 +48,35 @@ __global__ __launch_bounds__(256) void confidence_kernel(
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
-  if (lane == 0) conf[row] = 1.f / (1.f + expf(-(s + bias)));
+  if (lane == 0) {
+    float z = s + bias;
+    if (temps) {
+      const float t = temps[k];
+      if (t > 0.f && t <= 3.0e38f)
+        z = z / t;
+      else
+        flag(status, DSPARK_DEV_BAD_CONF);
+    }
+    conf[row] = 1.f / (1.f + expf(-z));
+  }
 }
 
 hipError_t launch_confidence(int B, int gamma, int H, int V, int rank, int dtype,
                              const void* hidden, const void* W1, const int32_t* anchor,
-                             const int32_t* tokens, const float* w, float bias, float* conf,
-                             int32_t* status, hipStream_t stream) {
+                             const int32_t* tokens, const float* w, float bias,
+                             const float* temps, float* conf, int32_t* status,
+                             hipStream_t stream) {
   const int rows = B * gamma;
   const dim3 grid((rows + 3) / 4), blk(256);
   TraceScope ts("confidence_kernel", stream);
   if (dtype == DSPARK_BF16)
     confidence_kernel<uint16_t><<<grid, blk, 0, stream>>>(
         B, gamma, H, V, rank, static_cast<const uint16_t*>(hidden),
-        static_cast<const uint16_t*>(W1), anchor, tokens, w, bias, conf, status);
+        static_cast<const uint16_t*>(W1), anchor, tokens, w, bias, temps, conf, status);
   else
     confidence_kernel<float><<<grid, blk, 0, stream>>>(
         B, gamma, H, V, rank, static_cast<const float*>(hidden), static_cast<const float*>(W1),
-        anchor, tokens, w, bias, conf, status);
+        anchor, tokens, w, bias, temps, conf, status);
   return hipGetLastError();
 }
 

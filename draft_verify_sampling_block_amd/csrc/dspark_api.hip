@@ -160,7 +160,21 @@ int dspark_confidence(int B, int gamma, int H, int V, int rank, int dtype, const
   REQUIRE_PTR(hidden); REQUIRE_PTR(W1); REQUIRE_PTR(anchor); REQUIRE_PTR(tokens);
   REQUIRE_PTR(w); REQUIRE_PTR(conf); OPT_PTR(status);
   return hip_status(fn, dspark::launch_confidence(B, gamma, H, V, rank, dtype, hidden, W1, anchor,
-                                                  tokens, w, bias, conf, status, stream));
+                                                  tokens, w, bias, nullptr, conf, status, stream));
+}
+
+int dspark_confidence_sts(int B, int gamma, int H, int V, int rank, int dtype,
+                          const void* hidden, const void* W1, const int32_t* anchor,
+                          const int32_t* tokens, const float* w, float bias, const float* temps,
+                          float* conf, int32_t* status, hipStream_t stream) {
+  const char* fn = "dspark_confidence_sts";
+  int rc = check_dims(fn, B, gamma, V, rank, dtype);
+  if (rc) return rc;
+  if (H < 8 || H % 8) return fail(DSPARK_EINVAL, "%s: H=%d must be a positive multiple of 8", fn, H);
+  REQUIRE_PTR(hidden); REQUIRE_PTR(W1); REQUIRE_PTR(anchor); REQUIRE_PTR(tokens);
+  REQUIRE_PTR(w); REQUIRE_PTR(temps); REQUIRE_PTR(conf); OPT_PTR(status);
+  return hip_status(fn, dspark::launch_confidence(B, gamma, H, V, rank, dtype, hidden, W1, anchor,
+                                                  tokens, w, bias, temps, conf, status, stream));
 }
 
 size_t dspark_schedule_workspace(int R, int gamma) {

@@ -46,8 +46,9 @@ hipError_t launch_draft_block_rnn(int B, int gamma, int V, int rank, int H, int 
 
 hipError_t launch_confidence(int B, int gamma, int H, int V, int rank, int dtype,
                              const void* hidden, const void* W1, const int32_t* anchor,
-                             const int32_t* tokens, const float* w, float bias, float* conf,
-                             int32_t* status, hipStream_t stream);
+                             const int32_t* tokens, const float* w, float bias,
+                             const float* temps, float* conf, int32_t* status,
+                             hipStream_t stream);   // temps [gamma] or NULL
 
 constexpr int kScheduleMaxKeys = 8192;
 constexpr int kScheduleMergeKeys = 4096;   // candidates ranked by run searches

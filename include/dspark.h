@@ -176,6 +176,28 @@ int dspark_confidence(int B, int gamma, int H, int V, int rank, int dtype,
                       int32_t* status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * dspark_confidence_sts: the confidence head with sequential temperature
+ * scaling ([billytse] 5.2: the raw head is overconfident, and STS calibrates
+ * the cumulative probability from left to right; [weigao] part 3: the
+ * scheduler needs absolute probabilities).  The pages give no formula; this
+ * library's reading: one temperature per block position divides that
+ * position's logit,
+ *     conf[b,k] = sigmoid( (w . [hidden[b,k] ; W1[prev_k]] + bias) / temps[k] ),
+ * and the scheduler's survival is the running product of these calibrated
+ * conditionals (still non-increasing, so admitted sets stay prefixes).  The
+ * temperatures are fitted offline, position by position from the left,
+ * against the cumulative survival of calibration drafts.  temps [gamma] fp32
+ * device array; temps[k] == 1 gives exactly dspark_confidence's value; a
+ * temperature that is not finite and positive leaves the logit unchanged and
+ * sets DSPARK_DEV_BAD_CONF.  Other arguments as dspark_confidence.
+ * ---------------------------------------------------------------------- */
+int dspark_confidence_sts(int B, int gamma, int H, int V, int rank, int dtype,
+                          const void* hidden, const void* W1,
+                          const int32_t* anchor, const int32_t* tokens,
+                          const float* w, float bias, const float* temps, float* conf,
+                          int32_t* status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * dspark_schedule: hardware-aware prefix scheduler ([weigao] part 4;
  * [billytse] 6-7; [xhh] scheduler Q&A).
  *     a[r,j]  = prod_{i<=j} conf[r,i]        (fp64, left to right)
