@@ -180,3 +180,77 @@ def check_tv(wl, W1_64, W2_64, tokens, tv, label, rows=None):
         worst = max(worst, abs(float(tv[b, k]) - r))
     return dict(rows=len(todo), max_abs=worst, mean_label=float(np.mean(1.0 - np.array(
         [ref["tv"][b, k] for b, k in todo]))))
+
+
+def check_end_to_end(wl, out):
+    """The oracle's own step from the inputs alone (draft, confidence,
+    scheduler or the fixed length, verify), compared with the device step.
+
+    Requests are compared independently.  A request whose drafted tokens
+    differ must show the first difference at a draw whose oracle margin is
+    within BAND (the device token's interval within BAND of u); its later
+    positions and its verification follow different drafts and are not
+    compared.  The scheduler is compared when every request drafted the same
+    tokens (its verify lengths bit-exact, or an explained near-tie of Theta).
+    A request with identical drafts and verify length must accept the same
+    count unless |u - p/q| <= BAND at the first difference, and emit the same
+    final token unless its final draw's margin is within BAND.
+    """
+    B, gamma = out["tokens"].shape
+    W1_64, W2_64 = O.f64(wl.W1), O.f64(wl.W2)
+    d = O.draft_block(wl.U, W1_64, W2_64, wl.anchor, wl.temperature, wl.uniforms)
+    rep = dict(requests=B, draft_identical=0, draft_explained=0, conf_rows=0,
+               verify_identical=0, verify_explained=0, schedule="compared")
+    same = np.zeros(B, dtype=bool)
+    for b in range(B):
+        diff = np.nonzero(out["tokens"][b] != d["tokens"][b])[0]
+        if len(diff) == 0:
+            same[b] = True
+            rep["draft_identical"] += 1
+            for k in range(gamma):
+                _req(close(out["q_tok"][b, k], d["q_tok"][b, k]), f"e2e q_tok ({b},{k})")
+            continue
+        k = int(diff[0])
+        _req(d["margin"][b, k] <= BAND,
+             f"e2e draft ({b},{k}): device {out['tokens'][b, k]} vs oracle {d['tokens'][b, k]} "
+             f"(margin {d['margin'][b, k]:.3g})")
+        rep["draft_explained"] += 1
+    c = O.confidence(wl.hidden, W1_64, wl.anchor, d["tokens"], wl.w, wl.b0)
+    for b in np.nonzero(same)[0]:
+        for k in range(gamma):
+            _req(close(out["conf"][b, k], c[b, k]), f"e2e confidence ({b},{k})")
+            rep["conf_rows"] += 1
+    if out["sched"]:
+        s = O.schedule(c, wl.sps)
+        ell_o = s["ell"]
+        if same.all():
+            if not np.array_equal(np.asarray(out["ell"], dtype=np.int64), ell_o):
+                # only a Theta comparison decided within rounding may differ:
+                # the device's fp32 confidences against the oracle's fp64 ones
+                s_dev = O.schedule(out["conf"].astype(np.float64), wl.sps)
+                _req(np.array_equal(np.asarray(out["ell"], dtype=np.int64), s_dev["ell"]),
+                     "e2e scheduler differs from the oracle's on the device's confidences")
+                rep["schedule"] = "explained by fp32 confidences"
+        else:
+            rep["schedule"] = "not compared (drafts differ)"
+    else:
+        ell_o = np.full(B, gamma, dtype=np.int64)
+    v = O.verify(wl.target, wl.U, W1_64, W2_64, wl.anchor, d["tokens"], d["q_tok"],
+                 wl.temperature, wl.uniforms, ell_o)
+    for b in np.nonzero(same)[0]:
+        if int(out["ell"][b]) != int(ell_o[b]):
+            continue
+        n_o, n_g = int(v["n_accepted"][b]), int(out["n_accepted"][b])
+        if n_o != n_g:
+            k = min(n_o, n_g)
+            gap = abs(float(wl.uniforms[b, k, 1]) - v["ratio"][b, k])
+            _req(gap <= BAND, f"e2e accepted length of {b}: device {n_g} vs oracle {n_o}")
+            rep["verify_explained"] += 1
+            continue
+        y_g, y_o = int(out["out_tokens"][b, n_g]), int(v["out_tokens"][b, n_o])
+        if y_g != y_o:
+            _req(v["final_margin"][b] <= BAND, f"e2e final token of {b}: {y_g} vs {y_o}")
+            rep["verify_explained"] += 1
+        else:
+            rep["verify_identical"] += 1
+    return rep
