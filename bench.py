@@ -83,7 +83,7 @@ def draft_kernel_bytes(wl, kernel):
     """
     e = 2 if wl.dtype == "bf16" else 4
     B, g, V, r = wl.B, wl.gamma, wl.V, wl.rank
-    if kernel == "pdraft_kernel":
+    if kernel in ("pdraft_kernel", "pdraft_pipe_kernel"):
         return (e * B * g * V + e * r * V + e * B * g * r
                 + 4 * B + 4 * B + 4 * B * g + 4 * B * g * 4)
     return e * B * V + e * B * r + e * r * V / g
@@ -98,7 +98,7 @@ def draft_intermediate_bytes(wl, kernel):
     B, g = wl.B, wl.gamma
     greedy = int(np.sum(~(np.asarray(wl.temperature) > 0)))
     per_pos = 2 * (8 * B * nT + 4 * greedy * nT)
-    return g * per_pos if kernel == "pdraft_kernel" else per_pos
+    return g * per_pos if kernel in ("pdraft_kernel", "pdraft_pipe_kernel") else per_pos
 
 
 KERNEL_SOURCES = ["draft_verify_sampling_block_amd/csrc/draft.hip",
@@ -394,7 +394,8 @@ def main():
     dom = max(tr, key=lambda k: tr[k][1])
     kern_ms = {k: v[1] / v[0] for k, v in tr.items()}
     per_step_ms = {k: v[1] / args.steps for k, v in tr.items()}
-    draft_kernel = "pdraft_kernel" if "pdraft_kernel" in kern_ms else "draft_stats_kernel"
+    draft_kernel = next((k for k in ("pdraft_pipe_kernel", "pdraft_kernel") if k in kern_ms),
+                        "draft_stats_kernel")
     stats_bytes = draft_kernel_bytes(wl, draft_kernel)
     avg_s = kern_ms[draft_kernel] / 1e3
     achieved = stats_bytes / avg_s / 1e9

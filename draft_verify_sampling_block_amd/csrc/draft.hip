@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "dspark_common.hpp"
+#include "draft_tile.hpp"
 #include "dspark_launch.hpp"
 #include "trace.hpp"
 
@@ -32,85 +33,6 @@ namespace dspark {
 
 template <typename T>
 constexpr bool kIsBf16 = std::is_same<T, uint16_t>::value;
-
-// ---------------------------------------------------------------------------
-// Shared pieces
-// ---------------------------------------------------------------------------
-
-struct TileStats {
-  uint64_t* ms;   // [B][nT] (max, sum) as two fp32: max over the tile of y' = z + bias
-                  // (unscaled logits), sum over the tile of exp((y' - max) / T)
-  int32_t* arg;   // [B][nT] lowest vocabulary index attaining the max (greedy rows only)
-};
-__device__ inline uint64_t pack_ms(float mx, float s) {
-  return (uint64_t)__float_as_uint(mx) | ((uint64_t)__float_as_uint(s) << 32);
-}
-__device__ inline float ms_max(uint64_t v) { return __uint_as_float((uint32_t)v); }
-__device__ inline float ms_sum(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
-
-// inverse temperature of a request; 0 marks greedy
-__device__ inline float inv_temp(float T) { return (T > 0.f) ? 1.f / T : 0.f; }
-
-// Summand of the tile mass: exp((y' - m') / T) as 2^(y' ce - m' ce) with
-// ce = log2(e) / T and mc = m' ce.  The statistics pass and the sampler's
-// recompute evaluate exactly this expression.
-__device__ inline float tile_term(float yp, float ce, float mc) {
-  return __builtin_amdgcn_exp2f(__builtin_fmaf(yp, ce, -mc));
-}
-
-// Reduction of one block-tile for this lane's request (column c): acc holds
-// y' = base logit + bias (-inf past V); gives the tile max, lowest argmax
-// (when `any_greedy`, which is wave-uniform) and exp-sum, combined over the
-// two half-waves so both lanes of the request hold them.  `it` is the lane's
-// inverse temperature (0 = greedy).
-struct TileStat {
-  float mx, s;
-  int arg;
-};
-__device__ inline TileStat tile_reduce(const f32x16_t acc[kSub], int vt, float it,
-                                       bool any_greedy) {
-  const int h = (threadIdx.x & 63) >> 5;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < kSub; ++t) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, acc[t][j]);
-  }
-  float lo, hi;
-  half_pair(mx, lo, hi);
-  mx = fmaxf(lo, hi);
-  int arg = 0x7fffffff;
-  if (any_greedy) {
-    int off = 0x7fffffff;   // lowest in-lane offset 32t + j attaining the max
-#pragma unroll
-    for (int t = kSub - 1; t >= 0; --t) {
-#pragma unroll
-      for (int j = 15; j >= 0; --j) off = (acc[t][j] == mx) ? 32 * t + j : off;
-    }
-    arg = off == 0x7fffffff ? off : vt * kTileV + 16 * h + off;
-    int alo, ahi;
-    half_pair(arg, alo, ahi);
-    arg = min(alo, ahi);
-  }
-  const float ce = it * kLog2e, mc = mx * ce;
-  float s = 0.f;
-#pragma unroll
-  for (int t = 0; t < kSub; ++t) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s += tile_term(acc[t][j], ce, mc);
-  }
-  half_pair(s, lo, hi);
-  return TileStat{mx, lo + hi, arg};
-}
-
-// store the statistics of request b (< B) for tile vt (device-coherent);
-// the argmax only for a greedy request (inverse temperature `it` 0)
-__device__ inline void store_tile_stat(const TileStats& ts, int b, int nT, int vt,
-                                       const TileStat& st, float it) {
-  const size_t i = (size_t)b * nT + vt;
-  st_dev(ts.ms + i, pack_ms(st.mx, st.s));
-  if (!(it > 0.f)) st_dev(ts.arg + i, st.arg);
-}
 
 // Shared-memory state of the per-request sampler (block-wide).
 struct SampShared {
@@ -879,8 +801,9 @@ __global__ void pdraft_reset_kernel(uint32_t* f0, int n0, uint32_t* f1, int n1) 
 // ---------------------------------------------------------------------------
 
 namespace {
-// 0 auto, 1 multi-launch, 2-4 persistent only (3: 8 waves, 4: 4 waves);
-// process-wide, read by every call
+// 0 auto, 1 multi-launch, 2-4 the earlier persistent kernel only (3: 8
+// waves, 4: 4 waves), 5-7 the pipelined kernel only (6: one 32-request block
+// per window, 7: two); process-wide, read by every call
 std::atomic<int> g_draft_path{0};
 
 struct DevInfo {
@@ -917,7 +840,9 @@ static size_t stats_bytes(int B, int V) { return align256((size_t)B * n_tiles(V)
 size_t draft_workspace_bytes(int B, int gamma, int V, int rank, int dtype) {
   (void)gamma; (void)rank; (void)dtype;
   const size_t flags = align256((size_t)kPdMaxGroups * kPdFlagStride * 4) + align256((size_t)B * 4);
-  return 3 * stats_bytes(B, V) + flags;
+  const size_t persistent = 3 * stats_bytes(B, V) + flags;
+  const size_t pipe = draft_pipe_workspace_bytes(B, V);
+  return persistent > pipe ? persistent : pipe;
 }
 
 static TileStats carve_stats(void* ws, int B, int V) {
@@ -1007,6 +932,17 @@ hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, cons
   // only, so without one the per-position launches (which never wait) run
   const int path = get_draft_path();
   const bool persist = path != 1 && status != nullptr;
+  // the pipelined kernel first (automatic setting, or 5), then the
+  // earlier persistent kernel (automatic, or 2-4)
+  if (dtype == DSPARK_BF16 && persist && (path == 0 || path == 5)) {
+    const DevInfo di = dev_info();
+    hipError_t e = hipErrorNotSupported;
+    if (di.coop && di.cus > 0)
+      e = draft_pipe(B, gamma, V, rank, di.cus, 200LL * di.wall_khz, static_cast<const uint16_t*>(U),
+                     static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2), anchor,
+                     temperature, uniforms, tokens, q_tok, row_max, row_logZ, status, ws, stream);
+    if (e != hipErrorNotSupported || path == 5) return e;
+  }
   if (dtype == DSPARK_BF16) {
     auto* u = static_cast<const uint16_t*>(U);
     auto* w1 = static_cast<const uint16_t*>(W1);

@@ -1,0 +1,878 @@
+// Pipelined single-launch draft kernel (bf16, rank <= 256).
+//
+// [billytse] 3.2-3.3: position k's token is drawn from softmax(U_k + W1[prev]
+// W2), prev being the token drawn at position k - 1 (the anchor at k = 0);
+// positions are sampled left to right, requests independently of each other.
+//
+// One cooperative launch with two roles:
+//
+//  * tile groups (work-groups 0 .. Pt-1): each owns a contiguous run of
+//    64-entry vocabulary tiles whose W2 rows stay on chip for the whole block
+//    (8 tiles in registers, one per wave, up to 2 more in LDS).  The requests
+//    are cut into windows of up to 64 (two 32-request blocks); the windows of
+//    all positions are processed in order (position-major).  Per window every
+//    wave runs its block-tasks (tile x 32 requests: bias on the matrix cores
+//    with the accumulators started at the base logits, then the tile
+//    reduction), and the statistics go out as one 8-byte word per (request,
+//    tile) plus one per (request, group): the group's max and its exp-sum
+//    relative to that max, tagged with the parity of the position.
+//
+//  * draw groups (work-groups Pt .. Pt+Pd-1): one wave per request draws its
+//    token as soon as every tile group's word of that request is in: an fp64
+//    scan over the Pt group words finds the group where the cumulative mass
+//    crosses u * Z, a scan over that group's tile words the tile, and a
+//    recompute of that one tile's 64 logits (W2 rows, the previous token's W1
+//    row and the base logits) the entry.  The token goes out in the request's
+//    flag word.
+//
+// While a window's tokens are drawn the tile groups already run the next
+// window (other requests), so with two or more windows per position the
+// draws and the exchanges stay off the critical path; the tile groups wait
+// only when a window's previous tokens are not in yet.
+//
+// Waits between work-groups are bounded by the device wall clock; a wait
+// that gives up raises DSPARK_DEV_TIMEOUT, after which every other wait gives
+// up at once so the grid always drains (results are then undefined but every
+// output stays in range).
+#include <type_traits>
+
+#include "dspark_common.hpp"
+#include "draft_tile.hpp"
+#include "dspark_launch.hpp"
+#include "trace.hpp"
+
+namespace dspark {
+
+constexpr int kPpWaves = 8;
+constexpr int kPpRegTiles = 8;                          // register tiles (one per wave)
+constexpr int kPpLdsTiles = 2;                          // LDS tiles per tile group
+constexpr int kPpMaxTiles = kPpRegTiles + kPpLdsTiles;  // tiles per tile group
+constexpr int kPpSlots = kPpRegTiles + 2 * kPpLdsTiles; // statistics slots (LDS tiles by half)
+constexpr int kPpRowBytes = kTileM * (2 * kMaxKSteps + 1) * 16;   // W1 rows of one window
+constexpr int kPpMaxTileGroups = 256;                   // group words: 4 per lane of a wave
+constexpr int kPpMaxDrawGroups = 16;
+constexpr int kPpDrawLds = 1024;                        // per draw wave: W1 row + 64 masses
+static_assert(kPpWaves * kPpDrawLds <= kLdsTileBytes, "draw scratch lives in ldsX");
+
+struct PpArgs {
+  int B, gamma, V, rank;
+  int Pt, Pd;   // tile groups [0, Pt), draw groups [Pt, Pt + Pd)
+  const uint16_t* U;
+  const uint16_t* W1;
+  const uint16_t* W2;
+  const int32_t* anchor;
+  const float* temperature;
+  const float* uniforms;
+  int32_t* tokens;
+  float* q_tok;
+  float* row_max;
+  float* row_logZ;
+  int32_t* status;
+  uint64_t* tw;         // [B][nT] tile words (max, exp-sum | parity << 63)
+  uint64_t* gw;         // [B][Pt] group words (max, exp-sum or argmax | parity << 63)
+  uint32_t* tok_flag;   // [B] ((k + 1) << 24) | token k
+  long long spin_cap;   // wall-clock ticks a wait may last
+};
+
+// tiles of tile group q (contiguous, the first nT % Pt groups one more)
+__host__ __device__ inline int pp_tcount(int q, int nT, int Pt) {
+  return nT / Pt + (q < nT % Pt ? 1 : 0);
+}
+__host__ __device__ inline int pp_tbase(int q, int nT, int Pt) {
+  return q * (nT / Pt) + (q < nT % Pt ? q : nT % Pt);
+}
+
+__device__ inline double wave_incl_scan(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Bounded wait of one wave: true once done() holds on every lane; false
+// when the wall-clock cap passed (DSPARK_DEV_TIMEOUT raised here) or another
+// wait already gave up.
+template <typename Done>
+__device__ inline bool pp_wait(Done&& done, long long cap, int32_t* status) {
+  const long long t0 = wall_clock64();
+  for (int it = 0;; ++it) {
+    if (__all(done())) return true;
+    if ((it & 15) == 15) {
+      const bool late = wall_clock64() - t0 > cap;
+      const bool gave_up = ld_dev(status) & DSPARK_DEV_TIMEOUT;
+      if (late || gave_up) {
+        if (late && (threadIdx.x & 63) == 0) flag(status, DSPARK_DEV_TIMEOUT);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Draw role: one wave draws token k of request b
+// ---------------------------------------------------------------------------
+template <int KS>
+__device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
+  const int lane = threadIdx.x & 63;
+  const int B = a.B, V = a.V, gamma = a.gamma, rank = a.rank, Pt = a.Pt;
+  const int nT = n_tiles(V);
+  (void)B;
+  // the previous token: the anchor, or the flag word this wave's lane 0
+  // stored for position k - 1 (read back by the same lane)
+  int pv = 0;
+  if (lane == 0) pv = k == 0 ? a.anchor[b] : (int)(ld_dev(a.tok_flag + b) & 0xFFFFFFu);
+  const int prev = clamp_token(__shfl(pv, 0, kWave), V, nullptr);
+  // the previous token's W1 row into this wave's LDS (needed only by the
+  // crossing-tile recompute; requested first so it is in by then)
+  if (lane < rank / 8)
+    __builtin_amdgcn_global_load_lds(a.W1 + (size_t)prev * rank + 8 * lane, wl, 16, 0, 0);
+  const float Tb = a.temperature[b];
+  const bool greedy = !(Tb > 0.f);
+  const double u = (double)a.uniforms[((size_t)b * (gamma + 1) + k) * 2 + 0];
+  const size_t out = (size_t)b * gamma + k;
+  auto emit = [&](int tok, float q, float rmax, float rlz) {
+    if (lane == 0) {
+      st_dev(a.tok_flag + b, ((uint32_t)(k + 1) << 24) | (uint32_t)tok);
+      a.tokens[out] = tok;
+      a.q_tok[out] = q;
+      a.row_max[out] = rmax;
+      a.row_logZ[out] = rlz;
+    }
+  };
+
+  // the group words of (b, k): lane l holds groups 4l .. 4l + 3.  Two
+  // polls are kept in flight (each checked while the next is under way), so
+  // words that land between polls are seen half a round trip sooner.
+  const uint64_t want = (uint64_t)((k + 1) & 1);
+  const uint64_t* gwb = a.gw + (size_t)b * Pt;
+  uint64_t r[4], ra[4], rb[4];
+  auto issue = [&](uint64_t (&x)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (4 * lane + i < Pt) ? ld_dev(gwb + 4 * lane + i) : (want << 63);
+  };
+  auto ready = [&](const uint64_t (&x)[4]) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok &= (x[i] >> 63) == want;
+    return __all(ok) != 0;
+  };
+  {
+    const long long t0 = wall_clock64();
+    issue(ra);
+    for (int it = 0;; ++it) {
+      issue(rb);
+      if (ready(ra)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = ra[i];
+        break;
+      }
+      issue(ra);
+      if (ready(rb)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = rb[i];
+        break;
+      }
+      if ((it & 7) == 7) {
+        const bool late = wall_clock64() - t0 > a.spin_cap;
+        if (late || (ld_dev(a.status) & DSPARK_DEV_TIMEOUT)) {
+          if (late && lane == 0) flag(a.status, DSPARK_DEV_TIMEOUT);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = rb[i];
+          break;
+        }
+      }
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);   // tile-word loads stay after the group words
+
+  float gm[4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    gm[i] = (4 * lane + i < Pt) ? __uint_as_float((uint32_t)r[i]) : -INFINITY;
+    mloc = fmaxf(mloc, gm[i]);
+  }
+  const float M = wave_max(mloc);
+  auto payload = [&](int i) { return (uint32_t)(r[i] >> 32) & 0x7FFFFFFFu; };
+
+  if (greedy) {
+    // the lowest group attaining the max holds the lowest argmax
+    int fi = 4;
+#pragma unroll
+    for (int i = 3; i >= 0; --i)
+      if (4 * lane + i < Pt && gm[i] == M) fi = i;
+    const unsigned long long hit = __ballot(fi < 4);
+    int tok = 0;
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      uint32_t pl = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i == fi) pl = payload(i);
+      tok = (int)__shfl((int)pl, src, kWave);
+    }
+    if (!hit || !(M == M) || tok < 0 || tok >= V) {
+      if (lane == 0) flag(a.status, DSPARK_DEV_NONFINITE);
+      tok = 0;
+    }
+    emit(tok, 1.f, M, 0.f);
+    return;
+  }
+
+  // mass of group q relative to the row max, in fp64; scan over the groups
+  const float scale = 1.f / Tb;
+  const float ce = scale * kLog2e;
+  double gmass[4];
+  double lsum = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    gmass[i] = (4 * lane + i < Pt)
+                   ? (double)__uint_as_float(payload(i)) *
+                         (double)__builtin_amdgcn_exp2f((gm[i] - M) * ce)
+                   : 0.0;
+    lsum += gmass[i];
+  }
+  const double incl = wave_incl_scan(lsum);
+  double excl = __shfl_up(incl, 1, kWave);
+  if (lane == 0) excl = 0.0;
+  const double Z = __shfl(incl, kWave - 1, kWave);
+  // u * Z can round up to Z: the target is kept below Z, so exactly one
+  // lane's interval [excl, incl) holds it (consecutive intervals share ends)
+  double target = u * Z;
+  if (!(target < Z)) target = nextafter(Z, 0.0);
+  const float ms = M * scale;
+  const bool finite = isfinite(M) && isfinite(Z) && Z > 0.0;
+  const bool mine = finite && lsum > 0.0 && excl <= target && target < incl;
+  int fg = -1;
+  double before = excl;
+  if (mine) {
+    double run = excl, lastb = excl;
+    int lastg = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (gmass[i] > 0.0) {
+        lastg = i;
+        lastb = run;
+        if (fg < 0 && target < run + gmass[i]) {
+          fg = i;
+          before = run;
+        }
+      }
+      run += gmass[i];
+    }
+    if (fg < 0) {
+      fg = lastg;
+      before = lastb;
+    }
+  }
+  const unsigned long long gh = __ballot(mine);
+  if (!gh) {
+    if (lane == 0) flag(a.status, DSPARK_DEV_NONFINITE);
+    emit(0, 0.f, ms, __logf((float)Z));
+    return;
+  }
+  const int gsrc = __builtin_ctzll(gh);
+  const int gq = 4 * gsrc + __shfl(fg, gsrc, kWave);
+  const double gbefore = __shfl(before, gsrc, kWave);
+
+  // that group's tile words: lane t holds tile tb + t
+  const int tb = pp_tbase(gq, nT, Pt), tc = pp_tcount(gq, nT, Pt);
+  // (tagged with the position's parity like the group words; stored before
+  // them, so normally in already)
+  uint64_t w = 0;
+  pp_wait(
+      [&]() {
+        if (lane >= tc) return true;
+        w = ld_dev(a.tw + (size_t)b * nT + tb + lane);
+        return (w >> 63) == want;
+      },
+      a.spin_cap, a.status);
+  float tm = -INFINITY;
+  double tmass = 0.0;
+  if (lane < tc) {
+    tm = ms_max(w);
+    tmass = (double)__uint_as_float((uint32_t)(w >> 32) & 0x7FFFFFFFu) *
+            (double)__builtin_amdgcn_exp2f((tm - M) * ce);
+  }
+  const double tincl = wave_incl_scan(tmass);
+  double texcl = __shfl_up(tincl, 1, kWave);
+  if (lane == 0) texcl = 0.0;
+  const double rt = target - gbefore;
+  const unsigned long long th = __ballot(tmass > 0.0 && rt < tincl);
+  const unsigned long long tpos = __ballot(tmass > 0.0);
+  if (!tpos) {
+    if (lane == 0) flag(a.status, DSPARK_DEV_NONFINITE);
+    emit(0, 0.f, ms, __logf((float)Z));
+    return;
+  }
+  const int tl = th ? __builtin_ctzll(th) : 63 - __builtin_clzll(tpos);
+  const int vt = tb + tl;
+  const float mvt = __shfl(tm, tl, kWave);
+  const double tbefore = gbefore + __shfl(texcl, tl, kWave);
+  const double tscale = (double)__builtin_amdgcn_exp2f((mvt - M) * ce);
+  const float mc = mvt * ce;
+
+  // recompute tile vt: lane (g, rho) sums k-rows rho, rho + 8, ... for the
+  // entries v0 + 8g .. + 7; the eight partial sums of an entry are then
+  // added across the lanes of the same g
+  const int v0 = vt * kTileV;
+  const int g8 = lane & 7, rho = lane >> 3;
+  const int col = min(v0 + 8 * g8, V - 8);   // pieces past V: any valid address
+  constexpr int NR = 2 * KS;                 // k-rows per lane (rank / 8)
+  u32x4_t wv[NR];
+#pragma unroll
+  for (int m = 0; m < NR; ++m)
+    wv[m] = *reinterpret_cast<const u32x4_t*>(a.W2 + (size_t)(rho + 8 * m) * V + col);
+  const u32x4_t uv = __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4_t*>(a.U + out * V + col));
+  const uint16_t* wrow = reinterpret_cast<const uint16_t*>(wl);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const float ak = bf16_to_f32(wrow[rho + 8 * m]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wd = wv[m][e >> 1];
+      const float w2 = (e & 1) ? __uint_as_float(wd & 0xFFFF0000u) : __uint_as_float(wd << 16);
+      acc[e] = __builtin_fmaf(ak, w2, acc[e]);
+    }
+  }
+#pragma unroll
+  for (int o = 8; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+  }
+  float* es = reinterpret_cast<float*>(wl + 512);
+  if (rho == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wd = uv[e >> 1];
+      const float ub = (e & 1) ? __uint_as_float(wd & 0xFFFF0000u) : __uint_as_float(wd << 16);
+      const float z = ub + acc[e];
+      es[8 * g8 + e] = (v0 + 8 * g8 + e < V) ? tile_term(z, ce, mc) : 0.f;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  const double ej = (double)es[lane];
+  const double rr = (target - tbefore) / tscale;
+  const double eincl = wave_incl_scan(ej);
+  const unsigned long long hit = __ballot(ej > 0.0 && rr < eincl);
+  const unsigned long long pos = __ballot(ej > 0.0);
+  const int pick = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
+  const double epick = __shfl(ej, pick, kWave);
+  emit(v0 + pick, (float)(epick * tscale / Z), ms, __logf((float)Z));
+}
+
+// ---------------------------------------------------------------------------
+// The kernel
+// ---------------------------------------------------------------------------
+template <int KS>
+__global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a) {
+  constexpr int nq = 2 * KS;
+  constexpr int nc = nq + 1;   // 16-byte chunks per padded LDS row
+  __shared__ __attribute__((aligned(16))) char ldsL[kPpLdsTiles * kLdsTileBytes];
+  // W1 rows of the current and the next window: two separate arrays, so
+  // that the compiler can tell a gather into one from the reads of the
+  // other and lets them overlap
+  __shared__ __attribute__((aligned(16))) char ldsR0[kPpRowBytes];
+  __shared__ __attribute__((aligned(16))) char ldsR1[kPpRowBytes];
+  // third W2 tile image while the resident tiles are staged; then 4 KB per
+  // wave for passing the base logits to the matrix layout (tile groups) or
+  // the draw waves' scratch
+  __shared__ __attribute__((aligned(16))) char ldsX[kLdsTileBytes];
+  // per window parity: statistics of the window's block-tasks per slot and
+  // row (register tile of wave w: slot w; half t of LDS tile i: slot 8 + 2i + t)
+  __shared__ float s_mx[2][kPpSlots][kTileM], s_sum[2][kPpSlots][kTileM];
+  __shared__ int s_arg[2][kPpSlots][kTileM];
+  // inverse temperatures of a window's requests, by window index mod 3 (the
+  // group words of window j - 1, the tasks of window j and the gather for window
+  // j + 1 overlap)
+  __shared__ float s_it[3][kTileM];
+  __shared__ int s_done[2];   // waves done with the window of each parity
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the lane id from the mbcnt instructions (rematerialised where needed
+  // instead of held in a register the task loop would have to spill)
+  const int lane = __lane_id();
+
+  if ((int)blockIdx.x >= a.Pt) {
+    // draw role: wave w of draw group g draws requests g + Pd (w + 8 m),
+    // m = 0, 1, ... of every position, in the order the tile groups complete
+    // them; consecutive requests go to different draw groups, so a window's
+    // draws (and their W2 reads) spread over all of them
+    const int g = (int)blockIdx.x - a.Pt;
+    char* wl = ldsX + wave * kPpDrawLds;
+    for (int k = 0; k < a.gamma; ++k)
+      for (int b = g + a.Pd * wave; b < a.B; b += a.Pd * kPpWaves) pp_draw<KS>(a, b, k, wl);
+    return;
+  }
+
+  const int p = blockIdx.x, Pt = a.Pt;
+  const int c = lane & 31, h = lane >> 5;
+  const int B = a.B, V = a.V, gamma = a.gamma, rank = a.rank;
+  const int nT = n_tiles(V);
+  const int tcount = pp_tcount(p, nT, Pt), tbase = pp_tbase(p, nT, Pt);
+  auto slot_tile = [&](int slot) { return slot < tcount ? tbase + slot : nT; };
+
+  // Resident W2 tiles (W2 is [rank, V]): the blocks of the eight register
+  // tiles are loaded in one shot and pass three at a time through three LDS
+  // images (the two LDS tile areas and ldsX) into registers; then the LDS
+  // tiles are staged in place.
+  auto img = [&](int j) { return j < 2 ? ldsL + j * kLdsTileBytes : ldsX; };
+  const int nbk = w2_blocks(rank);
+  constexpr int nthr = kPpWaves * 64;
+  constexpr int kQ = (32 * KS + nthr - 1) / nthr;
+  auto load_slot = [&](int sl, W2Block (&bk)[kQ]) {
+    const int tl = min(slot_tile(sl), nT - 1);
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+      w2_block_load(a.W2, V, tl * kTileV, min((int)threadIdx.x + nthr * q, nbk - 1), bk[q]);
+  };
+  auto store_slot = [&](int sl, const W2Block (&bk)[kQ], char* dst) {
+    if (slot_tile(sl) < nT) {
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int sb = (int)threadIdx.x + nthr * q;
+        if (sb < nbk) w2_block_store(bk[q], sb, dst, nq);
+      }
+    }
+  };
+  bf16x8_t wreg[KS][kSub];
+  {
+    W2Block blk[kPpRegTiles][kQ];
+#pragma unroll
+    for (int j = 0; j < kPpRegTiles; ++j) load_slot(j, blk[j]);
+    W2Block lblk[kPpLdsTiles][kQ];
+#pragma unroll
+    for (int r0 = 0; r0 < kPpRegTiles; r0 += 3) {
+#pragma unroll
+      for (int j = r0; j < r0 + 3 && j < kPpRegTiles; ++j) store_slot(j, blk[j], img(j - r0));
+      if (r0 + 3 >= kPpRegTiles) {
+#pragma unroll
+        for (int j = 0; j < kPpLdsTiles; ++j) load_slot(kPpRegTiles + j, lblk[j]);
+      }
+      __syncthreads();
+      if (wave >= r0 && wave < r0 + 3) wreg_from_lds<KS>(img(wave - r0), wreg);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < kPpLdsTiles; ++j) store_slot(kPpRegTiles + j, lblk[j], img(j));
+  }
+  const int nL = (tcount > kPpRegTiles ? 1 : 0) + (tcount > kPpRegTiles + 1 ? 1 : 0);
+  const bool hasreg = wave < tcount;
+  // half-tasks of a window: 2 per LDS tile; half i goes to wave i + 4
+  const int hidx = (wave + 4) & 7;
+  const bool hashalf = hidx < 2 * nL;
+  const int ntask = (hasreg ? 1 : 0) + (hashalf ? 1 : 0);   // per window, every window
+
+  // windows: position-major, 32 requests each
+  const int nch = (B + kTileM - 1) / kTileM;
+  const int nwin = gamma * nch;
+
+  // one-task ring of base logits (they do not depend on drafted tokens);
+  // past the last task the slot loads a safe address, so every task issues
+  // the same four loads
+  struct Slot {
+    URow<uint16_t> u;
+  };
+  Slot ring;
+  int fj = 0, ft = 0;   // next task to fetch (window, index in the window)
+  auto fetch_next = [&](Slot& sl) __attribute__((always_inline)) {
+    if (ft >= ntask) {
+      ++fj;
+      ft = 0;
+    }
+    const bool real = fj < nwin && ntask > 0;
+    const bool reg = hasreg && ft == 0;
+    const int k = real ? fj / nch : 0;
+    const int b = (real ? (fj % nch) * kTileM : 0) + c;
+    const int tile = reg ? tbase + wave : tbase + kPpRegTiles + (hidx >> 1);
+    const int sub = reg ? -1 : (hidx & 1);
+    const int v0 = tile * kTileV;
+    // whole 128-byte row pieces: load i covers rows 8i .. 8i + 7 of the
+    // block, lane L taking 16 bytes (chunk L % 8) of row 8i + L / 8; a half
+    // task's sub-tile (64 bytes per row) takes loads 0 and 1, 16 rows each,
+    // and loads 2 and 3 read a safe address (every task issues four loads)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = reg ? 8 * i + (lane >> 3) : 16 * i + (lane >> 2);
+      const int off = reg ? 8 * (lane & 7) : 32 * sub + 8 * (lane & 3);
+      const int bq = b - c + r;
+      const bool in = real && (reg || i < 2) && bq < B && v0 + off < V;
+      const uint16_t* pp = in ? a.U + ((size_t)bq * gamma + k) * V + v0 + off : a.U + 8 * i;
+      sl.u.w[i >> 1][i & 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pp));
+    }
+    ++ft;
+  };
+  // The ring slot's row pieces passed to the matrix layout through this
+  // wave's 4 KB of LDS (row r at 128 r, chunk q at 16 (q ^ (r % 8)), so that
+  // eight consecutive rows read at one chunk hit eight distinct bank groups):
+  // lane (c, h) gets the entries 32 t + 16 h .. + 15 of request c for t = 0, 1
+  // (a half task: its sub-tile's entries 16 h .. + 15 in part 0).
+  char* rs = ldsX + wave * 4096;
+  auto restage = [&](const URow<uint16_t>& in, bool reg, URow<uint16_t>& out) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (reg || i < 2) {
+        const int r = reg ? 8 * i + (lane >> 3) : 16 * i + (lane >> 2);
+        const int q = reg ? (lane & 7) : (lane & 3);
+        *reinterpret_cast<u32x4_t*>(rs + r * 128 + 16 * (q ^ (r & 7))) = in.w[i >> 1][i & 1];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kSub; ++t) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int q = (reg ? 4 * t : 0) + 2 * h + e;
+        if (reg || t == 0)
+          out.w[t][e] = *reinterpret_cast<const u32x4_t*>(rs + c * 128 + 16 * (q ^ (c & 7)));
+      }
+    }
+  };
+
+  // Gather of window jn's rows into `dst` by waves 0..3, eight rows each
+  // (previous tokens `tok` in lanes 0..7; lanes past the window's requests
+  // hold token 0 and inverse temperature 0).  Waves 4..7, which run the LDS
+  // tiles' half tasks, issue no row DMA: a wave with a DMA in flight waits
+  // for it before its next LDS read.  Completion: the caller's wait.
+  constexpr int kGw = 4, kRpw = kTileM / kGw;   // gathering waves, rows each
+  auto gather = [&](int jn, char* dst, int tok) __attribute__((always_inline)) {
+    const int nrows = min(kTileM, B - (jn % nch) * kTileM);
+    const int row = wave * kRpw + lane;
+    if (lane < kRpw) {
+      const int bq = (jn % nch) * kTileM + row;
+      s_it[jn % 3][row] = row < nrows ? inv_temp(a.temperature[bq]) : 0.f;
+    }
+    char* wd = dst + (size_t)(wave * kRpw) * nc * 16;
+    constexpr int nslots = kRpw * nc;
+#pragma unroll
+    for (int g = 0; g * 64 < nslots; ++g) {
+      const int s = g * 64 + lane;
+      const int rl = s / nc, q = s - rl * nc;
+      const int tk = __shfl(tok, min(rl, kRpw - 1), kWave);
+      if (s < nslots)
+        __builtin_amdgcn_global_load_lds(a.W1 + (size_t)tk * rank + (q < nq ? q : 0) * 8,
+                                         wd + g * 1024, 16, 0, 0);
+    }
+  };
+  // Previous tokens of this wave's rows of window jn (lanes 0..7): issue
+  // one flag load per lane, then (later, so the load is in flight meanwhile)
+  // check that every one is in and take the tokens.  Position 0 takes the
+  // anchors.
+  auto poll_issue = [&](int jn) __attribute__((always_inline)) {
+    const int row = wave * kRpw + lane;
+    const int bq = (jn % nch) * kTileM + row;
+    const bool real = lane < kRpw && bq < B;
+    if (jn / nch == 0) return real ? (uint32_t)a.anchor[bq] : 0u;
+    return real ? ld_dev(a.tok_flag + bq) : 0xFFFFFFFFu;
+  };
+  auto poll_check = [&](int jn, uint32_t v, int& tok) __attribute__((always_inline)) {
+    const int kn = jn / nch;
+    const int row = wave * kRpw + lane;
+    const bool real = lane < kRpw && (jn % nch) * kTileM + row < B;
+    if (kn == 0) {
+      tok = real ? clamp_token((int)v, V, a.status) : 0;
+      return true;
+    }
+    tok = real ? clamp_token((int)(v & 0xFFFFFFu), V, nullptr) : 0;
+    return __all(v >= ((uint32_t)kn << 24)) != 0;
+  };
+  auto wait_tokens = [&](int jn, int& tok) __attribute__((always_inline)) {
+    pp_wait([&]() { return poll_check(jn, poll_issue(jn), tok); }, a.spin_cap, a.status);
+  };
+  const bool gathers = wave < kGw;
+
+  // Window j's group words, written by the last wave to finish its tasks
+  // (lanes 0..31 = the window's requests): the LDS tiles' tile words (their
+  // two halves combined here) and per request the group's max and exp-sum
+  // relative to it (the argmax for a greedy request), tagged with the
+  // position's parity (bit 63).  The register tiles' words went out from
+  // their tasks.
+  auto finish_window = [&](int j) __attribute__((always_inline)) {
+    const int pb = j & 1;
+    const int r0 = (j % nch) * kTileM;
+    const uint64_t tag = (uint64_t)(((j / nch) + 1) & 1) << 63;   // parity of the position
+    const bool act = lane < kTileM && r0 + lane < B;
+    const int bq = r0 + lane;
+    const float it = act ? s_it[j % 3][lane] : 0.f;
+    const bool greedy = !(it > 0.f);
+    const float ce = it * kLog2e;
+    // every slot's statistics read at once (unconditionally: slots past the
+    // group's tiles are masked afterwards), so the reads share one wait
+    float lmx[kPpSlots], lsm[kPpSlots];
+    int lag[kPpSlots];
+#pragma unroll
+    for (int s = 0; s < kPpSlots; ++s) {
+      lmx[s] = s_mx[pb][s][lane & 31];
+      lsm[s] = s_sum[pb][s][lane & 31];
+      lag[s] = s_arg[pb][s][lane & 31];
+    }
+    float tmx[kPpMaxTiles], tsm[kPpMaxTiles];
+    int targ[kPpMaxTiles];
+    float gmx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kPpMaxTiles; ++s) {
+      const bool in = act && s < tcount;
+      if (s < kPpRegTiles) {
+        tmx[s] = lmx[s];
+        tsm[s] = lsm[s];
+        targ[s] = lag[s];
+      } else {
+        const int s0 = kPpRegTiles + 2 * (s - kPpRegTiles);
+        const float m0 = lmx[s0], m1 = lmx[s0 + 1];
+        const float m = fmaxf(m0, m1);
+        tmx[s] = m;
+        targ[s] = (m0 == m) ? lag[s0] : lag[s0 + 1];
+        tsm[s] = greedy ? 0.f
+                        : lsm[s0] * __builtin_amdgcn_exp2f((m0 - m) * ce) +
+                              lsm[s0 + 1] * __builtin_amdgcn_exp2f((m1 - m) * ce);
+        if (in && !greedy)
+          st_dev(a.tw + (size_t)bq * nT + tbase + s,
+                 (uint64_t)((pack_ms(m, tsm[s]) & ~(1ull << 63)) | tag));
+      }
+      if (!in) tmx[s] = -INFINITY;
+      gmx = fmaxf(gmx, tmx[s]);
+    }
+    uint32_t pl = 0;
+    if (greedy) {
+      int ga = 0x7fffffff;
+#pragma unroll
+      for (int s = kPpMaxTiles - 1; s >= 0; --s)
+        if (s < tcount && tmx[s] == gmx) ga = targ[s];
+      pl = (uint32_t)ga;
+    } else {
+      float gs = 0.f;
+#pragma unroll
+      for (int s = 0; s < kPpMaxTiles; ++s)
+        if (s < tcount) gs += tsm[s] * __builtin_amdgcn_exp2f((tmx[s] - gmx) * ce);
+      pl = __float_as_uint(gs);
+    }
+    if (act)
+      st_dev(a.gw + (size_t)bq * Pt + p,
+             (uint64_t)(((uint64_t)__float_as_uint(gmx) | ((uint64_t)(pl & 0x7FFFFFFFu) << 32)) | tag));
+  };
+  // waves with tasks in every window; the one whose count completes a
+  // window writes its group words
+  const int nwt = tcount < kPpWaves ? tcount : kPpWaves;
+  // (relaxed LDS atomic: the work-group's LDS serves each wave's accesses in
+  // order, so the statistics a wave stored before its count are in place
+  // for the wave that reads the full count; acquire/release would also
+  // wait for this wave's base-logit loads in flight)
+  auto task_done = [&](int j) __attribute__((always_inline)) {
+    int prev = 0;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(&s_done[j & 1], 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+    prev = __shfl(prev, 0, kWave);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (prev == nwt - 1) {
+      if (lane == 0)
+        __hip_atomic_store(&s_done[j & 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      finish_window(j);
+    }
+  };
+
+  // run the wave's task `ft_run` of window j (parity buffers PB), taking the
+  // base logits from the ring slot and refilling it with the next task
+  auto run_task = [&](auto pbc, int j, bool reg) __attribute__((always_inline)) {
+    constexpr int pb = decltype(pbc)::value;
+    const char* rows = pb ? ldsR1 : ldsR0;
+    const int b = (j % nch) * kTileM + c;
+    const float it = s_it[j % 3][c];
+    const bool any_greedy = __ballot((b < B) && !(it > 0.f)) != 0;
+    auto bfrag = [&](int ks) { return lds_frag(rows, c, 2 * ks + h, nq); };
+    if (reg) {
+      const int tile = tbase + wave;
+      const int v0 = tile * kTileV;
+      URow<uint16_t> u;
+      restage(ring.u, true, u);
+      fetch_next(ring);
+      f32x16_t acc[kSub];
+      if (v0 + kTileV <= V) {
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) {
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) acc[t][jj] = urow_at(u, t, jj);
+        }
+      } else {
+        init_acc<uint16_t>(u, V - (v0 + 16 * h), acc);
+      }
+      bias_tile_regA<KS>(bfrag, wreg, acc);
+      const TileStat st = tile_reduce(acc, tile, it, any_greedy);
+      if (h == 0) {
+        s_mx[pb][wave][c] = st.mx;
+        s_sum[pb][wave][c] = st.s;
+        s_arg[pb][wave][c] = st.arg;
+        if (b < B && it > 0.f)
+          st_dev(a.tw + (size_t)b * nT + tile,
+                 (uint64_t)((pack_ms(st.mx, st.s) & ~(1ull << 63)) |
+                            ((uint64_t)(((j / nch) + 1) & 1) << 63)));
+      }
+    } else {
+      const int li = hidx >> 1, t = hidx & 1;
+      const int tile = tbase + kPpRegTiles + li;
+      const int v0 = tile * kTileV;
+      const int rem = V - (v0 + 32 * t + 16 * h);
+      URow<uint16_t> u;
+      restage(ring.u, false, u);
+      fetch_next(ring);
+      f32x16_t acc;   // the sub-tile's entries sit in part 0
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) acc[jj] = (jj < rem) ? urow_at(u, 0, jj) : -INFINITY;
+      bias_subtile_ldsA<KS>(bfrag, ldsL + li * kLdsTileBytes, t, acc);
+      const TileStat st = half_reduce(acc, tile, t, it, any_greedy);
+      if (h == 0) {
+        const int slot = kPpRegTiles + 2 * li + t;
+        s_mx[pb][slot][c] = st.mx;
+        s_sum[pb][slot][c] = st.s;
+        s_arg[pb][slot][c] = st.arg;
+      }
+    }
+  };
+
+  constexpr int kWaitAll = 0;   // s_waitcnt immediate: every counter at zero
+
+  // One window of parity PB.  With two or more windows per position the
+  // next window's previous tokens were drawn from statistics published one
+  // or more windows ago: they are polled at the top, the rows gathered into
+  // the other buffer as soon as they are in (mid-window), and only a late
+  // draw makes the window end wait.  With one window per position the next
+  // window needs this window's own draws: wait, gather, then go on.
+  // `gc`: whether this wave gathers rows (waves 0..3).  The two kinds of
+  // wave run separate copies of the loop, so that no row DMA appears in the
+  // code the other waves run (the compiler makes every LDS access after a
+  // possible DMA wait for all loads in flight, the base-logit ring included).
+  auto window = [&](auto pbc, auto gc, int j) __attribute__((always_inline)) {
+    constexpr int pb = decltype(pbc)::value;
+    constexpr bool gat = decltype(gc)::value;
+    char* nxt = pb ? ldsR0 : ldsR1;
+    const bool more = j + 1 < nwin;
+    if constexpr (gat) {
+      int tok = 0;
+      bool staged = !more || nch == 1;
+      // the flag loads stay in flight during the register task
+      const uint32_t pv = staged ? 0u : poll_issue(j + 1);
+      if (hasreg) run_task(pbc, j, true);
+      if (ntask > 0) task_done(j);   // before the DMA: LDS accesses after it wait for it
+      if (!staged) {
+        if (!poll_check(j + 1, pv, tok)) wait_tokens(j + 1, tok);
+        gather(j + 1, nxt, tok);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitAll);   // this wave's rows are in
+      __syncthreads();
+      if (nch == 1 && more) {
+        wait_tokens(j + 1, tok);
+        gather(j + 1, nxt, tok);
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+        __syncthreads();
+      }
+    } else {
+      if (hasreg) run_task(pbc, j, true);
+      if (hashalf) run_task(pbc, j, false);
+      if (ntask > 0) task_done(j);
+      __syncthreads();
+      if (nch == 1 && more) __syncthreads();
+    }
+  };
+
+  // window 0: the anchors' rows
+  if (threadIdx.x < 2) s_done[threadIdx.x] = 0;
+  fetch_next(ring);
+  auto run = [&](auto gc) __attribute__((always_inline)) {
+    constexpr bool gat = decltype(gc)::value;
+    if constexpr (gat) {
+      int tok = 0;
+      poll_check(0, poll_issue(0), tok);
+      gather(0, ldsR0, tok);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __syncthreads();
+    for (int j = 0; j < nwin; j += 2) {
+      window(std::integral_constant<int, 0>{}, gc, j);
+      if (j + 1 < nwin) window(std::integral_constant<int, 1>{}, gc, j + 1);
+    }
+  };
+  if (gathers) run(std::true_type{});
+  else run(std::false_type{});
+}
+
+// zero the group words [0, n0) and the token flags [0, n1)
+__global__ void pdraft_pipe_reset_kernel(uint64_t* g, int n0, uint32_t* f, int n1) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n0) g[i] = 0ull;
+  if (i < n1) f[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+size_t draft_pipe_workspace_bytes(int B, int V) {
+  return align256((size_t)B * n_tiles(V) * 8) + align256((size_t)B * kPpMaxTileGroups * 8) +
+         align256((size_t)B * 4);
+}
+
+// Pt / Pd for this shape on a device with P compute units; false when the
+// pipelined kernel cannot run (too few groups to keep every W2 tile on chip).
+bool draft_pipe_plan(int B, int V, int P, int& Pt, int& Pd) {
+  const int nT = n_tiles(V);
+  Pd = min(kPpMaxDrawGroups, (B + kPpWaves - 1) / kPpWaves);
+  Pt = min(min(P - Pd, nT), kPpMaxTileGroups);
+  return Pd >= 1 && Pt >= 1 && (long long)Pt * kPpMaxTiles >= nT;
+}
+
+template <int KS>
+static hipError_t launch_pipe(const PpArgs& a0, hipStream_t stream) {
+  PpArgs a = a0;
+  const void* kern = reinterpret_cast<const void*>(pdraft_pipe_kernel<KS>);
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kPpWaves * 64, 0) != hipSuccess ||
+      occ < 1)
+    return hipErrorNotSupported;
+  {
+    TraceScope t("pdraft_pipe_reset_kernel", stream);
+    const int n0 = a.B * a.Pt;
+    const int n = n0 > a.B ? n0 : a.B;
+    pdraft_pipe_reset_kernel<<<dim3((n + 255) / 256), dim3(256), 0, stream>>>(a.gw, n0,
+                                                                              a.tok_flag, a.B);
+  }
+  TraceScope t("pdraft_pipe_kernel", stream);
+  void* args[] = {&a};
+  return hipLaunchCooperativeKernel(kern, dim3(a.Pt + a.Pd), dim3(kPpWaves * 64), args, 0,
+                                    stream);
+}
+
+hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_cap,
+                      const uint16_t* U, const uint16_t* W1, const uint16_t* W2,
+                      const int32_t* anchor, const float* temperature, const float* uniforms,
+                      int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
+                      int32_t* status, void* ws, hipStream_t stream) {
+  PpArgs a;
+  if (!draft_pipe_plan(B, V, P, a.Pt, a.Pd)) return hipErrorNotSupported;
+  a.B = B; a.gamma = gamma; a.V = V; a.rank = rank;
+  a.U = U; a.W1 = W1; a.W2 = W2; a.anchor = anchor; a.temperature = temperature;
+  a.uniforms = uniforms; a.tokens = tokens; a.q_tok = q_tok; a.row_max = row_max;
+  a.row_logZ = row_logZ; a.status = status;
+  char* w = static_cast<char*>(ws);
+  a.tw = reinterpret_cast<uint64_t*>(w);
+  w += align256((size_t)B * n_tiles(V) * 8);
+  a.gw = reinterpret_cast<uint64_t*>(w);
+  w += align256((size_t)B * kPpMaxTileGroups * 8);
+  a.tok_flag = reinterpret_cast<uint32_t*>(w);
+  a.spin_cap = spin_cap;
+  switch (rank) {
+    case 32: return launch_pipe<2>(a, stream);
+    case 64: return launch_pipe<4>(a, stream);
+    case 128: return launch_pipe<8>(a, stream);
+    default: return launch_pipe<16>(a, stream);
+  }
+}
+
+}  // namespace dspark

@@ -14,9 +14,19 @@ constexpr int kMaxVocab = 262144;   // largest vocabulary the kernels take
 size_t draft_workspace_bytes(int B, int gamma, int V, int rank, int dtype);
 // 0 = automatic (persistent kernel when possible), 1 = multi-launch only,
 // 2 = persistent only (fails with hipErrorNotSupported where it cannot run),
-// 3 / 4 = persistent only with 8 / 4 waves per work-group
+// 3 / 4 = persistent only with 8 / 4 waves per work-group, 5 = the pipelined
+// kernel only
 int set_draft_path(int path);   // returns the previous setting
 int get_draft_path();
+// The pipelined single-launch draft kernel (draft_pipe.hip): workspace
+// bytes, and the launch on a device with P compute units;
+// hipErrorNotSupported where it cannot run.
+size_t draft_pipe_workspace_bytes(int B, int V);
+hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_cap,
+                      const uint16_t* U, const uint16_t* W1, const uint16_t* W2,
+                      const int32_t* anchor, const float* temperature, const float* uniforms,
+                      int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
+                      int32_t* status, void* ws, hipStream_t stream);
 // compute units of the current device (cached per device)
 int device_cu_count();
 hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U,

@@ -375,15 +375,22 @@ int dspark_trace_summary(char* buf, size_t len);
  * Drafting implementation choice (process-wide; for tests and benchmarks).
  * The setting is one atomic word read by every later dspark_draft_block
  * call, from any host thread: the one exception to "keep no state".
- * 0 = automatic (default): the persistent single-launch kernel for bf16
- *     inputs when the device supports cooperative launch and the vocabulary
- *     fits its resident tiles, else one launch pair per position;
+ * 0 = automatic (default): for bf16 inputs on a device with cooperative
+ *     launch, the pipelined single-launch kernel (request windows of 32
+ *     drafted while the previous windows' tokens are drawn by dedicated
+ *     work-groups), else the earlier single-launch kernel, else one launch
+ *     pair per position;
  * 1 = always one launch pair per position;
- * 2 = persistent only: dspark_draft_block returns DSPARK_EHIP where it
- *     cannot run;
- * 3, 4 = persistent only, with 8 (one register-resident W2 tile each) or
- *     4 (two each) waves per work-group; 2 picks 8.
- * All settings return identical results.
+ * 2 = the earlier single-launch kernel only: dspark_draft_block returns
+ *     DSPARK_EHIP where it cannot run;
+ * 3, 4 = that kernel only, with 8 (one register-resident W2 tile each) or
+ *     4 (two each) waves per work-group; 2 picks 8;
+ * 5 = the pipelined kernel only (DSPARK_EHIP where it cannot run).
+ * Settings 1-4 return identical bits.  The pipelined kernel draws from the
+ * same statistics with the group and tile masses summed in another order
+ * (a token can differ only where the uniform lies within about 1e-6 of a
+ * boundary of the inverse CDF; q and the row statistics differ in the last
+ * bits).
  * Returns the previous setting, or DSPARK_EINVAL for another value.
  * ---------------------------------------------------------------------- */
 int dspark_set_draft_path(int path);
