@@ -34,6 +34,7 @@
 // that gives up raises DSPARK_DEV_TIMEOUT, after which every other wait gives
 // up at once so the grid always drains (results are then undefined but every
 // output stays in range).
+#include <algorithm>
 #include <type_traits>
 
 #include "dspark_common.hpp"
@@ -803,9 +804,16 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
   else run(std::false_type{});
 }
 
-// zero the group words [0, n0) and the token flags [0, n1)
-__global__ void pdraft_pipe_reset_kernel(uint64_t* g, int n0, uint32_t* f, int n1) {
+// Zero the tile words [0, nt), the group words [0, n0) and the token flags
+// [0, n1) before a call.  A tile or group word is taken as written at
+// position k when its tag bit is (k + 1) % 2: within a call the word a wait
+// can meet in place of the fresh one is the previous position's (the other
+// parity), and the zeroed words keep the last position of the previous call
+// from passing for position 0 of this one.
+__global__ void pdraft_pipe_reset_kernel(uint64_t* t, int nt, uint64_t* g, int n0, uint32_t* f,
+                                         int n1) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nt) t[i] = 0ull;
   if (i < n0) g[i] = 0ull;
   if (i < n1) f[i] = 0u;
 }
@@ -838,10 +846,10 @@ static hipError_t launch_pipe(const PpArgs& a0, hipStream_t stream) {
     return hipErrorNotSupported;
   {
     TraceScope t("pdraft_pipe_reset_kernel", stream);
-    const int n0 = a.B * a.Pt;
-    const int n = n0 > a.B ? n0 : a.B;
-    pdraft_pipe_reset_kernel<<<dim3((n + 255) / 256), dim3(256), 0, stream>>>(a.gw, n0,
-                                                                              a.tok_flag, a.B);
+    const int nt = a.B * n_tiles(a.V), n0 = a.B * a.Pt;
+    const int n = std::max(nt, std::max(n0, a.B));
+    pdraft_pipe_reset_kernel<<<dim3((n + 255) / 256), dim3(256), 0, stream>>>(
+        a.tw, nt, a.gw, n0, a.tok_flag, a.B);
   }
   TraceScope t("pdraft_pipe_kernel", stream);
   void* args[] = {&a};
