@@ -204,14 +204,17 @@ def dspark_schedule_workspace(R, gamma) -> int:
     return int(load().dspark_schedule_workspace(R, gamma))
 
 
-def _workspace(nbytes: int, device, given=None):
+def _workspace(nbytes: int, device, given=None, zeroed=False):
+    """The caller's workspace, checked, or a new one (zero-filled when the call
+    needs to find it so: the draft workspace)."""
     if given is not None:
         _need(given, "workspace", torch.uint8, None, device)
         if given.dim() != 1 or given.numel() < nbytes:
             raise DsparkError(-4, f"workspace must be a 1-D uint8 tensor of at least {nbytes} "
                                   f"bytes, got shape {tuple(given.shape)}")
         return given
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    alloc = torch.zeros if zeroed else torch.empty
+    return alloc(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def dspark_draft_block(U, W1, W2, anchor, temperature, uniforms, *, tokens=None, q_tok=None,
@@ -233,7 +236,7 @@ def dspark_draft_block(U, W1, W2, anchor, temperature, uniforms, *, tokens=None,
     row_logZ = _out(row_logZ, "row_logZ", torch.float32, (B, gamma), dev)
     status = _status(status, dev)
     need = dspark_draft_block_workspace(B, gamma, V, rank, dt)
-    ws = _workspace(need, dev, workspace)
+    ws = _workspace(need, dev, workspace, zeroed=True)
     _check(lib.dspark_draft_block(B, gamma, V, rank, dt, _ptr(U), _ptr(W1), _ptr(W2), _ptr(anchor),
                                   _ptr(temperature), _ptr(uniforms), _ptr(tokens), _ptr(q_tok),
                                   _ptr(row_max), _ptr(row_logZ), _ptr(status), _ptr(ws),

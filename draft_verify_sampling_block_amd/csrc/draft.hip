@@ -802,8 +802,8 @@ __global__ void pdraft_reset_kernel(uint32_t* f0, int n0, uint32_t* f1, int n1) 
 
 namespace {
 // 0 auto, 1 multi-launch, 2-4 the earlier persistent kernel only (3: 8
-// waves, 4: 4 waves), 5-7 the pipelined kernel only (6: one 32-request block
-// per window, 7: two); process-wide, read by every call
+// waves, 4: 4 waves), 5 the pipelined kernel only; process-wide, read by
+// every call
 std::atomic<int> g_draft_path{0};
 
 struct DevInfo {
@@ -837,16 +837,24 @@ int get_draft_path() { return g_draft_path.load(); }
 
 static size_t stats_bytes(int B, int V) { return align256((size_t)B * n_tiles(V) * 4); }
 
+// The workspace: a header holding the pipelined kernel's start barrier (at
+// the same place for every shape, zero-filled before the first call; nothing
+// else writes there), the statistics and flags of the multi-launch and
+// earlier persistent kernels (cleared by those paths), then the pipelined
+// kernel's exchange words (zeroed by that kernel before use).
+constexpr size_t kWsHeader = kDraftPipeHeaderBytes;
+static size_t persistent_ws_bytes(int B, int V) {
+  const size_t flags = align256((size_t)kPdMaxGroups * kPdFlagStride * 4) + align256((size_t)B * 4);
+  return 3 * stats_bytes(B, V) + flags;
+}
+
 size_t draft_workspace_bytes(int B, int gamma, int V, int rank, int dtype) {
   (void)gamma; (void)rank; (void)dtype;
-  const size_t flags = align256((size_t)kPdMaxGroups * kPdFlagStride * 4) + align256((size_t)B * 4);
-  const size_t persistent = 3 * stats_bytes(B, V) + flags;
-  const size_t pipe = draft_pipe_workspace_bytes(B, V);
-  return persistent > pipe ? persistent : pipe;
+  return kWsHeader + persistent_ws_bytes(B, V) + draft_pipe_workspace_bytes(B, V);
 }
 
 static TileStats carve_stats(void* ws, int B, int V) {
-  char* w = static_cast<char*>(ws);
+  char* w = static_cast<char*>(ws) + kWsHeader;
   TileStats ts;
   ts.ms = reinterpret_cast<uint64_t*>(w);                          // 2 x stats_bytes
   ts.arg = reinterpret_cast<int32_t*>(w + 2 * stats_bytes(B, V));
@@ -907,7 +915,7 @@ static hipError_t draft_persistent(int B, int gamma, int V, int rank, const uint
   a.uniforms = uniforms; a.tokens = tokens; a.q_tok = q_tok; a.row_max = row_max;
   a.row_logZ = row_logZ; a.status = status;
   a.ts = carve_stats(ws, B, V);
-  char* fl = static_cast<char*>(ws) + 3 * stats_bytes(B, V);
+  char* fl = static_cast<char*>(ws) + kWsHeader + 3 * stats_bytes(B, V);
   a.stats_flag = reinterpret_cast<uint32_t*>(fl);
   a.tok_flag = reinterpret_cast<uint32_t*>(fl + align256((size_t)kPdMaxGroups * kPdFlagStride * 4));
   a.spin_cap = 200LL * di.wall_khz;  // 0.2 s: reached only if a group never arrives
@@ -940,7 +948,9 @@ hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, cons
     if (di.coop && di.cus > 0)
       e = draft_pipe(B, gamma, V, rank, di.cus, 200LL * di.wall_khz, static_cast<const uint16_t*>(U),
                      static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2), anchor,
-                     temperature, uniforms, tokens, q_tok, row_max, row_logZ, status, ws, stream);
+                     temperature, uniforms, tokens, q_tok, row_max, row_logZ, status,
+                     static_cast<uint32_t*>(ws),
+                     static_cast<char*>(ws) + kWsHeader + persistent_ws_bytes(B, V), stream);
     if (e != hipErrorNotSupported || path == 5) return e;
   }
   if (dtype == DSPARK_BF16) {

@@ -9,13 +9,14 @@
 //  * tile groups (work-groups 0 .. Pt-1): each owns a contiguous run of
 //    64-entry vocabulary tiles whose W2 rows stay on chip for the whole block
 //    (8 tiles in registers, one per wave, up to 2 more in LDS).  The requests
-//    are cut into windows of up to 64 (two 32-request blocks); the windows of
-//    all positions are processed in order (position-major).  Per window every
-//    wave runs its block-tasks (tile x 32 requests: bias on the matrix cores
-//    with the accumulators started at the base logits, then the tile
-//    reduction), and the statistics go out as one 8-byte word per (request,
-//    tile) plus one per (request, group): the group's max and its exp-sum
-//    relative to that max, tagged with the parity of the position.
+//    are cut into windows of 32; the windows of all positions are processed
+//    in order (position-major).  Per window every wave runs its block-task
+//    (tile x 32 requests: bias on the matrix cores with the accumulators
+//    started at the base logits, then the tile reduction; an LDS tile is
+//    split into two half tasks), and the statistics go out as one 8-byte word
+//    per (request, tile) plus one per (request, group): the group's max and
+//    its exp-sum relative to that max, tagged with the parity of the
+//    position.
 //
 //  * draw groups (work-groups Pt .. Pt+Pd-1): one wave per request draws its
 //    token as soon as every tile group's word of that request is in: an fp64
@@ -30,10 +31,23 @@
 // draws and the exchanges stay off the critical path; the tile groups wait
 // only when a window's previous tokens are not in yet.
 //
+// The exchange words live in the caller's workspace and need no clearing
+// launch: every work-group zeroes the words it writes (a tile group its tile
+// words and its column of group words, a draw wave its requests' token
+// flags), then arrives at a start barrier, and no exchange word is read
+// before every work-group has arrived.  A zero word carries tag 0, which
+// position 0 (tag 1) never takes as written.  The barrier lives in a header
+// at a fixed place in the workspace: a call number E (read by everyone at
+// the start, advanced by the first draw group once everyone has arrived)
+// and one arrival word per work-group, set to E + 1, so no two work-groups
+// write the same word and no arrival of an earlier call passes for one of
+// this call.
+// The workspace only has to be zero-filled once, before its first use.
+//
 // Waits between work-groups are bounded by the device wall clock; a wait
 // that gives up raises DSPARK_DEV_TIMEOUT, after which every other wait gives
 // up at once so the grid always drains (results are then undefined but every
-// output stays in range).
+// output stays in range, and the workspace must be zero-filled again).
 #include <algorithm>
 #include <type_traits>
 
@@ -69,9 +83,11 @@ struct PpArgs {
   float* row_max;
   float* row_logZ;
   int32_t* status;
-  uint64_t* tw;         // [B][nT] tile words (max, exp-sum | parity << 63)
+  uint64_t* tw;         // [nT][B] tile words (max, exp-sum | parity << 63); a window's
+                        // 32 requests write 256 contiguous bytes per tile
   uint64_t* gw;         // [B][Pt] group words (max, exp-sum or argmax | parity << 63)
   uint32_t* tok_flag;   // [B] ((k + 1) << 24) | token k
+  uint32_t* hdr;        // start barrier: [0] call number, [64 + g] arrival of group g
   long long spin_cap;   // wall-clock ticks a wait may last
 };
 
@@ -111,6 +127,51 @@ __device__ inline bool pp_wait(Done&& done, long long cap, int32_t* status) {
     }
     __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// Start barrier (see the top of the file).  pp_call: the call number, read
+// by wave 0 before anything else; pp_arrive: once this work-group's zeroing
+// stores are complete, thread 0 marks it arrived; pp_wait_all: the first
+// draw group (idle until the first statistics arrive) waits until every
+// arrival word reads E + 1 and then advances the call number (every
+// work-group read it before arriving), which is what the other work-groups
+// wait for.  Each work-group reads the header from one wave, and only that
+// draw group reads the arrival words, so the few header lines are not
+// swamped by reads from every wave of the grid.
+constexpr int kPpHdrArrive = 64;   // header word of work-group 0's arrival
+static_assert((kPpHdrArrive + kPpMaxTileGroups + kPpMaxDrawGroups) * 4 <= kDraftPipeHeaderBytes,
+              "the header holds every work-group's arrival word");
+__device__ inline bool pp_wave0() {   // a wave-uniform (scalar) test
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+}
+__device__ inline uint32_t pp_call(const PpArgs& a) {
+  return pp_wave0() ? __builtin_amdgcn_readfirstlane(ld_dev(a.hdr)) : 0u;
+}
+// (The zeroing stores are device-scope stores like every other exchange
+// word's; each wave waits until its own have completed, so the arrival is
+// marked after all of the work-group's.)
+__device__ inline void pp_arrive(const PpArgs& a, uint32_t E) {
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's zeroing stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) st_dev(a.hdr + kPpHdrArrive + blockIdx.x, E + 1u);
+}
+__device__ inline void pp_wait_all(const PpArgs& a, uint32_t E) {
+  const int G = a.Pt + a.Pd, lane = threadIdx.x & 63;
+  if (pp_wave0()) {
+    if ((int)blockIdx.x == a.Pt) {
+      const bool ok = pp_wait(
+          [&]() {
+            bool in = true;
+            for (int g = lane; g < G; g += kWave) in &= ld_dev(a.hdr + kPpHdrArrive + g) == E + 1u;
+            return in;
+          },
+          a.spin_cap, a.status);
+      if (ok && lane == 0) st_dev(a.hdr, E + 1u);
+    } else {
+      pp_wait([&]() { return ld_dev(a.hdr) == E + 1u; }, a.spin_cap, a.status);
+    }
+  }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -288,7 +349,7 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
   pp_wait(
       [&]() {
         if (lane >= tc) return true;
-        w = ld_dev(a.tw + (size_t)b * nT + tb + lane);
+        w = ld_dev(a.tw + (size_t)(tb + lane) * B + b);
         return (w >> 63) == want;
       },
       a.spin_cap, a.status);
@@ -409,6 +470,12 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
     // draws (and their W2 reads) spread over all of them
     const int g = (int)blockIdx.x - a.Pt;
     char* wl = ldsX + wave * kPpDrawLds;
+    const uint32_t E = pp_call(a);
+    // this wave's requests' token flags start at zero
+    for (int b = g + a.Pd * wave; b < a.B; b += a.Pd * kPpWaves)
+      if (lane == 0) st_dev(a.tok_flag + b, 0u);
+    pp_arrive(a, E);
+    pp_wait_all(a, E);
     for (int k = 0; k < a.gamma; ++k)
       for (int b = g + a.Pd * wave; b < a.B; b += a.Pd * kPpWaves) pp_draw<KS>(a, b, k, wl);
     return;
@@ -420,6 +487,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
   const int nT = n_tiles(V);
   const int tcount = pp_tcount(p, nT, Pt), tbase = pp_tbase(p, nT, Pt);
   auto slot_tile = [&](int slot) { return slot < tcount ? tbase + slot : nT; };
+
 
   // Resident W2 tiles (W2 is [rank, V]): the blocks of the eight register
   // tiles are loaded in one shot and pass three at a time through three LDS
@@ -444,6 +512,16 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
       }
     }
   };
+  // This group zeroes its tile words and its column of group words and
+  // arrives at the start barrier before anything else (the stores' wait then
+  // holds no W2 loads); it waits for the others once its W2 tiles are staged
+  // (outside the window loop's function, whose registers it would crowd).
+  const uint32_t E = pp_call(a);
+  for (int i = (int)threadIdx.x; i < B * tcount; i += kPpWaves * 64)
+    st_dev(a.tw + (size_t)tbase * B + i, (uint64_t)0);   // rows tbase .. + tcount - 1
+  for (int bq = (int)threadIdx.x; bq < B; bq += kPpWaves * 64)
+    st_dev(a.gw + (size_t)bq * Pt + p, (uint64_t)0);
+  pp_arrive(a, E);
   bf16x8_t wreg[KS][kSub];
   {
     W2Block blk[kPpRegTiles][kQ];
@@ -465,6 +543,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
 #pragma unroll
     for (int j = 0; j < kPpLdsTiles; ++j) store_slot(kPpRegTiles + j, lblk[j], img(j));
   }
+  pp_wait_all(a, E);   // every work-group has zeroed its words
   const int nL = (tcount > kPpRegTiles ? 1 : 0) + (tcount > kPpRegTiles + 1 ? 1 : 0);
   const bool hasreg = wave < tcount;
   // half-tasks of a window: 2 per LDS tile; half i goes to wave i + 4
@@ -634,7 +713,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
                         : lsm[s0] * __builtin_amdgcn_exp2f((m0 - m) * ce) +
                               lsm[s0 + 1] * __builtin_amdgcn_exp2f((m1 - m) * ce);
         if (in && !greedy)
-          st_dev(a.tw + (size_t)bq * nT + tbase + s,
+          st_dev(a.tw + (size_t)(tbase + s) * B + bq,
                  (uint64_t)((pack_ms(m, tsm[s]) & ~(1ull << 63)) | tag));
       }
       if (!in) tmx[s] = -INFINITY;
@@ -712,7 +791,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
         s_sum[pb][wave][c] = st.s;
         s_arg[pb][wave][c] = st.arg;
         if (b < B && it > 0.f)
-          st_dev(a.tw + (size_t)b * nT + tile,
+          st_dev(a.tw + (size_t)tile * B + b,
                  (uint64_t)((pack_ms(st.mx, st.s) & ~(1ull << 63)) |
                             ((uint64_t)(((j / nch) + 1) & 1) << 63)));
       }
@@ -804,20 +883,6 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
   else run(std::false_type{});
 }
 
-// Zero the tile words [0, nt), the group words [0, n0) and the token flags
-// [0, n1) before a call.  A tile or group word is taken as written at
-// position k when its tag bit is (k + 1) % 2: within a call the word a wait
-// can meet in place of the fresh one is the previous position's (the other
-// parity), and the zeroed words keep the last position of the previous call
-// from passing for position 0 of this one.
-__global__ void pdraft_pipe_reset_kernel(uint64_t* t, int nt, uint64_t* g, int n0, uint32_t* f,
-                                         int n1) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nt) t[i] = 0ull;
-  if (i < n0) g[i] = 0ull;
-  if (i < n1) f[i] = 0u;
-}
-
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -844,13 +909,6 @@ static hipError_t launch_pipe(const PpArgs& a0, hipStream_t stream) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kPpWaves * 64, 0) != hipSuccess ||
       occ < 1)
     return hipErrorNotSupported;
-  {
-    TraceScope t("pdraft_pipe_reset_kernel", stream);
-    const int nt = a.B * n_tiles(a.V), n0 = a.B * a.Pt;
-    const int n = std::max(nt, std::max(n0, a.B));
-    pdraft_pipe_reset_kernel<<<dim3((n + 255) / 256), dim3(256), 0, stream>>>(
-        a.tw, nt, a.gw, n0, a.tok_flag, a.B);
-  }
   TraceScope t("pdraft_pipe_kernel", stream);
   void* args[] = {&a};
   return hipLaunchCooperativeKernel(kern, dim3(a.Pt + a.Pd), dim3(kPpWaves * 64), args, 0,
@@ -861,7 +919,7 @@ hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_c
                       const uint16_t* U, const uint16_t* W1, const uint16_t* W2,
                       const int32_t* anchor, const float* temperature, const float* uniforms,
                       int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
-                      int32_t* status, void* ws, hipStream_t stream) {
+                      int32_t* status, uint32_t* hdr, void* ws, hipStream_t stream) {
   PpArgs a;
   if (!draft_pipe_plan(B, V, P, a.Pt, a.Pd)) return hipErrorNotSupported;
   a.B = B; a.gamma = gamma; a.V = V; a.rank = rank;
@@ -874,6 +932,7 @@ hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_c
   a.gw = reinterpret_cast<uint64_t*>(w);
   w += align256((size_t)B * kPpMaxTileGroups * 8);
   a.tok_flag = reinterpret_cast<uint32_t*>(w);
+  a.hdr = hdr;
   a.spin_cap = spin_cap;
   switch (rank) {
     case 32: return launch_pipe<2>(a, stream);

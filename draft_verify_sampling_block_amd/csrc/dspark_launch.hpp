@@ -20,13 +20,17 @@ int set_draft_path(int path);   // returns the previous setting
 int get_draft_path();
 // The pipelined single-launch draft kernel (draft_pipe.hip): workspace
 // bytes, and the launch on a device with P compute units;
-// hipErrorNotSupported where it cannot run.
+// hipErrorNotSupported where it cannot run.  `hdr`: its start-barrier
+// header (kDraftPipeHeaderBytes, at the same place for every call and
+// zero-filled before the first; nothing else writes it); `ws`: its exchange
+// words (any content).
+constexpr size_t kDraftPipeHeaderBytes = 1536;
 size_t draft_pipe_workspace_bytes(int B, int V);
 hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_cap,
                       const uint16_t* U, const uint16_t* W1, const uint16_t* W2,
                       const int32_t* anchor, const float* temperature, const float* uniforms,
                       int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
-                      int32_t* status, void* ws, hipStream_t stream);
+                      int32_t* status, uint32_t* hdr, void* ws, hipStream_t stream);
 // compute units of the current device (cached per device)
 int device_cu_count();
 hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U,

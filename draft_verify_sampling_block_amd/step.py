@@ -80,7 +80,8 @@ class Step:
         self.ratio = torch.empty((B, g), dtype=torch.float32, device=dev)
         from . import dspark_draft_block_workspace, dspark_verify_workspace, _dtype_code
         dt = _dtype_code(d.U)
-        self.ws_draft = torch.empty(max(256, dspark_draft_block_workspace(B, g, d.V, d.rank, dt)),
+        # the draft workspace starts zero-filled; every draft call leaves it so
+        self.ws_draft = torch.zeros(max(256, dspark_draft_block_workspace(B, g, d.V, d.rank, dt)),
                                     dtype=torch.uint8, device=dev)
         self.ws_verify = torch.empty(max(256, dspark_verify_workspace(B, g, d.V, d.rank, dt)),
                                      dtype=torch.uint8, device=dev)

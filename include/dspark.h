@@ -100,7 +100,12 @@ const char* dspark_version(void);
  * out: tokens [B,gamma] int32; q_tok [B,gamma] fp32 = q_k(x_k);
  *      row_max [B,gamma] = max_v z/T (max z when greedy);
  *      row_logZ [B,gamma] = log sum_v exp(z/T - row_max) (0 when greedy).
- * workspace: dspark_draft_block_workspace(...) bytes of device memory.
+ * workspace: dspark_draft_block_workspace(...) bytes of device memory,
+ *      zero-filled before its first use (e.g. one hipMemset after the
+ *      allocation).  Every call leaves it ready for the next one (whatever
+ *      its shape or dtype), so a workspace kept for later calls needs no
+ *      clearing, except after a call that raised DSPARK_DEV_TIMEOUT: zero it
+ *      again then.  Calls that share one workspace must not overlap.
  * No full probability row is ever written.
  * The single-launch (persistent) implementation synchronises its work-groups
  * with bounded waits and reports a wait that gave up (DSPARK_DEV_TIMEOUT)

@@ -36,11 +36,15 @@ def test_status_strings_and_version(lib):
 
 
 def test_workspace_queries(lib):
+    # a 1536-byte header (the pipelined kernel's start barrier), the
     # per-64-entry-tile max, argmax and exp-sum, then the persistent kernel's
-    # flag words (4096 groups x 128 bytes, one word per request), 256-byte aligned
+    # flag words (4096 groups x 128 bytes, one word per request), then the
+    # pipelined kernel's region (a word per request and tile, 256 group words
+    # per request, a token flag per request), each part 256-byte aligned
     a256 = lambda n: (n + 255) // 256 * 256
     nT = (151936 + 63) // 64
-    expect = 3 * a256(128 * nT * 4) + a256(4096 * 32 * 4) + a256(128 * 4)
+    expect = 1536 + 3 * a256(128 * nT * 4) + a256(4096 * 32 * 4) + a256(128 * 4)
+    expect += a256(128 * nT * 8) + a256(128 * 256 * 8) + a256(128 * 4)
     assert dv.dspark_draft_block_workspace(128, 15, 151936, 256, 1) == expect
     assert dv.dspark_draft_block_workspace(128, 15, 151937, 256, 1) == 0  # invalid V
     assert dv.dspark_verify_workspace(4, 5, 1024, 32, 0) > 0

@@ -273,6 +273,41 @@ def test_draft_paths_agree(name):
     print(f"pipelined: {rep}, tokens equal to the per-position launches: {same:.4f}", flush=True)
 
 
+def test_draft_workspace_reuse_across_shapes():
+    """One workspace serves calls of changing batch, block length, vocabulary,
+    rank and dtype, through the pipelined kernel and the per-position
+    launches, with no clearing between them: each call gives the bits a
+    fresh zero-filled workspace gives."""
+    import draft_verify_sampling_block_amd as dv
+    from draft_verify_sampling_block_amd.step import upload
+    # (B, gamma, V, rank, dtype, draft path)
+    cases = [(96, 5, 20000, 64, "bf16", 5), (40, 4, 20000, 64, "bf16", 5),
+             (128, 3, 30000, 256, "bf16", 5), (17, 6, 9000, 128, "bf16", 1),
+             (33, 3, 12000, 64, "f32", 0), (17, 6, 9000, 128, "bf16", 5),
+             (96, 5, 20000, 64, "bf16", 5)]
+    need = max(dv.dspark_draft_block_workspace(B, g, V, r, 1) for B, g, V, r, _, _ in cases)
+    shared = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (B, g, V, r, dt, path) in enumerate(cases):
+        _say(f"workspace reuse: B={B} gamma={g} V={V} rank={r} {dt} path {path}")
+        wl = make_custom(B, g, V, r, 16, dt, "mixture", seed=21 + i % 6, temperature=0.8,
+                         greedy_frac=0.2)
+        d = upload(wl, "cuda", scheduler=False)
+        outs = []
+        old = dv.dspark_set_draft_path(path)
+        try:
+            for ws in (shared, None):
+                st = torch.zeros((1,), dtype=torch.int32, device="cuda")
+                o = dv.dspark_draft_block(d.U, d.W1, d.W2, d.anchor, d.temperature, d.uniforms,
+                                          status=st, workspace=ws)
+                torch.cuda.synchronize()
+                assert int(st.item()) == 0
+                outs.append({k: v.cpu().numpy() for k, v in o.items()})
+        finally:
+            dv.dspark_set_draft_path(old)
+        for k in outs[0]:
+            assert np.array_equal(outs[0][k], outs[1][k]), k
+
+
 def test_repeat_is_deterministic():
     _say("determinism")
     wl = SMALL["bf16-ragged-V1000-B40"]()
