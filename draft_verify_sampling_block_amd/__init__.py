@@ -25,7 +25,7 @@ __all__ = [
     "dspark_schedule", "dspark_schedule_noalloc", "dspark_schedule_capacity", "dspark_schedule_threshold", "dspark_verify",
     "dspark_tv_label", "dspark_tv_label_workspace", "dspark_draft_block_workspace",
     "dspark_draft_block_rnn", "dspark_draft_block_rnn_workspace", "dspark_verify_rnn",
-    "dspark_confidence_sts",
+    "dspark_confidence_sts", "dspark_draft_block_conf",
     "dspark_verify_workspace", "dspark_schedule_workspace", "exported_names", "header_names",
     "dspark_trace_enable", "dspark_trace_summary", "dspark_set_draft_path",
     "DSPARK_F32", "DSPARK_BF16", "DEV_FLAGS",
@@ -59,6 +59,8 @@ _SIGS = {
     "dspark_version": (ctypes.c_char_p, []),
     "dspark_draft_block_workspace": (_SZ, [_I, _I, _I, _I, _I]),
     "dspark_draft_block": (_I, [_I, _I, _I, _I, _I] + [_P] * 11 + [_P, _SZ, _P]),
+    "dspark_draft_block_conf": (_I, [_I] * 6 + [_P] * 8 + [ctypes.c_float] + [_P] * 6
+                                + [_P, _P, _SZ, _P]),
     "dspark_confidence": (_I, [_I] * 6 + [_P] * 5 + [ctypes.c_float, _P, _P, _P]),
     "dspark_confidence_sts": (_I, [_I] * 6 + [_P] * 5 + [ctypes.c_float, _P, _P, _P, _P]),
     "dspark_schedule_workspace": (_SZ, [_I, _I]),
@@ -242,6 +244,44 @@ def dspark_draft_block(U, W1, W2, anchor, temperature, uniforms, *, tokens=None,
                                   _ptr(row_max), _ptr(row_logZ), _ptr(status), _ptr(ws),
                                   ws.numel(), _stream()))
     return dict(tokens=tokens, q_tok=q_tok, row_max=row_max, row_logZ=row_logZ)
+
+
+def dspark_draft_block_conf(U, W1, W2, anchor, temperature, uniforms, hidden, w, bias=0.0,
+                            temps=None, *, tokens=None, q_tok=None, row_max=None,
+                            row_logZ=None, conf=None, status=None, workspace=None):
+    """Markov-head block drafting and the confidence head of the drafted block
+    in one call.  As dspark_draft_block, plus hidden [B,gamma,H] (dtype of U),
+    w [H+rank] fp32, bias, temps [gamma] fp32 or None; returns dict(tokens,
+    q_tok, row_max, row_logZ, conf)."""
+    lib = load()
+    B, gamma, V = U.shape
+    rank = W1.shape[1]
+    H = hidden.shape[2]
+    dt = _dtype_code(U)
+    dev = U.device
+    _need(U, "U"); _need(W1, "W1", U.dtype, (V, rank), dev); _need(W2, "W2", U.dtype, (rank, V), dev)
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, gamma + 1, 2), dev)
+    _need(hidden, "hidden", U.dtype, (B, gamma, H), dev)
+    _need(w, "w", torch.float32, (H + rank,), dev)
+    if temps is not None:
+        _need(temps, "temps", torch.float32, (gamma,), dev)
+    tokens = _out(tokens, "tokens", torch.int32, (B, gamma), dev)
+    q_tok = _out(q_tok, "q_tok", torch.float32, (B, gamma), dev)
+    row_max = _out(row_max, "row_max", torch.float32, (B, gamma), dev)
+    row_logZ = _out(row_logZ, "row_logZ", torch.float32, (B, gamma), dev)
+    conf = _out(conf, "conf", torch.float32, (B, gamma), dev)
+    status = _status(status, dev)
+    need = dspark_draft_block_workspace(B, gamma, V, rank, dt)
+    ws = _workspace(need, dev, workspace, zeroed=True)
+    _check(lib.dspark_draft_block_conf(B, gamma, V, rank, H, dt, _ptr(U), _ptr(W1), _ptr(W2),
+                                       _ptr(anchor), _ptr(temperature), _ptr(uniforms),
+                                       _ptr(hidden), _ptr(w), ctypes.c_float(bias), _ptr(temps),
+                                       _ptr(tokens), _ptr(q_tok), _ptr(row_max), _ptr(row_logZ),
+                                       _ptr(conf), _ptr(status), _ptr(ws), ws.numel(),
+                                       _stream()))
+    return dict(tokens=tokens, q_tok=q_tok, row_max=row_max, row_logZ=row_logZ, conf=conf)
 
 
 def dspark_draft_block_rnn_workspace(B, gamma, V, rank, H, dtype) -> int:

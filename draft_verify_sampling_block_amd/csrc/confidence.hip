@@ -4,12 +4,14 @@
 // state and the Markov embedding of the previous token, squashed by a
 // sigmoid.  [xhh] non-anticipation note: position k reads x_{k-1} (the
 // anchor for k = 0), never x_k.  One wave per (b, k): the H + rank dot
-// product is read with 16-byte loads and reduced across the wave in fp32.
+// product is read with 16-byte loads and reduced across the wave in fp32
+// (conf_row.hpp, which the single-launch draft kernel's draw waves share).
 //
 // With per-position temperatures (dspark_confidence_sts: sequential
 // temperature scaling, [billytse] 5.2; [weigao] part 3) the logit of
 // position k is divided by temps[k] before the sigmoid; a temperature that
 // is not finite and positive leaves the logit unchanged and is flagged.
+#include "conf_row.hpp"
 #include "dspark_common.hpp"
 #include "dspark_launch.hpp"
 #include "trace.hpp"
@@ -28,37 +30,9 @@ __global__ __launch_bounds__(256) void confidence_kernel(
   const int b = row / gamma, k = row % gamma;
   int prev = (k == 0) ? anchor[b] : tokens[(size_t)b * gamma + k - 1];
   prev = clamp_token(prev, V, status);
-  const T* hrow = hidden + (size_t)row * H;
-  const T* erow = W1 + (size_t)prev * rank;
-  float s = 0.f;
-  for (int i = 8 * lane; i < H; i += 8 * kWave) {
-    float hv[8];
-    load8_f32_stream(hrow + i, hv);
-    const float4 w0 = *reinterpret_cast<const float4*>(w + i);
-    const float4 w1 = *reinterpret_cast<const float4*>(w + i + 4);
-    s += hv[0] * w0.x + hv[1] * w0.y + hv[2] * w0.z + hv[3] * w0.w;
-    s += hv[4] * w1.x + hv[5] * w1.y + hv[6] * w1.z + hv[7] * w1.w;
-  }
-  for (int i = 8 * lane; i < rank; i += 8 * kWave) {
-    float ev[8];
-    load8_f32(erow + i, ev);
-    const float* we = w + H + i;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) s += ev[t] * we[t];
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
-  if (lane == 0) {
-    float z = s + bias;
-    if (temps) {
-      const float t = temps[k];
-      if (t > 0.f && t <= 3.0e38f)
-        z = z / t;
-      else
-        flag(status, DSPARK_DEV_BAD_CONF);
-    }
-    conf[row] = 1.f / (1.f + expf(-z));
-  }
+  const float dot = conf_dot_wave<T>(hidden + (size_t)row * H, W1 + (size_t)prev * rank, w, H,
+                                     rank, lane);
+  if (lane == 0) conf[row] = conf_from_dot(dot, bias, temps, k, status);
 }
 
 hipError_t launch_confidence(int B, int gamma, int H, int V, int rank, int dtype,

@@ -931,17 +931,26 @@ static hipError_t draft_persistent(int B, int gamma, int V, int rank, const uint
   return hipLaunchCooperativeKernel(kern, dim3(P), dim3(nw * 64), args, 0, stream);
 }
 
+static hipError_t draft_block_only(int B, int gamma, int V, int rank, int dtype, const void* U,
+                                   const void* W1, const void* W2, const int32_t* anchor,
+                                   const float* temperature, const float* uniforms,
+                                   int32_t* tokens, float* q_tok, float* row_max,
+                                   float* row_logZ, int32_t* status, void* ws,
+                                   hipStream_t stream);
+
+// With `cf`, the confidence head too: inside the pipelined kernel (its draw
+// waves evaluate it), else by the head's own launch after the draft.
 hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U,
                               const void* W1, const void* W2, const int32_t* anchor,
                               const float* temperature, const float* uniforms, int32_t* tokens,
                               float* q_tok, float* row_max, float* row_logZ, int32_t* status,
-                              void* ws, hipStream_t stream) {
-  // the persistent kernel reports a timed-out wait through the status word
-  // only, so without one the per-position launches (which never wait) run
+                              void* ws, hipStream_t stream, const ConfIn* cf) {
+  // the single-launch kernels report a timed-out wait through the status
+  // word only, so without one the per-position launches (which never wait)
+  // run; the pipelined kernel first (automatic setting, or 5), then the
+  // earlier persistent kernel (automatic, or 2-4)
   const int path = get_draft_path();
   const bool persist = path != 1 && status != nullptr;
-  // the pipelined kernel first (automatic setting, or 5), then the
-  // earlier persistent kernel (automatic, or 2-4)
   if (dtype == DSPARK_BF16 && persist && (path == 0 || path == 5)) {
     const DevInfo di = dev_info();
     hipError_t e = hipErrorNotSupported;
@@ -950,9 +959,25 @@ hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, cons
                      static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2), anchor,
                      temperature, uniforms, tokens, q_tok, row_max, row_logZ, status,
                      static_cast<uint32_t*>(ws),
-                     static_cast<char*>(ws) + kWsHeader + persistent_ws_bytes(B, V), stream);
+                     static_cast<char*>(ws) + kWsHeader + persistent_ws_bytes(B, V), cf, stream);
     if (e != hipErrorNotSupported || path == 5) return e;
   }
+  hipError_t e = draft_block_only(B, gamma, V, rank, dtype, U, W1, W2, anchor, temperature,
+                                  uniforms, tokens, q_tok, row_max, row_logZ, status, ws, stream);
+  if (e != hipSuccess || !cf) return e;
+  return launch_confidence(B, gamma, cf->H, V, rank, dtype, cf->hidden, W1, anchor, tokens, cf->w,
+                           cf->bias, cf->temps, cf->conf, status, stream);
+}
+
+// the draft by the earlier persistent kernel or the per-position launches
+static hipError_t draft_block_only(int B, int gamma, int V, int rank, int dtype, const void* U,
+                                   const void* W1, const void* W2, const int32_t* anchor,
+                                   const float* temperature, const float* uniforms,
+                                   int32_t* tokens, float* q_tok, float* row_max,
+                                   float* row_logZ, int32_t* status, void* ws,
+                                   hipStream_t stream) {
+  const int path = get_draft_path();
+  const bool persist = path != 1 && status != nullptr;
   if (dtype == DSPARK_BF16) {
     auto* u = static_cast<const uint16_t*>(U);
     auto* w1 = static_cast<const uint16_t*>(W1);

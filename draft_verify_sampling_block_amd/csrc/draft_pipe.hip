@@ -51,6 +51,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "conf_row.hpp"
 #include "dspark_common.hpp"
 #include "draft_tile.hpp"
 #include "dspark_launch.hpp"
@@ -59,6 +60,7 @@
 namespace dspark {
 
 constexpr int kPpWaves = 8;
+constexpr int kBufferDword3 = 0x00020000;   // buffer descriptor word 3 (CDNA: raw bytes)
 constexpr int kPpRegTiles = 8;                          // register tiles (one per wave)
 constexpr int kPpLdsTiles = 2;                          // LDS tiles per tile group
 constexpr int kPpMaxTiles = kPpRegTiles + kPpLdsTiles;  // tiles per tile group
@@ -89,6 +91,13 @@ struct PpArgs {
   uint32_t* tok_flag;   // [B] ((k + 1) << 24) | token k
   uint32_t* hdr;        // start barrier: [0] call number, [64 + g] arrival of group g
   long long spin_cap;   // wall-clock ticks a wait may last
+  // the confidence head (conf NULL: not evaluated)
+  const uint16_t* hidden;   // [B][gamma][H]
+  const float* cw;          // [H + rank]
+  const float* temps;       // [gamma] or NULL
+  float* conf;              // [B][gamma]
+  float cbias;
+  int H;
 };
 
 // tiles of tile group q (contiguous, the first nT % Pt groups one more)
@@ -192,6 +201,15 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
   // crossing-tile recompute; requested first so it is in by then)
   if (lane < rank / 8)
     __builtin_amdgcn_global_load_lds(a.W1 + (size_t)prev * rank + 8 * lane, wl, 16, 0, 0);
+  // The confidence of (b, k) needs only the previous token, known now: the
+  // wave evaluates it while the position's statistics are still being
+  // formed (the same code, hence the same bits, as the head's own kernel).
+  if (a.conf) {
+    const float dot = conf_dot_wave<uint16_t>(a.hidden + ((size_t)b * gamma + k) * a.H,
+                                              a.W1 + (size_t)prev * rank, a.cw, a.H, rank, lane);
+    if (lane == 0)
+      a.conf[(size_t)b * gamma + k] = conf_from_dot(dot, a.cbias, a.temps, k, a.status);
+  }
   const float Tb = a.temperature[b];
   const bool greedy = !(Tb > 0.f);
   const double u = (double)a.uniforms[((size_t)b * (gamma + 1) + k) * 2 + 0];
@@ -385,10 +403,17 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
   const int g8 = lane & 7, rho = lane >> 3;
   const int col = min(v0 + 8 * g8, V - 8);   // pieces past V: any valid address
   constexpr int NR = 2 * KS;                 // k-rows per lane (rank / 8)
+  // (buffer loads: one per-lane byte offset plus a scalar one per k-row step,
+  // where 64-bit addresses for every step would be held in registers across
+  // the draw loop)
   u32x4_t wv[NR];
+  {
+    const __amdgpu_buffer_rsrc_t w2r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.W2), (short)0, rank * V * 2, kBufferDword3);
+    const int vo = (rho * V + col) * 2;
 #pragma unroll
-  for (int m = 0; m < NR; ++m)
-    wv[m] = *reinterpret_cast<const u32x4_t*>(a.W2 + (size_t)(rho + 8 * m) * V + col);
+    for (int m = 0; m < NR; ++m) wv[m] = __builtin_amdgcn_raw_buffer_load_b128(w2r, vo, m * 16 * V, 0);
+  }
   const u32x4_t uv = __builtin_nontemporal_load(
       reinterpret_cast<const u32x4_t*>(a.U + out * V + col));
   const uint16_t* wrow = reinterpret_cast<const uint16_t*>(wl);
@@ -470,6 +495,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
     // draws (and their W2 reads) spread over all of them
     const int g = (int)blockIdx.x - a.Pt;
     char* wl = ldsX + wave * kPpDrawLds;
+
     const uint32_t E = pp_call(a);
     // this wave's requests' token flags start at zero
     for (int b = g + a.Pd * wave; b < a.B; b += a.Pd * kPpWaves)
@@ -919,7 +945,8 @@ hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_c
                       const uint16_t* U, const uint16_t* W1, const uint16_t* W2,
                       const int32_t* anchor, const float* temperature, const float* uniforms,
                       int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
-                      int32_t* status, uint32_t* hdr, void* ws, hipStream_t stream) {
+                      int32_t* status, uint32_t* hdr, void* ws, const ConfIn* cf,
+                      hipStream_t stream) {
   PpArgs a;
   if (!draft_pipe_plan(B, V, P, a.Pt, a.Pd)) return hipErrorNotSupported;
   a.B = B; a.gamma = gamma; a.V = V; a.rank = rank;
@@ -933,6 +960,12 @@ hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_c
   w += align256((size_t)B * kPpMaxTileGroups * 8);
   a.tok_flag = reinterpret_cast<uint32_t*>(w);
   a.hdr = hdr;
+  a.hidden = cf ? static_cast<const uint16_t*>(cf->hidden) : nullptr;
+  a.cw = cf ? cf->w : nullptr;
+  a.temps = cf ? cf->temps : nullptr;
+  a.conf = cf ? cf->conf : nullptr;
+  a.cbias = cf ? cf->bias : 0.f;
+  a.H = cf ? cf->H : 0;
   a.spin_cap = spin_cap;
   switch (rank) {
     case 32: return launch_pipe<2>(a, stream);

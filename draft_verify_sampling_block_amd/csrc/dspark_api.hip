@@ -115,6 +115,35 @@ int dspark_draft_block(int B, int gamma, int V, int rank, int dtype, const void*
                                                    row_logZ, status, workspace, stream));
 }
 
+int dspark_draft_block_conf(int B, int gamma, int V, int rank, int H, int dtype, const void* U,
+                            const void* W1, const void* W2, const int32_t* anchor,
+                            const float* temperature, const float* uniforms, const void* hidden,
+                            const float* w, float bias, const float* temps, int32_t* tokens,
+                            float* q_tok, float* row_max, float* row_logZ, float* conf,
+                            int32_t* status, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  const char* fn = "dspark_draft_block_conf";
+  int rc = check_dims(fn, B, gamma, V, rank, dtype);
+  if (rc) return rc;
+  if (H < 8 || H % 8) return fail(DSPARK_EINVAL, "%s: H=%d must be a positive multiple of 8", fn, H);
+  REQUIRE_PTR(U); REQUIRE_PTR(W1); REQUIRE_PTR(W2); REQUIRE_PTR(anchor);
+  REQUIRE_PTR(temperature); REQUIRE_PTR(uniforms); REQUIRE_PTR(hidden); REQUIRE_PTR(w);
+  REQUIRE_PTR(tokens); REQUIRE_PTR(q_tok); REQUIRE_PTR(row_max); REQUIRE_PTR(row_logZ);
+  REQUIRE_PTR(conf); OPT_PTR(temps); OPT_PTR(status);
+  if (!status && dspark::get_draft_path() >= 2)
+    return fail(DSPARK_EINVAL, "%s: the persistent-only draft paths need a status word (a "
+                "timed-out wait is reported there only)", fn);
+  const size_t need = dspark::draft_workspace_bytes(B, gamma, V, rank, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
+  const dspark::ConfIn cf{hidden, w, bias, temps, conf, H};
+  return hip_status(fn, dspark::launch_draft_block(B, gamma, V, rank, dtype, U, W1, W2, anchor,
+                                                   temperature, uniforms, tokens, q_tok, row_max,
+                                                   row_logZ, status, workspace, stream, &cf));
+}
+
 size_t dspark_draft_block_rnn_workspace(int B, int gamma, int V, int rank, int H, int dtype) {
   if (check_dims("dspark_draft_block_rnn_workspace", B, gamma, V, rank, dtype) != DSPARK_OK)
     return 0;

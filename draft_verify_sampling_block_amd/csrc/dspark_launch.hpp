@@ -25,19 +25,31 @@ int get_draft_path();
 // zero-filled before the first; nothing else writes it); `ws`: its exchange
 // words (any content).
 constexpr size_t kDraftPipeHeaderBytes = 1536;
+// The confidence head evaluated alongside the draft: hidden [B,gamma,H]
+// (the draft's dtype), w [H+rank], bias, temps [gamma] or NULL, out conf
+// [B,gamma].
+struct ConfIn {
+  const void* hidden;
+  const float* w;
+  float bias;
+  const float* temps;
+  float* conf;
+  int H;
+};
 size_t draft_pipe_workspace_bytes(int B, int V);
 hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_cap,
                       const uint16_t* U, const uint16_t* W1, const uint16_t* W2,
                       const int32_t* anchor, const float* temperature, const float* uniforms,
                       int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
-                      int32_t* status, uint32_t* hdr, void* ws, hipStream_t stream);
+                      int32_t* status, uint32_t* hdr, void* ws, const ConfIn* cf,
+                      hipStream_t stream);
 // compute units of the current device (cached per device)
 int device_cu_count();
 hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, const void* U,
                               const void* W1, const void* W2, const int32_t* anchor,
                               const float* temperature, const float* uniforms, int32_t* tokens,
                               float* q_tok, float* row_max, float* row_logZ, int32_t* status,
-                              void* ws, hipStream_t stream);
+                              void* ws, hipStream_t stream, const ConfIn* cf = nullptr);
 
 // RNN head (rnn.hip, draft.hip): the recurrence's workspace (pre-activations
 // of the hidden part for every position, two state buffers), its launches,

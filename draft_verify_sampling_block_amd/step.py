@@ -11,7 +11,7 @@ import dataclasses
 import numpy as np
 import torch
 
-from . import dspark_confidence, dspark_draft_block, dspark_schedule, dspark_verify
+from . import dspark_draft_block_conf, dspark_schedule, dspark_verify
 
 
 @dataclasses.dataclass
@@ -98,11 +98,11 @@ class Step:
         if status is None:
             self.status.zero_()
             status = self.status
-        dspark_draft_block(d.U, d.W1, d.W2, d.anchor, d.temperature, d.uniforms,
-                           tokens=self.tokens, q_tok=self.q_tok, row_max=self.row_max,
-                           row_logZ=self.row_logZ, status=status, workspace=self.ws_draft)
-        dspark_confidence(d.hidden, d.W1, d.anchor, self.tokens, d.w, d.b0, conf=self.conf,
-                          status=status)
+        # the draft and the confidence head of the drafted block in one call
+        dspark_draft_block_conf(d.U, d.W1, d.W2, d.anchor, d.temperature, d.uniforms, d.hidden,
+                                d.w, d.b0, tokens=self.tokens, q_tok=self.q_tok,
+                                row_max=self.row_max, row_logZ=self.row_logZ, conf=self.conf,
+                                status=status, workspace=self.ws_draft)
         if d.sps is not None:
             dspark_schedule(self.conf, d.sps, ell=self.ell, order=self.order, stats=self.stats,
                             status=status, workspace=self.ws_sched)

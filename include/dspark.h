@@ -123,6 +123,32 @@ int dspark_draft_block(int B, int gamma, int V, int rank, int dtype,
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * dspark_draft_block_conf: dspark_draft_block and the confidence head of the
+ * drafted block in one call ([billytse] 3.3 and 5; [weigao] parts 2-3: the
+ * head scores position k from its hidden state and the token drawn before
+ * it, so each score is available as soon as that token is).  conf[b,k] is
+ * bit for bit what dspark_confidence (temps NULL) or dspark_confidence_sts
+ * (temps given) returns for the drafted tokens.  The single-launch kernel's
+ * draw waves evaluate the head while they wait for each position's
+ * statistics, which saves the head's launch; where that kernel does not run
+ * the head's own kernel follows the draft (same results).
+ * in : as dspark_draft_block, plus hidden [B,gamma,H] (dtype; H % 8 == 0),
+ *      w [H+rank] fp32, bias, temps [gamma] fp32 or NULL
+ * out: as dspark_draft_block, plus conf [B,gamma] fp32
+ * workspace, status and errors as dspark_draft_block.
+ * ---------------------------------------------------------------------- */
+int dspark_draft_block_conf(int B, int gamma, int V, int rank, int H, int dtype,
+                            const void* U, const void* W1, const void* W2,
+                            const int32_t* anchor, const float* temperature,
+                            const float* uniforms,
+                            const void* hidden, const float* w, float bias,
+                            const float* temps,
+                            int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
+                            float* conf,
+                            int32_t* status, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * dspark_draft_block_rnn: block drafting with the RNN head instead of the
  * Markov head ([weigao] part 2, the _rnn_step description; [billytse] 3.3:
  * a recurrent state lets each position see the whole block prefix).

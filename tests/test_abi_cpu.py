@@ -68,6 +68,16 @@ def test_host_validation_rejects_before_launch(lib):
     assert lib.dspark_draft_block(4, 5, 1024, 32, 0, *([fake] * 11), fake, 16, None) == -4
     assert lib.dspark_draft_block(4, 5, 1024, 32, 0, *([fake + 8] + [fake] * 10), fake, 1 << 30,
                                   None) == -3
+    # the fused draft + confidence call: H a positive multiple of 8, every
+    # pointer but temps and status given, the draft's workspace
+    cf = lambda H, ptrs, ws, nbytes: lib.dspark_draft_block_conf(
+        4, 5, 1024, 32, H, 0, *ptrs[:8], 0.0, None, *ptrs[8:], None, ws, nbytes, None)
+    assert cf(20, [fake] * 13, fake, 1 << 30) == -1                      # H % 8
+    assert cf(0, [fake] * 13, fake, 1 << 30) == -1
+    rc = cf(24, [fake] * 7 + [None] + [fake] * 5, fake, 1 << 30)         # w missing
+    assert rc == -1 and b"'w' is NULL" in lib.dspark_last_error()
+    assert cf(24, [fake] * 12 + [None], fake, 1 << 30) == -1             # conf missing
+    assert cf(24, [fake] * 13, fake, 16) == -4                           # workspace
     assert lib.dspark_schedule(9000, 1, fake, fake, 10, fake, None, None, None, None, 0, None) == -5
     assert lib.dspark_schedule(4, 2, fake, fake, 0, fake, None, None, None, None, 0, None) == -1
     assert lib.dspark_schedule_noalloc(9000, 1, fake, fake, 10, fake, None, None, None, None) == -5

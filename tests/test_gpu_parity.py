@@ -308,6 +308,56 @@ def test_draft_workspace_reuse_across_shapes():
             assert np.array_equal(outs[0][k], outs[1][k]), k
 
 
+CONF_CASES = {
+    "bf16-ragged-V1000-B40": lambda: SMALL["bf16-ragged-V1000-B40"](),
+    "bf16-greedy-mix-T0.7": lambda: SMALL["bf16-greedy-mix-T0.7"](),
+    "fp32-strong-bias-ragged": lambda: SMALL["fp32-strong-bias-ragged"](),
+    "bf16-B300-rank128-V5000": lambda: make_custom(300, 3, 5000, 128, 24, "bf16", "mixture",
+                                                   seed=9, temperature=0.8, greedy_frac=0.2),
+    "qwen3-4b-block7 B=32 gamma=7 V=151936 full size": lambda: make_config(1),
+    "long-proposal-g15 B=128 gamma=15 V=151936 full size": lambda: make_config(3),
+}
+
+
+@pytest.mark.parametrize("name", list(CONF_CASES))
+def test_draft_block_conf_matches_the_separate_calls(name):
+    """dspark_draft_block_conf gives the bits of dspark_draft_block followed by
+    dspark_confidence (no temperatures) or dspark_confidence_sts (with them),
+    through the pipelined kernel (its draw waves evaluate the head) and
+    through the per-position launches (the head's own kernel follows)."""
+    import draft_verify_sampling_block_amd as dv
+    from draft_verify_sampling_block_amd.step import upload
+    wl = CONF_CASES[name]()
+    d = upload(wl, "cuda", scheduler=False)
+    rng = np.random.default_rng(5)
+    temps = torch.tensor(rng.uniform(0.5, 2.0, wl.gamma).astype(np.float32), device="cuda")
+    keys = ("tokens", "q_tok", "row_max", "row_logZ")
+    for path in (0, 1):
+        for tp in (None, temps):
+            _say(f"{name}: draft path {path}, temperatures {'given' if tp is not None else 'none'}")
+            old = dv.dspark_set_draft_path(path)
+            try:
+                st = torch.zeros((1,), dtype=torch.int32, device="cuda")
+                f = dv.dspark_draft_block_conf(d.U, d.W1, d.W2, d.anchor, d.temperature,
+                                               d.uniforms, d.hidden, d.w, d.b0, tp, status=st)
+                st2 = torch.zeros((1,), dtype=torch.int32, device="cuda")
+                o = dv.dspark_draft_block(d.U, d.W1, d.W2, d.anchor, d.temperature, d.uniforms,
+                                          status=st2)
+                if tp is None:
+                    c = dv.dspark_confidence(d.hidden, d.W1, d.anchor, o["tokens"], d.w, d.b0,
+                                             status=st2)
+                else:
+                    c = dv.dspark_confidence_sts(d.hidden, d.W1, d.anchor, o["tokens"], d.w, d.b0,
+                                                 tp, status=st2)
+                torch.cuda.synchronize()
+            finally:
+                dv.dspark_set_draft_path(old)
+            assert int(st.item()) == 0 and int(st2.item()) == 0
+            for k in keys:
+                assert torch.equal(f[k], o[k]), k
+            assert torch.equal(f["conf"], c)
+
+
 def test_repeat_is_deterministic():
     _say("determinism")
     wl = SMALL["bf16-ragged-V1000-B40"]()
