@@ -1,15 +1,17 @@
 """Benchmark one decode step of the DSpark sampling path on one MI355X.
 
-A step = dspark_draft_block -> dspark_confidence -> dspark_schedule (or the
-fixed verify length) -> dspark_verify over one batch, inputs resident in
-HBM.  Prints ONE JSON line.
+A step = dspark_draft_block_conf (the draft and the confidence head in one
+call: one launch where the single-launch draft kernel runs, whose draw waves
+evaluate the head) -> dspark_schedule (or the fixed verify length) ->
+dspark_verify over one batch, inputs resident in HBM.  Prints ONE JSON
+line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
                     [--no-cpu-baseline] [--cpu-requests N]
 
 value      = B * gamma / (time per step), drafted-and-verified positions/s
-roofline   = the draft kernel (pdraft_kernel, or draft_stats_kernel where the
-             per-position launches run): algorithmic bytes per
+roofline   = the draft kernel (pdraft_pipe_kernel, or pdraft_kernel /
+             draft_stats_kernel where those run): algorithmic bytes per
              launch / its mean duration, timed with per-launch HIP events in a
              second pass over the same K steps (events are kept out of the
              pass that gives `value`)
@@ -69,13 +71,16 @@ def algorithmic_bytes(wl, ell, n_acc):
             + 4 * B * (g + 1) * 2 + 4 * B * g * 4 + 4 * B * (g + 1))
 
 
-def draft_kernel_bytes(wl, kernel):
+def draft_kernel_bytes(wl, kernel, with_conf=False):
     """Algorithmic bytes of one launch of the draft kernel `kernel`: the
     draft's share of the step's bytes, each input read once.
 
-    pdraft_kernel (one launch per block of gamma positions): every U row, the
-    W2 factor once, the gathered W1 rows (one per position and request), the
-    anchors, temperatures and draw uniforms, and the four [B, gamma] outputs.
+    pdraft_pipe_kernel / pdraft_kernel (one launch per block of gamma
+    positions): every U row, the W2 factor once, the gathered W1 rows (one per
+    position and request), the anchors, temperatures and draw uniforms, and
+    the four [B, gamma] outputs; with the confidence head evaluated in the
+    same launch (with_conf), also the hidden states and the confidences (the
+    head's W1 rows are the gathered ones).
     draft_stats_kernel (one launch per position): that position's U rows and
     W1 rows, and 1/gamma of W2 (the per-position launches read W2 again each
     time; the step needs it once).  The kernels' own tile statistics are
@@ -84,8 +89,9 @@ def draft_kernel_bytes(wl, kernel):
     e = 2 if wl.dtype == "bf16" else 4
     B, g, V, r = wl.B, wl.gamma, wl.V, wl.rank
     if kernel in ("pdraft_kernel", "pdraft_pipe_kernel"):
+        conf = (e * B * g * wl.H + 4 * B * g) if with_conf else 0
         return (e * B * g * V + e * r * V + e * B * g * r
-                + 4 * B + 4 * B + 4 * B * g + 4 * B * g * 4)
+                + 4 * B + 4 * B + 4 * B * g + 4 * B * g * 4 + conf)
     return e * B * V + e * B * r + e * r * V / g
 
 
@@ -102,6 +108,9 @@ def draft_intermediate_bytes(wl, kernel):
 
 
 KERNEL_SOURCES = ["draft_verify_sampling_block_amd/csrc/draft.hip",
+                  "draft_verify_sampling_block_amd/csrc/draft_pipe.hip",
+                  "draft_verify_sampling_block_amd/csrc/draft_tile.hpp",
+                  "draft_verify_sampling_block_amd/csrc/conf_row.hpp",
                   "draft_verify_sampling_block_amd/csrc/dspark_common.hpp",
                   "draft_verify_sampling_block_amd/csrc/dspark_launch.hpp"]
 
@@ -396,7 +405,9 @@ def main():
     per_step_ms = {k: v[1] / args.steps for k, v in tr.items()}
     draft_kernel = next((k for k in ("pdraft_pipe_kernel", "pdraft_kernel") if k in kern_ms),
                         "draft_stats_kernel")
-    stats_bytes = draft_kernel_bytes(wl, draft_kernel)
+    # the confidence head runs inside the draft launch unless its own kernel ran
+    conf_fused = draft_kernel == "pdraft_pipe_kernel" and "confidence_kernel" not in kern_ms
+    stats_bytes = draft_kernel_bytes(wl, draft_kernel, with_conf=conf_fused)
     avg_s = kern_ms[draft_kernel] / 1e3
     achieved = stats_bytes / avg_s / 1e9
     traffic = counter_traffic(draft_kernel, cfg)
@@ -426,6 +437,7 @@ def main():
                      "traffic_over_alg": None if traffic is None else traffic / stats_bytes,
                      "bytes_per_launch": stats_bytes,
                      "intermediate_bytes": draft_intermediate_bytes(wl, draft_kernel),
+                     "confidence_in_launch": conf_fused,
                      "mean_launch_us": avg_s * 1e6},
         "step": {"bytes_alg": bytes_step, "hbm_gbs": bytes_step / (ms / 1e3) / 1e9,
                  "hbm_frac": bytes_step / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,

@@ -33,6 +33,11 @@ def test_draft_kernel_bytes():
     want = (2 * 3 * 4 * 200 + 2 * 32 * 200 + 2 * 3 * 4 * 32
             + 4 * 3 + 4 * 3 + 4 * 3 * 4 + 4 * 3 * 4 * 4)
     assert bench.draft_kernel_bytes(wl, "pdraft_kernel") == want
+    assert bench.draft_kernel_bytes(wl, "pdraft_pipe_kernel") == want
+    # with the confidence head in the same launch: the hidden states [B, gamma, H]
+    # and the confidences (its W1 rows are the gathered ones)
+    assert bench.draft_kernel_bytes(wl, "pdraft_pipe_kernel", with_conf=True) == (
+        want + 2 * 3 * 4 * 16 + 4 * 3 * 4)
     nT = (200 + 63) // 64
     greedy = int(np.sum(~(np.asarray(wl.temperature) > 0)))
     assert greedy == 1
