@@ -802,8 +802,8 @@ __global__ void pdraft_reset_kernel(uint32_t* f0, int n0, uint32_t* f1, int n1) 
 
 namespace {
 // 0 auto, 1 multi-launch, 2-4 the earlier persistent kernel only (3: 8
-// waves, 4: 4 waves), 5 the pipelined kernel only; process-wide, read by
-// every call
+// waves, 4: 4 waves), 5 the pipelined kernel only, 6 the same by a
+// cooperative launch; process-wide, read by every call
 std::atomic<int> g_draft_path{0};
 
 struct DevInfo {
@@ -951,16 +951,17 @@ hipError_t launch_draft_block(int B, int gamma, int V, int rank, int dtype, cons
   // earlier persistent kernel (automatic, or 2-4)
   const int path = get_draft_path();
   const bool persist = path != 1 && status != nullptr;
-  if (dtype == DSPARK_BF16 && persist && (path == 0 || path == 5)) {
+  if (dtype == DSPARK_BF16 && persist && (path == 0 || path == 5 || path == 6)) {
     const DevInfo di = dev_info();
     hipError_t e = hipErrorNotSupported;
-    if (di.coop && di.cus > 0)
+    if (di.cus > 0 && (path != 6 || di.coop))
       e = draft_pipe(B, gamma, V, rank, di.cus, 200LL * di.wall_khz, static_cast<const uint16_t*>(U),
                      static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2), anchor,
                      temperature, uniforms, tokens, q_tok, row_max, row_logZ, status,
                      static_cast<uint32_t*>(ws),
-                     static_cast<char*>(ws) + kWsHeader + persistent_ws_bytes(B, V), cf, stream);
-    if (e != hipErrorNotSupported || path == 5) return e;
+                     static_cast<char*>(ws) + kWsHeader + persistent_ws_bytes(B, V), cf,
+                     path == 6, stream);
+    if (e != hipErrorNotSupported || path >= 5) return e;
   }
   hipError_t e = draft_block_only(B, gamma, V, rank, dtype, U, W1, W2, anchor, temperature,
                                   uniforms, tokens, q_tok, row_max, row_logZ, status, ws, stream);

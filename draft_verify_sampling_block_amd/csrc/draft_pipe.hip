@@ -927,8 +927,14 @@ bool draft_pipe_plan(int B, int V, int P, int& Pt, int& Pd) {
   return Pd >= 1 && Pt >= 1 && (long long)Pt * kPpMaxTiles >= nT;
 }
 
+// Every work-group must be resident at once (they wait for one another):
+// the grid is at most one work-group per compute unit and the occupancy
+// check admits one per unit.  A plain launch on the stream's queue places
+// them all as soon as the units are free; a cooperative launch guarantees
+// it even beside other work on the device, but goes through a queue of its
+// own, whose hand-over costs about 10 us on each side of the kernel.
 template <int KS>
-static hipError_t launch_pipe(const PpArgs& a0, hipStream_t stream) {
+static hipError_t launch_pipe(const PpArgs& a0, bool coop, hipStream_t stream) {
   PpArgs a = a0;
   const void* kern = reinterpret_cast<const void*>(pdraft_pipe_kernel<KS>);
   int occ = 0;
@@ -937,15 +943,17 @@ static hipError_t launch_pipe(const PpArgs& a0, hipStream_t stream) {
     return hipErrorNotSupported;
   TraceScope t("pdraft_pipe_kernel", stream);
   void* args[] = {&a};
-  return hipLaunchCooperativeKernel(kern, dim3(a.Pt + a.Pd), dim3(kPpWaves * 64), args, 0,
-                                    stream);
+  if (coop)
+    return hipLaunchCooperativeKernel(kern, dim3(a.Pt + a.Pd), dim3(kPpWaves * 64), args, 0,
+                                      stream);
+  return hipLaunchKernel(kern, dim3(a.Pt + a.Pd), dim3(kPpWaves * 64), args, 0, stream);
 }
 
 hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_cap,
                       const uint16_t* U, const uint16_t* W1, const uint16_t* W2,
                       const int32_t* anchor, const float* temperature, const float* uniforms,
                       int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
-                      int32_t* status, uint32_t* hdr, void* ws, const ConfIn* cf,
+                      int32_t* status, uint32_t* hdr, void* ws, const ConfIn* cf, bool coop,
                       hipStream_t stream) {
   PpArgs a;
   if (!draft_pipe_plan(B, V, P, a.Pt, a.Pd)) return hipErrorNotSupported;
@@ -968,10 +976,10 @@ hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_c
   a.H = cf ? cf->H : 0;
   a.spin_cap = spin_cap;
   switch (rank) {
-    case 32: return launch_pipe<2>(a, stream);
-    case 64: return launch_pipe<4>(a, stream);
-    case 128: return launch_pipe<8>(a, stream);
-    default: return launch_pipe<16>(a, stream);
+    case 32: return launch_pipe<2>(a, coop, stream);
+    case 64: return launch_pipe<4>(a, coop, stream);
+    case 128: return launch_pipe<8>(a, coop, stream);
+    default: return launch_pipe<16>(a, coop, stream);
   }
 }
 

@@ -80,8 +80,8 @@ const char* dspark_last_error(void) { return g_err; }
 const char* dspark_version(void) { return "libdspark 0.1 gfx950"; }
 
 int dspark_set_draft_path(int path) {
-  if (path < 0 || path > 5)
-    return fail(DSPARK_EINVAL, "dspark_set_draft_path: path %d is not in 0..5", path);
+  if (path < 0 || path > 6)
+    return fail(DSPARK_EINVAL, "dspark_set_draft_path: path %d is not in 0..6", path);
   const int old = dspark::set_draft_path(path);
   return old;
 }

@@ -41,7 +41,7 @@ hipError_t draft_pipe(int B, int gamma, int V, int rank, int P, long long spin_c
                       const uint16_t* U, const uint16_t* W1, const uint16_t* W2,
                       const int32_t* anchor, const float* temperature, const float* uniforms,
                       int32_t* tokens, float* q_tok, float* row_max, float* row_logZ,
-                      int32_t* status, uint32_t* hdr, void* ws, const ConfIn* cf,
+                      int32_t* status, uint32_t* hdr, void* ws, const ConfIn* cf, bool coop,
                       hipStream_t stream);
 // compute units of the current device (cached per device)
 int device_cu_count();

@@ -406,18 +406,25 @@ int dspark_trace_summary(char* buf, size_t len);
  * Drafting implementation choice (process-wide; for tests and benchmarks).
  * The setting is one atomic word read by every later dspark_draft_block
  * call, from any host thread: the one exception to "keep no state".
- * 0 = automatic (default): for bf16 inputs on a device with cooperative
- *     launch, the pipelined single-launch kernel (request windows of 32
- *     drafted while the previous windows' tokens are drawn by dedicated
- *     work-groups), else the earlier single-launch kernel, else one launch
+ * 0 = automatic (default): for bf16 inputs, the pipelined single-launch
+ *     kernel (request windows of 32 drafted while the previous windows'
+ *     tokens are drawn by dedicated work-groups; one work-group per compute
+ *     unit, launched on the stream's own queue, so its work-groups must find
+ *     the compute units free: with other work running beside it on the
+ *     device they start as units free up, and a wait that outlasts 0.2 s
+ *     reports DSPARK_DEV_TIMEOUT), else the earlier single-launch kernel
+ *     (cooperative launch), else one launch
  *     pair per position;
  * 1 = always one launch pair per position;
  * 2 = the earlier single-launch kernel only: dspark_draft_block returns
  *     DSPARK_EHIP where it cannot run;
  * 3, 4 = that kernel only, with 8 (one register-resident W2 tile each) or
  *     4 (two each) waves per work-group; 2 picks 8;
- * 5 = the pipelined kernel only (DSPARK_EHIP where it cannot run).
- * Settings 1-4 return identical bits.  The pipelined kernel draws from the
+ * 5 = the pipelined kernel only (DSPARK_EHIP where it cannot run);
+ * 6 = the pipelined kernel by a cooperative launch (every work-group
+ *     resident whatever else the device runs; the launch goes through a
+ *     queue of its own, about 20 us more per call).
+ * Settings 1-4 return identical bits, and so do 5 and 6.  The pipelined kernel draws from the
  * same statistics with the group and tile masses summed in another order
  * (a token can differ only where the uniform lies within about 1e-6 of a
  * boundary of the inverse CDF; q and the row statistics differ in the last

@@ -244,7 +244,7 @@ def test_draft_paths_agree(name):
     wl = PATH_CASES[name]()
     d = upload(wl, "cuda", scheduler=False)
     res = {}
-    for path in (1, 3, 4, 5):
+    for path in (1, 3, 4, 5, 6):
         _say(f"{name}: draft path {path}")
         old = dv.dspark_set_draft_path(path)
         try:
@@ -259,6 +259,9 @@ def test_draft_paths_agree(name):
     for path in (3, 4):
         for i, key in enumerate(("tokens", "q_tok", "row_max", "row_logZ")):
             assert np.array_equal(res[1][i], res[path][i]), (path, key)
+    # the pipelined kernel by a plain and by a cooperative launch: the same bits
+    for i, key in enumerate(("tokens", "q_tok", "row_max", "row_logZ")):
+        assert np.array_equal(res[5][i], res[6][i]), key
     assert all(res[p][4] == 0 for p in res), {p: res[p][4] for p in res}
     B, g = wl.B, wl.gamma
     rows = None
