@@ -647,6 +647,8 @@ __global__ __launch_bounds__(kVtWaves * 64, 1) void verify_tile_stats_kernel(
   else walk(std::false_type{});
 }
 
+constexpr int kFinPer = kMaxTiles / 256;   // chunk sums per thread of the finish kernel
+
 template <typename T, int KS>
 __global__ __launch_bounds__(256) void verify_finish_kernel(
     int B, int gamma, int V, int rank, const T* __restrict__ target, const T* __restrict__ U,
@@ -662,29 +664,71 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
   __shared__ int s_tile, s_pick;
   __shared__ double s_before;
   __shared__ float se[kTileV];
+  __shared__ int s_j, s_prev;
 
   const int b = blockIdx.x, tid = threadIdx.x;
   const int nT = n_tiles(V);
+  // Everything that does not wait for the first rejection is requested at
+  // once: the verify length, the temperature, the request's accept flags
+  // and drafted tokens (wave 0, one slot per lane), the anchor, this
+  // thread's residual chunk sums and the draw uniform.
   const int L = clamp_ell(ell, b, gamma, nullptr);
-  const int j = first_reject(ws, b, gamma, L);
+  const float Tb = temperature[b];
+  const bool greedy = !(Tb > 0.f);
+  const int per = (nT + blockDim.x - 1) / blockDim.x;   // <= kFinPer
+  const int c0 = min(nT, tid * per), c1 = min(nT, c0 + per);
+  const float* fc = ws.fchunk + (size_t)b * nT;
+  const float* pc = ws.pchunk + (size_t)b * nT;
+  float fcv[kFinPer];
+#pragma unroll
+  for (int i = 0; i < kFinPer; ++i) fcv[i] = (!greedy && c0 + i < c1) ? fc[c0 + i] : 0.f;
+  const double u = (double)uniforms[((size_t)b * (gamma + 1) + gamma) * 2 + 0];
+  if (tid < kWave) {
+    const int lane = tid;
+    const int acc = lane < gamma ? ws.wacc[(size_t)b * gamma + lane] : 1;
+    const int tok = lane < gamma ? tokens[(size_t)b * gamma + lane] : 0;
+    const int anc = anchor[b];
+    // the first slot among the L tested whose flag is 0 (L when all pass)
+    const unsigned long long rej = __ballot(lane < L && acc == 0);
+    const int jj = rej ? __builtin_ctzll(rej) : L;
+    const int tk = __shfl(tok, jj > 0 ? jj - 1 : 0, kWave);
+    if (lane == 0) {
+      s_j = jj;
+      s_prev = jj < L ? (ws.emb_rows ? b * gamma + jj : clamp_token(jj == 0 ? anc : tk, V, nullptr))
+                      : -1;
+    }
+  }
+  __syncthreads();
+  const int j = s_j;
   const bool residual = j < L;
   const int slot = residual ? j : L;
   const int n = residual ? j : L;
-  const float Tb = temperature[b];
-  const bool greedy = !(Tb > 0.f);
   const size_t sk = (size_t)b * (gamma + 1) + slot;
 
   int y = 0;
   if (greedy) {
     y = ws.rArg[sk];
   } else {
+    // the crossing tile's recompute operands that do not wait for the scan:
+    // the weights' constants and the previous token's W1 row
+    const int mrow = b % kTileM;
+    const int lane = tid & 63, c = lane & 31, h = lane >> 5;
+    const bool mine = tid < (bf ? kSub : 1) * kWave && c == mrow;
+    const int prev = s_prev;
+    const float it = 1.f / Tb;
+    const float M = ws.rM[sk], LZ = ws.rLZ[sk];
+    const float mq = residual ? row_max[(size_t)b * gamma + slot] : 0.f;
+    const float lzq = residual ? row_logZ[(size_t)b * gamma + slot] : 0.f;
+    bf16x8_t bfrag[bf ? KS : 1];
+    if constexpr (bf) {
+      if (residual && tid < kSub * kWave)
+        load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), mine ? prev : -1, bfrag);
+    }
     // residual tile sums; fall back to p when the residual has no mass
-    const float* fc = ws.fchunk + (size_t)b * nT;
-    const float* pc = ws.pchunk + (size_t)b * nT;
-    const int per = (nT + blockDim.x - 1) / blockDim.x;
-    const int c0 = min(nT, tid * per), c1 = min(nT, c0 + per);
     double local = 0.0;
-    for (int cc = c0; cc < c1; ++cc) local += (double)fc[cc];
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i)
+      if (c0 + i < c1) local += (double)fcv[i];
     double start, end;
     double S = block_scan_interval(local, red, &start, &end);
     bool use_p = false;
@@ -692,11 +736,13 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
       use_p = true;
       if (tid == 0) flag(status, DSPARK_DEV_DEGENERATE);
       local = 0.0;
-      for (int cc = c0; cc < c1; ++cc) local += (double)pc[cc];
+#pragma unroll
+      for (int i = 0; i < kFinPer; ++i) {
+        fcv[i] = c0 + i < c1 ? pc[c0 + i] : 0.f;
+        if (c0 + i < c1) local += (double)fcv[i];
+      }
       S = block_scan_interval(local, red, &start, &end);
     }
-    const float* cs = use_p ? pc : fc;
-    const double u = (double)uniforms[((size_t)b * (gamma + 1) + gamma) * 2 + 0];
     const double tgt = u * S;
     const bool finite = S > 0.0 && isfinite(S);
     const int last_pos = block_max_int(local > 0.0 ? tid : -1, red);
@@ -706,11 +752,15 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
         ((start <= tgt && tgt < end) || (tid == last_pos && tgt >= end))) {
       double run = start, before = start, lastb = start;
       int found = -1, lastc = -1;
-      for (int cc = c0; cc < c1; ++cc) {
-        const double sc = (double)cs[cc];
-        if (sc > 0.0) { lastc = cc; lastb = run; }
-        if (sc > 0.0 && tgt < run + sc) { found = cc; before = run; break; }
-        run += sc;
+#pragma unroll
+      for (int i = 0; i < kFinPer; ++i) {   // the thread's chunks, in order
+        const int cc = c0 + i;
+        const double sc = (double)fcv[i];
+        if (cc < c1 && found < 0) {
+          if (sc > 0.0) { lastc = cc; lastb = run; }
+          if (sc > 0.0 && tgt < run + sc) { found = cc; before = run; }
+          run += sc;
+        }
       }
       if (found < 0) { found = lastc; before = lastb; }
       s_tile = found;
@@ -727,15 +777,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
       // and 1 take sub-tiles 0 and 1 (A gathered from the tile's raw W2
       // rows), fp32: wave 0 takes both
       const int v0 = vt * kTileV;
-      const int mrow = b % kTileM;
-      const int lane = tid & 63, c = lane & 31, h = lane >> 5;
       const int tw = tid >> 6;   // bf16: the sub-tile of waves 0 and 1
-      const bool mine = tid < (bf ? kSub : 1) * kWave && c == mrow;
-      const int prev = !residual ? -1
-                       : ws.emb_rows ? b * gamma + j
-                                     : clamp_token(j == 0 ? anchor[b]
-                                                          : tokens[(size_t)b * gamma + j - 1],
-                                                   V, nullptr);
       URow<T> tr, ur;
       load_urow<T>(tr, target + sk * V, v0, V, mine, target);
       load_urow<T>(ur, U + ((size_t)b * gamma + slot) * V, v0, V, mine && residual, U);
@@ -744,9 +786,6 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
       if (residual) {
         if constexpr (bf) {
           dma_tile_raw(reinterpret_cast<const uint16_t*>(W2), V, v0, rank, w2s);
-          bf16x8_t bfrag[KS];
-          if (tid < kSub * kWave)
-            load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), mine ? prev : -1, bfrag);
           __builtin_amdgcn_s_waitcnt(0);
           __syncthreads();
           auto bf_ = [&](int ks) { return bfrag[ks]; };
@@ -761,10 +800,6 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
         }
       }
       if (mine) {
-        const float it = 1.f / Tb;
-        const float M = ws.rM[sk], LZ = ws.rLZ[sk];
-        const float mq = residual ? row_max[(size_t)b * gamma + slot] : 0.f;
-        const float lzq = residual ? row_logZ[(size_t)b * gamma + slot] : 0.f;
         const int rem = V - (v0 + 16 * h);
 #pragma unroll
         for (int t = 0; t < kSub; ++t) {
@@ -783,18 +818,22 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(
         }
       }
       __syncthreads();
-      if (tid == 0) {
+      // the entry: the first with positive weight whose running sum passes
+      // the target (else the last positive one), one entry per lane of
+      // wave 0 with the running sums as a wave scan
+      if (tid < kWave) {
         const double rr = tgt - s_before;
-        double run = 0.0;
-        int pick = -1, lastp = -1;
-        for (int i = 0; i < kTileV; ++i) {
-          const double e = (double)se[i];
-          if (e > 0.0) lastp = i;
-          run += e;
-          if (e > 0.0 && rr < run) { pick = i; break; }
+        const double e = (double)se[tid];
+        double run = e;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const double nb = __shfl_up(run, o, kWave);
+          if (tid >= o) run += nb;
         }
-        if (pick < 0) pick = lastp < 0 ? 0 : lastp;
-        s_pick = v0 + pick;
+        const unsigned long long hit = __ballot(e > 0.0 && rr < run);
+        const unsigned long long pos = __ballot(e > 0.0);
+        const int pick = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
+        if (tid == 0) s_pick = v0 + pick;
       }
       __syncthreads();
       y = s_pick;
