@@ -124,12 +124,12 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def counter_traffic(kernel, cfg):
+def counter_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the recorded rocprofv3 counters
-    (profiles/<kernel>-config<cfg>.counters.txt), scaled by the plain-copy
-    calibration recorded with them; None when absent or when the kernel
-    sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}-config{cfg}.counters.txt")
+    (profiles/<kernel>-<workload>.counters.txt, the workload by name), scaled
+    by the plain-copy calibration recorded with them; None when absent or
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}-{workload}.counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -410,7 +410,7 @@ def main():
     stats_bytes = draft_kernel_bytes(wl, draft_kernel, with_conf=conf_fused)
     avg_s = kern_ms[draft_kernel] / 1e3
     achieved = stats_bytes / avg_s / 1e9
-    traffic = counter_traffic(draft_kernel, cfg)
+    traffic = counter_traffic(draft_kernel, spec.name)
     kb_read = kernel_bytes_read(wl, ell, n_acc)
     bytes_step = algorithmic_bytes(wl, ell, n_acc)
 

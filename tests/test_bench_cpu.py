@@ -56,12 +56,12 @@ def test_tv_label_bytes():
 
 
 def test_counter_traffic_follows_the_source_hash(monkeypatch, tmp_path):
-    rec = os.path.join(bench.ROOT, "profiles", "pdraft_kernel-config3.counters.txt")
+    rec = os.path.join(bench.ROOT, "profiles", "pdraft_pipe_kernel-long-proposal-g15.counters.txt")
     kv = dict(line.strip().split("=", 1) for line in open(rec)
               if "=" in line and not line.startswith("#"))
     want = (float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
             + float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])) * 1024.0
-    got = bench.counter_traffic("pdraft_kernel", 3)
+    got = bench.counter_traffic("pdraft_pipe_kernel", "long-proposal-g15")
     if kv["source_sha256"] == bench.kernel_source_hash():
         assert got == want
     else:
@@ -70,11 +70,11 @@ def test_counter_traffic_follows_the_source_hash(monkeypatch, tmp_path):
     fake_root = tmp_path
     (fake_root / "profiles").mkdir()
     text = open(rec).read().replace(kv["source_sha256"], "0" * 64)
-    (fake_root / "profiles" / "pdraft_kernel-config3.counters.txt").write_text(text)
+    (fake_root / "profiles" / "pdraft_pipe_kernel-long-proposal-g15.counters.txt").write_text(text)
     monkeypatch.setattr(bench, "ROOT", str(fake_root))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "f" * 64)
-    assert bench.counter_traffic("pdraft_kernel", 3) is None
-    assert bench.counter_traffic("pdraft_kernel", 4) is None   # nothing recorded
+    assert bench.counter_traffic("pdraft_pipe_kernel", "long-proposal-g15") is None
+    assert bench.counter_traffic("pdraft_pipe_kernel", "high-concurrency") is None   # none recorded
 
 
 def test_kernel_bytes_per_launch():
