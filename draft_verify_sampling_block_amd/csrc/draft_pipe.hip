@@ -695,71 +695,91 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
   const bool gathers = wave < kGw;
 
   // Window j's group words, written by the last wave to finish its tasks
-  // (lanes 0..31 = the window's requests): the LDS tiles' tile words (their
+  // (column c = the window's request c): the LDS tiles' tile words (their
   // two halves combined here) and per request the group's max and exp-sum
   // relative to it (the argmax for a greedy request), tagged with the
   // position's parity (bit 63).  The register tiles' words went out from
-  // their tasks.
+  // their tasks.  The two half-waves split the tiles: half h takes register
+  // tiles 4h .. 4h + 3 and LDS tile 8 + h, and the halves' maxima, sums and
+  // argmax candidates are exchanged once.
+  static_assert(kPpRegTiles == 8 && kPpLdsTiles == 2, "the split assumes 8 + 2 tiles");
   auto finish_window = [&](int j) __attribute__((always_inline)) {
     const int pb = j & 1;
     const int r0 = (j % nch) * kTileM;
     const uint64_t tag = (uint64_t)(((j / nch) + 1) & 1) << 63;   // parity of the position
-    const bool act = lane < kTileM && r0 + lane < B;
-    const int bq = r0 + lane;
-    const float it = act ? s_it[j % 3][lane] : 0.f;
+    const bool act = r0 + c < B;
+    const int bq = r0 + c;
+    const float it = act ? s_it[j % 3][c] : 0.f;
     const bool greedy = !(it > 0.f);
     const float ce = it * kLog2e;
-    // every slot's statistics read at once (unconditionally: slots past the
-    // group's tiles are masked afterwards), so the reads share one wait
-    float lmx[kPpSlots], lsm[kPpSlots];
-    int lag[kPpSlots];
+    // this half's slots, read at once (unconditionally: slots past the
+    // group's tiles are masked afterwards): register tiles 4h + i, then
+    // the two halves of LDS tile 8 + h
+    float lmx[6], lsm[6];
+    int lag[6];
 #pragma unroll
-    for (int s = 0; s < kPpSlots; ++s) {
-      lmx[s] = s_mx[pb][s][lane & 31];
-      lsm[s] = s_sum[pb][s][lane & 31];
-      lag[s] = s_arg[pb][s][lane & 31];
+    for (int i = 0; i < 6; ++i) {
+      const int sl = i < 4 ? 4 * h + i : kPpRegTiles + 2 * h + (i - 4);
+      lmx[i] = s_mx[pb][sl][c];
+      lsm[i] = s_sum[pb][sl][c];
+      lag[i] = s_arg[pb][sl][c];
     }
-    float tmx[kPpMaxTiles], tsm[kPpMaxTiles];
-    int targ[kPpMaxTiles];
-    float gmx = -INFINITY;
+    float tmx[5], tsm[5];
+    int targ[5];
 #pragma unroll
-    for (int s = 0; s < kPpMaxTiles; ++s) {
-      const bool in = act && s < tcount;
-      if (s < kPpRegTiles) {
-        tmx[s] = lmx[s];
-        tsm[s] = lsm[s];
-        targ[s] = lag[s];
-      } else {
-        const int s0 = kPpRegTiles + 2 * (s - kPpRegTiles);
-        const float m0 = lmx[s0], m1 = lmx[s0 + 1];
-        const float m = fmaxf(m0, m1);
-        tmx[s] = m;
-        targ[s] = (m0 == m) ? lag[s0] : lag[s0 + 1];
-        tsm[s] = greedy ? 0.f
-                        : lsm[s0] * __builtin_amdgcn_exp2f((m0 - m) * ce) +
-                              lsm[s0 + 1] * __builtin_amdgcn_exp2f((m1 - m) * ce);
-        if (in && !greedy)
-          st_dev(a.tw + (size_t)(tbase + s) * B + bq,
-                 (uint64_t)((pack_ms(m, tsm[s]) & ~(1ull << 63)) | tag));
-      }
-      if (!in) tmx[s] = -INFINITY;
-      gmx = fmaxf(gmx, tmx[s]);
+    for (int i = 0; i < 4; ++i) {
+      tmx[i] = lmx[i];
+      tsm[i] = lsm[i];
+      targ[i] = lag[i];
     }
+    {
+      const int tl = kPpRegTiles + h;   // this half's LDS tile
+      const float m0 = lmx[4], m1 = lmx[5];
+      const float m = fmaxf(m0, m1);
+      tmx[4] = m;
+      targ[4] = (m0 == m) ? lag[4] : lag[5];
+      tsm[4] = greedy ? 0.f
+                      : lsm[4] * __builtin_amdgcn_exp2f((m0 - m) * ce) +
+                            lsm[5] * __builtin_amdgcn_exp2f((m1 - m) * ce);
+      if (act && tl < tcount && !greedy)
+        st_dev(a.tw + (size_t)(tbase + tl) * B + bq,
+               (uint64_t)((pack_ms(m, tsm[4]) & ~(1ull << 63)) | tag));
+    }
+    // tile index (within the group) of entry i of this half
+    auto tidx = [&](int i) { return i < 4 ? 4 * h + i : kPpRegTiles + h; };
+    float hmx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      if (!(act && tidx(i) < tcount)) tmx[i] = -INFINITY;
+      hmx = fmaxf(hmx, tmx[i]);
+    }
+    float mlo, mhi;
+    half_pair(hmx, mlo, mhi);
+    const float gmx = fmaxf(mlo, mhi);
     uint32_t pl = 0;
     if (greedy) {
-      int ga = 0x7fffffff;
+      // the lowest tile index attaining the max, then its argmax
+      int bi = 0x7fffffff, ba = 0x7fffffff;
 #pragma unroll
-      for (int s = kPpMaxTiles - 1; s >= 0; --s)
-        if (s < tcount && tmx[s] == gmx) ga = targ[s];
-      pl = (uint32_t)ga;
+      for (int i = 4; i >= 0; --i)
+        if (tidx(i) < tcount && tmx[i] == gmx && tidx(i) < bi) {
+          bi = tidx(i);
+          ba = targ[i];
+        }
+      int bilo, bihi, balo, bahi;
+      half_pair(bi, bilo, bihi);
+      half_pair(ba, balo, bahi);
+      pl = (uint32_t)(bilo <= bihi ? balo : bahi);
     } else {
-      float gs = 0.f;
+      float hs = 0.f;
 #pragma unroll
-      for (int s = 0; s < kPpMaxTiles; ++s)
-        if (s < tcount) gs += tsm[s] * __builtin_amdgcn_exp2f((tmx[s] - gmx) * ce);
-      pl = __float_as_uint(gs);
+      for (int i = 0; i < 5; ++i)
+        if (tidx(i) < tcount) hs += tsm[i] * __builtin_amdgcn_exp2f((tmx[i] - gmx) * ce);
+      float slo, shi;
+      half_pair(hs, slo, shi);
+      pl = __float_as_uint(slo + shi);
     }
-    if (act)
+    if (act && h == 0)
       st_dev(a.gw + (size_t)bq * Pt + p,
              (uint64_t)(((uint64_t)__float_as_uint(gmx) | ((uint64_t)(pl & 0x7FFFFFFFu) << 32)) | tag));
   };
