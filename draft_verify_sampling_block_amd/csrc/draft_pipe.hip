@@ -108,14 +108,68 @@ __host__ __device__ inline int pp_tbase(int q, int nT, int Pt) {
   return q * (nT / Pt) + (q < nT % Pt ? q : nT % Pt);
 }
 
+// Cross-lane steps of the draw, none through the LDS crossbar: DPP moves
+// within 16-lane rows, the row broadcasts and the whole-wave shift, the
+// row-pair and half-wave swaps, and reads of one lane into a scalar.
+// DPP control words: quad_perm p0 | p1 << 2 | p2 << 4 | p3 << 6, row_shr:n
+// 0x110 + n, row_ror:n 0x120 + n, wave_shr:1 0x138, row_bcast:15 0x142,
+// row_bcast:31 0x143.
+template <int Ctrl, int RowMask = 0xf>
+__device__ inline uint32_t dpp_u(uint32_t x) {   // lanes without a source read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, Ctrl, RowMask, 0xf, true);
+}
+template <int Ctrl, int RowMask = 0xf>
+__device__ inline double dpp_d(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t lo = dpp_u<Ctrl, RowMask>((uint32_t)b);
+  const uint64_t hi = dpp_u<Ctrl, RowMask>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+template <int Ctrl>
+__device__ inline float dpp_f(float x) {
+  return __uint_as_float(dpp_u<Ctrl>(__float_as_uint(x)));
+}
+// lane l's value (l wave-uniform)
+__device__ inline int lane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ inline float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ inline double lane_d(double x, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+// values of the even (lo) and odd (hi) 16-lane row of this lane's row pair
+__device__ inline void row_pair(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+// inclusive prefix sum over the wave's 64 lanes (within each row by
+// doubling steps, then the rows' totals carried into the rows after them)
 __device__ inline double wave_incl_scan(double v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double n = __shfl_up(v, o, kWave);
-    if (lane >= o) v += n;
-  }
+  v += dpp_d<0x111>(v);
+  v += dpp_d<0x112>(v);
+  v += dpp_d<0x114>(v);
+  v += dpp_d<0x118>(v);
+  v += dpp_d<0x142, 0xa>(v);
+  v += dpp_d<0x143, 0xc>(v);
   return v;
+}
+// the preceding lane's value (0 in lane 0)
+__device__ inline double wave_prev(double v) { return dpp_d<0x138>(v); }
+__device__ inline float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x128>(v));
+  float lo, hi;
+  row_pair(v, lo, hi);
+  v = fmaxf(lo, hi);
+  half_pair(v, lo, hi);
+  return fmaxf(lo, hi);
 }
 
 // Bounded wait of one wave: true once done() holds on every lane; false
@@ -196,7 +250,7 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
   // stored for position k - 1 (read back by the same lane)
   int pv = 0;
   if (lane == 0) pv = k == 0 ? a.anchor[b] : (int)(ld_dev(a.tok_flag + b) & 0xFFFFFFu);
-  const int prev = clamp_token(__shfl(pv, 0, kWave), V, nullptr);
+  const int prev = clamp_token(lane_i(pv, 0), V, nullptr);
   // the previous token's W1 row into this wave's LDS (needed only by the
   // crossing-tile recompute; requested first so it is in by then)
   if (lane < rank / 8)
@@ -276,7 +330,7 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
     gm[i] = (4 * lane + i < Pt) ? __uint_as_float((uint32_t)r[i]) : -INFINITY;
     mloc = fmaxf(mloc, gm[i]);
   }
-  const float M = wave_max(mloc);
+  const float M = wave_max_dpp(mloc);
   auto payload = [&](int i) { return (uint32_t)(r[i] >> 32) & 0x7FFFFFFFu; };
 
   if (greedy) {
@@ -293,7 +347,7 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (i == fi) pl = payload(i);
-      tok = (int)__shfl((int)pl, src, kWave);
+      tok = lane_i((int)pl, src);
     }
     if (!hit || !(M == M) || tok < 0 || tok >= V) {
       if (lane == 0) flag(a.status, DSPARK_DEV_NONFINITE);
@@ -317,9 +371,8 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
     lsum += gmass[i];
   }
   const double incl = wave_incl_scan(lsum);
-  double excl = __shfl_up(incl, 1, kWave);
-  if (lane == 0) excl = 0.0;
-  const double Z = __shfl(incl, kWave - 1, kWave);
+  const double excl = wave_prev(incl);
+  const double Z = lane_d(incl, kWave - 1);
   // u * Z can round up to Z: the target is kept below Z, so exactly one
   // lane's interval [excl, incl) holds it (consecutive intervals share ends)
   double target = u * Z;
@@ -356,8 +409,8 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
     return;
   }
   const int gsrc = __builtin_ctzll(gh);
-  const int gq = 4 * gsrc + __shfl(fg, gsrc, kWave);
-  const double gbefore = __shfl(before, gsrc, kWave);
+  const int gq = 4 * gsrc + lane_i(fg, gsrc);
+  const double gbefore = lane_d(before, gsrc);
 
   // that group's tile words: lane t holds tile tb + t
   const int tb = pp_tbase(gq, nT, Pt), tc = pp_tcount(gq, nT, Pt);
@@ -379,8 +432,7 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
             (double)__builtin_amdgcn_exp2f((tm - M) * ce);
   }
   const double tincl = wave_incl_scan(tmass);
-  double texcl = __shfl_up(tincl, 1, kWave);
-  if (lane == 0) texcl = 0.0;
+  const double texcl = wave_prev(tincl);
   const double rt = target - gbefore;
   const unsigned long long th = __ballot(tmass > 0.0 && rt < tincl);
   const unsigned long long tpos = __ballot(tmass > 0.0);
@@ -391,8 +443,8 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
   }
   const int tl = th ? __builtin_ctzll(th) : 63 - __builtin_clzll(tpos);
   const int vt = tb + tl;
-  const float mvt = __shfl(tm, tl, kWave);
-  const double tbefore = gbefore + __shfl(texcl, tl, kWave);
+  const float mvt = lane_f(tm, tl);
+  const double tbefore = gbefore + lane_d(texcl, tl);
   const double tscale = (double)__builtin_amdgcn_exp2f((mvt - M) * ce);
   const float mc = mvt * ce;
 
@@ -430,10 +482,21 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
       acc[e] = __builtin_fmaf(ak, w2, acc[e]);
     }
   }
+  // the partial sums of lanes g8, g8 + 8, ..., g8 + 56 added in pairs:
+  // across half rows (row_ror:8), across the rows of a pair, across halves
 #pragma unroll
-  for (int o = 8; o < kWave; o <<= 1) {
+  for (int e = 0; e < 8; ++e) acc[e] += dpp_f<0x128>(acc[e]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+  for (int e = 0; e < 8; ++e) {
+    float lo, hi;
+    row_pair(acc[e], lo, hi);
+    acc[e] = lo + hi;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float lo, hi;
+    half_pair(acc[e], lo, hi);
+    acc[e] = lo + hi;
   }
   float* es = reinterpret_cast<float*>(wl + 512);
   if (rho == 0) {
@@ -452,7 +515,7 @@ __device__ void pp_draw(const PpArgs& a, int b, int k, char* wl) {
   const unsigned long long hit = __ballot(ej > 0.0 && rr < eincl);
   const unsigned long long pos = __ballot(ej > 0.0);
   const int pick = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
-  const double epick = __shfl(ej, pick, kWave);
+  const double epick = lane_d(ej, pick);
   emit(v0 + pick, (float)(epick * tscale / Z), ms, __logf((float)Z));
 }
 
@@ -643,18 +706,16 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
   };
 
   // Gather of window jn's rows into `dst` by waves 0..3, eight rows each
-  // (previous tokens `tok` in lanes 0..7; lanes past the window's requests
-  // hold token 0 and inverse temperature 0).  Waves 4..7, which run the LDS
+  // (previous tokens `tok` and temperatures `tv` in lanes 0..7, the latter
+  // loaded ahead by temp_issue; lanes past the window's requests hold
+  // token 0 and inverse temperature 0).  Waves 4..7, which run the LDS
   // tiles' half tasks, issue no row DMA: a wave with a DMA in flight waits
   // for it before its next LDS read.  Completion: the caller's wait.
   constexpr int kGw = 4, kRpw = kTileM / kGw;   // gathering waves, rows each
-  auto gather = [&](int jn, char* dst, int tok) __attribute__((always_inline)) {
+  auto gather = [&](int jn, char* dst, int tok, float tv) __attribute__((always_inline)) {
     const int nrows = min(kTileM, B - (jn % nch) * kTileM);
     const int row = wave * kRpw + lane;
-    if (lane < kRpw) {
-      const int bq = (jn % nch) * kTileM + row;
-      s_it[jn % 3][row] = row < nrows ? inv_temp(a.temperature[bq]) : 0.f;
-    }
+    if (lane < kRpw) s_it[jn % 3][row] = row < nrows ? inv_temp(tv) : 0.f;
     char* wd = dst + (size_t)(wave * kRpw) * nc * 16;
     constexpr int nslots = kRpw * nc;
 #pragma unroll
@@ -666,6 +727,13 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
         __builtin_amdgcn_global_load_lds(a.W1 + (size_t)tk * rank + (q < nq ? q : 0) * 8,
                                          wd + g * 1024, 16, 0, 0);
     }
+  };
+  // Temperatures of this wave's rows of window jn (lanes 0..7), loaded well
+  // before the gather that takes them.
+  auto temp_issue = [&](int jn) __attribute__((always_inline)) {
+    const int row = wave * kRpw + lane;
+    const int bq = (jn % nch) * kTileM + row;
+    return (lane < kRpw && bq < B) ? a.temperature[bq] : 0.f;
   };
   // Previous tokens of this wave's rows of window jn (lanes 0..7): issue
   // one flag load per lane, then (later, so the load is in flight meanwhile)
@@ -883,19 +951,20 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
     if constexpr (gat) {
       int tok = 0;
       bool staged = !more || nch == 1;
-      // the flag loads stay in flight during the register task
+      // the flag and temperature loads stay in flight during the register task
       const uint32_t pv = staged ? 0u : poll_issue(j + 1);
+      const float tv = more ? temp_issue(j + 1) : 0.f;
       if (hasreg) run_task(pbc, j, true);
       if (ntask > 0) task_done(j);   // before the DMA: LDS accesses after it wait for it
       if (!staged) {
         if (!poll_check(j + 1, pv, tok)) wait_tokens(j + 1, tok);
-        gather(j + 1, nxt, tok);
+        gather(j + 1, nxt, tok, tv);
       }
       __builtin_amdgcn_s_waitcnt(kWaitAll);   // this wave's rows are in
       __syncthreads();
       if (nch == 1 && more) {
         wait_tokens(j + 1, tok);
-        gather(j + 1, nxt, tok);
+        gather(j + 1, nxt, tok, tv);
         __builtin_amdgcn_s_waitcnt(kWaitAll);
         __syncthreads();
       }
@@ -915,8 +984,9 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
     constexpr bool gat = decltype(gc)::value;
     if constexpr (gat) {
       int tok = 0;
+      const float tv = temp_issue(0);
       poll_check(0, poll_issue(0), tok);
-      gather(0, ldsR0, tok);
+      gather(0, ldsR0, tok, tv);
     }
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
