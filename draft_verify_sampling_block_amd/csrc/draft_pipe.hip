@@ -718,13 +718,17 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
     if (lane < kRpw) s_it[jn % 3][row] = row < nrows ? inv_temp(tv) : 0.f;
     char* wd = dst + (size_t)(wave * kRpw) * nc * 16;
     constexpr int nslots = kRpw * nc;
+    constexpr int ng = (nslots + 63) / 64;
+    // every slot's token requested before the first is used (one wait)
+    int tk[ng];
 #pragma unroll
-    for (int g = 0; g * 64 < nslots; ++g) {
+    for (int g = 0; g < ng; ++g) tk[g] = __shfl(tok, min((g * 64 + lane) / nc, kRpw - 1), kWave);
+#pragma unroll
+    for (int g = 0; g < ng; ++g) {
       const int s = g * 64 + lane;
       const int rl = s / nc, q = s - rl * nc;
-      const int tk = __shfl(tok, min(rl, kRpw - 1), kWave);
       if (s < nslots)
-        __builtin_amdgcn_global_load_lds(a.W1 + (size_t)tk * rank + (q < nq ? q : 0) * 8,
+        __builtin_amdgcn_global_load_lds(a.W1 + (size_t)tk[g] * rank + (q < nq ? q : 0) * 8,
                                          wd + g * 1024, 16, 0, 0);
     }
   };
@@ -864,7 +868,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
     if (lane == 0)
       prev = __hip_atomic_fetch_add(&s_done[j & 1], 1, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_WORKGROUP);
-    prev = __shfl(prev, 0, kWave);
+    prev = lane_i(prev, 0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (prev == nwt - 1) {
       if (lane == 0)
