@@ -685,13 +685,20 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
   // lane (c, h) gets the entries 32 t + 16 h .. + 15 of request c for t = 0, 1
   // (a half task: its sub-tile's entries 16 h .. + 15 in part 0).
   char* rs = ldsX + wave * 4096;
-  auto restage = [&](const URow<uint16_t>& in, bool reg, URow<uint16_t>& out) __attribute__((always_inline)) {
+  // `vb` is the task's first vocabulary entry (the tile, or a half task's
+  // sub-tile): a lane whose 8-entry chunk lies at or past V writes -inf
+  // there, so the accumulators start at -inf past the vocabulary with no
+  // per-entry test (V % 8 == 0: a chunk is wholly inside or outside).
+  auto restage = [&](const URow<uint16_t>& in, bool reg, int vb, URow<uint16_t>& out) __attribute__((always_inline)) {
+    const int q = reg ? (lane & 7) : (lane & 3);
+    const bool past = vb + 8 * q >= V;
+    const u32x4_t ninf = {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};   // bf16 -inf
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (reg || i < 2) {
         const int r = reg ? 8 * i + (lane >> 3) : 16 * i + (lane >> 2);
-        const int q = reg ? (lane & 7) : (lane & 3);
-        *reinterpret_cast<u32x4_t*>(rs + r * 128 + 16 * (q ^ (r & 7))) = in.w[i >> 1][i & 1];
+        *reinterpret_cast<u32x4_t*>(rs + r * 128 + 16 * (q ^ (r & 7))) =
+            past ? ninf : in.w[i >> 1][i & 1];
       }
     }
 #pragma unroll
@@ -890,17 +897,13 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
       const int tile = tbase + wave;
       const int v0 = tile * kTileV;
       URow<uint16_t> u;
-      restage(ring.u, true, u);
+      restage(ring.u, true, v0, u);
       fetch_next(ring);
       f32x16_t acc[kSub];
-      if (v0 + kTileV <= V) {
 #pragma unroll
-        for (int t = 0; t < kSub; ++t) {
+      for (int t = 0; t < kSub; ++t) {
 #pragma unroll
-          for (int jj = 0; jj < 16; ++jj) acc[t][jj] = urow_at(u, t, jj);
-        }
-      } else {
-        init_acc<uint16_t>(u, V - (v0 + 16 * h), acc);
+        for (int jj = 0; jj < 16; ++jj) acc[t][jj] = urow_at(u, t, jj);
       }
       bias_tile_regA<KS>(bfrag, wreg, acc);
       const TileStat st = tile_reduce(acc, tile, it, any_greedy);
@@ -917,13 +920,12 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
       const int li = hidx >> 1, t = hidx & 1;
       const int tile = tbase + kPpRegTiles + li;
       const int v0 = tile * kTileV;
-      const int rem = V - (v0 + 32 * t + 16 * h);
       URow<uint16_t> u;
-      restage(ring.u, false, u);
+      restage(ring.u, false, v0 + 32 * t, u);
       fetch_next(ring);
       f32x16_t acc;   // the sub-tile's entries sit in part 0
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) acc[jj] = (jj < rem) ? urow_at(u, 0, jj) : -INFINITY;
+      for (int jj = 0; jj < 16; ++jj) acc[jj] = urow_at(u, 0, jj);
       bias_subtile_ldsA<KS>(bfrag, ldsL + li * kLdsTileBytes, t, acc);
       const TileStat st = half_reduce(acc, tile, t, it, any_greedy);
       if (h == 0) {
