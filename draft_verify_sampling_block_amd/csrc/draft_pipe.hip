@@ -632,7 +632,19 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
 #pragma unroll
     for (int j = 0; j < kPpLdsTiles; ++j) store_slot(kPpRegTiles + j, lblk[j], img(j));
   }
-  pp_wait_all(a, E);   // every work-group has zeroed its words
+  // the statistics slots this group has no task for hold empty statistics
+  // (both parities, written once; tasks write only their own slots)
+  for (int e = (int)threadIdx.x; e < 2 * kPpSlots * kTileM; e += kPpWaves * 64) {
+    const int sl = (e / kTileM) % kPpSlots, pe = e / (kPpSlots * kTileM), cc = e % kTileM;
+    const int ti = sl < kPpRegTiles ? sl : kPpRegTiles + ((sl - kPpRegTiles) >> 1);
+    if (ti >= tcount) {
+      s_mx[pe][sl][cc] = -INFINITY;
+      s_sum[pe][sl][cc] = 0.f;
+      s_arg[pe][sl][cc] = 0x7fffffff;
+    }
+  }
+  pp_wait_all(a, E);   // every work-group has zeroed its words (and the barrier
+                       // makes the empty statistics visible)
   const int nL = (tcount > kPpRegTiles ? 1 : 0) + (tcount > kPpRegTiles + 1 ? 1 : 0);
   const bool hasreg = wave < tcount;
   // half-tasks of a window: 2 per LDS tile; half i goes to wave i + 4
@@ -791,9 +803,9 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
     const float it = act ? s_it[j % 3][c] : 0.f;
     const bool greedy = !(it > 0.f);
     const float ce = it * kLog2e;
-    // this half's slots, read at once (unconditionally: slots past the
-    // group's tiles are masked afterwards): register tiles 4h + i, then
-    // the two halves of LDS tile 8 + h
+    // this half's slots, read at once: register tiles 4h + i, then the two
+    // halves of LDS tile 8 + h (a slot the group has no tile for holds the
+    // empty statistics written before the first window: max -inf, sum 0)
     float lmx[6], lsm[6];
     int lag[6];
 #pragma unroll
@@ -817,9 +829,10 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
       const float m = fmaxf(m0, m1);
       tmx[4] = m;
       targ[4] = (m0 == m) ? lag[4] : lag[5];
-      tsm[4] = greedy ? 0.f
-                      : lsm[4] * __builtin_amdgcn_exp2f((m0 - m) * ce) +
-                            lsm[5] * __builtin_amdgcn_exp2f((m1 - m) * ce);
+      tsm[4] = (greedy || !(m > -INFINITY))
+                   ? 0.f
+                   : lsm[4] * __builtin_amdgcn_exp2f((m0 - m) * ce) +
+                         lsm[5] * __builtin_amdgcn_exp2f((m1 - m) * ce);
       if (act && tl < tcount && !greedy)
         st_dev(a.tw + (size_t)(tbase + tl) * B + bq,
                (uint64_t)((pack_ms(m, tsm[4]) & ~(1ull << 63)) | tag));
@@ -828,10 +841,8 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
     auto tidx = [&](int i) { return i < 4 ? 4 * h + i : kPpRegTiles + h; };
     float hmx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      if (!(act && tidx(i) < tcount)) tmx[i] = -INFINITY;
-      hmx = fmaxf(hmx, tmx[i]);
-    }
+    for (int i = 0; i < 5; ++i) hmx = fmaxf(hmx, tmx[i]);
+    if (!act) hmx = -INFINITY;
     float mlo, mhi;
     half_pair(hmx, mlo, mhi);
     const float gmx = fmaxf(mlo, mhi);
@@ -841,7 +852,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
       int bi = 0x7fffffff, ba = 0x7fffffff;
 #pragma unroll
       for (int i = 4; i >= 0; --i)
-        if (tidx(i) < tcount && tmx[i] == gmx && tidx(i) < bi) {
+        if (tmx[i] == gmx && tidx(i) < bi) {
           bi = tidx(i);
           ba = targ[i];
         }
@@ -853,7 +864,7 @@ __global__ __launch_bounds__(kPpWaves * 64, 1) void pdraft_pipe_kernel(PpArgs a)
       float hs = 0.f;
 #pragma unroll
       for (int i = 0; i < 5; ++i)
-        if (tidx(i) < tcount) hs += tsm[i] * __builtin_amdgcn_exp2f((tmx[i] - gmx) * ce);
+        hs += tsm[i] * __builtin_amdgcn_exp2f((tmx[i] - gmx) * ce);
       float slo, shi;
       half_pair(hs, slo, shi);
       pl = __float_as_uint(slo + shi);
