@@ -10,7 +10,7 @@
 //                         k <= ell[b]: target-row max / argmax / log-sum-exp,
 //                         p(x_k), ratio and the accept flag; the first
 //                         rejected slot is read off the flags afterwards.
-//   verify_tile_stats     (bf16, B <= 128) or verify_init + verify_plan +
+//   verify_tile_stats     (bf16, B <= 128) or verify_plan +
 //   / verify_final_stats  verify_final_stats: vocabulary-parallel tiles (as
 //                         in drafting): per-chunk sums of the residual
 //                         max(0, p_j - q_j) (q_j recomputed bit-identically
@@ -90,10 +90,6 @@ __device__ inline int first_reject(const VerifyWs& ws, int b, int gamma, int L) 
 
 }  // namespace
 
-__global__ void verify_init_kernel(int32_t* any_res) {
-  if (threadIdx.x == 0) *any_res = 0;
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void verify_rows_kernel(
     int B, int gamma, int V, const T* __restrict__ target, const int32_t* __restrict__ tokens,
@@ -103,6 +99,9 @@ __global__ __launch_bounds__(256) void verify_rows_kernel(
   __shared__ double red[8];
   const int k = blockIdx.x / B, b = blockIdx.x % B;
   const int tid = threadIdx.x;
+  // the residual flag starts clear; verify_plan_kernel, which runs after
+  // this launch, raises it
+  if (blockIdx.x == 0 && tid == 0) *ws.any_res = 0;
   const int L = clamp_ell(ell, b, gamma, tid == 0 ? status : nullptr);
   if (k > L) return;  // uniform: every thread reads the same ell[b]
 
@@ -892,10 +891,6 @@ static hipError_t verify_impl(int B, int gamma, int V, int rank, const T* target
     }
   }
   if (!tiles) {
-    {
-      TraceScope t0("verify_init_kernel", stream);
-      verify_init_kernel<<<dim3(1), dim3(64), 0, stream>>>(ws.any_res);
-    }
     {
       TraceScope tp("verify_plan_kernel", stream);
       verify_plan_kernel<<<dim3((B + 255) / 256), dim3(256), 0, stream>>>(B, gamma, V, ell,
