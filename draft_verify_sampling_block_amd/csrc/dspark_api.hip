@@ -211,10 +211,10 @@ size_t dspark_schedule_workspace(int R, int gamma) {
   return dspark::schedule_workspace_bytes(R, gamma);
 }
 
-namespace {
-// checks shared by the scheduler entry points (all but the workspace)
-int check_schedule_args(const char* fn, int R, int gamma, const float* conf, int32_t* ell,
-                        int32_t* order, double* stats, int32_t* status) {
+// checks shared by the scheduler entry points (all but the workspace);
+// static: file-local despite the C linkage of this block
+static int check_schedule_args(const char* fn, int R, int gamma, const float* conf,
+                               int32_t* ell, int32_t* order, double* stats, int32_t* status) {
   if (R < 1) return fail(DSPARK_EINVAL, "%s: R=%d must be >= 1", fn, R);
   if (gamma < 1 || gamma > 64) return fail(DSPARK_EINVAL, "%s: gamma=%d outside [1,64]", fn, gamma);
   if ((long long)R * gamma > dspark::kScheduleMaxKeys)
@@ -223,9 +223,9 @@ int check_schedule_args(const char* fn, int R, int gamma, const float* conf, int
   REQUIRE_PTR(conf); REQUIRE_PTR(ell); OPT_PTR(order); OPT_PTR(stats); OPT_PTR(status);
   return DSPARK_OK;
 }
-int check_schedule(const char* fn, int R, int gamma, const float* conf, int32_t* ell,
-                   int32_t* order, double* stats, int32_t* status, void* workspace,
-                   size_t workspace_bytes) {
+static int check_schedule(const char* fn, int R, int gamma, const float* conf, int32_t* ell,
+                          int32_t* order, double* stats, int32_t* status, void* workspace,
+                          size_t workspace_bytes) {
   const int rc = check_schedule_args(fn, R, gamma, conf, ell, order, stats, status);
   if (rc) return rc;
   const size_t need = dspark::schedule_workspace_bytes(R, gamma);
@@ -235,7 +235,6 @@ int check_schedule(const char* fn, int R, int gamma, const float* conf, int32_t*
     return fail(DSPARK_EALIGN, "%s: workspace not 16-byte aligned", fn);
   return DSPARK_OK;
 }
-}  // namespace
 
 int dspark_schedule(int R, int gamma, const float* conf, const double* sps, int sps_len,
                     int32_t* ell, int32_t* order, double* stats, int32_t* status,
