@@ -28,6 +28,22 @@ def test_header_symbols_are_exported(lib):
     assert not missing, missing
 
 
+def test_no_undeclared_c_symbols_exported(lib):
+    # every unmangled function the library exports is one the header declares
+    # (helpers inside the extern "C" block must be file-local)
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", dv.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines()
+                if len(ln.split()) == 3 and ln.split()[1] == "T"}
+    c_names = {n for n in exported if not n.startswith("_Z")}
+    assert c_names, "no C symbols found"
+    assert c_names <= set(dv.header_names()), sorted(c_names - set(dv.header_names()))
+
+
 def test_status_strings_and_version(lib):
     assert lib.dspark_status_str(0) == b"DSPARK_OK"
     for code in (-1, -2, -3, -4, -5, -6):
