@@ -389,12 +389,46 @@ __global__ __launch_bounds__(256) void verify_final_stats_kernel(
       const bool live = rb < nRB;
       const int b = rb * kTileM + c;
       const FinalRow mine = pl.mine;
-      bf16x8_t bfrag[KS];
-      load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), mine.mode == 1 ? mine.prev : -1,
-                     bfrag);
+      // the block's W1 rows (previous tokens of residual requests) loaded as
+      // whole 128-byte segments, 8 rows per load (pass q, load j: row
+      // 8 j + lane / 8, piece 8 q + lane % 8 of the row's 2 KS pieces of 16
+      // bytes), then passed to the B-operand layout through the wave's LDS
+      // area like the target rows: lane (c, h) takes pieces 2 ks + h of row c
+      // (rank 32: rows of 64 bytes, loaded per lane as before)
+      constexpr int kW1 = KS >= 4 ? KS : 1;
+      const int tokc = mine.mode == 1 ? mine.prev : -1;
+      u32x4_t w1raw[kW1];
+      if constexpr (KS >= 4) {
+        const uint16_t* w1 = reinterpret_cast<const uint16_t*>(W1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tr = __shfl(tokc, 8 * j + lr, kWave);   // lane r < 32 holds request r
+          const uint16_t* row = w1 + (size_t)(tr >= 0 ? tr : 0) * (16 * KS) + 8 * lp;
+#pragma unroll
+          for (int q = 0; q < KS / 4; ++q)
+            w1raw[4 * q + j] = *reinterpret_cast<const u32x4_t*>(row + 64 * q);
+        }
+      }
       URow<uint16_t> tp, up;
       restage(ld, tp, up);
       fetch(ld, rb + 4, pl_next);
+      bf16x8_t bfrag[KS];
+      if constexpr (KS < 4) load_bfrag<KS>(reinterpret_cast<const uint16_t*>(W1), tokc, bfrag);
+#pragma unroll
+      for (int q = 0; q < KS / 4; ++q) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<u32x4_t*>(stg + (8 * j + lr) * 128 + 16 * (lp ^ lr)) = w1raw[4 * q + j];
+        asm volatile("" ::: "memory");   // the wave's LDS accesses stay in this order
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int pc = 2 * kk + h;
+          bfrag[4 * q + kk] = tokc >= 0
+              ? *reinterpret_cast<const bf16x8_t*>(stg + c * 128 + 16 * (pc ^ (c & 7)))
+              : bf16x8_t{};
+        }
+        asm volatile("" ::: "memory");
+      }
       pl = pl_next;
       plans(rb + 8, pl_next);
       if (rb == wave) {
