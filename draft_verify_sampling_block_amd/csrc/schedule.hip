@@ -191,7 +191,7 @@ __device__ inline void survival_keys(int R, int gamma, const float* __restrict__
 // together, and their counts are added by shuffles.  The order is total, so
 // the ranks are a permutation of [0, N).
 constexpr int kRankRuns = 16;
-constexpr int kRankSplit = 8;
+constexpr int kRankSplit = 16;
 constexpr int kRankThreads = 256;   // kRankThreads / kRankSplit candidates per group
 __global__ __launch_bounds__(kRankThreads) void schedule_rank_kernel(
     int R, int gamma, const float* __restrict__ conf, int32_t* __restrict__ rank_out) {
